@@ -1,0 +1,222 @@
+"""Benchmark: temporal decode ms/frame at B = 1, 32 blocks, context 3000, bf16 weights.
+
+One step = one decode frame through libpp (embedding sum, 32 blocks, final RMSNorm) with
+the ring full (3000 visible keys per head and layer). Weights are random (0.02 N(0,1),
+bfloat16), drawn on the device; the ring is filled with N(0,1) bfloat16 keys/values.
+Everything is resident in HBM before the timed region starts.
+
+Prints ONE JSON line (rank 0). Extra fields: frames_per_s, achieved_GBps (whole frame,
+algorithmic bytes), roofline (dominant kernel: the fused RMSNorm + W_in + SiLU-product
+GEMV, timed with HIP events on the launch stream), cpu_baseline (the oracle on a bounded
+sample), and optional depformer / prefill lines when those workloads are requested.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "temporal decode ms/frame (B=1, 32 blocks, ctx 3000) + achieved HBM GB/s"
+
+
+def frame_bytes(cfg, n_keys):
+    """Algorithmic HBM bytes of one decode frame: every weight once, every visible K/V
+    once, one new K/V slot, 17 embedding rows (bf16)."""
+    D, F, L, H, dh = cfg["d_model"], cfg["d_ff"], cfg["n_layers"], cfg["n_heads"], cfg["d_head"]
+    weights = L * (3 * D * D + D * D + 2 * F * D + D * F) * 2
+    kv_read = L * 2 * H * n_keys * dh * 2
+    kv_write = L * 2 * D * 2
+    emb = 17 * D * 2
+    return weights + kv_read + kv_write + emb
+
+
+def w_in_bytes(cfg):
+    """Algorithmic bytes of one fused RMSNorm + W_in + SiLU-product launch: the
+    [2F, D] bf16 matrix, the fp32 input vector and norm scale, the fp32 output."""
+    D, F = cfg["d_model"], cfg["d_ff"]
+    return 2 * F * D * 2 + D * 4 + D * 4 + F * 4
+
+
+def make_device_weights(cfg, seed):
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    D, F, L = cfg["d_model"], cfg["d_ff"], cfg["n_layers"]
+
+    def mat(r, c):
+        t = torch.empty((r, c), dtype=torch.bfloat16, device="cuda")
+        for i in range(0, r, 4096):
+            blk = torch.randn((min(4096, r - i), c), generator=g, device="cuda", dtype=torch.float32)
+            t[i:i + blk.shape[0]] = (blk * 0.02).to(torch.bfloat16)
+        return t
+
+    def norm(n):
+        return 1.0 + 0.02 * torch.randn(n, generator=g, device="cuda", dtype=torch.float32)
+
+    W = {"text_emb.weight": mat(cfg["text_vocab"], D)}
+    for i in range(cfg["n_audio"]):
+        W["emb.%d.weight" % i] = mat(cfg["audio_vocab"], D)
+    for l in range(L):
+        p = "transformer.layers.%d." % l
+        W[p + "self_attn.in_proj_weight"] = mat(3 * D, D)
+        W[p + "self_attn.out_proj.weight"] = mat(D, D)
+        W[p + "gating.linear_in.weight"] = mat(2 * F, D)
+        W[p + "gating.linear_out.weight"] = mat(D, F)
+        W[p + "norm1.alpha"] = norm(D)
+        W[p + "norm2.alpha"] = norm(D)
+    W["out_norm.alpha"] = norm(D)
+    return W
+
+
+def fill_ring(kv, cfg, seed):
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    C = cfg["context"]
+    per_layer = 2 * cfg["n_heads"] * C * cfg["d_head"]
+    buf = torch.empty(cfg["n_layers"] * per_layer, dtype=torch.bfloat16, device="cuda")
+    for l in range(cfg["n_layers"]):
+        buf[l * per_layer:(l + 1) * per_layer] = torch.randn(per_layer, generator=g, device="cuda").to(torch.bfloat16)
+    kv.load(buf, C)
+    del buf
+
+
+def cpu_baseline(cfg, seconds_budget=25.0):
+    """The oracle (fp64 NumPy) on a bounded sample: one decode frame through 2 of the 32
+    full-width blocks at 3000 visible keys, scaled x16 to a 32-block ms/frame."""
+    from oracle import temporal as O
+    from personaplex_temporal_transformer_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    n_l = 2
+    sc = synth.with_(cfg, n_layers=n_l)
+    W = synth.temporal_weights(sc, 8, "bf16", with_text_head=False)
+    frames = synth.cache_frames(sc, cfg["context"], 9)
+    ks = [frames[l, 0, 0].transpose(1, 0, 2) for l in range(n_l)]
+    vs = [frames[l, 1, 0].transpose(1, 0, 2) for l in range(n_l)]
+    ids = synth.stream_ids(sc, 1, 10)
+    times = []
+    t_end = time.time() + seconds_budget
+    while time.time() < t_end or not times:
+        cache = O.cache_from_blocks(ks, vs, np.arange(cfg["context"]), n_l)
+        t0 = time.time()
+        x = O.decode_step(O.embed(ids[0], W, sc), cfg["context"], cache, W, sc)
+        O.final(x, W, sc)
+        times.append(time.time() - t0)
+        if len(times) >= 3:
+            break
+    ms = min(times) * 1000.0 * cfg["n_layers"] / n_l
+    return {"value": ms, "unit": "ms/frame", "cores": int(cores), "kind": "oracle",
+            "sample": "one decode frame through 2 of 32 full-width blocks at 3000 visible keys "
+                      "(fp64 NumPy), best of %d, scaled x16 to 32 blocks" % len(times)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", type=int, default=-1, help="1: HIP graph replay, 0: direct launches, -1: auto")
+    ap.add_argument("--trace-layer", type=int, default=16)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from personaplex_temporal_transformer_amd import pp, synth
+
+    cfg = dict(synth.FULL_TEMPORAL)
+    t0 = time.time()
+    W = make_device_weights(cfg, 8)
+    model = pp.TemporalModel(cfg, W, "bf16")
+    kv = model.kv_alloc()
+    fill_ring(kv, cfg, 9)
+    torch.cuda.synchronize()
+    print("setup %.1f s" % (time.time() - t0), file=sys.stderr, flush=True)
+    ids = synth.stream_ids(cfg, args.warmup + 2 * args.steps + 4, 10)
+    h = torch.empty(cfg["d_model"], device="cuda")
+    C = cfg["context"]
+
+    def run(n, first, graph, trace_layer=-1):
+        model.set_graph(graph)
+        model.trace(trace_layer)
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(n):
+            model.decode_step(kv, ids[first + i], h)
+        end.record()
+        torch.cuda.synchronize()
+        tr = model.trace_read() if trace_layer >= 0 else (0, 0.0)
+        model.trace(-1)
+        return start.elapsed_time(end) / n, tr
+
+    # warm-up (also captures the graph), then pick the launch mode when asked to
+    run(args.warmup, 0, True)
+    mode = args.graph
+    probe = {}
+    if mode < 0:
+        for g in (True, False):
+            probe[g] = run(max(3, args.steps // 10), args.warmup, g)[0]
+        mode = 1 if probe[True] <= probe[False] else 0
+    # timed region: K frames; the dominant kernel is bracketed with HIP events on the
+    # launch stream in one layer per frame (direct launches when traced)
+    ms, (n_tr, us_win) = run(args.steps, args.warmup, bool(mode), args.trace_layer if mode == 0 else -1)
+    if mode == 1:
+        # graph replay cannot host per-launch events: time the kernel in a direct-launch pass
+        _, (n_tr, us_win) = run(args.steps, args.warmup, False, args.trace_layer)
+    pos, _ = kv.info()
+    fb = frame_bytes(cfg, C)
+    win_b = w_in_bytes(cfg)
+    achieved_win = win_b / (us_win * 1e-6) / 1e9 if us_win > 0 else None
+    out = {
+        "metric": METRIC,
+        "value": round(ms, 4),
+        "unit": "ms/frame",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (random-init bf16 weights 0.02*N(0,1), ring filled with N(0,1) bf16, random IDs)",
+        "config": {"workload": "full 32-block temporal decode, B=1, ring full at 3000 frames, "
+                               "positions 3000+ (keys wrap), d_model 4096, 32 heads x 128, d_ff 11264",
+                   "global_batch": 1, "seq_len": C, "parallelism": "none (1 GPU)",
+                   "launch": "hip graph" if mode == 1 else "direct"},
+        "frames_per_s": round(1000.0 / ms, 2),
+        "stream_tokens_per_s": round(17 * 1000.0 / ms, 1),
+        "achieved_GBps": round(fb / (ms * 1e-3) / 1e9, 1),
+        "frame_bytes": fb,
+        "frame_roofline_frac": round(fb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "kernel": "k_gemv RMSNorm+W_in+SiLU-product (layer %d)" % args.trace_layer,
+                     "achieved": round(achieved_win, 1) if achieved_win else None, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved_win / HBM_PEAK_GBPS, 4) if achieved_win else None,
+                     "traffic": None, "bytes_per_launch": win_b, "mean_us": round(us_win, 3),
+                     "launches_timed": n_tr},
+        "launch_probe_ms": {("graph" if k else "direct"): round(v, 4) for k, v in probe.items()},
+        "final_position": pos,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,228 @@
+/*
+ * pp.h -- C ABI of libpp: the per-frame forward of the PersonaPlex/Moshi temporal
+ * transformer and its 16-position depth transformer on an AMD Instinct MI355X (gfx950).
+ *
+ * What is computed follows "PersonaPlex native LM audit" (Clockless Inkling,
+ * personaplex-research page): section 3 "Native temporal computation" (embedding sum,
+ * the pre-norm block, RoPE, causal context mask, final norm and text head), section 4
+ * "Native depth computation" (per-position depth inputs, blocks and heads) and
+ * section 6 "Three distinct caches" (the temporal ring KV cache and the per-frame depth
+ * cache). The device-resident, fixed, in-place cache follows the lessons of "Learnings:
+ * PersonaPlex/Moshi full-duplex S2S export + real-time ORT inference" (onnxruntime/mobius
+ * issue #369), sections 3a-3c and the follow-up on in-place KV.
+ *
+ * Conventions for every call
+ *  - Pointers named *_dev are device pointers (memory on the current HIP device,
+ *    allocated by the caller); pointers named *_host are host pointers. Neither is
+ *    retained after the call returns, except the weight pointers given at create time,
+ *    which must stay valid and unchanged until the handle is destroyed.
+ *  - Linear weights are row-major [out_features, in_features]: y = W x.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Every call that touches the
+ *    device is asynchronous on that stream; outputs are valid once it is synchronised.
+ *  - Every call returns a pp_status. Argument, ID, capacity and device errors are
+ *    detected on the host and returned BEFORE anything is enqueued; PP_E_HIP reports a
+ *    HIP runtime error. pp_last_error() gives a message for the calling thread.
+ *  - There is no CPU fallback: creating a handle fails with PP_E_DEVICE unless the
+ *    current device is a gfx950 GPU.
+ *  - Handles are not thread-safe; calls on one handle must not overlap.
+ */
+#ifndef PP_H
+#define PP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PP_OK = 0,
+  PP_E_ARG = 1,       /* bad pointer, size, config or handle */
+  PP_E_ID = 2,        /* a stream ID outside [-1, vocab) (includes -2) */
+  PP_E_CAPACITY = 3,  /* prefill longer than the ring or the workspace, or not at position 0 */
+  PP_E_DEVICE = 4,    /* no gfx950 device current */
+  PP_E_HIP = 5,       /* HIP runtime error */
+  PP_E_DTYPE = 6      /* unsupported weight dtype */
+} pp_status;
+
+typedef enum { PP_F32 = 0, PP_BF16 = 1 } pp_dtype;
+
+/* ------------------------------------------------------------------ temporal model */
+
+/* Shapes of the temporal transformer. Full size: 32 layers, d_model 4096, 32 heads of
+ * 128, d_ff (gated hidden width) 11264, context 3000, text vocab 32001 (IDs 0..32000),
+ * audio vocab 2049 (IDs 0..2048), 16 audio streams, rope_theta 1e4, eps 1e-8.
+ * Requirements: d_model == n_heads * d_head; d_head is 64 or 128; d_model and d_ff are
+ * multiples of 8. wdtype (a pp_dtype) is the type of every weight matrix and
+ * embedding table AND of the KV ring; norm scales are always float32. */
+typedef struct {
+  int32_t n_layers, d_model, n_heads, d_head, d_ff, context;
+  int32_t text_vocab, audio_vocab, n_audio;
+  int32_t wdtype;
+  double rope_theta;
+  double eps;
+} pp_temporal_config;
+
+/* Weights (device pointers; the pointer ARRAYS are host arrays, copied at create).
+ * Names follow the constructor's parameters (audit section 5):
+ *   text_emb    text_emb.weight                               [text_vocab, d_model]
+ *   audio_emb   emb.{0..n_audio-1}.weight (agent cb0-7, user cb0-7) [audio_vocab, d_model]
+ *   norm1/2     transformer.layers.{l}.norm{1,2}.alpha         [d_model] float32
+ *   w_qkv       transformer.layers.{l}.self_attn.in_proj_weight [3*d_model, d_model]
+ *               rows: Q | K | V, head h owns rows h*d_head .. h*d_head+d_head-1 of each
+ *   w_o         transformer.layers.{l}.self_attn.out_proj.weight [d_model, d_model]
+ *   w_in        transformer.layers.{l}.gating.linear_in.weight  [2*d_ff, d_model]
+ *               rows 0..d_ff-1 are the SiLU-gated half g, the rest the linear half z
+ *   w_out       transformer.layers.{l}.gating.linear_out.weight [d_model, d_ff]
+ *   out_norm    out_norm.alpha                                 [d_model] float32
+ *   text_head   text_linear.weight                              [text_vocab-1, d_model] or NULL */
+typedef struct {
+  const void* text_emb;
+  const void* const* audio_emb;
+  const float* const* norm1;
+  const float* const* norm2;
+  const void* const* w_qkv;
+  const void* const* w_o;
+  const void* const* w_in;
+  const void* const* w_out;
+  const float* out_norm;
+  const void* text_head;
+} pp_temporal_weights;
+
+typedef struct pp_model pp_model;
+typedef struct pp_kv pp_kv;
+
+/* Create a temporal model on the current device. max_batch must be 1 in this version
+ * (the pages' server runs B = 1). max_prefill_T (0..context) sizes the prefill
+ * workspace. The library allocates its workspace here (hipMalloc); weights are not
+ * copied. */
+pp_status pp_temporal_create(const pp_temporal_config* cfg, const pp_temporal_weights* w,
+                             int32_t max_batch, int32_t max_prefill_T, pp_model** out);
+pp_status pp_temporal_destroy(pp_model* m);
+
+/* The temporal KV ring of one session: n_layers x [2][batch][n_heads][context][d_head]
+ * of wdtype, allocated once (hipMalloc) and never grown. Keys are stored after RoPE,
+ * values raw. Absolute position p lives in slot p mod context; a query at position p
+ * sees the keys with 0 <= p - key_position < context (audit section 3, declared mask).
+ * bytes = n_layers*2*batch*n_heads*context*d_head*sizeof(wdtype): 1,572,864,000 at
+ * full size, bf16, B = 1 (audit section 6). */
+pp_status pp_kv_alloc(const pp_model* m, int32_t batch, pp_kv** out);
+pp_status pp_kv_free(pp_kv* kv);
+/* Position := 0. No byte is cleared: slots become visible again only once rewritten. */
+pp_status pp_kv_reset(pp_kv* kv);
+pp_status pp_kv_info(const pp_kv* kv, int64_t* position, uint64_t* bytes);
+/* Restore: copy n_frames frames [n_layers][2][batch][n_heads][n_frames][d_head] (wdtype,
+ * keys already rotated for positions 0..n_frames-1) from src_dev into slots
+ * 0..n_frames-1 and set position := n_frames. 0 < n_frames <= context. */
+pp_status pp_kv_load(pp_kv* kv, const void* src_dev, int32_t n_frames, void* stream);
+/* Copy the whole ring [n_layers][2][batch][n_heads][context][d_head] to dst_dev. */
+pp_status pp_kv_store(const pp_kv* kv, void* dst_dev, void* stream);
+
+/* Embedding sum (audit section 3, 'Input embedding sum'): for each of batch*T frames,
+ * x = sum over the n_audio+1 streams of that stream's table row, in stream order,
+ * accumulated in float32; ID -1 adds nothing (an exact zero vector).
+ * ids_host [batch][T][n_audio+1]: stream 0 = agent text, 1..8 agent audio, 9..16 user
+ * audio. Any ID < -1 or >= that stream's vocab gives PP_E_ID. x_out_dev [batch][T][d_model]. */
+pp_status pp_embed_sum(const pp_model* m, const int32_t* ids_host, int32_t batch, int32_t T,
+                       float* x_out_dev, void* stream);
+
+/* One decode frame at the ring's current position p (audit section 3): embedding sum,
+ * n_layers pre-norm blocks (RMSNorm in float32 -> fused QKV -> RoPE on Q and K at p ->
+ * write K, V to slot p mod context -> attention over the visible keys -> W_O + residual ->
+ * RMSNorm -> W_in -> SiLU(g)*z -> W_out + residual), then the final RMSNorm.
+ * ids_host [batch][n_audio+1]. h_out_dev [batch][d_model] float32 receives the final-norm
+ * hidden state; text_logits_dev [batch][text_vocab-1] float32, if not NULL, the text-head
+ * logits (needs a text_head weight). The position then advances by one; past `context`
+ * frames the ring wraps and positions keep counting. */
+pp_status pp_temporal_decode_step(pp_model* m, pp_kv* kv, const int32_t* ids_host,
+                                  float* h_out_dev, float* text_logits_dev, void* stream);
+
+/* Full-sequence forward of T frames at positions 0..T-1 into an empty ring (position
+ * must be 0, 1 <= T <= min(context, max_prefill_T)), causal attention over the frames,
+ * K/V written to slots 0..T-1; position := T afterwards, so decode continues at T.
+ * ids_host [batch][T][n_audio+1]; h_out_dev [batch][T][d_model] float32 final-norm hidden. */
+pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* ids_host, int32_t T,
+                              float* h_out_dev, void* stream);
+
+/* ------------------------------------------------------------------ depth transformer */
+
+/* Shapes of the depth transformer (audit section 4). Full size: 6 layers, d_model 1024,
+ * 16 heads of 64, d_ff 2816, 16 steps (weights_per_step), window 8, text vocab 32001,
+ * audio vocab 2049, 2048 logits per step, d_temporal 4096, eps 1e-8. Requirements:
+ * d_model == n_heads * d_head, d_head <= 128, window >= 1, n_steps <= 32. */
+typedef struct {
+  int32_t n_layers, d_model, n_heads, d_head, d_ff, n_steps, window;
+  int32_t text_vocab, audio_vocab, n_out, d_temporal;
+  int32_t wdtype;
+  double eps;
+} pp_depth_config;
+
+/* Depth weights (device pointers; host pointer arrays copied at create):
+ *   in_proj   depformer_in.{q}.weight, q < n_steps                  [d_model, d_temporal]
+ *   text_emb  depformer_text_emb.weight                              [text_vocab, d_model]
+ *   audio_emb depformer_emb.{q}.weight, q < n_steps-1 (input of q+1)  [audio_vocab, d_model]
+ *   w_qkv     depformer.layers.{m}.self_attn.in_proj_weight  [n_steps*3*d_model, d_model]
+ *             step q uses rows q*3*d_model .. (q+1)*3*d_model-1 (Q | K | V)
+ *   w_o       depformer.layers.{m}.self_attn.out_proj.weight [n_steps*d_model, d_model]
+ *             step q uses rows q*d_model .. (q+1)*d_model-1
+ *   w_in      depformer.layers.{m}.gating.{q}.linear_in.weight, index m*n_steps+q [2*d_ff, d_model]
+ *   w_out     depformer.layers.{m}.gating.{q}.linear_out.weight, index m*n_steps+q [d_model, d_ff]
+ *   norm1/2   depformer.layers.{m}.norm{1,2}.alpha, shared by all steps  [d_model] float32
+ *   head      linears.{q}.weight                                          [n_out, d_model] */
+typedef struct {
+  const void* const* in_proj;
+  const void* text_emb;
+  const void* const* audio_emb;
+  const void* const* w_qkv;
+  const void* const* w_o;
+  const void* const* w_in;
+  const void* const* w_out;
+  const float* const* norm1;
+  const float* const* norm2;
+  const void* const* head;
+} pp_depth_weights;
+
+typedef struct pp_depformer pp_depformer;
+
+pp_status pp_depformer_create(const pp_depth_config* cfg, const pp_depth_weights* w,
+                              pp_depformer** out);
+pp_status pp_depformer_destroy(pp_depformer* d);
+
+/* One frame of the depth loop (audit section 4): for q = 0..n_steps-1,
+ * z = in_proj[q] h + (q == 0 ? text_emb[text token] : audio_emb[q-1][code of q-1]);
+ * n_layers blocks on the step-q weights (no RoPE; position q attends to the positions
+ * q' of this frame with 0 <= q - q' < window; the depth cache starts empty each call);
+ * logits_q = head[q] z. The code of position q is forced_host[q] when >= 0, else the
+ * argmax of logits_q (lowest index on ties); it feeds position q+1 on the device.
+ * h_dev [batch][d_temporal] float32 (the final-norm temporal hidden state);
+ * text_token_host [batch]; forced_host [batch][n_steps] or NULL (all selected);
+ * codes_dev [batch][n_steps] int32 out; logits_dev [batch][n_steps][n_out] float32 or NULL.
+ * batch must be 1. A text token outside [0, text_vocab) or a forced code outside
+ * [-1, n_out) gives PP_E_ID. */
+pp_status pp_depformer_step(pp_depformer* d, const float* h_dev, const int32_t* text_token_host,
+                            const int32_t* forced_host, int32_t batch, int32_t* codes_dev,
+                            float* logits_dev, void* stream);
+
+/* ------------------------------------------------------------------ diagnostics */
+
+/* Message of the last error on the calling thread ("" if none). */
+const char* pp_last_error(void);
+
+/* Decode-step launch mode of a temporal model: 0 = launch each kernel, 1 = replay a
+ * captured HIP graph of the layer stack (default). */
+pp_status pp_temporal_set_graph(pp_model* m, int32_t enable);
+
+/* Kernel timing for roofline reports: when layer >= 0, every decode step brackets the
+ * W_in (RMSNorm + gate/linear projection + SiLU product) kernel of that layer with HIP
+ * events on the caller's stream; pp_temporal_trace_read synchronises those events and
+ * returns their count and mean duration in microseconds, then clears them. layer = -1
+ * turns timing off. At most 4096 bracketed launches are kept. */
+pp_status pp_temporal_trace(pp_model* m, int32_t layer);
+pp_status pp_temporal_trace_read(pp_model* m, int64_t* count, double* mean_us);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PP_H */

@@ -31,7 +31,7 @@ def f64(a):
     a = np.asarray(a)
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
-    return a.astype(np.float64)
+    return np.asarray(a, dtype=np.float64)
 
 
 # --------------------------------------------------------------------------- embedding

@@ -1,0 +1,454 @@
+// C ABI of libpp (declared in include/pp.h): argument and ID validation, workspace and
+// KV-ring ownership, and the launch order of one decode step / prefill / depth frame.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+#include "model.h"
+#include "pp.h"
+
+using namespace pp;
+
+// ------------------------------------------------------------------ errors
+
+static thread_local std::string g_err;
+
+pp_status pp_fail(pp_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+extern "C" const char* pp_last_error(void) { return g_err.c_str(); }
+
+pp_status pp_device_check(int* n_cu) {
+  int dev = -1, count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count == 0)
+    return pp_fail(PP_E_DEVICE, "no HIP device visible");
+  if (hipGetDevice(&dev) != hipSuccess) return pp_fail(PP_E_DEVICE, "no current HIP device");
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+    return pp_fail(PP_E_DEVICE, "hipGetDeviceProperties failed");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return pp_fail(PP_E_DEVICE, std::string("libpp is built for gfx950; current device is ") +
+                                    prop.gcnArchName);
+  *n_cu = prop.multiProcessorCount;
+  return PP_OK;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  return v && *v ? std::atoi(v) : dflt;
+}
+
+// ------------------------------------------------------------------ temporal model
+
+static pp_status validate_temporal_config(const pp_temporal_config* c) {
+  if (!c) return pp_fail(PP_E_ARG, "config is NULL");
+  if (c->wdtype != PP_F32 && c->wdtype != PP_BF16) return pp_fail(PP_E_DTYPE, "wdtype must be PP_F32 or PP_BF16");
+  if (c->n_layers < 1 || c->d_model < 8 || c->n_heads < 1 || c->context < 1 || c->d_ff < 8)
+    return pp_fail(PP_E_ARG, "non-positive dimension in config");
+  if (c->d_head != 64 && c->d_head != 128) return pp_fail(PP_E_ARG, "d_head must be 64 or 128");
+  if (c->n_heads * c->d_head != c->d_model) return pp_fail(PP_E_ARG, "d_model != n_heads * d_head");
+  if (c->d_model % 8 || c->d_ff % 8) return pp_fail(PP_E_ARG, "d_model and d_ff must be multiples of 8");
+  if (c->d_model > 16384 || c->d_ff > 16384) return pp_fail(PP_E_ARG, "d_model/d_ff above 16384 unsupported");
+  if (c->n_audio < 0 || c->n_audio + 1 > kMaxStreams) return pp_fail(PP_E_ARG, "n_audio out of range");
+  if (c->text_vocab < 2 || c->audio_vocab < 1) return pp_fail(PP_E_ARG, "vocab sizes must be positive");
+  if (!(c->rope_theta > 0) || !(c->eps >= 0)) return pp_fail(PP_E_ARG, "rope_theta must be > 0, eps >= 0");
+  return PP_OK;
+}
+
+extern "C" pp_status pp_temporal_create(const pp_temporal_config* cfg, const pp_temporal_weights* w,
+                                        int32_t max_batch, int32_t max_prefill_T, pp_model** out) {
+  if (!out) return pp_fail(PP_E_ARG, "out is NULL");
+  *out = nullptr;
+  pp_status st = validate_temporal_config(cfg);
+  if (st) return st;
+  if (!w) return pp_fail(PP_E_ARG, "weights are NULL");
+  if (max_batch != 1) return pp_fail(PP_E_ARG, "max_batch must be 1 in this version");
+  if (max_prefill_T < 0 || max_prefill_T > cfg->context)
+    return pp_fail(PP_E_CAPACITY, "max_prefill_T must be in [0, context]");
+  int n_cu = 0;
+  if ((st = pp_device_check(&n_cu))) return st;
+  const int L = cfg->n_layers;
+  if (!w->text_emb || !w->out_norm || (cfg->n_audio > 0 && !w->audio_emb) || !w->norm1 || !w->norm2 ||
+      !w->w_qkv || !w->w_o || !w->w_in || !w->w_out)
+    return pp_fail(PP_E_ARG, "a required weight pointer is NULL");
+  for (int i = 0; i < cfg->n_audio; ++i)
+    if (!w->audio_emb[i]) return pp_fail(PP_E_ARG, "audio_emb[" + std::to_string(i) + "] is NULL");
+  for (int l = 0; l < L; ++l)
+    if (!w->norm1[l] || !w->norm2[l] || !w->w_qkv[l] || !w->w_o[l] || !w->w_in[l] || !w->w_out[l])
+      return pp_fail(PP_E_ARG, "layer " + std::to_string(l) + " has a NULL weight");
+
+  pp_model* m = new pp_model();
+  m->cfg = *cfg;
+  m->bf16 = cfg->wdtype == PP_BF16;
+  m->n_cu = n_cu;
+  (void)hipGetDevice(&m->device);
+  m->text_emb = w->text_emb;
+  m->audio_emb.assign(w->audio_emb, w->audio_emb + cfg->n_audio);
+  m->norm1.assign(w->norm1, w->norm1 + L);
+  m->norm2.assign(w->norm2, w->norm2 + L);
+  m->w_qkv.assign(w->w_qkv, w->w_qkv + L);
+  m->w_o.assign(w->w_o, w->w_o + L);
+  m->w_in.assign(w->w_in, w->w_in + L);
+  m->w_out.assign(w->w_out, w->w_out + L);
+  m->out_norm = w->out_norm;
+  m->text_head = w->text_head;
+  m->max_batch = max_batch;
+  m->max_T = max_prefill_T;
+  m->use_graph = env_int("PP_GRAPH", 1) != 0;
+  m->gemv_waves = env_int("PP_GEMV_WAVES_PER_CU", 8) * n_cu;
+
+  const int D = cfg->d_model, F = cfg->d_ff, H = cfg->n_heads, dh = cfg->d_head;
+  // attention splits: >= 2 blocks per CU over all heads, <= 2048 keys per block
+  int S = (2 * n_cu + H - 1) / H;
+  if (S > 64) S = 64;
+  const int min_s = (cfg->context + 2047) / 2048;
+  if (S < min_s) S = min_s;
+  if (S < 1) S = 1;
+  m->S = env_int("PP_ATTN_SPLITS", S);
+  if (m->S < min_s) m->S = min_s;
+
+  st = m->alloc_decode(D, F, H, dh);
+  if (!st) st = m->alloc_prefill();
+  if (st) {
+    delete m;
+    return st;
+  }
+  *out = m;
+  return PP_OK;
+}
+
+pp_status pp_model::alloc_decode(int D, int F, int H, int dh) {
+  size_t bytes = 0;
+  auto take = [&](size_t n) { size_t off = bytes; bytes += (n + 255) / 256 * 256; return off; };
+  const size_t ox = take(sizeof(float) * D), oq = take(sizeof(float) * D), oo = take(sizeof(float) * D);
+  const size_t os = take(sizeof(float) * F), op = take(sizeof(float) * (size_t)H * S * (dh + 2));
+  const size_t oc = take(sizeof(int) * H), ost = take(sizeof(long long) * 4);
+  if (hipMalloc(&ws, bytes) != hipSuccess) return pp_fail(PP_E_HIP, "hipMalloc of decode workspace failed");
+  if (hipMemset(ws, 0, bytes) != hipSuccess) return pp_fail(PP_E_HIP, "hipMemset of decode workspace failed");
+  char* b = static_cast<char*>(ws);
+  x = reinterpret_cast<float*>(b + ox);
+  q = reinterpret_cast<float*>(b + oq);
+  o = reinterpret_cast<float*>(b + oo);
+  s = reinterpret_cast<float*>(b + os);
+  part = reinterpret_cast<float*>(b + op);
+  counters = reinterpret_cast<int*>(b + oc);
+  state = reinterpret_cast<long long*>(b + ost);
+  return PP_OK;
+}
+
+pp_model::~pp_model() {
+  for (hipEvent_t e : trace_ev) (void)hipEventDestroy(e);
+  free_prefill();
+  if (ws) (void)hipFree(ws);
+  if (ids_pinned) (void)hipHostFree(ids_pinned);
+  if (ids_event) (void)hipEventDestroy(ids_event);
+}
+
+extern "C" pp_status pp_temporal_destroy(pp_model* m) {
+  if (!m) return pp_fail(PP_E_ARG, "model is NULL");
+  delete m;
+  return PP_OK;
+}
+
+extern "C" pp_status pp_temporal_set_graph(pp_model* m, int32_t enable) {
+  if (!m) return pp_fail(PP_E_ARG, "model is NULL");
+  m->use_graph = enable != 0;
+  return PP_OK;
+}
+
+// ------------------------------------------------------------------ KV ring
+
+extern "C" pp_status pp_kv_alloc(const pp_model* m, int32_t batch, pp_kv** out) {
+  if (!m || !out) return pp_fail(PP_E_ARG, "NULL argument");
+  *out = nullptr;
+  if (batch < 1 || batch > m->max_batch) return pp_fail(PP_E_ARG, "batch outside [1, max_batch]");
+  const pp_temporal_config& c = m->cfg;
+  const size_t esz = m->bf16 ? 2 : 4;
+  const size_t bytes = (size_t)c.n_layers * 2 * batch * c.n_heads * c.context * c.d_head * esz;
+  pp_kv* kv = new pp_kv();
+  kv->m = const_cast<pp_model*>(m);
+  kv->B = batch;
+  kv->bytes = bytes;
+  if (hipMalloc(&kv->ring, bytes) != hipSuccess) {
+    delete kv;
+    return pp_fail(PP_E_HIP, "hipMalloc of the KV ring (" + std::to_string(bytes) + " bytes) failed");
+  }
+  *out = kv;
+  return PP_OK;
+}
+
+pp_kv::~pp_kv() {
+  if (exec) (void)hipGraphExecDestroy(exec);
+  if (graph) (void)hipGraphDestroy(graph);
+  if (ring) (void)hipFree(ring);
+}
+
+extern "C" pp_status pp_kv_free(pp_kv* kv) {
+  if (!kv) return pp_fail(PP_E_ARG, "kv is NULL");
+  delete kv;
+  return PP_OK;
+}
+
+extern "C" pp_status pp_kv_reset(pp_kv* kv) {
+  if (!kv) return pp_fail(PP_E_ARG, "kv is NULL");
+  kv->pos = 0;
+  return PP_OK;
+}
+
+extern "C" pp_status pp_kv_info(const pp_kv* kv, int64_t* position, uint64_t* bytes) {
+  if (!kv) return pp_fail(PP_E_ARG, "kv is NULL");
+  if (position) *position = kv->pos;
+  if (bytes) *bytes = kv->bytes;
+  return PP_OK;
+}
+
+extern "C" pp_status pp_kv_load(pp_kv* kv, const void* src_dev, int32_t n_frames, void* stream) {
+  if (!kv || !src_dev) return pp_fail(PP_E_ARG, "NULL argument");
+  const pp_temporal_config& c = kv->m->cfg;
+  if (n_frames < 1 || n_frames > c.context) return pp_fail(PP_E_CAPACITY, "n_frames outside [1, context]");
+  const size_t esz = kv->m->bf16 ? 2 : 4;
+  const size_t rows = (size_t)c.n_layers * 2 * kv->B * c.n_heads;
+  const size_t w = (size_t)n_frames * c.d_head * esz;
+  hipError_t e = hipMemcpy2DAsync(kv->ring, (size_t)c.context * c.d_head * esz, src_dev, w, w, rows,
+                                  hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("pp_kv_load: ") + hipGetErrorString(e));
+  kv->pos = n_frames;
+  return PP_OK;
+}
+
+extern "C" pp_status pp_kv_store(const pp_kv* kv, void* dst_dev, void* stream) {
+  if (!kv || !dst_dev) return pp_fail(PP_E_ARG, "NULL argument");
+  hipError_t e = hipMemcpyAsync(dst_dev, kv->ring, kv->bytes, hipMemcpyDeviceToDevice,
+                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("pp_kv_store: ") + hipGetErrorString(e));
+  return PP_OK;
+}
+
+// ------------------------------------------------------------------ embedding
+
+pp_status pp_model::check_ids(const int32_t* ids, size_t frames) const {
+  const int ns = cfg.n_audio + 1;
+  for (size_t f = 0; f < frames; ++f)
+    for (int k = 0; k < ns; ++k) {
+      const int32_t id = ids[f * ns + k];
+      const int32_t vocab = k == 0 ? cfg.text_vocab : cfg.audio_vocab;
+      if (id < -1 || id >= vocab)
+        return pp_fail(PP_E_ID, "frame " + std::to_string(f) + " stream " + std::to_string(k) + ": ID " +
+                                    std::to_string(id) + " outside [-1, " + std::to_string(vocab) + ")");
+    }
+  return PP_OK;
+}
+
+void pp_model::embed_tables(EmbedArgs& a) const {
+  a.tables[0] = text_emb;
+  for (int i = 0; i < cfg.n_audio; ++i) a.tables[i + 1] = audio_emb[i];
+  a.n_streams = cfg.n_audio + 1;
+  a.D = cfg.d_model;
+}
+
+pp_status pp_model::stage_ids(const int32_t* ids_host, size_t n, hipStream_t s) {
+  // IDs go through a pinned buffer owned by the model; the event guards its reuse.
+  if (n > ids_cap) {
+    if (ids_pinned) {
+      (void)hipEventSynchronize(ids_event);
+      (void)hipHostFree(ids_pinned);
+    }
+    ids_pinned = nullptr;
+    if (hipHostMalloc(reinterpret_cast<void**>(&ids_pinned), n * sizeof(int32_t)) != hipSuccess)
+      return pp_fail(PP_E_HIP, "hipHostMalloc of the ID staging buffer failed");
+    ids_cap = n;
+  }
+  if (!ids_event && hipEventCreateWithFlags(&ids_event, hipEventDisableTiming) != hipSuccess)
+    return pp_fail(PP_E_HIP, "hipEventCreate failed");
+  (void)hipEventSynchronize(ids_event);
+  std::memcpy(ids_pinned, ids_host, n * sizeof(int32_t));
+  hipError_t e = hipMemcpyAsync(ids_dev, ids_pinned, n * sizeof(int32_t), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipEventRecord(ids_event, s);
+  if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("staging IDs: ") + hipGetErrorString(e));
+  return PP_OK;
+}
+
+extern "C" pp_status pp_embed_sum(const pp_model* mc, const int32_t* ids_host, int32_t batch, int32_t T,
+                                  float* x_out_dev, void* stream) {
+  pp_model* m = const_cast<pp_model*>(mc);
+  if (!m || !ids_host || !x_out_dev) return pp_fail(PP_E_ARG, "NULL argument");
+  if (batch < 1 || batch > m->max_batch || T < 1) return pp_fail(PP_E_ARG, "batch or T out of range");
+  const size_t frames = (size_t)batch * T;
+  pp_status st = m->check_ids(ids_host, frames);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  EmbedArgs a{};
+  m->embed_tables(a);
+  a.out = x_out_dev;
+  a.rows = (int)frames;
+  if (frames == 1) {
+    for (int k = 0; k < a.n_streams; ++k) a.ids_arg[k] = ids_host[k];
+  } else {
+    if (frames > (size_t)m->max_T * m->max_batch)
+      return pp_fail(PP_E_CAPACITY, "batch*T exceeds the model's prefill workspace (max_prefill_T)");
+    if ((st = m->stage_ids(ids_host, frames * a.n_streams, s))) return st;
+    a.ids_dev = m->ids_dev;
+  }
+  hipError_t e = launch_embed(a, m->bf16, s);
+  if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("embed: ") + hipGetErrorString(e));
+  return PP_OK;
+}
+
+// ------------------------------------------------------------------ decode step
+
+hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced) {
+  const pp_temporal_config& c = cfg;
+  const int D = c.d_model, F = c.d_ff, H = c.n_heads, dh = c.d_head, C = c.context;
+  const size_t esz = bf16 ? 2 : 4;
+  const size_t per_kv = (size_t)kv->B * H * C * dh * esz;
+  hipError_t e = hipSuccess;
+  for (int l = 0; l < c.n_layers && e == hipSuccess; ++l) {
+    char* kbase = static_cast<char*>(kv->ring) + (size_t)(2 * l) * per_kv;
+    char* vbase = kbase + per_kv;
+
+    GemvArgs g{};
+    g.W = w_qkv[l]; g.x = x; g.alpha = norm1[l]; g.eps = (float)c.eps; g.K = D;
+    g.n_groups = 3 * D / 4; g.out = q; g.D = D; g.dh = dh; g.C = C; g.kc = kbase; g.vc = vbase;
+    g.state = state; g.log_theta = std::log(c.rope_theta);
+    e = launch_gemv(PRO_RMSNORM, EPI_QKV, bf16, 4, g, gemv_waves, s);
+    if (e != hipSuccess) break;
+
+    AttnDecodeArgs at{};
+    at.q = q; at.k = kbase; at.v = vbase; at.state = state; at.C = C; at.H = H; at.S = S;
+    at.scale = 1.0f / std::sqrt((float)dh); at.part = part; at.counters = counters; at.out = o;
+    e = launch_attn_decode(at, bf16, dh, s);
+    if (e != hipSuccess) break;
+
+    GemvArgs go{};
+    go.W = w_o[l]; go.x = o; go.K = D; go.n_groups = D / 2; go.out = x;
+    e = launch_gemv(PRO_COPY, EPI_RESID, bf16, 2, go, gemv_waves, s);
+    if (e != hipSuccess) break;
+
+    const bool tr = traced && l == trace_layer && trace_used + 2 <= trace_ev.size();
+    if (tr) (void)hipEventRecord(trace_ev[trace_used], s);
+    GemvArgs gi{};
+    gi.W = w_in[l]; gi.x = x; gi.alpha = norm2[l]; gi.eps = (float)c.eps; gi.K = D;
+    gi.n_groups = F / 2; gi.out = this->s; gi.F = F;
+    e = launch_gemv(PRO_RMSNORM, EPI_SWIGLU, bf16, 4, gi, gemv_waves, s);
+    if (tr) {
+      (void)hipEventRecord(trace_ev[trace_used + 1], s);
+      trace_used += 2;
+    }
+    if (e != hipSuccess) break;
+
+    GemvArgs gw{};
+    gw.W = w_out[l]; gw.x = this->s; gw.K = F; gw.n_groups = D / 2; gw.out = x;
+    e = launch_gemv(PRO_COPY, EPI_RESID, bf16, 2, gw, gemv_waves, s);
+  }
+  return e;
+}
+
+pp_status pp_model::run_layers(pp_kv* kv, hipStream_t s) {
+  const bool traced = trace_layer >= 0;
+  if (!use_graph || traced) {
+    hipError_t e = enqueue_layers(kv, s, traced);
+    if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("decode launch: ") + hipGetErrorString(e));
+    return PP_OK;
+  }
+  if (!kv->exec || kv->exec_model_gen != graph_gen) {
+    if (kv->exec) (void)hipGraphExecDestroy(kv->exec);
+    if (kv->graph) (void)hipGraphDestroy(kv->graph);
+    kv->exec = nullptr;
+    kv->graph = nullptr;
+    hipStream_t cap;
+    if (hipStreamCreateWithFlags(&cap, hipStreamNonBlocking) != hipSuccess)
+      return pp_fail(PP_E_HIP, "hipStreamCreate for graph capture failed");
+    hipError_t e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+      hipError_t le = enqueue_layers(kv, cap, false);
+      e = hipStreamEndCapture(cap, &kv->graph);
+      if (le != hipSuccess) e = le;
+    }
+    if (e == hipSuccess) e = hipGraphInstantiate(&kv->exec, kv->graph, nullptr, nullptr, 0);
+    (void)hipStreamDestroy(cap);
+    if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("decode graph capture: ") + hipGetErrorString(e));
+    kv->exec_model_gen = graph_gen;
+  }
+  hipError_t e = hipGraphLaunch(kv->exec, s);
+  if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("decode graph launch: ") + hipGetErrorString(e));
+  return PP_OK;
+}
+
+extern "C" pp_status pp_temporal_decode_step(pp_model* m, pp_kv* kv, const int32_t* ids_host,
+                                             float* h_out_dev, float* text_logits_dev, void* stream) {
+  if (!m || !kv || !ids_host || !h_out_dev) return pp_fail(PP_E_ARG, "NULL argument");
+  if (kv->m != m) return pp_fail(PP_E_ARG, "kv ring belongs to another model");
+  if (text_logits_dev && !m->text_head) return pp_fail(PP_E_ARG, "text logits requested but the model has no text head");
+  pp_status st = m->check_ids(ids_host, (size_t)kv->B);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const pp_temporal_config& c = m->cfg;
+
+  EmbedArgs a{};
+  m->embed_tables(a);
+  for (int k = 0; k < a.n_streams; ++k) a.ids_arg[k] = ids_host[k];
+  a.out = m->x;
+  a.rows = 1;
+  a.state = m->state;
+  a.pos = kv->pos;
+  hipError_t e = launch_embed(a, m->bf16, s);
+  if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("embed: ") + hipGetErrorString(e));
+
+  if ((st = m->run_layers(kv, s))) return st;
+
+  e = launch_rmsnorm_rows(m->x, m->out_norm, (float)c.eps, c.d_model, 1, h_out_dev, nullptr, s);
+  if (e == hipSuccess && text_logits_dev) {
+    GemvArgs g{};
+    g.W = m->text_head; g.x = m->x; g.alpha = m->out_norm; g.eps = (float)c.eps; g.K = c.d_model;
+    g.n_groups = (c.text_vocab - 1) / 2; g.out = text_logits_dev;
+    if ((c.text_vocab - 1) % 2 == 0) {
+      e = launch_gemv(PRO_RMSNORM, EPI_STORE, m->bf16, 2, g, m->gemv_waves, s);
+    } else {
+      return pp_fail(PP_E_ARG, "text head rows must be even");
+    }
+  }
+  if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("final norm / text head: ") + hipGetErrorString(e));
+  kv->pos += 1;
+  return PP_OK;
+}
+
+// ------------------------------------------------------------------ kernel timing
+
+extern "C" pp_status pp_temporal_trace(pp_model* m, int32_t layer) {
+  if (!m) return pp_fail(PP_E_ARG, "model is NULL");
+  if (layer >= m->cfg.n_layers) return pp_fail(PP_E_ARG, "layer out of range");
+  if (layer >= 0 && m->trace_ev.empty()) {
+    m->trace_ev.resize(4096);
+    for (auto& ev : m->trace_ev)
+      if (hipEventCreate(&ev) != hipSuccess) return pp_fail(PP_E_HIP, "hipEventCreate failed");
+  }
+  m->trace_layer = layer < 0 ? -1 : layer;
+  m->trace_used = 0;
+  return PP_OK;
+}
+
+extern "C" pp_status pp_temporal_trace_read(pp_model* m, int64_t* count, double* mean_us) {
+  if (!m || !count || !mean_us) return pp_fail(PP_E_ARG, "NULL argument");
+  double tot = 0;
+  int64_t n = 0;
+  for (size_t i = 0; i + 1 < m->trace_used; i += 2) {
+    float ms = 0;
+    if (hipEventSynchronize(m->trace_ev[i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, m->trace_ev[i], m->trace_ev[i + 1]) != hipSuccess)
+      return pp_fail(PP_E_HIP, "reading trace events failed");
+    tot += ms;
+    ++n;
+  }
+  *count = n;
+  *mean_us = n ? tot * 1000.0 / n : 0.0;
+  m->trace_used = 0;
+  return PP_OK;
+}

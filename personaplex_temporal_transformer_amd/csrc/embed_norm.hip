@@ -1,0 +1,77 @@
+// Embedding sum and row RMSNorm kernels.
+//
+// Embedding sum: "PersonaPlex native LM audit", section 3 'Input embedding sum' -- the
+// frame's input is the plain sum of one row from each of the 17 stream tables (text,
+// 8 agent audio, 8 user audio); ID -1 contributes an exact zero vector.
+// RMSNorm: same page, section 3 'One of the 32 temporal blocks' -- float32 arithmetic,
+// x * alpha / sqrt(mean(x^2) + eps), no mean subtraction.
+#include "device.h"
+#include "internal.h"
+
+namespace pp {
+
+// One thread owns 4 consecutive features of one frame; it adds the streams' rows in
+// stream order 0..n-1 in float32 (a fixed order, so the result is reproducible).
+template <typename WT>
+__global__ __launch_bounds__(kBlock) void k_embed_sum(EmbedArgs a) {
+  const int row = blockIdx.y;
+  const int d = (blockIdx.x * kBlock + threadIdx.x) * 4;
+  if (a.state && row == 0 && blockIdx.x == 0 && threadIdx.x == 0) a.state[0] = a.pos;
+  if (d >= a.D) return;
+  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+  for (int k = 0; k < a.n_streams; ++k) {
+    const int id = a.ids_dev ? a.ids_dev[(size_t)row * a.n_streams + k] : a.ids_arg[k];
+    if (id < 0) continue;  // -1: no input (other negatives are rejected on the host)
+    const WT* r = static_cast<const WT*>(a.tables[k]) + (size_t)id * a.D + d;
+    acc0 += Elem<WT>::load1(r + 0);
+    acc1 += Elem<WT>::load1(r + 1);
+    acc2 += Elem<WT>::load1(r + 2);
+    acc3 += Elem<WT>::load1(r + 3);
+  }
+  f32x4 v = {acc0, acc1, acc2, acc3};
+  *reinterpret_cast<f32x4*>(a.out + (size_t)row * a.D + d) = v;
+}
+
+hipError_t launch_embed(const EmbedArgs& a, bool bf16, hipStream_t s) {
+  dim3 grid((a.D / 4 + kBlock - 1) / kBlock, a.rows);
+  if (bf16)
+    hipLaunchKernelGGL(k_embed_sum<bf16_t>, grid, dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_embed_sum<float>, grid, dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+// One block per row; float32 statistics; writes float32 and/or bfloat16 output.
+__global__ __launch_bounds__(kBlock) void k_rmsnorm_rows(const float* __restrict__ x,
+                                                         const float* __restrict__ alpha, float eps,
+                                                         int D, float* __restrict__ out_f32,
+                                                         uint16_t* __restrict__ out_bf16) {
+  __shared__ float red[4];
+  const float* xr = x + (size_t)blockIdx.x * D;
+  float ss = 0.f;
+  for (int i = threadIdx.x * 4; i < D; i += kBlock * 4) {
+    f32x4 v = *reinterpret_cast<const f32x4*>(xr + i);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  const float r = 1.0f / sqrtf(block_sum_256(ss, red) / (float)D + eps);
+  for (int i = threadIdx.x * 4; i < D; i += kBlock * 4) {
+    f32x4 v = *reinterpret_cast<const f32x4*>(xr + i);
+    f32x4 al = *reinterpret_cast<const f32x4*>(alpha + i);
+    f32x4 y = (v * r) * al;
+    if (out_f32) *reinterpret_cast<f32x4*>(out_f32 + (size_t)blockIdx.x * D + i) = y;
+    if (out_bf16) {
+      uint16_t* o = out_bf16 + (size_t)blockIdx.x * D + i;
+      o[0] = f32_to_bf16(y.x); o[1] = f32_to_bf16(y.y);
+      o[2] = f32_to_bf16(y.z); o[3] = f32_to_bf16(y.w);
+    }
+  }
+}
+
+hipError_t launch_rmsnorm_rows(const float* x, const float* alpha, float eps, int D, int rows,
+                               float* out_f32, void* out_bf16, hipStream_t s) {
+  hipLaunchKernelGGL(k_rmsnorm_rows, dim3(rows), dim3(kBlock), 0, s, x, alpha, eps, D, out_f32,
+                     static_cast<uint16_t*>(out_bf16));
+  return hipGetLastError();
+}
+
+}  // namespace pp

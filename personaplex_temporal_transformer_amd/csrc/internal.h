@@ -1,0 +1,76 @@
+// Internal interfaces between the C ABI (api.cpp) and the kernel files (*.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pp {
+
+constexpr int kMaxStreams = 32;   // text + audio streams of the embedding sum
+constexpr int kBlock = 256;       // threads per workgroup (4 waves) for every kernel here
+
+// ---------------------------------------------------------------- embedding sum
+struct EmbedArgs {
+  const void* tables[kMaxStreams];  // stream k -> table [vocab_k][D]
+  int32_t ids_arg[kMaxStreams];     // one frame's IDs when ids_dev == nullptr
+  const int32_t* ids_dev;           // [rows][n_streams] device IDs (prefill) or nullptr
+  float* out;                       // [rows][D]
+  long long* state;                 // if non-null, state[0] := pos (decode position)
+  long long pos;
+  int n_streams, D, rows;
+};
+hipError_t launch_embed(const EmbedArgs& a, bool bf16, hipStream_t s);
+
+// ---------------------------------------------------------------- GEMV family (decode)
+enum GemvPro { PRO_COPY = 0, PRO_RMSNORM = 1 };
+enum GemvEpi {
+  EPI_STORE = 0,   // out[row] = W x
+  EPI_RESID = 1,   // out[row] += W x                       (residual stream, fp32)
+  EPI_QKV = 2,     // RoPE on Q and K, q -> out, K and V -> ring slot
+  EPI_SWIGLU = 3,  // rows i (g) and F + i (z): out[i] = SiLU(g) * z
+  EPI_DEPTH_QKV = 4,  // depth QKV: q -> out, K and V -> depth cache row (fp32), no RoPE
+};
+
+struct GemvArgs {
+  const void* W;        // [rows][K] row-major
+  const float* x;       // [K] input vector
+  const float* alpha;   // [K] RMSNorm scale (PRO_RMSNORM)
+  float eps;
+  int K;
+  int n_groups;         // row groups; a group is rows_per_group rows
+  float* out;
+  // EPI_QKV / EPI_DEPTH_QKV
+  int D, dh, C;         // model width, head width, ring capacity (slots)
+  void* kc;             // K ring of this layer, batch 0: [H][C][dh]   (depth: [H][C][dh] fp32)
+  void* vc;
+  const long long* state;  // state[0] = position of this frame (slot = pos mod C)
+  double log_theta;
+  int slot_override;    // depth: >= 0 gives the cache row directly
+  // EPI_SWIGLU
+  int F;
+  // a second bias-like input added to the output (depth: embedding row), or null
+  const float* add;
+};
+// rows_per_group: 2 or 4; waves: total waves of the launch (0 = choose).
+hipError_t launch_gemv(int pro, int epi, bool bf16, int rows_per_group, const GemvArgs& a,
+                       int waves, hipStream_t s);
+
+// ---------------------------------------------------------------- attention (decode)
+struct AttnDecodeArgs {
+  const float* q;       // [H][dh], after RoPE
+  const void* k;        // ring of this layer, batch 0: [H][C][dh]
+  const void* v;
+  const long long* state;
+  int C, H, S;          // S = splits of the key range per head
+  float scale;
+  float* part;          // [H][S][dh + 2] partial (o, m, l)
+  int* counters;        // [H], zero outside a launch
+  float* out;           // [H * dh]
+};
+hipError_t launch_attn_decode(const AttnDecodeArgs& a, bool bf16, int dh, hipStream_t s);
+
+// ---------------------------------------------------------------- row RMSNorm
+hipError_t launch_rmsnorm_rows(const float* x, const float* alpha, float eps, int D, int rows,
+                               float* out_f32, void* out_bf16, hipStream_t s);
+
+}  // namespace pp

@@ -1,0 +1,85 @@
+// Handle types behind the opaque pointers of pp.h (host side only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <string>
+#include <vector>
+
+#include "internal.h"
+#include "pp.h"
+
+pp_status pp_fail(pp_status st, const std::string& msg);
+pp_status pp_device_check(int* n_cu);
+int env_int(const char* name, int dflt);
+
+struct pp_kv;
+
+struct pp_model {
+  pp_temporal_config cfg{};
+  bool bf16 = true;
+  int device = 0, n_cu = 0;
+  int max_batch = 1, max_T = 0;
+
+  // weights (caller-owned device memory)
+  const void* text_emb = nullptr;
+  std::vector<const void*> audio_emb;
+  std::vector<const float*> norm1, norm2;
+  std::vector<const void*> w_qkv, w_o, w_in, w_out;
+  const float* out_norm = nullptr;
+  const void* text_head = nullptr;
+
+  // decode workspace (one hipMalloc)
+  void* ws = nullptr;
+  float* x = nullptr;        // residual stream [D] float32
+  float* q = nullptr;        // rotated query [D]
+  float* o = nullptr;        // attention output [D]
+  float* s = nullptr;        // SiLU(g) * z [F]
+  float* part = nullptr;     // attention partials [H][S][dh + 2]
+  int* counters = nullptr;   // [H]
+  long long* state = nullptr;  // [0] = position of the frame being decoded
+  int S = 16;                // attention splits per head
+  int gemv_waves = 2048;     // waves per GEMV launch
+
+  // prefill workspace (one hipMalloc, sized by max_T)
+  void* pws = nullptr;
+  int32_t* ids_dev = nullptr;  // [max_T][n_streams]
+  float* px = nullptr;         // residual stream [T][D] float32
+  void* pu = nullptr;          // normalised rows, bf16 [T][D] (f32 path: float32)
+  void* pq = nullptr;          // rotated Q [H][T][dh]
+  void* pa = nullptr;          // attention output [T][D]
+  void* pg = nullptr;          // SiLU(g)*z [T][F]
+
+  int32_t* ids_pinned = nullptr;
+  size_t ids_cap = 0;
+  hipEvent_t ids_event = nullptr;
+
+  // launch mode and timing
+  bool use_graph = true;
+  int graph_gen = 0;
+  int trace_layer = -1;
+  std::vector<hipEvent_t> trace_ev;
+  size_t trace_used = 0;
+
+  ~pp_model();
+  pp_status alloc_decode(int D, int F, int H, int dh);
+  pp_status alloc_prefill();
+  void free_prefill();
+  pp_status check_ids(const int32_t* ids, size_t frames) const;
+  void embed_tables(pp::EmbedArgs& a) const;
+  pp_status stage_ids(const int32_t* ids_host, size_t n, hipStream_t s);
+  hipError_t enqueue_layers(pp_kv* kv, hipStream_t s, bool traced);
+  pp_status run_layers(pp_kv* kv, hipStream_t s);
+};
+
+struct pp_kv {
+  pp_model* m = nullptr;
+  void* ring = nullptr;   // [L][2][B][H][C][dh]
+  size_t bytes = 0;
+  int B = 1;
+  int64_t pos = 0;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  int exec_model_gen = -1;
+  ~pp_kv();
+};

@@ -1,0 +1,186 @@
+"""GPU parity of the temporal decode path (embedding sum, blocks, final norm, text head)
+against the oracle, through the C ABI. Tolerances: max abs error 1e-4 for the fp32
+path; max |err| / max |ref| <= 2e-2 for the bf16 path; bit-exact for ID gathering and
+cache indexing."""
+
+import numpy as np
+import pytest
+
+from oracle import temporal as O
+from personaplex_temporal_transformer_amd import pp, synth
+from tests.helpers import max_abs_err, norm_max_err, require_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+FP32_TOL = 1e-4
+BF16_TOL = 2e-2
+
+
+def _model(cfg, W, wdtype, max_T=0):
+    require_gpu()
+    dW = to_device(W)
+    return pp.TemporalModel(cfg, dW, wdtype, max_prefill_T=max_T), dW
+
+
+def _decode_all(model, kv, ids, with_logits=True):
+    import torch
+    T, D = ids.shape[0], model.cfg["d_model"]
+    h = torch.empty((T, D), dtype=torch.float32, device="cuda")
+    lg = torch.empty((T, model.cfg["text_vocab"] - 1), dtype=torch.float32, device="cuda") if with_logits else None
+    for t in range(T):
+        model.decode_step(kv, ids[t], h[t], lg[t] if with_logits else None)
+    torch.cuda.synchronize()
+    return h.cpu().numpy(), (lg.cpu().numpy() if with_logits else None)
+
+
+# ----------------------------------------------------------------------------- fp32, tiny
+
+@pytest.mark.parametrize("context", [3000, 4])
+@pytest.mark.parametrize("graph", [True, False])
+def test_tiny_fp32_decode_matches_oracle(context, graph):
+    cfg = synth.with_(synth.TINY_TEMPORAL, context=context)
+    W = synth.temporal_weights(cfg, 0, "fp32")
+    ids = synth.stream_ids(cfg, 16, 1)
+    model, _ = _model(cfg, W, "fp32")
+    model.set_graph(graph)
+    kv = model.kv_alloc()
+    h, lg = _decode_all(model, kv, ids)
+    want_h, want_lg = O.forward_full(ids, W, cfg, with_logits=True)
+    print("tiny fp32 C=%d graph=%s: h err %.3g, logits err %.3g" %
+          (context, graph, max_abs_err(h, want_h), max_abs_err(lg, want_lg)))
+    assert max_abs_err(h, want_h) <= FP32_TOL
+    assert max_abs_err(lg, want_lg) <= FP32_TOL
+    assert kv.info()[0] == 16
+
+
+def test_graph_and_direct_launch_are_bit_identical_and_reset_replays():
+    cfg = synth.TINY_TEMPORAL
+    W = synth.temporal_weights(cfg, 5, "fp32")
+    ids = synth.stream_ids(cfg, 12, 6)
+    model, _ = _model(cfg, W, "fp32")
+    kv = model.kv_alloc()
+    model.set_graph(True)
+    a, _ = _decode_all(model, kv, ids, with_logits=False)
+    kv.reset()
+    assert kv.info()[0] == 0
+    model.set_graph(False)
+    b, _ = _decode_all(model, kv, ids, with_logits=False)
+    assert np.array_equal(a, b)
+
+
+def test_invalid_ids_rejected_before_enqueue():
+    import torch
+    cfg = synth.TINY_TEMPORAL
+    W = synth.temporal_weights(cfg, 0, "fp32", with_text_head=False)
+    model, _ = _model(cfg, W, "fp32")
+    kv = model.kv_alloc()
+    h = torch.zeros(cfg["d_model"], device="cuda")
+    for k, bad in ((0, -2), (0, 32001), (9, 2049), (16, -7)):
+        ids = np.zeros(17, np.int32)
+        ids[k] = bad
+        with pytest.raises(pp.PPError) as e:
+            model.decode_step(kv, ids, h)
+        assert e.value.status == pp.PP_E_ID
+    assert kv.info()[0] == 0
+    with pytest.raises(pp.PPError) as e:
+        model.decode_step(kv, np.zeros(17, np.int32), h, logits_out=h)   # no text head
+    assert e.value.status == pp.PP_E_ARG
+
+
+# ----------------------------------------------------------------------------- gather
+
+@pytest.mark.parametrize("cfg_name", ["tiny", "full"])
+def test_embed_sum_bit_exact(cfg_name):
+    import torch
+    cfg = synth.TINY_TEMPORAL if cfg_name == "tiny" else synth.with_(synth.FULL_TEMPORAL, n_layers=1)
+    W = synth.temporal_weights(cfg, 11, "bf16", with_text_head=False)
+    dW = to_device(W)
+    model = pp.TemporalModel(cfg, dW, "bf16", max_prefill_T=64)
+    ids = synth.stream_ids(cfg, 64, 12)
+    ids[3] = -1                       # a frame with no input at all -> exact zeros
+    ids[5, :] = [32000] + [2048] * 16  # the initial IDs are valid rows
+    x = torch.empty((64, cfg["d_model"]), device="cuda")
+    model.embed_sum(ids, x)
+    x1 = torch.empty((cfg["d_model"],), device="cuda")
+    model.embed_sum(ids[7], x1)       # single-frame path (IDs as kernel arguments)
+    torch.cuda.synchronize()
+    got = x.cpu().numpy()
+    for t in range(64):
+        want = O.embed(ids[t], W, cfg, precision="f32")
+        assert np.array_equal(got[t], want), t
+    assert np.all(got[3] == 0)
+    assert np.array_equal(x1.cpu().numpy(), got[7])
+    bad = ids.copy()
+    bad[10, 4] = -2
+    with pytest.raises(pp.PPError) as e:
+        model.embed_sum(bad, x)
+    assert e.value.status == pp.PP_E_ID
+
+
+# ----------------------------------------------------------------------------- one full block
+
+def _full_block_case(n_prefill, seed_w=2, seed_kv=3, seed_ids=4, n_layers=1):
+    import torch
+    cfg = synth.with_(synth.FULL_TEMPORAL, n_layers=n_layers)
+    W = synth.temporal_weights(cfg, seed_w, "bf16", with_text_head=True, shared_layer=n_layers > 1)
+    model, _ = _model(cfg, W, "bf16")
+    kv = model.kv_alloc()
+    frames = synth.cache_frames(cfg, n_prefill, seed_kv)      # [L, 2, 1, H, n, dh] bf16 bits
+    src = torch.from_numpy(frames.view(np.int16)).cuda()
+    kv.load(src, n_prefill)
+    ids = synth.stream_ids(cfg, 2, seed_ids)
+    return cfg, W, model, kv, frames, ids
+
+
+def _oracle_cache(cfg, frames):
+    n = frames.shape[4]
+    ks = [frames[l, 0, 0].transpose(1, 0, 2) for l in range(cfg["n_layers"])]
+    vs = [frames[l, 1, 0].transpose(1, 0, 2) for l in range(cfg["n_layers"])]
+    return O.cache_from_blocks(ks, vs, np.arange(n), cfg["n_layers"])
+
+
+def test_full_width_block_decode_bf16():
+    """One 4096-wide block, ring pre-filled with 200 frames, new frame at position 200."""
+    import torch
+    cfg, W, model, kv, frames, ids = _full_block_case(200)
+    C, H, dh = cfg["context"], cfg["n_heads"], cfg["d_head"]
+    before = torch.empty(kv.info()[1] // 2, dtype=torch.int16, device="cuda")
+    kv.store(before)
+    h = torch.empty(cfg["d_model"], device="cuda")
+    lg = torch.empty(cfg["text_vocab"] - 1, device="cuda")
+    model.decode_step(kv, ids[0], h, lg)
+    after = torch.empty_like(before)
+    kv.store(after)
+    torch.cuda.synchronize()
+
+    cache = _oracle_cache(cfg, frames)
+    x = O.decode_step(O.embed(ids[0], W, cfg), 200, cache, W, cfg)
+    want_h, want_lg = O.final(x, W, cfg, with_logits=True)
+    eh, el = norm_max_err(h.cpu().numpy(), want_h), norm_max_err(lg.cpu().numpy(), want_lg)
+    print("full block bf16: h err %.3g, logits err %.3g" % (eh, el))
+    assert eh <= BF16_TOL and el <= BF16_TOL
+
+    b = before.cpu().numpy().view(np.uint16).reshape(1, 2, 1, H, C, dh)
+    a = after.cpu().numpy().view(np.uint16).reshape(1, 2, 1, H, C, dh)
+    changed = np.any(a != b, axis=-1)                    # [1, 2, 1, H, C]
+    assert changed[..., 200].all()
+    changed[..., 200] = False
+    assert not changed.any()                             # only slot 200 was written
+    _, k_new, v_new = cache.layers[0][-1]
+    kk = O.f64(a[0, 0, 0, :, 200])
+    vv = O.f64(a[0, 1, 0, :, 200])
+    assert norm_max_err(kk, k_new[0]) <= BF16_TOL
+    assert norm_max_err(vv, v_new[0]) <= BF16_TOL
+
+
+def test_two_runs_are_bit_identical():
+    import torch
+    cfg, W, model, kv, frames, ids = _full_block_case(200)
+    h1 = torch.empty(cfg["d_model"], device="cuda")
+    h2 = torch.empty_like(h1)
+    model.decode_step(kv, ids[0], h1)
+    src = torch.from_numpy(frames.view(np.int16)).cuda()
+    kv.load(src, 200)
+    model.decode_step(kv, ids[0], h2)
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2)
