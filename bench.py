@@ -75,6 +75,62 @@ def make_device_weights(cfg, seed):
     return W
 
 
+def depth_frame_bytes(dc):
+    """Algorithmic bytes of one depth frame: every per-step weight slice once (in_proj,
+    QKV/O slices, FFN pair, head) plus one embedding row per position (bf16)."""
+    D, F, S, L = dc["d_model"], dc["d_ff"], dc["n_steps"], dc["n_layers"]
+    per_step = D * dc["d_temporal"] + L * (3 * D * D + D * D + 2 * F * D + D * F) + dc["n_out"] * D + D
+    return S * per_step * 2
+
+
+def bench_depformer(steps, warmup):
+    """Depth transformer frames (16 positions, greedy selection) at full size, bf16."""
+    import torch
+    from personaplex_temporal_transformer_amd import pp, synth
+    dc = dict(synth.FULL_DEPTH)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    D, F, S, L = dc["d_model"], dc["d_ff"], dc["n_steps"], dc["n_layers"]
+
+    def mat(r, c):
+        return (0.02 * torch.randn((r, c), generator=g, device="cuda")).to(torch.bfloat16)
+
+    W = {"depformer_text_emb.weight": mat(dc["text_vocab"], D)}
+    for q in range(S):
+        W["depformer_in.%d.weight" % q] = mat(D, dc["d_temporal"])
+        W["linears.%d.weight" % q] = mat(dc["n_out"], D)
+        if q < S - 1:
+            W["depformer_emb.%d.weight" % q] = mat(dc["audio_vocab"], D)
+    for m in range(L):
+        p = "depformer.layers.%d." % m
+        W[p + "self_attn.in_proj_weight"] = mat(S * 3 * D, D)
+        W[p + "self_attn.out_proj.weight"] = mat(S * D, D)
+        for q in range(S):
+            W[p + "gating.%d.linear_in.weight" % q] = mat(2 * F, D)
+            W[p + "gating.%d.linear_out.weight" % q] = mat(D, F)
+        W[p + "norm1.alpha"] = 1.0 + 0.02 * torch.randn(D, generator=g, device="cuda")
+        W[p + "norm2.alpha"] = 1.0 + 0.02 * torch.randn(D, generator=g, device="cuda")
+    d = pp.Depformer(dc, W, "bf16")
+    h = torch.randn(dc["d_temporal"], generator=g, device="cuda")
+    codes = torch.empty(S, dtype=torch.int32, device="cuda")
+    for i in range(warmup):
+        d.step(h, i % 32000, codes)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(steps):
+        d.step(h, (7 * i) % 32000, codes)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    nb = depth_frame_bytes(dc)
+    d.close()
+    del W
+    return {"ms_per_frame": round(ms, 4), "frame_bytes": nb, "achieved_GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "steps": steps,
+            "workload": "depth transformer, 16 positions greedy, 6 layers x 1024, window 8, bf16"}
+
+
 def fill_ring(kv, cfg, seed):
     import torch
     g = torch.Generator(device="cuda")
@@ -129,6 +185,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", type=int, default=-1, help="1: HIP graph replay, 0: direct launches, -1: auto")
     ap.add_argument("--trace-layer", type=int, default=16)
+    ap.add_argument("--no-depformer", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -213,6 +270,12 @@ def main():
         "launch_probe_ms": {("graph" if k else "direct"): round(v, 4) for k, v in probe.items()},
         "final_position": pos,
     }
+    if not args.no_depformer:
+        model.close()
+        kv.close()
+        del W
+        torch.cuda.empty_cache()
+        out["depformer"] = bench_depformer(max(10, args.steps // 2), 3)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(out), flush=True)

@@ -204,6 +204,9 @@ pp_status pp_depformer_step(pp_depformer* d, const float* h_dev, const int32_t* 
                             const int32_t* forced_host, int32_t batch, int32_t* codes_dev,
                             float* logits_dev, void* stream);
 
+/* Depth-step launch mode: 0 = launch each kernel, 1 = replay a captured HIP graph (default). */
+pp_status pp_depformer_set_graph(pp_depformer* d, int32_t enable);
+
 /* ------------------------------------------------------------------ diagnostics */
 
 /* Message of the last error on the calling thread ("" if none). */

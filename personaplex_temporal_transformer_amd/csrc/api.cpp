@@ -57,6 +57,7 @@ static pp_status validate_temporal_config(const pp_temporal_config* c) {
   if (c->n_heads * c->d_head != c->d_model) return pp_fail(PP_E_ARG, "d_model != n_heads * d_head");
   if (c->d_model % 8 || c->d_ff % 8) return pp_fail(PP_E_ARG, "d_model and d_ff must be multiples of 8");
   if (c->d_model > 16384 || c->d_ff > 16384) return pp_fail(PP_E_ARG, "d_model/d_ff above 16384 unsupported");
+  if (c->context > 64 * 2048) return pp_fail(PP_E_ARG, "context above 131072 unsupported");
   if (c->n_audio < 0 || c->n_audio + 1 > kMaxStreams) return pp_fail(PP_E_ARG, "n_audio out of range");
   if (c->text_vocab < 2 || c->audio_vocab < 1) return pp_fail(PP_E_ARG, "vocab sizes must be positive");
   if (!(c->rope_theta > 0) || !(c->eps >= 0)) return pp_fail(PP_E_ARG, "rope_theta must be > 0, eps >= 0");
@@ -103,16 +104,17 @@ extern "C" pp_status pp_temporal_create(const pp_temporal_config* cfg, const pp_
   m->max_batch = max_batch;
   m->max_T = max_prefill_T;
   m->use_graph = env_int("PP_GRAPH", 1) != 0;
-  m->gemv_waves = env_int("PP_GEMV_WAVES_PER_CU", 8) * n_cu;
+  m->gemv_blocks = env_int("PP_GEMV_BLOCKS_PER_CU", 1) * n_cu;
 
   const int D = cfg->d_model, F = cfg->d_ff, H = cfg->n_heads, dh = cfg->d_head;
-  // attention splits: >= 2 blocks per CU over all heads, <= 2048 keys per block
-  int S = (2 * n_cu + H - 1) / H;
+  // attention splits: about one block per CU over all heads, <= 2048 keys per block
+  int S = (n_cu + H - 1) / H;
   if (S > 64) S = 64;
   const int min_s = (cfg->context + 2047) / 2048;
   if (S < min_s) S = min_s;
   if (S < 1) S = 1;
   m->S = env_int("PP_ATTN_SPLITS", S);
+  if (m->S > 64) m->S = 64;
   if (m->S < min_s) m->S = min_s;
 
   st = m->alloc_decode(D, F, H, dh);
@@ -130,7 +132,8 @@ pp_status pp_model::alloc_decode(int D, int F, int H, int dh) {
   auto take = [&](size_t n) { size_t off = bytes; bytes += (n + 255) / 256 * 256; return off; };
   const size_t ox = take(sizeof(float) * D), oq = take(sizeof(float) * D), oo = take(sizeof(float) * D);
   const size_t os = take(sizeof(float) * F), op = take(sizeof(float) * (size_t)H * S * (dh + 2));
-  const size_t oc = take(sizeof(int) * H), ost = take(sizeof(long long) * 4);
+  const size_t ost = take(sizeof(long long) * 4);
+  const size_t orp = take(sizeof(float) * dh);
   if (hipMalloc(&ws, bytes) != hipSuccess) return pp_fail(PP_E_HIP, "hipMalloc of decode workspace failed");
   if (hipMemset(ws, 0, bytes) != hipSuccess) return pp_fail(PP_E_HIP, "hipMemset of decode workspace failed");
   char* b = static_cast<char*>(ws);
@@ -139,8 +142,8 @@ pp_status pp_model::alloc_decode(int D, int F, int H, int dh) {
   o = reinterpret_cast<float*>(b + oo);
   s = reinterpret_cast<float*>(b + os);
   part = reinterpret_cast<float*>(b + op);
-  counters = reinterpret_cast<int*>(b + oc);
   state = reinterpret_cast<long long*>(b + ost);
+  rope = reinterpret_cast<float*>(b + orp);
   return PP_OK;
 }
 
@@ -316,28 +319,28 @@ hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced) {
 
     GemvArgs g{};
     g.W = w_qkv[l]; g.x = x; g.alpha = norm1[l]; g.eps = (float)c.eps; g.K = D;
-    g.n_groups = 3 * D / 4; g.out = q; g.D = D; g.dh = dh; g.C = C; g.kc = kbase; g.vc = vbase;
-    g.state = state; g.log_theta = std::log(c.rope_theta);
-    e = launch_gemv(PRO_RMSNORM, EPI_QKV, bf16, 4, g, gemv_waves, s);
+    g.n_groups = 3 * D / 2; g.out = q; g.D = D; g.dh = dh; g.C = C; g.kc = kbase; g.vc = vbase;
+    g.state = state; g.rope = rope;
+    e = launch_gemv(PRO_RMSNORM, EPI_QKV, bf16, 2, g, gemv_blocks, s);
     if (e != hipSuccess) break;
 
     AttnDecodeArgs at{};
     at.q = q; at.k = kbase; at.v = vbase; at.state = state; at.C = C; at.H = H; at.S = S;
-    at.scale = 1.0f / std::sqrt((float)dh); at.part = part; at.counters = counters; at.out = o;
+    at.scale = 1.0f / std::sqrt((float)dh); at.part = part; at.out = o;
     e = launch_attn_decode(at, bf16, dh, s);
     if (e != hipSuccess) break;
 
     GemvArgs go{};
     go.W = w_o[l]; go.x = o; go.K = D; go.n_groups = D / 2; go.out = x;
-    e = launch_gemv(PRO_COPY, EPI_RESID, bf16, 2, go, gemv_waves, s);
+    e = launch_gemv(PRO_COPY, EPI_RESID, bf16, 2, go, gemv_blocks, s);
     if (e != hipSuccess) break;
 
     const bool tr = traced && l == trace_layer && trace_used + 2 <= trace_ev.size();
     if (tr) (void)hipEventRecord(trace_ev[trace_used], s);
     GemvArgs gi{};
     gi.W = w_in[l]; gi.x = x; gi.alpha = norm2[l]; gi.eps = (float)c.eps; gi.K = D;
-    gi.n_groups = F / 2; gi.out = this->s; gi.F = F;
-    e = launch_gemv(PRO_RMSNORM, EPI_SWIGLU, bf16, 4, gi, gemv_waves, s);
+    gi.n_groups = F; gi.out = this->s; gi.F = F;
+    e = launch_gemv(PRO_RMSNORM, EPI_SWIGLU, bf16, 2, gi, gemv_blocks, s);
     if (tr) {
       (void)hipEventRecord(trace_ev[trace_used + 1], s);
       trace_used += 2;
@@ -346,7 +349,7 @@ hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced) {
 
     GemvArgs gw{};
     gw.W = w_out[l]; gw.x = this->s; gw.K = F; gw.n_groups = D / 2; gw.out = x;
-    e = launch_gemv(PRO_COPY, EPI_RESID, bf16, 2, gw, gemv_waves, s);
+    e = launch_gemv(PRO_COPY, EPI_RESID, bf16, 2, gw, gemv_blocks, s);
   }
   return e;
 }
@@ -399,6 +402,9 @@ extern "C" pp_status pp_temporal_decode_step(pp_model* m, pp_kv* kv, const int32
   a.rows = 1;
   a.state = m->state;
   a.pos = kv->pos;
+  a.rope = m->rope;
+  a.dh = c.d_head;
+  a.log_theta = std::log(c.rope_theta);
   hipError_t e = launch_embed(a, m->bf16, s);
   if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("embed: ") + hipGetErrorString(e));
 
@@ -410,7 +416,7 @@ extern "C" pp_status pp_temporal_decode_step(pp_model* m, pp_kv* kv, const int32
     g.W = m->text_head; g.x = m->x; g.alpha = m->out_norm; g.eps = (float)c.eps; g.K = c.d_model;
     g.n_groups = (c.text_vocab - 1) / 2; g.out = text_logits_dev;
     if ((c.text_vocab - 1) % 2 == 0) {
-      e = launch_gemv(PRO_RMSNORM, EPI_STORE, m->bf16, 2, g, m->gemv_waves, s);
+      e = launch_gemv(PRO_RMSNORM, EPI_STORE, m->bf16, 2, g, m->gemv_blocks, s);
     } else {
       return pp_fail(PP_E_ARG, "text head rows must be even");
     }

@@ -9,16 +9,18 @@
 //
 // Split-K over keys: block (s, h) handles an equal share of head h's keys, so
 // H x S blocks stream the K and V bytes once, 16 bytes per lane, with a chunk of keys per
-// load batch in flight. Each block keeps its scores in LDS, forms float32 partial
-// (o, max, sum); the last block to finish a head (a device-scope counter) merges the S
-// partials in split order -- a fixed order, so results are bit-reproducible -- and
-// resets the counter.
+// load batch in flight. Each block keeps its scores in LDS and forms a float32 partial
+// (o, max, sum). The S partials of a head are merged in split order -- a fixed order, so
+// results are bit-reproducible -- by a small combine kernel. (Merging inside the split
+// kernel by the last block to finish needs device-scope release/acquire fences, which on
+// this multi-XCD part write back and invalidate L2 and measured slower.)
 #include "device.h"
 #include "internal.h"
 
 namespace pp {
 
 constexpr int kMaxChunk = 2048;   // keys per block (host keeps ceil(C / S) <= this)
+constexpr int kMaxSplits = 64;
 
 template <typename KT, int DH>
 __global__ __launch_bounds__(kBlock) void k_attn_decode(AttnDecodeArgs a) {
@@ -29,7 +31,6 @@ __global__ __launch_bounds__(kBlock) void k_attn_decode(AttnDecodeArgs a) {
   __shared__ float sc[kMaxChunk];
   __shared__ float red[4];
   __shared__ float osum[KPP][DH + 1];
-  __shared__ int last;
 
   const int s = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int sub = tid % LPK, kg = tid / LPK;
@@ -120,28 +121,30 @@ __global__ __launch_bounds__(kBlock) void k_attn_decode(AttnDecodeArgs a) {
     part[DH + 1] = l;
   }
 
-  // ---- the last block of head h merges the S partials
-  __threadfence();
+}
+
+// Merge the S partials (o_s, m_s, l_s) of head h in split order:
+// o = sum_s exp(m_s - M) o_s / sum_s exp(m_s - M) l_s with M = max_s m_s.
+// All partials of the head are first loaded into LDS in one parallel round.
+template <int DH>
+__global__ __launch_bounds__(kBlock) void k_attn_combine(AttnDecodeArgs a) {
+  __shared__ float pp[kMaxSplits * (DH + 2)];
+  const int h = blockIdx.x, t = threadIdx.x;
+  const float* ph = a.part + (size_t)h * a.S * (DH + 2);
+  for (int i = t; i < a.S * (DH + 2); i += kBlock) pp[i] = ph[i];
   __syncthreads();
-  if (tid == 0) last = (atomicAdd(&a.counters[h], 1) == a.S - 1);
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  if (tid < DH) {
-    const float* ph = a.part + (size_t)h * a.S * (DH + 2);
-    float M = -INFINITY;
-    for (int i = 0; i < a.S; ++i) M = fmaxf(M, __builtin_nontemporal_load(ph + i * (DH + 2) + DH));
-    float L = 0.f, o = 0.f;
-    for (int i = 0; i < a.S; ++i) {
-      const float mi = __builtin_nontemporal_load(ph + i * (DH + 2) + DH);
-      if (mi == -INFINITY) continue;
-      const float w = expf(mi - M);
-      L += w * __builtin_nontemporal_load(ph + i * (DH + 2) + DH + 1);
-      o += w * __builtin_nontemporal_load(ph + i * (DH + 2) + tid);
-    }
-    a.out[h * DH + tid] = o / L;
+  if (t >= DH) return;
+  float M = -INFINITY;
+  for (int i = 0; i < a.S; ++i) M = fmaxf(M, pp[i * (DH + 2) + DH]);
+  float L = 0.f, o = 0.f;
+  for (int i = 0; i < a.S; ++i) {
+    const float mi = pp[i * (DH + 2) + DH];
+    if (mi == -INFINITY) continue;  // empty split
+    const float w = expf(mi - M);
+    L += w * pp[i * (DH + 2) + DH + 1];
+    o += w * pp[i * (DH + 2) + t];
   }
-  if (tid == 0) a.counters[h] = 0;
+  a.out[h * DH + t] = o / L;
 }
 
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, bool bf16, int dh, hipStream_t s) {
@@ -151,6 +154,10 @@ hipError_t launch_attn_decode(const AttnDecodeArgs& a, bool bf16, int dh, hipStr
   else if (!bf16 && dh == 128) hipLaunchKernelGGL((k_attn_decode<float, 128>), grid, block, 0, s, a);
   else if (!bf16 && dh == 64) hipLaunchKernelGGL((k_attn_decode<float, 64>), grid, block, 0, s, a);
   else return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (dh == 128) hipLaunchKernelGGL((k_attn_combine<128>), dim3(a.H), dim3(kBlock), 0, s, a);
+  else hipLaunchKernelGGL((k_attn_combine<64>), dim3(a.H), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 

@@ -16,7 +16,17 @@ template <typename WT>
 __global__ __launch_bounds__(kBlock) void k_embed_sum(EmbedArgs a) {
   const int row = blockIdx.y;
   const int d = (blockIdx.x * kBlock + threadIdx.x) * 4;
-  if (a.state && row == 0 && blockIdx.x == 0 && threadIdx.x == 0) a.state[0] = a.pos;
+  if (a.state && row == 0 && blockIdx.x == 0) {
+    if (threadIdx.x == 0) a.state[0] = a.pos;
+    if (a.rope && threadIdx.x < a.dh / 2) {
+      const int j = threadIdx.x;
+      const double ang = (double)a.pos * exp(-a.log_theta * (double)(2 * j) / (double)a.dh);
+      double sn, cs;
+      sincos(ang, &sn, &cs);
+      a.rope[2 * j] = (float)cs;
+      a.rope[2 * j + 1] = (float)sn;
+    }
+  }
   if (d >= a.D) return;
   float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
   for (int k = 0; k < a.n_streams; ++k) {

@@ -18,11 +18,20 @@ struct EmbedArgs {
   long long* state;                 // if non-null, state[0] := pos (decode position)
   long long pos;
   int n_streams, D, rows;
+  // RoPE table of this position (decode): rope[2j] = cos(pos * omega_j),
+  // rope[2j+1] = sin(pos * omega_j), omega_j = theta^(-2j/d_head), angles in float64
+  float* rope;
+  int dh;
+  double log_theta;
 };
 hipError_t launch_embed(const EmbedArgs& a, bool bf16, hipStream_t s);
 
 // ---------------------------------------------------------------- GEMV family (decode)
-enum GemvPro { PRO_COPY = 0, PRO_RMSNORM = 1 };
+enum GemvPro {
+  PRO_COPY = 0,        // x as given
+  PRO_RMSNORM = 1,     // alpha * x / sqrt(mean(x^2) + eps)
+  PRO_DEPTH_ATTN = 2,  // x = depth attention output computed from q and the depth cache
+};
 enum GemvEpi {
   EPI_STORE = 0,   // out[row] = W x
   EPI_RESID = 1,   // out[row] += W x                       (residual stream, fp32)
@@ -44,16 +53,27 @@ struct GemvArgs {
   void* kc;             // K ring of this layer, batch 0: [H][C][dh]   (depth: [H][C][dh] fp32)
   void* vc;
   const long long* state;  // state[0] = position of this frame (slot = pos mod C)
-  double log_theta;
+  const float* rope;       // [dh] cos/sin pairs of this frame's position
   int slot_override;    // depth: >= 0 gives the cache row directly
   // EPI_SWIGLU
   int F;
-  // a second bias-like input added to the output (depth: embedding row), or null
+  // a second input added to the output (EPI_STORE), or null
   const float* add;
+  // rows spread over several matrices: row r is row (r % rows_per_mat) of mats[r / rows_per_mat]
+  // (rows_per_mat = 0: one matrix W)
+  const void* mats[32];
+  int rows_per_mat;
+  // PRO_DEPTH_ATTN: position aq_pos of this frame's depth loop attends to the depth
+  // positions p with 0 <= aq_pos - p < awin; cache [aH][acap][adh] float32
+  const float* aq;
+  const float* ak;
+  const float* av;
+  int aH, adh, acap, aq_pos, awin;
+  float ascale;
 };
-// rows_per_group: 2 or 4; waves: total waves of the launch (0 = choose).
+// rows_per_group: 2 or 4; blocks: workgroups of 8 waves (normally one per CU).
 hipError_t launch_gemv(int pro, int epi, bool bf16, int rows_per_group, const GemvArgs& a,
-                       int waves, hipStream_t s);
+                       int blocks, hipStream_t s);
 
 // ---------------------------------------------------------------- attention (decode)
 struct AttnDecodeArgs {
@@ -64,7 +84,6 @@ struct AttnDecodeArgs {
   int C, H, S;          // S = splits of the key range per head
   float scale;
   float* part;          // [H][S][dh + 2] partial (o, m, l)
-  int* counters;        // [H], zero outside a launch
   float* out;           // [H * dh]
 };
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, bool bf16, int dh, hipStream_t s);
@@ -73,4 +92,30 @@ hipError_t launch_attn_decode(const AttnDecodeArgs& a, bool bf16, int dh, hipStr
 hipError_t launch_rmsnorm_rows(const float* x, const float* alpha, float eps, int D, int rows,
                                float* out_f32, void* out_bf16, hipStream_t s);
 
+}  // namespace pp
+
+namespace pp {
+// ---------------------------------------------------------------- depth transformer
+struct DepthSetupArgs {
+  const float* h_src;   // caller's temporal hidden [d_temporal]
+  float* h_dst;         // library copy
+  int d_temporal;
+  int32_t* ctrl;        // [0] = text token, [1 + q] = forced code of position q (-1: select)
+  int32_t text_token;
+  int32_t forced[32];
+  int n_steps;
+};
+hipError_t launch_depth_setup(const DepthSetupArgs& a, hipStream_t s);
+
+struct DepthSelectArgs {
+  const float* c_all;        // [n_steps][D] temporal-to-depth projections
+  const void* text_emb;      // [text_vocab][D]
+  const void* audio_emb[32]; // position q > 0 reads table q-1
+  const int32_t* ctrl;
+  const float* logits;       // [n_steps][n_out]
+  int32_t* codes;            // [n_steps]
+  float* z;                  // [D] residual of position q
+  int q, D, n_out, n_steps;
+};
+hipError_t launch_depth_select(const DepthSelectArgs& a, bool bf16, hipStream_t s);
 }  // namespace pp

@@ -36,10 +36,10 @@ struct pp_model {
   float* o = nullptr;        // attention output [D]
   float* s = nullptr;        // SiLU(g) * z [F]
   float* part = nullptr;     // attention partials [H][S][dh + 2]
-  int* counters = nullptr;   // [H]
   long long* state = nullptr;  // [0] = position of the frame being decoded
+  float* rope = nullptr;       // [dh] cos/sin table of that position
   int S = 16;                // attention splits per head
-  int gemv_waves = 2048;     // waves per GEMV launch
+  int gemv_blocks = 256;     // workgroups per GEMV launch (one per CU)
 
   // prefill workspace (one hipMalloc, sized by max_T)
   void* pws = nullptr;

@@ -22,7 +22,8 @@ STATUS_NAMES = {0: "PP_OK", 1: "PP_E_ARG", 2: "PP_E_ID", 3: "PP_E_CAPACITY", 4: 
 EXPORTS = ["pp_temporal_create", "pp_temporal_destroy", "pp_kv_alloc", "pp_kv_free", "pp_kv_reset",
            "pp_kv_info", "pp_kv_load", "pp_kv_store", "pp_embed_sum", "pp_temporal_decode_step",
            "pp_temporal_prefill", "pp_depformer_create", "pp_depformer_destroy", "pp_depformer_step",
-           "pp_last_error", "pp_temporal_set_graph", "pp_temporal_trace", "pp_temporal_trace_read"]
+           "pp_last_error", "pp_temporal_set_graph", "pp_temporal_trace", "pp_temporal_trace_read",
+           "pp_depformer_set_graph"]
 
 
 class PPError(RuntimeError):
@@ -91,6 +92,7 @@ def load():
         "pp_depformer_destroy": [VP],
         "pp_depformer_step": [VP, VP, P(I32), P(I32), I32, VP, VP, VP],
         "pp_temporal_set_graph": [VP, I32],
+        "pp_depformer_set_graph": [VP, I32],
         "pp_temporal_trace": [VP, I32],
         "pp_temporal_trace_read": [VP, P(I64), P(ctypes.c_double)],
     }
@@ -292,6 +294,9 @@ class Depformer:
             self.close()
         except Exception:
             pass
+
+    def set_graph(self, enable):
+        _check(load().pp_depformer_set_graph(self.handle, 1 if enable else 0))
 
     def step(self, h, text_token, codes_out, forced=None, logits_out=None, stream=None):
         tt, tp = _ids(np.atleast_1d(np.asarray(text_token, np.int32)))

@@ -1,0 +1,105 @@
+"""GPU parity of the depth transformer step against the oracle, through the C ABI.
+Forced codes make every position's input fixed, so logits compare element by element;
+greedy selection is checked as a valid argmax of the oracle's logits under the same
+choices (ties and near-ties may legitimately resolve either way)."""
+
+import numpy as np
+import pytest
+
+from oracle import depformer as DF
+from personaplex_temporal_transformer_amd import pp, synth
+from tests.helpers import max_abs_err, norm_max_err, require_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+FP32_TOL = 1e-4
+BF16_TOL = 2e-2
+
+
+def _run(cfg, W, wdtype, h, text_token, forced, graph=True):
+    import torch
+    require_gpu()
+    dW = to_device(W)
+    d = pp.Depformer(cfg, dW, wdtype)
+    d.set_graph(graph)
+    hd = torch.from_numpy(h.astype(np.float32)).cuda()
+    codes = torch.empty(cfg["n_steps"], dtype=torch.int32, device="cuda")
+    logits = torch.empty((cfg["n_steps"], cfg["n_out"]), device="cuda")
+    d.step(hd, text_token, codes, forced=forced, logits_out=logits)
+    torch.cuda.synchronize()
+    return d, codes.cpu().numpy(), logits.cpu().numpy()
+
+
+@pytest.mark.parametrize("window", [8, 16, 3])
+@pytest.mark.parametrize("graph", [True, False])
+def test_tiny_fp32_forced(window, graph):
+    cfg = synth.with_(synth.TINY_DEPTH, window=window)
+    W = synth.depth_weights(cfg, 0, "fp32")
+    h = synth.hidden(cfg["d_temporal"], 1)
+    forced = synth.depth_codes(cfg, 2)
+    _, codes, logits = _run(cfg, W, "fp32", h, 31999, forced, graph)
+    want_codes, want = DF.step_logits(h, 31999, forced, W, cfg)
+    err = max_abs_err(logits, want)
+    print("tiny depth fp32 window=%d graph=%s: logits err %.3g" % (window, graph, err))
+    assert np.array_equal(codes, forced)
+    assert err <= FP32_TOL
+
+
+def test_tiny_fp32_greedy_is_a_valid_argmax():
+    cfg = synth.TINY_DEPTH
+    W = synth.depth_weights(cfg, 3, "fp32")
+    h = synth.hidden(cfg["d_temporal"], 4)
+    _, codes, logits = _run(cfg, W, "fp32", h, 17, None)
+    _, want = DF.step_logits(h, 17, codes, W, cfg)   # oracle under the GPU's own choices
+    assert max_abs_err(logits, want) <= FP32_TOL
+    for q in range(cfg["n_steps"]):
+        assert want[q][codes[q]] >= np.max(want[q]) - 2 * FP32_TOL, q
+    # partially forced: forced positions keep their code, the rest select
+    forced = np.full(cfg["n_steps"], -1, np.int32)
+    forced[8:] = synth.depth_codes(cfg, 5)[8:]
+    _, codes2, logits2 = _run(cfg, W, "fp32", h, 17, forced)
+    assert np.array_equal(codes2[8:], forced[8:])
+    assert np.array_equal(codes2[:8], codes[:8])
+
+
+def test_windows_agree_before_they_bind():
+    cfg = synth.TINY_DEPTH
+    W = synth.depth_weights(cfg, 6, "fp32")
+    h = synth.hidden(cfg["d_temporal"], 7)
+    forced = synth.depth_codes(cfg, 8)
+    _, _, l8 = _run(cfg, W, "fp32", h, 5, forced)
+    _, _, l16 = _run(synth.with_(cfg, window=16), W, "fp32", h, 5, forced)
+    assert np.array_equal(l8[:8], l16[:8])
+
+
+def test_invalid_tokens_rejected():
+    import torch
+    cfg = synth.TINY_DEPTH
+    W = synth.depth_weights(cfg, 0, "fp32")
+    require_gpu()
+    d = pp.Depformer(cfg, to_device(W), "fp32")
+    hd = torch.zeros(cfg["d_temporal"], device="cuda")
+    codes = torch.empty(cfg["n_steps"], dtype=torch.int32, device="cuda")
+    for tok in (-1, 32001):
+        with pytest.raises(pp.PPError) as e:
+            d.step(hd, tok, codes)
+        assert e.value.status == pp.PP_E_ID
+    bad = np.full(cfg["n_steps"], -1, np.int32)
+    bad[4] = 2048
+    with pytest.raises(pp.PPError) as e:
+        d.step(hd, 0, codes, forced=bad)
+    assert e.value.status == pp.PP_E_ID
+
+
+def test_full_depth_bf16_forced():
+    """Full-size depth transformer (1024 wide, 6 layers, 16 positions, window 8), bf16."""
+    cfg = synth.FULL_DEPTH
+    W = synth.depth_weights(cfg, 5, "bf16")
+    h = synth.hidden(cfg["d_temporal"], 6)
+    forced = synth.depth_codes(cfg, 7)
+    d, codes, logits = _run(cfg, W, "bf16", h, 1234, forced)
+    _, want = DF.step_logits(h, 1234, forced, W, cfg)
+    err = norm_max_err(logits, want)
+    print("full depth bf16: logits err %.3g" % err)
+    assert np.array_equal(codes, forced)
+    assert err <= BF16_TOL
