@@ -57,7 +57,6 @@ static pp_status validate_temporal_config(const pp_temporal_config* c) {
   if (c->n_heads * c->d_head != c->d_model) return pp_fail(PP_E_ARG, "d_model != n_heads * d_head");
   if (c->d_model % 8 || c->d_ff % 8) return pp_fail(PP_E_ARG, "d_model and d_ff must be multiples of 8");
   if (c->d_model > 16384 || c->d_ff > 16384) return pp_fail(PP_E_ARG, "d_model/d_ff above 16384 unsupported");
-  if (c->context > 64 * 2048) return pp_fail(PP_E_ARG, "context above 131072 unsupported");
   if (c->n_audio < 0 || c->n_audio + 1 > kMaxStreams) return pp_fail(PP_E_ARG, "n_audio out of range");
   if (c->text_vocab < 2 || c->audio_vocab < 1) return pp_fail(PP_E_ARG, "vocab sizes must be positive");
   if (!(c->rope_theta > 0) || !(c->eps >= 0)) return pp_fail(PP_E_ARG, "rope_theta must be > 0, eps >= 0");
@@ -107,15 +106,10 @@ extern "C" pp_status pp_temporal_create(const pp_temporal_config* cfg, const pp_
   m->gemv_blocks = env_int("PP_GEMV_BLOCKS_PER_CU", 1) * n_cu;
 
   const int D = cfg->d_model, F = cfg->d_ff, H = cfg->n_heads, dh = cfg->d_head;
-  // attention splits: about one block per CU over all heads, <= 2048 keys per block
+  // attention splits: about one block per CU over all heads (at most 64)
   int S = (n_cu + H - 1) / H;
-  if (S > 64) S = 64;
-  const int min_s = (cfg->context + 2047) / 2048;
-  if (S < min_s) S = min_s;
-  if (S < 1) S = 1;
-  m->S = env_int("PP_ATTN_SPLITS", S);
-  if (m->S > 64) m->S = 64;
-  if (m->S < min_s) m->S = min_s;
+  S = env_int("PP_ATTN_SPLITS", S);
+  m->S = S < 1 ? 1 : (S > 64 ? 64 : S);
 
   st = m->alloc_decode(D, F, H, dh);
   if (!st) st = m->alloc_prefill();
@@ -348,8 +342,8 @@ hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced) {
     if (e != hipSuccess) break;
 
     GemvArgs gw{};
-    gw.W = w_out[l]; gw.x = this->s; gw.K = F; gw.n_groups = D / 2; gw.out = x;
-    e = launch_gemv(PRO_COPY, EPI_RESID, bf16, 2, gw, gemv_blocks, s);
+    gw.W = w_out[l]; gw.x = this->s; gw.K = F; gw.n_groups = D; gw.out = x;
+    e = launch_gemv(PRO_COPY, EPI_RESID, bf16, 1, gw, gemv_blocks, s);
   }
   return e;
 }

@@ -7,10 +7,9 @@
 // position p written into slot p mod C first, the visible keys are exactly the slots
 // 0 .. min(p+1, C)-1 (softmax does not depend on the order of keys).
 //
-// Split-K over keys: block (s, h) handles an equal share of head h's keys, so
-// H x S blocks stream the K and V bytes once, 16 bytes per lane, with a chunk of keys per
-// load batch in flight. Each block keeps its scores in LDS and forms a float32 partial
-// (o, max, sum). The S partials of a head are merged in split order -- a fixed order, so
+// Split-K over keys: block (s, h) handles an equal share of head h's keys, so H x S
+// blocks stream the K and V bytes once, 16 bytes per lane, and each forms a float32
+// partial (o, max, sum). The S partials of a head are merged in split order -- a fixed order, so
 // results are bit-reproducible -- by a small combine kernel. (Merging inside the split
 // kernel by the last block to finish needs device-scope release/acquire fences, which on
 // this multi-XCD part write back and invalidate L2 and measured slower.)
@@ -19,18 +18,24 @@
 
 namespace pp {
 
-constexpr int kMaxChunk = 2048;   // keys per block (host keeps ceil(C / S) <= this)
 constexpr int kMaxSplits = 64;
 
+constexpr int kAttnThreads = 512;
+
+// Block (s, h): one pass over its keys with an online softmax. A group of LPK lanes owns
+// one key row per pass (16 bytes per lane); KPP groups cover KPP keys per pass and NB
+// passes form a round. The K and V rows of the next round are loaded while the current
+// round is scored and accumulated. Each group keeps a running max m, sum l and output
+// o (its lanes' EPC dimensions); the groups are merged through LDS at the end.
 template <typename KT, int DH>
-__global__ __launch_bounds__(kBlock) void k_attn_decode(AttnDecodeArgs a) {
+__global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnDecodeArgs a) {
   constexpr int EPC = Elem<KT>::kPerChunk;  // elements per 16-byte chunk
   constexpr int LPK = DH / EPC;             // lanes per key row
-  constexpr int KPP = kBlock / LPK;         // keys per block pass
-  constexpr int NB = 8;                     // passes batched per load round
-  __shared__ float sc[kMaxChunk];
-  __shared__ float red[4];
-  __shared__ float osum[KPP][DH + 1];
+  constexpr int KPP = kAttnThreads / LPK;   // keys per pass
+  constexpr int NB = 8;                     // passes per round
+  constexpr int RK = KPP * NB;              // keys per round
+  __shared__ float gm[KPP], gl[KPP];
+  __shared__ float go[KPP][DH + 1];
 
   const int s = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int sub = tid % LPK, kg = tid / LPK;
@@ -45,82 +50,90 @@ __global__ __launch_bounds__(kBlock) void k_attn_decode(AttnDecodeArgs a) {
   const KT* kb = static_cast<const KT*>(a.k) + ((size_t)h * a.C + j0) * DH + sub * EPC;
   const KT* vb = static_cast<const KT*>(a.v) + ((size_t)h * a.C + j0) * DH + sub * EPC;
 
-  // ---- scores
-  for (int jb = 0; jb < cnt; jb += KPP * NB) {
-    u32x4 c[NB];
+  float m = -INFINITY, l = 0.f, acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+
+  auto issue = [&](u32x4 (&ck)[NB], u32x4 (&cv)[NB], int jb) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int j = jb + b * KPP + kg;
-      c[b] = j < cnt ? load_stream(kb + (size_t)j * DH) : u32x4{0u, 0u, 0u, 0u};
+      ck[b] = j < cnt ? load_stream(kb + (size_t)j * DH) : u32x4{0u, 0u, 0u, 0u};
+      cv[b] = j < cnt ? load_stream(vb + (size_t)j * DH) : u32x4{0u, 0u, 0u, 0u};
     }
+  };
+  auto consume = [&](const u32x4 (&ck)[NB], const u32x4 (&cv)[NB], int jb) {
+    float sc[NB];
+    float mb = -INFINITY;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int j = jb + b * KPP + kg;
       float kf[EPC];
-      Elem<KT>::widen(c[b], kf);
+      Elem<KT>::widen(ck[b], kf);
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < EPC; ++e) d += qv[e] * kf[e];
       d = group_sum<LPK>(d);
-      if (sub == 0 && j < cnt) sc[j] = d;
+      sc[b] = (jb + b * KPP + kg) < cnt ? d : -INFINITY;
+      mb = fmaxf(mb, sc[b]);
     }
-  }
-  __syncthreads();
-
-  // ---- softmax statistics of this chunk
-  float mx = -INFINITY;
-  for (int j = tid; j < cnt; j += kBlock) mx = fmaxf(mx, sc[j]);
-  mx = wave_max(mx);
-  if ((tid & 63) == 0) red[tid >> 6] = mx;
-  __syncthreads();
-  const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  float ls = 0.f;
-  for (int j = tid; j < cnt; j += kBlock) {
-    const float p = expf(sc[j] - m);
-    sc[j] = p;
-    ls += p;
-  }
-  const float l = cnt > 0 ? block_sum_256(ls, red) : 0.f;   // barrier inside: sc is ready
-
-  // ---- P V
-  float acc[EPC];
+    if (mb == -INFINITY) return;  // no key of this group in this round
+    const float mn = fmaxf(m, mb);
+    const float scale = expf(m - mn);  // m = -inf -> 0
+    l *= scale;
 #pragma unroll
-  for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
-  for (int jb = 0; jb < cnt; jb += KPP * NB) {
-    u32x4 c[NB];
+    for (int e = 0; e < EPC; ++e) acc[e] *= scale;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int j = jb + b * KPP + kg;
-      c[b] = j < cnt ? load_stream(vb + (size_t)j * DH) : u32x4{0u, 0u, 0u, 0u};
+      const float p = expf(sc[b] - mn);  // -inf -> 0
+      l += p;
+      float vf[EPC];
+      Elem<KT>::widen(cv[b], vf);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[e] += p * vf[e];
     }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int j = jb + b * KPP + kg;
-      if (j < cnt) {
-        float vf[EPC];
-        Elem<KT>::widen(c[b], vf);
-        const float p = sc[j];
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[e] += p * vf[e];
-      }
+    m = mn;
+  };
+
+  u32x4 ka[NB], va[NB], kb2[NB], vb2[NB];
+  if (cnt > 0) {
+    issue(ka, va, 0);
+    for (int jb = 0;; jb += 2 * RK) {
+      if (jb + RK < cnt) issue(kb2, vb2, jb + RK);
+      consume(ka, va, jb);
+      if (jb + RK >= cnt) break;
+      if (jb + 2 * RK < cnt) issue(ka, va, jb + 2 * RK);
+      consume(kb2, vb2, jb + RK);
+      if (jb + 2 * RK >= cnt) break;
     }
   }
-#pragma unroll
-  for (int e = 0; e < EPC; ++e) osum[kg][sub * EPC + e] = acc[e];
-  __syncthreads();
 
+  // ---- merge the KPP groups of this block
+  if (sub == 0) {
+    gm[kg] = m;
+    gl[kg] = l;
+  }
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) go[kg][sub * EPC + e] = acc[e];
+  __syncthreads();
   float* part = a.part + ((size_t)h * a.S + s) * (DH + 2);
   if (tid < DH) {
-    float o = 0.f;
-    for (int g = 0; g < KPP; ++g) o += osum[g][tid];
+    float M = -INFINITY;
+    for (int g = 0; g < KPP; ++g) M = fmaxf(M, gm[g]);
+    float L = 0.f, o = 0.f;
+    if (M != -INFINITY) {
+      for (int g = 0; g < KPP; ++g) {
+        if (gm[g] == -INFINITY) continue;
+        const float w = expf(gm[g] - M);
+        L += w * gl[g];
+        o += w * go[g][tid];
+      }
+    }
     part[tid] = o;
+    if (tid == 0) {
+      part[DH] = M;
+      part[DH + 1] = L;
+    }
   }
-  if (tid == 0) {
-    part[DH] = cnt > 0 ? m : -INFINITY;
-    part[DH + 1] = l;
-  }
-
 }
 
 // Merge the S partials (o_s, m_s, l_s) of head h in split order:
@@ -148,7 +161,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(AttnDecodeArgs a) {
 }
 
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, bool bf16, int dh, hipStream_t s) {
-  const dim3 grid(a.S, a.H), block(kBlock);
+  const dim3 grid(a.S, a.H), block(kAttnThreads);
   if (bf16 && dh == 128) hipLaunchKernelGGL((k_attn_decode<bf16_t, 128>), grid, block, 0, s, a);
   else if (bf16 && dh == 64) hipLaunchKernelGGL((k_attn_decode<bf16_t, 64>), grid, block, 0, s, a);
   else if (!bf16 && dh == 128) hipLaunchKernelGGL((k_attn_decode<float, 128>), grid, block, 0, s, a);

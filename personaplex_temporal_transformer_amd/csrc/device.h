@@ -56,24 +56,48 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-// Butterfly sum over the 64 lanes of a wave; every lane gets the total. The order of
-// additions is fixed, so results are bit-reproducible.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+// DPP lane moves inside a row of 16 lanes (no LDS traffic).
+__device__ __forceinline__ float dpp_xor1(float v) {  // quad_perm [1,0,3,2]
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {  // quad_perm [2,3,0,1]
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_half_mirror(float v) {  // lane i <-> 7 - i within 8
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_mirror(float v) {  // lane i <-> 15 - i within 16
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of W lanes (W = 8, 16, 32 or 64); every lane of a group gets
+// the same bits: each step adds two partial sums that are already equal across the lanes
+// involved, and float addition is commutative. The order is fixed, so results are
+// reproducible run to run.
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(W == 8 || W == 16 || W == 32 || W == 64, "group width");
+  v += dpp_xor1(v);
+  v += dpp_xor2(v);
+  v += dpp_half_mirror(v);
+  if (W >= 16) v += dpp_mirror(v);
+  if (W >= 32) v += __shfl_xor(v, 16, kWave);
+  if (W >= 64) v += __shfl_xor(v, 32, kWave);
   return v;
 }
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
   return v;
 }
-// Sum over aligned groups of `width` lanes (width a power of two <= 64).
-template <int W>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int off = W / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+
+// Workgroup barrier for LDS communication only: waits for this wave's LDS operations,
+// not for its outstanding global loads (a full __syncthreads() also drains the global
+// load counter, which would stall prefetched weight streams). The memory clobber keeps
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Block-wide sum for 256-thread blocks; `scratch` holds >= 4 floats of shared memory.

@@ -35,7 +35,7 @@ __device__ __forceinline__ int row_of(const GemvArgs& a, int g, int r) {
 }
 
 template <typename WT, int RB, int EPI>
-__device__ __forceinline__ void epilogue(const GemvArgs& a, int g, const float (&acc)[RB]) {
+__device__ __forceinline__ void epilogue(const GemvArgs& a, int g, const float (&acc)[RB], const float (&res)[RB]) {
   if (EPI == EPI_STORE) {
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
@@ -44,7 +44,7 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, int g, const float (
     }
   } else if (EPI == EPI_RESID) {
 #pragma unroll
-    for (int r = 0; r < RB; ++r) a.out[g * RB + r] += acc[r];
+    for (int r = 0; r < RB; ++r) a.out[g * RB + r] = res[r] + acc[r];
   } else if (EPI == EPI_SWIGLU) {
     constexpr int P = RB / 2;
 #pragma unroll
@@ -130,20 +130,25 @@ __device__ void depth_attention(const GemvArgs& a, float* x, float* sc) {
 }
 
 constexpr int kGemvWaves = 8;                 // waves per GEMV workgroup
-constexpr int kGemvThreads = kGemvWaves * kWave;
 
 // Rows are processed in groups of RB rows; a lane streams 16-byte chunks c = p*64*U +
 // u*64 + lane (u < U) of each row in pass p, so a wave reads 1 KB contiguous per load.
-// Block b owns the contiguous groups [b*G/nb, (b+1)*G/nb) -- equal shares, so the grid
-// (one block per CU) is balanced -- and its waves pull groups from an LDS counter.
-// Loads are double-buffered: the next (group, pass) is in flight while the current one
-// is multiplied and reduced. ONEPASS (a row fits in one pass): each lane keeps its slice
+// Block b owns the contiguous groups [b*G/nb, (b+1)*G/nb) -- equal shares, so a grid of
+// one block per CU is balanced -- and wave w takes groups w, w+NW, w+2NW, ... of them.
+//
+// Latency hiding: x is loaded first, then the first item's weights, and x is staged in
+// LDS while those weights are in flight (global loads complete in order, and the LDS-only
+// barrier does not wait for them). In the loop, as soon as a buffer has been consumed
+// it is refilled with the item two steps ahead, so two items of weights are in flight.
+// ONEPASS (a row fits in one pass of U chunks per lane): each lane then keeps its slice
 // of x in registers; otherwise x is read from LDS per pass.
-template <typename WT, int RB, int U, bool ONEPASS, int PRO, int EPI>
-__global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
+// MM: rows come from the pointer table a.mats (several matrices, rows_per_mat each);
+// FULL: every pass covers whole chunks (K / chunk is a multiple of 64*U), no guards.
+template <typename WT, int RB, int U, bool ONEPASS, int PRO, int EPI, bool MM, bool FULL, int XR>
+__global__ __launch_bounds__(kGemvWaves * 64) void k_gemv(GemvArgs a) {
+  constexpr int NW = kGemvWaves, NT = NW * 64;
   extern __shared__ float xs[];
-  __shared__ float red[kGemvWaves];
-  __shared__ int qnext;
+  __shared__ float red[NW];
   constexpr int EPC = Elem<WT>::kPerChunk;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int K = a.K;
@@ -151,151 +156,210 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
   const int np = ONEPASS ? 1 : (nch + kWave * U - 1) / (kWave * U);
   const int gb0 = (int)((long long)blockIdx.x * a.n_groups / gridDim.x);
   const int gb1 = (int)((long long)(blockIdx.x + 1) * a.n_groups / gridDim.x);
-  if (tid == 0) qnext = gb0 + kGemvWaves;
 
-  // ---- prologue: x (float32) -> LDS, optionally RMS-normalised
-  if (PRO == PRO_DEPTH_ATTN) {
-    depth_attention(a, xs, xs + K);
-  } else {
-    float ss = 0.f;
-    for (int i = tid * 4; i < K; i += kGemvThreads * 4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(a.x + i);
-      *reinterpret_cast<f32x4*>(xs + i) = v;
-      if (PRO == PRO_RMSNORM) ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-    }
-    if (PRO == PRO_RMSNORM) {
-      ss = wave_sum(ss);
-      __syncthreads();
-      if (lane == 0) red[wid] = ss;
-      __syncthreads();
-      float tot = 0.f;
+  // ---- weights of one (group, pass) item; the residual rows of a group are read
+  // before its weights (EPI_RESID), so waiting for them never waits for later weights
+  auto issue = [&](u32x4 (&buf)[RB][U], float (&res)[RB], int gg, int pp) {
+    if (EPI == EPI_RESID && pp == 0) {
 #pragma unroll
-      for (int w = 0; w < kGemvWaves; ++w) tot += red[w];
-      const float r = 1.0f / sqrtf(tot / (float)K + a.eps);
-      for (int i = tid * 4; i < K; i += kGemvThreads * 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(xs + i);
-        const f32x4 al = *reinterpret_cast<const f32x4*>(a.alpha + i);
-        *reinterpret_cast<f32x4*>(xs + i) = (v * r) * al;
+      for (int r = 0; r < RB; ++r) res[r] = a.out[gg * RB + r];
+    }
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int row = row_of<RB, EPI>(a, gg, r);
+      const char* rp;
+      if constexpr (MM)
+        rp = static_cast<const char*>(a.mats[row / a.rows_per_mat]) + (size_t)(row % a.rows_per_mat) * K * sizeof(WT);
+      else
+        rp = static_cast<const char*>(a.W) + (size_t)row * K * sizeof(WT);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = pp * kWave * U + u * kWave + lane;
+        if (FULL)
+          buf[r][u] = load_stream(rp + (size_t)c * 16);
+        else
+          buf[r][u] = c < nch ? load_stream(rp + (size_t)c * 16) : u32x4{0u, 0u, 0u, 0u};
       }
     }
-  }
-  __syncthreads();
+  };
+  auto next_g = [&](int gg, int pp) { return pp + 1 < np ? gg : gg + NW; };
+  auto next_p = [&](int pp) { return pp + 1 < np ? pp + 1 : 0; };
 
-  int g = gb0 + wid;
-  if (g >= gb1) return;
-
+  int ga = gb0 + wid, pa = 0;
+  int gb = next_g(ga, pa), pb = next_p(pa);
+  const int g_first = ga < gb1 ? ga : gb1 - 1;  // a valid group of this block (blocks <= groups)
+  u32x4 wa[RB][U], wb[RB][U];
+  float ra[RB], rb[RB];
   float xr[ONEPASS ? U : 1][EPC];
-  if (ONEPASS) {
+
+  if constexpr (PRO != PRO_DEPTH_ATTN) {
+    // x (and alpha) -> registers, XR float4 per thread, clamped so every load is
+    // unconditional; then the first item's weights; then x is staged in LDS (padded to
+    // XR*NT*4 floats, so the stores are unconditional too). Straight-line code lets the
+    // compiler wait for x alone, and lds_barrier() leaves the weight loads in flight.
+    f32x4 xv[XR], av[PRO == PRO_RMSNORM ? XR : 1];
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+      const int k = (i * NT + tid) * 4;
+      const int kc = k < K ? k : K - 4;
+      xv[i] = *reinterpret_cast<const f32x4*>(a.x + kc);
+      if (PRO == PRO_RMSNORM) av[i] = *reinterpret_cast<const f32x4*>(a.alpha + kc);
+    }
+    issue(wa, ra, g_first, 0);  // unconditional: every block has >= 1 group
+    float r = 1.f;
+    if (PRO == PRO_RMSNORM) {
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < XR; ++i) {
+        const float q = xv[i].x * xv[i].x + xv[i].y * xv[i].y + xv[i].z * xv[i].z + xv[i].w * xv[i].w;
+        ss += (i * NT + tid) * 4 < K ? q : 0.f;
+      }
+      ss = wave_sum(ss);
+      if (lane == 0) red[wid] = ss;
+      lds_barrier();
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) tot += red[w];
+      r = 1.0f / sqrtf(tot / (float)K + a.eps);
+    }
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+      f32x4 v = xv[i];
+      if (PRO == PRO_RMSNORM) v = (v * r) * av[i];
+      *reinterpret_cast<f32x4*>(xs + (i * NT + tid) * 4) = v;
+    }
+    lds_barrier();
+    if (ga >= gb1) return;
+    if (gb < gb1) issue(wb, rb, gb, pb);
+  } else {
+    depth_attention(a, xs, xs + K);
+    __syncthreads();
+    if (ga >= gb1) return;
+    issue(wa, ra, ga, pa);
+    if (gb < gb1) issue(wb, rb, gb, pb);
+  }
+  if constexpr (ONEPASS) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = u * kWave + lane;
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) xr[u][e] = c < nch ? xs[c * EPC + e] : 0.f;
+      for (int e = 0; e < EPC; e += 4) {
+        const f32x4 t = (FULL || c < nch) ? *reinterpret_cast<const f32x4*>(xs + c * EPC + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+        xr[u][e] = t.x; xr[u][e + 1] = t.y; xr[u][e + 2] = t.z; xr[u][e + 3] = t.w;
+      }
     }
   }
 
-  auto fetch = [&]() -> int {
-    int v = 0;
-    if (lane == 0) v = atomicAdd(&qnext, 1);
-    return __builtin_amdgcn_readfirstlane(v);
-  };
-  auto issue = [&](u32x4 (&buf)[RB][U], int gg, int pp) {
+  float acc[RB], rg[RB];  // rg: residual rows of the group being accumulated
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      const int row = row_of<RB, EPI>(a, gg, r);
-      const char* rp = a.rows_per_mat
-                           ? static_cast<const char*>(a.mats[row / a.rows_per_mat]) +
-                                 (size_t)(row % a.rows_per_mat) * K * sizeof(WT)
-                           : static_cast<const char*>(a.W) + (size_t)row * K * sizeof(WT);
+  for (int r = 0; r < RB; ++r) acc[r] = rg[r] = 0.f;
+
+  auto consume = [&](const u32x4 (&buf)[RB][U], const float (&res)[RB], int gg, int pp) {
+    // the residual was fetched with the group's first pass; the epilogue runs after its
+    // last pass, which may sit in the other buffer
+    if (EPI == EPI_RESID && pp == 0) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = pp * kWave * U + u * kWave + lane;
-        buf[r][u] = c < nch ? load_stream(rp + (size_t)c * 16) : u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int r = 0; r < RB; ++r) rg[r] = res[r];
     }
-  };
-  auto accumulate = [&](const u32x4 (&buf)[RB][U], int pp, float (&acc)[RB]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = pp * kWave * U + u * kWave + lane;
-      float xv[EPC];
+      float xw[EPC];
       if (ONEPASS) {
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) xv[e] = xr[u][e];
+        for (int e = 0; e < EPC; ++e) xw[e] = xr[u][e];
+      } else if (FULL || c < nch) {
+#pragma unroll
+        for (int e = 0; e < EPC; e += 4) {
+          const f32x4 t = *reinterpret_cast<const f32x4*>(xs + c * EPC + e);
+          xw[e] = t.x; xw[e + 1] = t.y; xw[e + 2] = t.z; xw[e + 3] = t.w;
+        }
       } else {
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) xv[e] = c < nch ? xs[c * EPC + e] : 0.f;
+        for (int e = 0; e < EPC; ++e) xw[e] = 0.f;
       }
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         float wf[EPC];
         Elem<WT>::widen(buf[r][u], wf);
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[r] += wf[e] * xv[e];
+        for (int e = 0; e < EPC; ++e) acc[r] += wf[e] * xw[e];
       }
+    }
+    if (pp + 1 == np) {
+#pragma unroll
+      for (int r = 0; r < RB; ++r) acc[r] = wave_sum(acc[r]);
+      if (lane == 0) epilogue<WT, RB, EPI>(a, gg, acc, rg);
+#pragma unroll
+      for (int r = 0; r < RB; ++r) acc[r] = 0.f;
     }
   };
 
-  u32x4 wa[RB][U], wb[RB][U];
-  float acc[RB];
-#pragma unroll
-  for (int r = 0; r < RB; ++r) acc[r] = 0.f;
-  int p = 0;
-  issue(wa, g, 0);
-  int gn = fetch();
-
-#define PP_GEMV_STEP(CUR, NXT)                                   \
-  {                                                              \
-    const bool last_pass = p + 1 == np;                          \
-    const int ng = last_pass ? gn : g;                           \
-    const int npp = last_pass ? 0 : p + 1;                       \
-    const bool more = ng < gb1;                                  \
-    if (more) issue(NXT, ng, npp);                               \
-    accumulate(CUR, p, acc);                                     \
-    if (last_pass) {                                             \
-      _Pragma("unroll") for (int r = 0; r < RB; ++r) acc[r] = wave_sum(acc[r]); \
-      if (lane == 0) epilogue<WT, RB, EPI>(a, g, acc);           \
-      _Pragma("unroll") for (int r = 0; r < RB; ++r) acc[r] = 0.f; \
-    }                                                            \
-    if (!more) break;                                            \
-    if (last_pass) gn = fetch();                                 \
-    g = ng;                                                      \
-    p = npp;                                                     \
-  }
+  // ---- 4. two buffers in flight: consume one, refill it two items ahead
   while (true) {
-    PP_GEMV_STEP(wa, wb)
-    PP_GEMV_STEP(wb, wa)
+    consume(wa, ra, ga, pa);
+    const int gc = next_g(gb, pb), pc = next_p(pb);
+    if (gb >= gb1) break;
+    if (gc < gb1) issue(wa, ra, gc, pc);
+    consume(wb, rb, gb, pb);
+    const int gd = next_g(gc, pc), pd = next_p(pc);
+    if (gc >= gb1) break;
+    if (gd < gb1) issue(wb, rb, gd, pd);
+    ga = gc; pa = pc;
+    gb = gd; pb = pd;
   }
-#undef PP_GEMV_STEP
+}
+
+template <typename WT, int RB, int U, bool OP, int PRO, int EPI, int XR>
+static void launch_x(const GemvArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+  constexpr int EPC = Elem<WT>::kPerChunk;
+  const bool full = (a.K / EPC) % (kWave * U) == 0;
+  if constexpr (PRO == PRO_COPY && EPI == EPI_STORE) {
+    if (a.rows_per_mat > 0) {
+      if (full) hipLaunchKernelGGL((k_gemv<WT, RB, U, OP, PRO, EPI, true, true, XR>), grid, block, lds, s, a);
+      else hipLaunchKernelGGL((k_gemv<WT, RB, U, OP, PRO, EPI, true, false, XR>), grid, block, lds, s, a);
+      return;
+    }
+  }
+  if (full) hipLaunchKernelGGL((k_gemv<WT, RB, U, OP, PRO, EPI, false, true, XR>), grid, block, lds, s, a);
+  else hipLaunchKernelGGL((k_gemv<WT, RB, U, OP, PRO, EPI, false, false, XR>), grid, block, lds, s, a);
+}
+
+// XR: float4 of x per thread in the prologue (the LDS copy of x is padded to XR*NT*4).
+template <typename WT, int RB, int U, bool OP, int PRO, int EPI>
+static void launch_u(const GemvArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+  constexpr int per = kGemvWaves * 64 * 4;
+  if (PRO == PRO_DEPTH_ATTN || a.K <= per) launch_x<WT, RB, U, OP, PRO, EPI, 1>(a, grid, block, lds, s);
+  else if (a.K <= 2 * per) launch_x<WT, RB, U, OP, PRO, EPI, 2>(a, grid, block, lds, s);
+  else launch_x<WT, RB, U, OP, PRO, EPI, 6>(a, grid, block, lds, s);
 }
 
 template <typename WT, int RB, int PRO, int EPI>
 static hipError_t dispatch_u(const GemvArgs& a, int blocks, hipStream_t s) {
   constexpr int EPC = Elem<WT>::kPerChunk;
   const int nch = a.K / EPC;
-  const size_t lds = (size_t)a.K * sizeof(float) + (PRO == PRO_DEPTH_ATTN ? 32 * 32 * sizeof(float) : 0);
-  const dim3 grid(blocks), block(kGemvThreads);
-  if (nch <= kWave * 1)
-    hipLaunchKernelGGL((k_gemv<WT, RB, 1, true, PRO, EPI>), grid, block, lds, s, a);
-  else if (nch <= kWave * 2)
-    hipLaunchKernelGGL((k_gemv<WT, RB, 2, true, PRO, EPI>), grid, block, lds, s, a);
-  else if (nch <= kWave * 4)
-    hipLaunchKernelGGL((k_gemv<WT, RB, 4, true, PRO, EPI>), grid, block, lds, s, a);
-  else if (nch <= kWave * 6)
-    hipLaunchKernelGGL((k_gemv<WT, RB, 6, true, PRO, EPI>), grid, block, lds, s, a);
-  else if (nch <= kWave * 8)
-    hipLaunchKernelGGL((k_gemv<WT, RB, 8, true, PRO, EPI>), grid, block, lds, s, a);
-  else if (nch % (kWave * 11) == 0)
-    hipLaunchKernelGGL((k_gemv<WT, RB, 11, false, PRO, EPI>), grid, block, lds, s, a);
-  else
-    hipLaunchKernelGGL((k_gemv<WT, RB, 8, false, PRO, EPI>), grid, block, lds, s, a);
+  constexpr int per = kGemvWaves * 64 * 4;
+  const size_t xpad = (size_t)(a.K + per - 1) / per * per;
+  const size_t lds = (PRO == PRO_DEPTH_ATTN ? (size_t)a.K + 32 * 32 : xpad) * sizeof(float);
+  const dim3 grid(blocks), block(kGemvWaves * 64);
+  if (a.K % 4 != 0 || a.K > 6 * per) return hipErrorInvalidValue;
+  if (a.rows_per_mat > 0 && (PRO != PRO_COPY || EPI != EPI_STORE)) return hipErrorInvalidValue;
+  if (nch <= kWave * 1) launch_u<WT, RB, 1, true, PRO, EPI>(a, grid, block, lds, s);
+  else if (nch <= kWave * 2) launch_u<WT, RB, 2, true, PRO, EPI>(a, grid, block, lds, s);
+  else if (nch <= kWave * 4) launch_u<WT, RB, 4, true, PRO, EPI>(a, grid, block, lds, s);
+  else if (nch <= kWave * 6) launch_u<WT, RB, 6, true, PRO, EPI>(a, grid, block, lds, s);
+  else if (nch <= kWave * 8) launch_u<WT, RB, 8, true, PRO, EPI>(a, grid, block, lds, s);
+  else if (RB == 1 && nch % (kWave * 11) == 0) launch_u<WT, RB, (RB == 1 ? 11 : 8), false, PRO, EPI>(a, grid, block, lds, s);
+  else launch_u<WT, RB, 8, false, PRO, EPI>(a, grid, block, lds, s);
   return hipGetLastError();
 }
 
 template <typename WT, int PRO, int EPI>
 static hipError_t dispatch_rb(int rb, const GemvArgs& a, int blocks, hipStream_t s) {
   if (rb == 2) return dispatch_u<WT, 2, PRO, EPI>(a, blocks, s);
-  if (rb == 4) return dispatch_u<WT, 4, PRO, EPI>(a, blocks, s);
+  if constexpr (EPI != EPI_SWIGLU && EPI != EPI_QKV) {
+    if (rb == 1) return dispatch_u<WT, 1, PRO, EPI>(a, blocks, s);
+  }
   return hipErrorInvalidValue;
 }
 

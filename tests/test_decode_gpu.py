@@ -35,10 +35,12 @@ def _decode_all(model, kv, ids, with_logits=True):
 
 # ----------------------------------------------------------------------------- fp32, tiny
 
-@pytest.mark.parametrize("context", [3000, 4])
+@pytest.mark.parametrize("context,d_ff", [(3000, 704), (4, 704), (3000, 2312)])
 @pytest.mark.parametrize("graph", [True, False])
-def test_tiny_fp32_decode_matches_oracle(context, graph):
-    cfg = synth.with_(synth.TINY_TEMPORAL, context=context)
+def test_tiny_fp32_decode_matches_oracle(context, d_ff, graph):
+    """d_ff 2312 makes the W_out rows (2312 floats) longer than one 512-chunk pass, so the
+    multi-pass GEMV path (x from LDS, ragged last pass) is covered at small scale."""
+    cfg = synth.with_(synth.TINY_TEMPORAL, context=context, d_ff=d_ff)
     W = synth.temporal_weights(cfg, 0, "fp32")
     ids = synth.stream_ids(cfg, 16, 1)
     model, _ = _model(cfg, W, "fp32")
@@ -46,8 +48,8 @@ def test_tiny_fp32_decode_matches_oracle(context, graph):
     kv = model.kv_alloc()
     h, lg = _decode_all(model, kv, ids)
     want_h, want_lg = O.forward_full(ids, W, cfg, with_logits=True)
-    print("tiny fp32 C=%d graph=%s: h err %.3g, logits err %.3g" %
-          (context, graph, max_abs_err(h, want_h), max_abs_err(lg, want_lg)))
+    print("tiny fp32 C=%d F=%d graph=%s: h err %.3g, logits err %.3g" %
+          (context, d_ff, graph, max_abs_err(h, want_h), max_abs_err(lg, want_lg)))
     assert max_abs_err(h, want_h) <= FP32_TOL
     assert max_abs_err(lg, want_lg) <= FP32_TOL
     assert kv.info()[0] == 16
