@@ -54,7 +54,7 @@ typedef enum { PP_F32 = 0, PP_BF16 = 1 } pp_dtype;
  * 128, d_ff (gated hidden width) 11264, context 3000, text vocab 32001 (IDs 0..32000),
  * audio vocab 2049 (IDs 0..2048), 16 audio streams, rope_theta 1e4, eps 1e-8.
  * Requirements: d_model == n_heads * d_head; d_head is 64 or 128; d_model and d_ff are
- * multiples of 8. wdtype (a pp_dtype) is the type of every weight matrix and
+ * multiples of 8 and at most 12288. wdtype (a pp_dtype) is the type of every weight matrix and
  * embedding table AND of the KV ring; norm scales are always float32. */
 typedef struct {
   int32_t n_layers, d_model, n_heads, d_head, d_ff, context;
@@ -150,7 +150,8 @@ pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* ids_host, i
 /* Shapes of the depth transformer (audit section 4). Full size: 6 layers, d_model 1024,
  * 16 heads of 64, d_ff 2816, 16 steps (weights_per_step), window 8, text vocab 32001,
  * audio vocab 2049, 2048 logits per step, d_temporal 4096, eps 1e-8. Requirements:
- * d_model == n_heads * d_head, d_head <= 128, window >= 1, n_steps <= 32. */
+ * d_model == n_heads * d_head <= 2048, d_head <= 128, window >= 1, n_steps <= 32,
+ * d_ff and d_temporal multiples of 8 and at most 12288, n_out even. */
 typedef struct {
   int32_t n_layers, d_model, n_heads, d_head, d_ff, n_steps, window;
   int32_t text_vocab, audio_vocab, n_out, d_temporal;

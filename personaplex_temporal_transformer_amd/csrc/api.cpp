@@ -56,7 +56,7 @@ static pp_status validate_temporal_config(const pp_temporal_config* c) {
   if (c->d_head != 64 && c->d_head != 128) return pp_fail(PP_E_ARG, "d_head must be 64 or 128");
   if (c->n_heads * c->d_head != c->d_model) return pp_fail(PP_E_ARG, "d_model != n_heads * d_head");
   if (c->d_model % 8 || c->d_ff % 8) return pp_fail(PP_E_ARG, "d_model and d_ff must be multiples of 8");
-  if (c->d_model > 16384 || c->d_ff > 16384) return pp_fail(PP_E_ARG, "d_model/d_ff above 16384 unsupported");
+  if (c->d_model > 12288 || c->d_ff > 12288) return pp_fail(PP_E_ARG, "d_model/d_ff above 12288 unsupported");
   if (c->n_audio < 0 || c->n_audio + 1 > kMaxStreams) return pp_fail(PP_E_ARG, "n_audio out of range");
   if (c->text_vocab < 2 || c->audio_vocab < 1) return pp_fail(PP_E_ARG, "vocab sizes must be positive");
   if (!(c->rope_theta > 0) || !(c->eps >= 0)) return pp_fail(PP_E_ARG, "rope_theta must be > 0, eps >= 0");
@@ -125,7 +125,8 @@ pp_status pp_model::alloc_decode(int D, int F, int H, int dh) {
   size_t bytes = 0;
   auto take = [&](size_t n) { size_t off = bytes; bytes += (n + 255) / 256 * 256; return off; };
   const size_t ox = take(sizeof(float) * D), oq = take(sizeof(float) * D), oo = take(sizeof(float) * D);
-  const size_t os = take(sizeof(float) * F), op = take(sizeof(float) * (size_t)H * S * (dh + 2));
+  const size_t os = take(sizeof(float) * F), op = take(sizeof(float) * (size_t)H * S * dh);
+  const size_t oml = take(sizeof(float) * (size_t)H * S * 2);
   const size_t ost = take(sizeof(long long) * 4);
   const size_t orp = take(sizeof(float) * dh);
   if (hipMalloc(&ws, bytes) != hipSuccess) return pp_fail(PP_E_HIP, "hipMalloc of decode workspace failed");
@@ -135,7 +136,8 @@ pp_status pp_model::alloc_decode(int D, int F, int H, int dh) {
   q = reinterpret_cast<float*>(b + oq);
   o = reinterpret_cast<float*>(b + oo);
   s = reinterpret_cast<float*>(b + os);
-  part = reinterpret_cast<float*>(b + op);
+  part_o = reinterpret_cast<float*>(b + op);
+  part_ml = reinterpret_cast<float*>(b + oml);
   state = reinterpret_cast<long long*>(b + ost);
   rope = reinterpret_cast<float*>(b + orp);
   return PP_OK;
@@ -320,13 +322,16 @@ hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced) {
 
     AttnDecodeArgs at{};
     at.q = q; at.k = kbase; at.v = vbase; at.state = state; at.C = C; at.H = H; at.S = S;
-    at.scale = 1.0f / std::sqrt((float)dh); at.part = part; at.out = o;
+    at.scale = 1.0f / std::sqrt((float)dh); at.part_o = part_o; at.part_ml = part_ml; at.out = o;
+    const bool merge_in_wo = S <= 8 && D <= 4096;
+    at.combine = merge_in_wo ? 0 : 1;
     e = launch_attn_decode(at, bf16, dh, s);
     if (e != hipSuccess) break;
 
     GemvArgs go{};
     go.W = w_o[l]; go.x = o; go.K = D; go.n_groups = D / 2; go.out = x;
-    e = launch_gemv(PRO_COPY, EPI_RESID, bf16, 2, go, gemv_blocks, s);
+    go.po = part_o; go.pml = part_ml; go.pS = S; go.adh = dh;
+    e = launch_gemv(merge_in_wo ? PRO_ATTN_MERGE : PRO_COPY, EPI_RESID, bf16, 2, go, gemv_blocks, s);
     if (e != hipSuccess) break;
 
     const bool tr = traced && l == trace_layer && trace_used + 2 <= trace_ev.size();
@@ -398,7 +403,12 @@ extern "C" pp_status pp_temporal_decode_step(pp_model* m, pp_kv* kv, const int32
   a.pos = kv->pos;
   a.rope = m->rope;
   a.dh = c.d_head;
-  a.log_theta = std::log(c.rope_theta);
+  // RoPE angles pos * theta^(-2j/d_head) formed in float64 on the host
+  for (int j = 0; j < c.d_head / 2; ++j) {
+    const double ang = (double)kv->pos * std::exp(-std::log(c.rope_theta) * (2.0 * j) / (double)c.d_head);
+    a.rope_cs[2 * j] = (float)std::cos(ang);
+    a.rope_cs[2 * j + 1] = (float)std::sin(ang);
+  }
   hipError_t e = launch_embed(a, m->bf16, s);
   if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("embed: ") + hipGetErrorString(e));
 

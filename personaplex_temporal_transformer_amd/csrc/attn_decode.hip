@@ -22,18 +22,20 @@ constexpr int kMaxSplits = 64;
 
 constexpr int kAttnThreads = 512;
 
-// Block (s, h): one pass over its keys with an online softmax. A group of LPK lanes owns
-// one key row per pass (16 bytes per lane); KPP groups cover KPP keys per pass and NB
-// passes form a round. The K and V rows of the next round are loaded while the current
-// round is scored and accumulated. Each group keeps a running max m, sum l and output
-// o (its lanes' EPC dimensions); the groups are merged through LDS at the end.
+// Block (s, h): one pass over its keys with an online softmax. A group of LPK lanes reads
+// one key row at a time (16 bytes per lane); the KPP groups of the block own contiguous,
+// equal runs of the block's keys. A round loads NB keys' K and V rows per thread with
+// buffer loads (slots past the group's run point out of range and read zeros without
+// memory traffic); the next round is always issued before the current one is consumed.
+// Each group keeps a running max m, sum l and output o (its lanes' EPC dimensions); the
+// groups are merged through LDS at the end.
 template <typename KT, int DH>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnDecodeArgs a) {
   constexpr int EPC = Elem<KT>::kPerChunk;  // elements per 16-byte chunk
   constexpr int LPK = DH / EPC;             // lanes per key row
-  constexpr int KPP = kAttnThreads / LPK;   // keys per pass
-  constexpr int NB = 8;                     // passes per round
-  constexpr int RK = KPP * NB;              // keys per round
+  constexpr int KPP = kAttnThreads / LPK;   // key groups per block
+  constexpr int NB = 12;                    // keys per group per round
+  constexpr int ROW = DH * (int)sizeof(KT); // bytes per key row
   __shared__ float gm[KPP], gl[KPP];
   __shared__ float go[KPP][DH + 1];
 
@@ -43,26 +45,32 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnDecodeArgs a) 
   const int n = pos + 1 < (long long)a.C ? (int)(pos + 1) : a.C;
   const int j0 = (int)((long long)s * n / a.S), j1 = (int)((long long)(s + 1) * n / a.S);
   const int cnt = j1 - j0;
+  const int per_g = (cnt + KPP - 1) / KPP;
+  const int gbeg = kg * per_g;
+  const int gend = gbeg + per_g < cnt ? gbeg + per_g : cnt;
+  const int rounds = (per_g + NB - 1) / NB;   // the same for every group
 
   float qv[EPC];
 #pragma unroll
   for (int e = 0; e < EPC; ++e) qv[e] = a.q[h * DH + sub * EPC + e] * a.scale;
-  const KT* kb = static_cast<const KT*>(a.k) + ((size_t)h * a.C + j0) * DH + sub * EPC;
-  const KT* vb = static_cast<const KT*>(a.v) + ((size_t)h * a.C + j0) * DH + sub * EPC;
+  const size_t base = ((size_t)h * a.C + j0) * DH;
+  const auto rk = make_rsrc(static_cast<const KT*>(a.k) + base, (uint32_t)cnt * ROW);
+  const auto rv = make_rsrc(static_cast<const KT*>(a.v) + base, (uint32_t)cnt * ROW);
 
   float m = -INFINITY, l = 0.f, acc[EPC];
 #pragma unroll
   for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
 
-  auto issue = [&](u32x4 (&ck)[NB], u32x4 (&cv)[NB], int jb) {
+  auto issue = [&](u32x4 (&ck)[NB], u32x4 (&cv)[NB], int r) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int j = jb + b * KPP + kg;
-      ck[b] = j < cnt ? load_stream(kb + (size_t)j * DH) : u32x4{0u, 0u, 0u, 0u};
-      cv[b] = j < cnt ? load_stream(vb + (size_t)j * DH) : u32x4{0u, 0u, 0u, 0u};
+      const int j = gbeg + r * NB + b;
+      const int off = (r < rounds && j < gend) ? j * ROW + sub * 16 : kBufOutOfRange;
+      ck[b] = buffer_load16_stream(rk, off);
+      cv[b] = buffer_load16_stream(rv, off);
     }
   };
-  auto consume = [&](const u32x4 (&ck)[NB], const u32x4 (&cv)[NB], int jb) {
+  auto consume = [&](const u32x4 (&ck)[NB], const u32x4 (&cv)[NB], int r) {
     float sc[NB];
     float mb = -INFINITY;
 #pragma unroll
@@ -73,18 +81,17 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnDecodeArgs a) 
 #pragma unroll
       for (int e = 0; e < EPC; ++e) d += qv[e] * kf[e];
       d = group_sum<LPK>(d);
-      sc[b] = (jb + b * KPP + kg) < cnt ? d : -INFINITY;
+      sc[b] = (gbeg + r * NB + b) < gend ? d : -INFINITY;
       mb = fmaxf(mb, sc[b]);
     }
-    if (mb == -INFINITY) return;  // no key of this group in this round
     const float mn = fmaxf(m, mb);
-    const float scale = expf(m - mn);  // m = -inf -> 0
-    l *= scale;
+    const float scale = mn == -INFINITY ? 1.f : expf(m - mn);  // m = -inf -> 0
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] *= scale;
+    l *= scale;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const float p = expf(sc[b] - mn);  // -inf -> 0
+      const float p = sc[b] == -INFINITY ? 0.f : expf(sc[b] - mn);
       l += p;
       float vf[EPC];
       Elem<KT>::widen(cv[b], vf);
@@ -94,17 +101,14 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnDecodeArgs a) 
     m = mn;
   };
 
-  u32x4 ka[NB], va[NB], kb2[NB], vb2[NB];
-  if (cnt > 0) {
-    issue(ka, va, 0);
-    for (int jb = 0;; jb += 2 * RK) {
-      if (jb + RK < cnt) issue(kb2, vb2, jb + RK);
-      consume(ka, va, jb);
-      if (jb + RK >= cnt) break;
-      if (jb + 2 * RK < cnt) issue(ka, va, jb + 2 * RK);
-      consume(kb2, vb2, jb + RK);
-      if (jb + 2 * RK >= cnt) break;
-    }
+  u32x4 ka[NB], va[NB], kb[NB], vb[NB];
+  issue(ka, va, 0);
+  for (int r = 0; r < rounds; r += 2) {
+    issue(kb, vb, r + 1);
+    consume(ka, va, r);
+    if (r + 1 >= rounds) break;
+    issue(ka, va, r + 2);
+    consume(kb, vb, r + 1);
   }
 
   // ---- merge the KPP groups of this block
@@ -115,7 +119,6 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnDecodeArgs a) 
 #pragma unroll
   for (int e = 0; e < EPC; ++e) go[kg][sub * EPC + e] = acc[e];
   __syncthreads();
-  float* part = a.part + ((size_t)h * a.S + s) * (DH + 2);
   if (tid < DH) {
     float M = -INFINITY;
     for (int g = 0; g < KPP; ++g) M = fmaxf(M, gm[g]);
@@ -128,10 +131,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnDecodeArgs a) 
         o += w * go[g][tid];
       }
     }
-    part[tid] = o;
+    a.part_o[((size_t)h * a.S + s) * DH + tid] = o;
     if (tid == 0) {
-      part[DH] = M;
-      part[DH + 1] = L;
+      a.part_ml[((size_t)h * a.S + s) * 2] = M;
+      a.part_ml[((size_t)h * a.S + s) * 2 + 1] = L;
     }
   }
 }
@@ -141,21 +144,21 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnDecodeArgs a) 
 // All partials of the head are first loaded into LDS in one parallel round.
 template <int DH>
 __global__ __launch_bounds__(kBlock) void k_attn_combine(AttnDecodeArgs a) {
-  __shared__ float pp[kMaxSplits * (DH + 2)];
+  __shared__ float po[kMaxSplits * DH], pml[kMaxSplits * 2];
   const int h = blockIdx.x, t = threadIdx.x;
-  const float* ph = a.part + (size_t)h * a.S * (DH + 2);
-  for (int i = t; i < a.S * (DH + 2); i += kBlock) pp[i] = ph[i];
+  for (int i = t; i < a.S * DH; i += kBlock) po[i] = a.part_o[(size_t)h * a.S * DH + i];
+  for (int i = t; i < a.S * 2; i += kBlock) pml[i] = a.part_ml[(size_t)h * a.S * 2 + i];
   __syncthreads();
   if (t >= DH) return;
   float M = -INFINITY;
-  for (int i = 0; i < a.S; ++i) M = fmaxf(M, pp[i * (DH + 2) + DH]);
+  for (int i = 0; i < a.S; ++i) M = fmaxf(M, pml[2 * i]);
   float L = 0.f, o = 0.f;
   for (int i = 0; i < a.S; ++i) {
-    const float mi = pp[i * (DH + 2) + DH];
+    const float mi = pml[2 * i];
     if (mi == -INFINITY) continue;  // empty split
     const float w = expf(mi - M);
-    L += w * pp[i * (DH + 2) + DH + 1];
-    o += w * pp[i * (DH + 2) + t];
+    L += w * pml[2 * i + 1];
+    o += w * po[i * DH + t];
   }
   a.out[h * DH + t] = o / L;
 }
@@ -168,7 +171,7 @@ hipError_t launch_attn_decode(const AttnDecodeArgs& a, bool bf16, int dh, hipStr
   else if (!bf16 && dh == 64) hipLaunchKernelGGL((k_attn_decode<float, 64>), grid, block, 0, s, a);
   else return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !a.combine) return e;
   if (dh == 128) hipLaunchKernelGGL((k_attn_combine<128>), dim3(a.H), dim3(kBlock), 0, s, a);
   else hipLaunchKernelGGL((k_attn_combine<64>), dim3(a.H), dim3(kBlock), 0, s, a);
   return hipGetLastError();

@@ -58,7 +58,8 @@ static pp_status validate_depth_config(const pp_depth_config* c) {
     return pp_fail(PP_E_ARG, "n_heads, n_steps <= 32 and d_head <= 128 required");
   if (c->d_model % 8 || c->d_ff % 8 || c->d_temporal % 8 || c->n_out % 2)
     return pp_fail(PP_E_ARG, "d_model, d_ff, d_temporal must be multiples of 8 and n_out even");
-  if (c->d_model > 16384 || c->d_ff > 16384 || c->d_temporal > 16384) return pp_fail(PP_E_ARG, "width above 16384");
+  if (c->d_model > 2048 || c->d_ff > 12288 || c->d_temporal > 12288)
+    return pp_fail(PP_E_ARG, "d_model above 2048 or d_ff/d_temporal above 12288 unsupported");
   if (c->n_out > c->audio_vocab) return pp_fail(PP_E_ARG, "n_out exceeds the audio embedding rows");
   return PP_OK;
 }

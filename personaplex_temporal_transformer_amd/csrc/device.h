@@ -56,6 +56,17 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Buffer loads: a resource over [base, base + bytes) makes lanes whose offset is out of
+// range read zeros without touching memory, so range guards need no branches (loads
+// stay straight-line and the compiler's waits stay precise).
+constexpr int kBufOutOfRange = 0x7ffffff0;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load16_stream(__amdgpu_buffer_rsrc_t r, int byte_offset) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 2 /* non-temporal */);
+}
+
 // DPP lane moves inside a row of 16 lanes (no LDS traffic).
 __device__ __forceinline__ float dpp_xor1(float v) {  // quad_perm [1,0,3,2]
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));

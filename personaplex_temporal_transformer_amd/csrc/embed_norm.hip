@@ -11,35 +11,41 @@
 namespace pp {
 
 // One thread owns 4 consecutive features of one frame; it adds the streams' rows in
-// stream order 0..n-1 in float32 (a fixed order, so the result is reproducible).
+// stream order 0..n-1 in float32 (a fixed order, so the result is reproducible). All
+// rows are loaded first (row 0 stands in for ID -1 and contributes +0.0, which leaves
+// the sum's bits unchanged: the running sum starts at +0.0 and can never become -0.0).
 template <typename WT>
 __global__ __launch_bounds__(kBlock) void k_embed_sum(EmbedArgs a) {
   const int row = blockIdx.y;
   const int d = (blockIdx.x * kBlock + threadIdx.x) * 4;
   if (a.state && row == 0 && blockIdx.x == 0) {
     if (threadIdx.x == 0) a.state[0] = a.pos;
-    if (a.rope && threadIdx.x < a.dh / 2) {
-      const int j = threadIdx.x;
-      const double ang = (double)a.pos * exp(-a.log_theta * (double)(2 * j) / (double)a.dh);
-      double sn, cs;
-      sincos(ang, &sn, &cs);
-      a.rope[2 * j] = (float)cs;
-      a.rope[2 * j + 1] = (float)sn;
-    }
+    if (a.rope && threadIdx.x < a.dh) a.rope[threadIdx.x] = a.rope_cs[threadIdx.x];
   }
   if (d >= a.D) return;
-  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
-  for (int k = 0; k < a.n_streams; ++k) {
-    const int id = a.ids_dev ? a.ids_dev[(size_t)row * a.n_streams + k] : a.ids_arg[k];
-    if (id < 0) continue;  // -1: no input (other negatives are rejected on the host)
-    const WT* r = static_cast<const WT*>(a.tables[k]) + (size_t)id * a.D + d;
-    acc0 += Elem<WT>::load1(r + 0);
-    acc1 += Elem<WT>::load1(r + 1);
-    acc2 += Elem<WT>::load1(r + 2);
-    acc3 += Elem<WT>::load1(r + 3);
+  float v[kMaxStreams][4];
+#pragma unroll
+  for (int k = 0; k < kMaxStreams; ++k) {
+    if (k < a.n_streams) {
+      const int id = a.ids_dev ? a.ids_dev[(size_t)row * a.n_streams + k] : a.ids_arg[k];
+      const WT* r = static_cast<const WT*>(a.tables[k]) + (size_t)(id < 0 ? 0 : id) * a.D + d;
+      const float keep = id < 0 ? 0.f : 1.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[k][e] = keep * Elem<WT>::load1(r + e);
+    }
   }
-  f32x4 v = {acc0, acc1, acc2, acc3};
-  *reinterpret_cast<f32x4*>(a.out + (size_t)row * a.D + d) = v;
+  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxStreams; ++k) {
+    if (k < a.n_streams) {
+      acc0 += v[k][0];
+      acc1 += v[k][1];
+      acc2 += v[k][2];
+      acc3 += v[k][3];
+    }
+  }
+  f32x4 out = {acc0, acc1, acc2, acc3};
+  *reinterpret_cast<f32x4*>(a.out + (size_t)row * a.D + d) = out;
 }
 
 hipError_t launch_embed(const EmbedArgs& a, bool bf16, hipStream_t s) {

@@ -9,6 +9,8 @@
 // Fused prologue / epilogues follow "PersonaPlex native LM audit", section 3 ('One of
 // the 32 temporal blocks', 'Positions, attention mask and final text head'):
 //   PRO_RMSNORM  x <- alpha * x / sqrt(mean(x^2) + eps) in float32
+//   PRO_ATTN_MERGE  x <- merge of the decode-attention split partials (online-softmax
+//                rescaling by exp(m_s - max m), divided by the merged sum)
 //   PRO_DEPTH_ATTN  x <- softmax attention of the depth query over this frame's depth
 //                cache (no RoPE; window 0 <= q - q' < win), recomputed by each workgroup
 //                ("PersonaPlex native LM audit", section 4, 'One depth block at position q')
@@ -90,10 +92,12 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, int g, const float (
   }
 }
 
-// Depth attention for every head into x[0 .. aH*adh): scores q.k * scale over the keys
-// of positions [aq_pos - awin + 1, aq_pos] (clipped at 0), softmax with max subtraction,
-// then the weighted sum of values. `sc` holds aH x 32 floats of scratch LDS.
-__device__ void depth_attention(const GemvArgs& a, float* x, float* sc) {
+// Depth attention for every head into x (element i stored at xpos(i)): scores
+// q.k * scale over the keys of positions [aq_pos - awin + 1, aq_pos] (clipped at 0),
+// softmax with max subtraction, then the weighted sum of values. `sc` holds aH x 32
+// floats of scratch LDS.
+template <class XPos>
+__device__ void depth_attention(const GemvArgs& a, float* x, float* sc, XPos xpos) {
   const int tid = threadIdx.x;
   const int k0 = a.aq_pos - a.awin + 1 > 0 ? a.aq_pos - a.awin + 1 : 0;
   const int nk = a.aq_pos - k0 + 1;
@@ -125,7 +129,7 @@ __device__ void depth_attention(const GemvArgs& a, float* x, float* sc) {
     const float* vh = a.av + ((size_t)h * a.acap + k0) * a.adh + d;
     float o = 0.f;
     for (int j = 0; j < nk; ++j) o += sc[h * 32 + j] * vh[(size_t)j * a.adh];
-    x[i] = o;
+    x[xpos(i)] = o;
   }
 }
 
@@ -156,6 +160,10 @@ __global__ __launch_bounds__(kGemvWaves * 64) void k_gemv(GemvArgs a) {
   const int np = ONEPASS ? 1 : (nch + kWave * U - 1) / (kWave * U);
   const int gb0 = (int)((long long)blockIdx.x * a.n_groups / gridDim.x);
   const int gb1 = (int)((long long)(blockIdx.x + 1) * a.n_groups / gridDim.x);
+  // LDS copy of x, quarter-chunk planes: float4 e of chunk c at (e * NCP + c) * 4, so the
+  // lanes of a wave (consecutive chunks) read consecutive 16-byte words, conflict-free.
+  constexpr int NCP = XR * NT * 4 / EPC;  // chunks per plane (padded)
+  auto xq_index = [&](int c, int e) { return (e * NCP + c) * 4; };
 
   // ---- weights of one (group, pass) item; the residual rows of a group are read
   // before its weights (EPI_RESID), so waiting for them never waits for later weights
@@ -192,7 +200,48 @@ __global__ __launch_bounds__(kGemvWaves * 64) void k_gemv(GemvArgs a) {
   float ra[RB], rb[RB];
   float xr[ONEPASS ? U : 1][EPC];
 
-  if constexpr (PRO != PRO_DEPTH_ATTN) {
+  if constexpr (PRO == PRO_ATTN_MERGE) {
+    // x = merged attention output. Thread t merges dims [8t, 8t+8) of one head from up to
+    // 8 split partials; the partials are loaded (clamped, unconditional) before the first
+    // item's weights, then merged and staged in LDS while the weights are in flight.
+    constexpr int SM = 8;
+    const int dh = a.adh;
+    const int d0 = tid * 8 < K ? tid * 8 : K - 8;
+    const int hh = d0 / dh, dd = d0 - hh * dh;
+    f32x4 ov[SM][2];
+    float mv[SM], lv[SM];
+#pragma unroll
+    for (int sp = 0; sp < SM; ++sp) {
+      const int sc = sp < a.pS ? sp : a.pS - 1;
+      const float* o = a.po + ((size_t)hh * a.pS + sc) * dh + dd;
+      ov[sp][0] = *reinterpret_cast<const f32x4*>(o);
+      ov[sp][1] = *reinterpret_cast<const f32x4*>(o + 4);
+      const float* ml = a.pml + ((size_t)hh * a.pS + sc) * 2;
+      mv[sp] = ml[0];
+      lv[sp] = ml[1];
+    }
+    issue(wa, ra, g_first, 0);
+    float M = -INFINITY;
+#pragma unroll
+    for (int sp = 0; sp < SM; ++sp) M = fmaxf(M, sp < a.pS ? mv[sp] : -INFINITY);
+    float L = 0.f;
+    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sp = 0; sp < SM; ++sp) {
+      const float w = (sp < a.pS && mv[sp] != -INFINITY) ? expf(mv[sp] - M) : 0.f;
+      L += w * lv[sp];
+      o0 += w * ov[sp][0];
+      o1 += w * ov[sp][1];
+    }
+    const float inv = 1.0f / L;
+    if (tid * 8 < K) {
+      *reinterpret_cast<f32x4*>(xs + xq_index(d0 / EPC, (d0 % EPC) / 4)) = o0 * inv;
+      *reinterpret_cast<f32x4*>(xs + xq_index((d0 + 4) / EPC, ((d0 + 4) % EPC) / 4)) = o1 * inv;
+    }
+    lds_barrier();
+    if (ga >= gb1) return;
+    if (gb < gb1) issue(wb, rb, gb, pb);
+  } else if constexpr (PRO != PRO_DEPTH_ATTN) {
     // x (and alpha) -> registers, XR float4 per thread, clamped so every load is
     // unconditional; then the first item's weights; then x is staged in LDS (padded to
     // XR*NT*4 floats, so the stores are unconditional too). Straight-line code lets the
@@ -226,13 +275,15 @@ __global__ __launch_bounds__(kGemvWaves * 64) void k_gemv(GemvArgs a) {
     for (int i = 0; i < XR; ++i) {
       f32x4 v = xv[i];
       if (PRO == PRO_RMSNORM) v = (v * r) * av[i];
-      *reinterpret_cast<f32x4*>(xs + (i * NT + tid) * 4) = v;
+      const int k = (i * NT + tid) * 4;  // float index; chunk k / EPC, quarter (k % EPC) / 4
+      *reinterpret_cast<f32x4*>(xs + xq_index(k / EPC, (k % EPC) / 4)) = v;
     }
     lds_barrier();
     if (ga >= gb1) return;
     if (gb < gb1) issue(wb, rb, gb, pb);
   } else {
-    depth_attention(a, xs, xs + K);
+    depth_attention(a, xs, xs + XR * NT * 4,
+                    [&](int i) { return xq_index(i / EPC, (i % EPC) / 4) + (i % 4); });
     __syncthreads();
     if (ga >= gb1) return;
     issue(wa, ra, ga, pa);
@@ -244,7 +295,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void k_gemv(GemvArgs a) {
       const int c = u * kWave + lane;
 #pragma unroll
       for (int e = 0; e < EPC; e += 4) {
-        const f32x4 t = (FULL || c < nch) ? *reinterpret_cast<const f32x4*>(xs + c * EPC + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 t = (FULL || c < nch) ? *reinterpret_cast<const f32x4*>(xs + xq_index(c, e / 4)) : f32x4{0.f, 0.f, 0.f, 0.f};
         xr[u][e] = t.x; xr[u][e + 1] = t.y; xr[u][e + 2] = t.z; xr[u][e + 3] = t.w;
       }
     }
@@ -271,7 +322,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void k_gemv(GemvArgs a) {
       } else if (FULL || c < nch) {
 #pragma unroll
         for (int e = 0; e < EPC; e += 4) {
-          const f32x4 t = *reinterpret_cast<const f32x4*>(xs + c * EPC + e);
+          const f32x4 t = *reinterpret_cast<const f32x4*>(xs + xq_index(c, e / 4));
           xw[e] = t.x; xw[e + 1] = t.y; xw[e + 2] = t.z; xw[e + 3] = t.w;
         }
       } else {
@@ -325,12 +376,17 @@ static void launch_x(const GemvArgs& a, dim3 grid, dim3 block, size_t lds, hipSt
   else hipLaunchKernelGGL((k_gemv<WT, RB, U, OP, PRO, EPI, false, false, XR>), grid, block, lds, s, a);
 }
 
-// XR: float4 of x per thread in the prologue (the LDS copy of x is padded to XR*NT*4).
+// XR: float4 of x per thread in the prologue; the LDS copy of x is padded to XR*NT*4
+// floats (plus the depth-attention scratch).
+constexpr int kXPer = kGemvWaves * 64 * 4;
+static int x_regs(int K) { return K <= kXPer ? 1 : (K <= 2 * kXPer ? 2 : 6); }
+
 template <typename WT, int RB, int U, bool OP, int PRO, int EPI>
-static void launch_u(const GemvArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
-  constexpr int per = kGemvWaves * 64 * 4;
-  if (PRO == PRO_DEPTH_ATTN || a.K <= per) launch_x<WT, RB, U, OP, PRO, EPI, 1>(a, grid, block, lds, s);
-  else if (a.K <= 2 * per) launch_x<WT, RB, U, OP, PRO, EPI, 2>(a, grid, block, lds, s);
+static void launch_u(const GemvArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+  const int xr = x_regs(a.K);
+  const size_t lds = ((size_t)xr * kXPer + (PRO == PRO_DEPTH_ATTN ? 32 * 32 : 0)) * sizeof(float);
+  if (xr == 1) launch_x<WT, RB, U, OP, PRO, EPI, 1>(a, grid, block, lds, s);
+  else if (xr == 2) launch_x<WT, RB, U, OP, PRO, EPI, 2>(a, grid, block, lds, s);
   else launch_x<WT, RB, U, OP, PRO, EPI, 6>(a, grid, block, lds, s);
 }
 
@@ -338,19 +394,18 @@ template <typename WT, int RB, int PRO, int EPI>
 static hipError_t dispatch_u(const GemvArgs& a, int blocks, hipStream_t s) {
   constexpr int EPC = Elem<WT>::kPerChunk;
   const int nch = a.K / EPC;
-  constexpr int per = kGemvWaves * 64 * 4;
-  const size_t xpad = (size_t)(a.K + per - 1) / per * per;
-  const size_t lds = (PRO == PRO_DEPTH_ATTN ? (size_t)a.K + 32 * 32 : xpad) * sizeof(float);
   const dim3 grid(blocks), block(kGemvWaves * 64);
-  if (a.K % 4 != 0 || a.K > 6 * per) return hipErrorInvalidValue;
+  if (a.K % EPC != 0 || a.K > 6 * kXPer) return hipErrorInvalidValue;
+  if (PRO == PRO_DEPTH_ATTN && a.K > kXPer) return hipErrorInvalidValue;
+  if (PRO == PRO_ATTN_MERGE && (a.K > kGemvWaves * 64 * 8 || a.pS < 1 || a.pS > 8 || a.adh % 8)) return hipErrorInvalidValue;
   if (a.rows_per_mat > 0 && (PRO != PRO_COPY || EPI != EPI_STORE)) return hipErrorInvalidValue;
-  if (nch <= kWave * 1) launch_u<WT, RB, 1, true, PRO, EPI>(a, grid, block, lds, s);
-  else if (nch <= kWave * 2) launch_u<WT, RB, 2, true, PRO, EPI>(a, grid, block, lds, s);
-  else if (nch <= kWave * 4) launch_u<WT, RB, 4, true, PRO, EPI>(a, grid, block, lds, s);
-  else if (nch <= kWave * 6) launch_u<WT, RB, 6, true, PRO, EPI>(a, grid, block, lds, s);
-  else if (nch <= kWave * 8) launch_u<WT, RB, 8, true, PRO, EPI>(a, grid, block, lds, s);
-  else if (RB == 1 && nch % (kWave * 11) == 0) launch_u<WT, RB, (RB == 1 ? 11 : 8), false, PRO, EPI>(a, grid, block, lds, s);
-  else launch_u<WT, RB, 8, false, PRO, EPI>(a, grid, block, lds, s);
+  if (nch <= kWave * 1) launch_u<WT, RB, 1, true, PRO, EPI>(a, grid, block, s);
+  else if (nch <= kWave * 2) launch_u<WT, RB, 2, true, PRO, EPI>(a, grid, block, s);
+  else if (nch <= kWave * 4) launch_u<WT, RB, 4, true, PRO, EPI>(a, grid, block, s);
+  else if (nch <= kWave * 6) launch_u<WT, RB, 6, true, PRO, EPI>(a, grid, block, s);
+  else if (nch <= kWave * 8) launch_u<WT, RB, 8, true, PRO, EPI>(a, grid, block, s);
+  else if (RB == 1 && nch % (kWave * 11) == 0) launch_u<WT, RB, (RB == 1 ? 11 : 8), false, PRO, EPI>(a, grid, block, s);
+  else launch_u<WT, RB, 8, false, PRO, EPI>(a, grid, block, s);
   return hipGetLastError();
 }
 
@@ -373,6 +428,7 @@ static hipError_t dispatch_kind(int pro, int epi, int rb, const GemvArgs& a, int
   if (pro == PRO_COPY && epi == EPI_STORE) return dispatch_rb<WT, PRO_COPY, EPI_STORE>(rb, a, blocks, s);
   if (pro == PRO_RMSNORM && epi == EPI_DEPTH_QKV) return dispatch_rb<WT, PRO_RMSNORM, EPI_DEPTH_QKV>(rb, a, blocks, s);
   if (pro == PRO_DEPTH_ATTN && epi == EPI_RESID) return dispatch_rb<WT, PRO_DEPTH_ATTN, EPI_RESID>(rb, a, blocks, s);
+  if (pro == PRO_ATTN_MERGE && epi == EPI_RESID) return dispatch_rb<WT, PRO_ATTN_MERGE, EPI_RESID>(rb, a, blocks, s);
   return hipErrorInvalidValue;
 }
 

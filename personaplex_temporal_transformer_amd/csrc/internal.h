@@ -18,11 +18,12 @@ struct EmbedArgs {
   long long* state;                 // if non-null, state[0] := pos (decode position)
   long long pos;
   int n_streams, D, rows;
-  // RoPE table of this position (decode): rope[2j] = cos(pos * omega_j),
-  // rope[2j+1] = sin(pos * omega_j), omega_j = theta^(-2j/d_head), angles in float64
+  // RoPE table of this position (decode), computed on the host in float64 and rounded:
+  // rope_cs[2j] = cos(pos * omega_j), rope_cs[2j+1] = sin(pos * omega_j), with
+  // omega_j = theta^(-2j/d_head); the kernel copies it to `rope` (device) for the step.
   float* rope;
   int dh;
-  double log_theta;
+  float rope_cs[128];
 };
 hipError_t launch_embed(const EmbedArgs& a, bool bf16, hipStream_t s);
 
@@ -31,6 +32,7 @@ enum GemvPro {
   PRO_COPY = 0,        // x as given
   PRO_RMSNORM = 1,     // alpha * x / sqrt(mean(x^2) + eps)
   PRO_DEPTH_ATTN = 2,  // x = depth attention output computed from q and the depth cache
+  PRO_ATTN_MERGE = 3,  // x = merge of the decode-attention split partials (<= 8 splits)
 };
 enum GemvEpi {
   EPI_STORE = 0,   // out[row] = W x
@@ -70,6 +72,10 @@ struct GemvArgs {
   const float* av;
   int aH, adh, acap, aq_pos, awin;
   float ascale;
+  // PRO_ATTN_MERGE: partial outputs [H][S][dh] and (max, sum) pairs [H][S][2]
+  const float* po;
+  const float* pml;
+  int pS;
 };
 // rows_per_group: 2 or 4; blocks: workgroups of 8 waves (normally one per CU).
 hipError_t launch_gemv(int pro, int epi, bool bf16, int rows_per_group, const GemvArgs& a,
@@ -83,8 +89,10 @@ struct AttnDecodeArgs {
   const long long* state;
   int C, H, S;          // S = splits of the key range per head
   float scale;
-  float* part;          // [H][S][dh + 2] partial (o, m, l)
-  float* out;           // [H * dh]
+  float* part_o;        // [H][S][dh] partial outputs (unnormalised)
+  float* part_ml;       // [H][S][2] partial (max, sum)
+  float* out;           // [H * dh], written by the combine kernel
+  int combine;          // 1: launch the combine kernel; 0: the consumer merges
 };
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, bool bf16, int dh, hipStream_t s);
 

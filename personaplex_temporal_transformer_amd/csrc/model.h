@@ -35,7 +35,8 @@ struct pp_model {
   float* q = nullptr;        // rotated query [D]
   float* o = nullptr;        // attention output [D]
   float* s = nullptr;        // SiLU(g) * z [F]
-  float* part = nullptr;     // attention partials [H][S][dh + 2]
+  float* part_o = nullptr;   // attention partial outputs [H][S][dh]
+  float* part_ml = nullptr;  // attention partial (max, sum) [H][S][2]
   long long* state = nullptr;  // [0] = position of the frame being decoded
   float* rope = nullptr;       // [dh] cos/sin table of that position
   int S = 16;                // attention splits per head
