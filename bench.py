@@ -44,6 +44,20 @@ def w_in_bytes(cfg):
     return 2 * F * D * 2 + D * 4 + D * 4 + F * 4
 
 
+def measured_traffic():
+    """HBM bytes per launch of the W_in kernel from the committed counter runs
+    (profiles/decode_w_in_traffic.json), or None once the GEMV source has changed since."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "decode_w_in_traffic.json")))
+        src = open(os.path.join(ROOT, "personaplex_temporal_transformer_amd", "csrc", "gemv.hip"), "rb").read()
+    except (OSError, ValueError):
+        return None
+    if rec.get("gemv_source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
 def make_device_weights(cfg, seed):
     import torch
     g = torch.Generator(device="cuda")
@@ -183,9 +197,11 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", type=int, default=-1, help="1: HIP graph replay, 0: direct launches, -1: auto")
+    ap.add_argument("--graph", type=int, default=0, help="1: time HIP graph replays, 0: direct launches")
     ap.add_argument("--trace-layer", type=int, default=16)
     ap.add_argument("--no-depformer", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the run, copy 1 GiB device-to-device 3 times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -222,20 +238,19 @@ def main():
         model.trace(-1)
         return start.elapsed_time(end) / n, tr
 
-    # warm-up (also captures the graph), then pick the launch mode when asked to
-    run(args.warmup, 0, True)
-    mode = args.graph
+    # warm-up, then K timed frames. The dominant kernel (layer `trace_layer`'s fused
+    # RMSNorm + W_in + SiLU-product GEMV) is bracketed with HIP events on the launch
+    # stream in every timed frame, which needs direct launches (a replayed graph cannot
+    # host per-launch events); --graph 1 times graph replays and the kernel separately.
+    run(args.warmup, 0, args.graph == 1)
     probe = {}
-    if mode < 0:
-        for g in (True, False):
-            probe[g] = run(max(3, args.steps // 10), args.warmup, g)[0]
-        mode = 1 if probe[True] <= probe[False] else 0
-    # timed region: K frames; the dominant kernel is bracketed with HIP events on the
-    # launch stream in one layer per frame (direct launches when traced)
-    ms, (n_tr, us_win) = run(args.steps, args.warmup, bool(mode), args.trace_layer if mode == 0 else -1)
-    if mode == 1:
-        # graph replay cannot host per-launch events: time the kernel in a direct-launch pass
+    if args.graph == 1:
+        ms, _ = run(args.steps, args.warmup, True)
         _, (n_tr, us_win) = run(args.steps, args.warmup, False, args.trace_layer)
+        mode = 1
+    else:
+        ms, (n_tr, us_win) = run(args.steps, args.warmup, False, args.trace_layer)
+        mode = 0
     pos, _ = kv.info()
     fb = frame_bytes(cfg, C)
     win_b = w_in_bytes(cfg)
@@ -265,11 +280,17 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "k_gemv RMSNorm+W_in+SiLU-product (layer %d)" % args.trace_layer,
                      "achieved": round(achieved_win, 1) if achieved_win else None, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved_win / HBM_PEAK_GBPS, 4) if achieved_win else None,
-                     "traffic": None, "bytes_per_launch": win_b, "mean_us": round(us_win, 3),
+                     "traffic": measured_traffic(), "bytes_per_launch": win_b, "mean_us": round(us_win, 3),
                      "launches_timed": n_tr},
-        "launch_probe_ms": {("graph" if k else "direct"): round(v, 4) for k, v in probe.items()},
         "final_position": pos,
     }
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     if not args.no_depformer:
         model.close()
         kv.close()
