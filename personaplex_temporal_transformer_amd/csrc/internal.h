@@ -127,3 +127,38 @@ struct DepthSelectArgs {
 };
 hipError_t launch_depth_select(const DepthSelectArgs& a, bool bf16, hipStream_t s);
 }  // namespace pp
+
+namespace pp {
+// ---------------------------------------------------------------- prefill
+enum GemmEpi { GEPI_QKV = 0, GEPI_RESID = 1, GEPI_SWIGLU = 2 };
+
+struct GemmArgs {
+  const void* A;        // [M][K] activations, row-major (bf16 or float32)
+  const void* B;        // weights, row-major [rows][K]
+  int M, N, K;          // N = output columns (GEPI_SWIGLU: N = F, B has 2F rows)
+  // GEPI_QKV: columns Q|K|V; RoPE on Q and K with rope[row][d] (cos, sin pairs);
+  // Q -> q_out [H][M][dh]; K, V -> ring slots (p0 + row) mod C of [H][C][dh]
+  void* q_out;
+  void* kc;
+  void* vc;
+  const float* rope;
+  int D, dh, C, p0;
+  float* x;             // GEPI_RESID: x[row][col] += (A W^T)[row][col], float32 [M][N]
+  void* s_out;          // GEPI_SWIGLU: [M][F] = SiLU(g) * z
+  int F;
+};
+hipError_t launch_gemm(int epi, bool bf16, const GemmArgs& g, int n_cu, hipStream_t s);
+
+struct AttnPrefillArgs {
+  const void* q;        // [H][T][dh] rotated queries (positions p0..p0+T-1)
+  const void* k;        // ring of this layer [H][C][dh]; key of position p in slot p mod C
+  const void* v;
+  void* out;            // [T][H*dh]
+  int T, H, C, p0;
+  float scale;
+};
+hipError_t launch_attn_prefill(const AttnPrefillArgs& a, bool bf16, int dh, hipStream_t s);
+
+// rope[t][2j] = cos((p0 + t) * omega_j), rope[t][2j+1] = sin(...), angles in float64
+hipError_t launch_rope_rows(float* rope, int T, int p0, int dh, double log_theta, hipStream_t s);
+}  // namespace pp

@@ -50,6 +50,7 @@ struct pp_model {
   void* pq = nullptr;          // rotated Q [H][T][dh]
   void* pa = nullptr;          // attention output [T][D]
   void* pg = nullptr;          // SiLU(g)*z [T][F]
+  float* prope = nullptr;      // RoPE table [T][dh] (cos, sin pairs)
 
   int32_t* ids_pinned = nullptr;
   size_t ids_cap = 0;

@@ -1,6 +1,11 @@
 // Full-sequence (prefill) path of the temporal model: workspace and launch order.
+//
+// "PersonaPlex native LM audit", section 3: every block of the temporal transformer
+// applied to T frames at positions 0..T-1 at once, causal attention among them, K and V
+// of every frame left in the ring so that decoding continues at position T.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <string>
 
 #include "internal.h"
@@ -10,13 +15,33 @@
 using namespace pp;
 
 pp_status pp_model::alloc_prefill() {
-  const int T = max_T > 0 ? max_T : 0;
+  const size_t T = max_T > 0 ? (size_t)max_T : 1;
+  const size_t D = cfg.d_model, F = cfg.d_ff, dh = cfg.d_head;
+  const size_t esz = bf16 ? 2 : 4;
   const int ns = cfg.n_audio + 1;
   size_t bytes = 0;
   auto take = [&](size_t n) { size_t off = bytes; bytes += (n + 255) / 256 * 256; return off; };
-  const size_t oid = take(sizeof(int32_t) * (size_t)(T > 0 ? T : 1) * ns);
+  const size_t oid = take(sizeof(int32_t) * T * ns);
+  size_t ox = 0, ou = 0, oq = 0, oa = 0, og = 0, orope = 0;
+  if (max_T > 0) {
+    ox = take(sizeof(float) * T * D);
+    ou = take(esz * T * D);
+    oq = take(esz * T * D);
+    oa = take(esz * T * D);
+    og = take(esz * T * F);
+    orope = take(sizeof(float) * T * dh);
+  }
   if (hipMalloc(&pws, bytes) != hipSuccess) return pp_fail(PP_E_HIP, "hipMalloc of prefill workspace failed");
-  ids_dev = reinterpret_cast<int32_t*>(static_cast<char*>(pws) + oid);
+  char* b = static_cast<char*>(pws);
+  ids_dev = reinterpret_cast<int32_t*>(b + oid);
+  if (max_T > 0) {
+    px = reinterpret_cast<float*>(b + ox);
+    pu = b + ou;
+    pq = b + oq;
+    pa = b + oa;
+    pg = b + og;
+    prope = reinterpret_cast<float*>(b + orope);
+  }
   return PP_OK;
 }
 
@@ -25,10 +50,84 @@ void pp_model::free_prefill() {
   pws = nullptr;
 }
 
+static pp_status hip_fail(const char* what, hipError_t e) {
+  return pp_fail(PP_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
 extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* ids_host, int32_t T,
                                          float* h_out_dev, void* stream) {
   if (!m || !kv || !ids_host || !h_out_dev) return pp_fail(PP_E_ARG, "NULL argument");
-  (void)T;
-  (void)stream;
-  return pp_fail(PP_E_ARG, "prefill is not available in this build");
+  if (kv->m != m) return pp_fail(PP_E_ARG, "kv ring belongs to another model");
+  if (kv->pos != 0) return pp_fail(PP_E_ARG, "prefill needs an empty ring (position 0); call pp_kv_reset");
+  const pp_temporal_config& c = m->cfg;
+  if (T < 1 || T > c.context || T > m->max_T)
+    return pp_fail(PP_E_CAPACITY, "T must be in [1, min(context, max_prefill_T)]");
+  const int D = c.d_model, F = c.d_ff, H = c.n_heads, dh = c.d_head, C = c.context;
+  if (m->bf16) {
+    if (D % 128 || F % 64) return pp_fail(PP_E_ARG, "bf16 prefill needs d_model % 128 == 0 and d_ff % 64 == 0");
+    if (dh != 64 && dh != 128) return pp_fail(PP_E_ARG, "bf16 prefill needs d_head 64 or 128");
+  } else if (dh != 64 && dh != 128) {
+    return pp_fail(PP_E_ARG, "prefill needs d_head 64 or 128");
+  }
+  pp_status st = m->check_ids(ids_host, (size_t)T * kv->B);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf = m->bf16;
+
+  EmbedArgs a{};
+  m->embed_tables(a);
+  a.out = m->px;
+  a.rows = T;
+  if ((st = m->stage_ids(ids_host, (size_t)T * a.n_streams, s))) return st;
+  a.ids_dev = m->ids_dev;
+  hipError_t e = launch_embed(a, bf, s);
+  if (e != hipSuccess) return hip_fail("prefill embed", e);
+  e = launch_rope_rows(m->prope, T, 0, dh, std::log(c.rope_theta), s);
+  if (e != hipSuccess) return hip_fail("prefill rope table", e);
+
+  const size_t esz = bf ? 2 : 4;
+  const size_t per_kv = (size_t)kv->B * H * C * dh * esz;
+  float* u32 = bf ? nullptr : static_cast<float*>(m->pu);
+  void* u16 = bf ? m->pu : nullptr;
+  for (int l = 0; l < c.n_layers; ++l) {
+    char* kbase = static_cast<char*>(kv->ring) + (size_t)(2 * l) * per_kv;
+    char* vbase = kbase + per_kv;
+    e = launch_rmsnorm_rows(m->px, m->norm1[l], (float)c.eps, D, T, u32, u16, s);
+    if (e != hipSuccess) return hip_fail("prefill norm1", e);
+
+    GemmArgs g{};
+    g.A = m->pu; g.B = m->w_qkv[l]; g.M = T; g.N = 3 * D; g.K = D;
+    g.q_out = m->pq; g.kc = kbase; g.vc = vbase; g.rope = m->prope;
+    g.D = D; g.dh = dh; g.C = C; g.p0 = 0;
+    e = launch_gemm(GEPI_QKV, bf, g, m->n_cu, s);
+    if (e != hipSuccess) return hip_fail("prefill QKV", e);
+
+    AttnPrefillArgs at{};
+    at.q = m->pq; at.k = kbase; at.v = vbase; at.out = m->pa;
+    at.T = T; at.H = H; at.C = C; at.p0 = 0; at.scale = 1.0f / std::sqrt((float)dh);
+    e = launch_attn_prefill(at, bf, dh, s);
+    if (e != hipSuccess) return hip_fail("prefill attention", e);
+
+    GemmArgs go{};
+    go.A = m->pa; go.B = m->w_o[l]; go.M = T; go.N = D; go.K = D; go.x = m->px;
+    e = launch_gemm(GEPI_RESID, bf, go, m->n_cu, s);
+    if (e != hipSuccess) return hip_fail("prefill W_O", e);
+
+    e = launch_rmsnorm_rows(m->px, m->norm2[l], (float)c.eps, D, T, u32, u16, s);
+    if (e != hipSuccess) return hip_fail("prefill norm2", e);
+
+    GemmArgs gi{};
+    gi.A = m->pu; gi.B = m->w_in[l]; gi.M = T; gi.N = F; gi.K = D; gi.F = F; gi.s_out = m->pg;
+    e = launch_gemm(GEPI_SWIGLU, bf, gi, m->n_cu, s);
+    if (e != hipSuccess) return hip_fail("prefill W_in", e);
+
+    GemmArgs gw{};
+    gw.A = m->pg; gw.B = m->w_out[l]; gw.M = T; gw.N = D; gw.K = F; gw.x = m->px;
+    e = launch_gemm(GEPI_RESID, bf, gw, m->n_cu, s);
+    if (e != hipSuccess) return hip_fail("prefill W_out", e);
+  }
+  e = launch_rmsnorm_rows(m->px, m->out_norm, (float)c.eps, D, T, h_out_dev, nullptr, s);
+  if (e != hipSuccess) return hip_fail("prefill final norm", e);
+  kv->pos = T;
+  return PP_OK;
 }
