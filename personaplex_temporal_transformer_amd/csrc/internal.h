@@ -146,6 +146,10 @@ struct GemmArgs {
   float* x;             // GEPI_RESID: x[row][col] += (A W^T)[row][col], float32 [M][N]
   void* s_out;          // GEPI_SWIGLU: [M][F] = SiLU(g) * z
   int F;
+  // GEPI_QKV, bf16 only: if non-null, V is also written transposed, vt[H][dh][vt_pitch],
+  // key t in column vt_perm(t) (bits 2 and 3 of t swapped), for the prefill attention
+  void* vt;
+  int vt_pitch;
 };
 hipError_t launch_gemm(int epi, bool bf16, const GemmArgs& g, int n_cu, hipStream_t s);
 
@@ -153,6 +157,8 @@ struct AttnPrefillArgs {
   const void* q;        // [H][T][dh] rotated queries (positions p0..p0+T-1)
   const void* k;        // ring of this layer [H][C][dh]; key of position p in slot p mod C
   const void* v;
+  const void* vt;       // bf16: V transposed as written by the QKV GEMM (p0 must be 0)
+  int vt_pitch;
   void* out;            // [T][H*dh]
   int T, H, C, p0;
   float scale;

@@ -51,6 +51,8 @@ struct pp_model {
   void* pa = nullptr;          // attention output [T][D]
   void* pg = nullptr;          // SiLU(g)*z [T][F]
   float* prope = nullptr;      // RoPE table [T][dh] (cos, sin pairs)
+  void* pvt = nullptr;         // bf16: V transposed [H][dh][vt_pitch] (zero past T)
+  int vt_pitch = 0;            // max_T rounded up to 64
 
   int32_t* ids_pinned = nullptr;
   size_t ids_cap = 0;

@@ -22,7 +22,8 @@ pp_status pp_model::alloc_prefill() {
   size_t bytes = 0;
   auto take = [&](size_t n) { size_t off = bytes; bytes += (n + 255) / 256 * 256; return off; };
   const size_t oid = take(sizeof(int32_t) * T * ns);
-  size_t ox = 0, ou = 0, oq = 0, oa = 0, og = 0, orope = 0;
+  size_t ox = 0, ou = 0, oq = 0, oa = 0, og = 0, orope = 0, ovt = 0;
+  vt_pitch = (int)((T + 63) / 64 * 64);
   if (max_T > 0) {
     ox = take(sizeof(float) * T * D);
     ou = take(esz * T * D);
@@ -30,6 +31,7 @@ pp_status pp_model::alloc_prefill() {
     oa = take(esz * T * D);
     og = take(esz * T * F);
     orope = take(sizeof(float) * T * dh);
+    if (bf16) ovt = take(2 * (size_t)cfg.n_heads * dh * vt_pitch);
   }
   if (hipMalloc(&pws, bytes) != hipSuccess) return pp_fail(PP_E_HIP, "hipMalloc of prefill workspace failed");
   char* b = static_cast<char*>(pws);
@@ -41,6 +43,12 @@ pp_status pp_model::alloc_prefill() {
     pa = b + oa;
     pg = b + og;
     prope = reinterpret_cast<float*>(b + orope);
+    if (bf16) {
+      pvt = b + ovt;
+      // columns past T are read by the attention (as zero-weighted values): keep them finite
+      if (hipMemset(pvt, 0, 2 * (size_t)cfg.n_heads * dh * vt_pitch) != hipSuccess)
+        return pp_fail(PP_E_HIP, "hipMemset of the prefill V copy failed");
+    }
   }
   return PP_OK;
 }
@@ -99,11 +107,12 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
     g.A = m->pu; g.B = m->w_qkv[l]; g.M = T; g.N = 3 * D; g.K = D;
     g.q_out = m->pq; g.kc = kbase; g.vc = vbase; g.rope = m->prope;
     g.D = D; g.dh = dh; g.C = C; g.p0 = 0;
+    g.vt = m->pvt; g.vt_pitch = m->vt_pitch;
     e = launch_gemm(GEPI_QKV, bf, g, m->n_cu, s);
     if (e != hipSuccess) return hip_fail("prefill QKV", e);
 
     AttnPrefillArgs at{};
-    at.q = m->pq; at.k = kbase; at.v = vbase; at.out = m->pa;
+    at.q = m->pq; at.k = kbase; at.v = vbase; at.vt = m->pvt; at.vt_pitch = m->vt_pitch; at.out = m->pa;
     at.T = T; at.H = H; at.C = C; at.p0 = 0; at.scale = 1.0f / std::sqrt((float)dh);
     e = launch_attn_prefill(at, bf, dh, s);
     if (e != hipSuccess) return hip_fail("prefill attention", e);

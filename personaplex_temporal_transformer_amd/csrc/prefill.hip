@@ -8,6 +8,8 @@
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulation); operands are bf16 (activations are
 // rounded to bf16 once per product), statistics and the residual stream stay fp32.
 // float32 path (small shapes, fp32 parity): plain FMA kernels with the same epilogues.
+#include <stdlib.h>
+
 #include "device.h"
 #include "internal.h"
 
@@ -66,26 +68,74 @@ __device__ __forceinline__ void gemm_store(const GemmArgs& g, int row, int col, 
 
 // ---------------------------------------------------------------- bf16 MFMA GEMM
 
-constexpr int GBM = 128, GBN = 128, GBK = 64, GLD = GBK + 8;  // LDS rows padded by 16 bytes
+constexpr int GBK = 64;
 
-// C[M][N] = A[M][K] B[N][K]^T for one 128 x 128 tile per workgroup (4 waves, each 64 x 64 as
-// 2 x 2 tiles of 32 x 32 x 16 MFMAs). The next k-tile is prefetched into registers while
-// the current one is multiplied from LDS. GEPI_SWIGLU: the B tile holds W_in rows
-// j0..j0+63 (g) and F+j0..F+j0+63 (z), and wave (wm, wn) multiplies g rows wn*32.. and z
-// rows 64+wn*32.., so g and z of the same output land in the same lane.
-template <int EPI>
-__global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[GBM * GLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[GBN * GLD];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w & 1, wn = w >> 1;
-  const int n_tm = (g.M + GBM - 1) / GBM;
-  const int n_tn = EPI == GEPI_SWIGLU ? g.F / 64 : g.N / GBN;
+// LDS tiles are rows of 64 bf16 (8 chunks of 16 bytes) without padding; chunk kc of row r
+// sits at r*8 + (kc ^ (r & 7)), so the 32 rows read by one MFMA fragment load spread over
+// all banks.
+__device__ __forceinline__ int swz(int r, int kc) { return r * 8 + (kc ^ (r & 7)); }
+
+// Column of key t in the transposed V copy: bits 2 and 3 of t swapped, so that within
+// each group of 16 keys the order is 0-3, 8-11, 4-7, 12-15 -- the order in which one
+// lane holds probabilities after the S^T product (see k_attn_prefill_bf16).
+__device__ __forceinline__ int vt_perm(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
+
+// 16 bytes per lane from a buffer into LDS: lane i's bytes land at LDS byte address
+// lds_base + 16*i (lds_base is wave-uniform, passed through M0). Issued from inline
+// assembly so that the compiler does not add a wait on these loads before every LDS read
+// (it cannot tell the pipeline stages apart); the kernel waits for them explicitly with
+// vm_wait_barrier. No other instruction in these kernels uses M0.
+__device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_base) : "memory");
+}
+
+// Buffer resource words for [base, base + bytes): raw addressing, no stride, reads past
+// the end return zero.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// LDS byte address of a __shared__ object (the low half of its generic address).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// Wait until at most N vector-memory operations of this wave are outstanding and all its
+// LDS operations are done, then synchronise the workgroup. Loads into LDS complete in
+// issue order, so N = the loads issued after the ones that must have landed.
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// C[M][N] = A[M][K] B[N][K]^T. Workgroup = WM x WN waves, tile BM x BN with BM = WM*32*MI,
+// BN = WN*64; wave (wm, wn) owns rows wm*32*MI.. and 64 columns as MI x 2 tiles of 32 x 32
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation). A and B k-tiles (64 wide) go from global
+// memory straight into LDS (buffer loads with the LDS flag: no registers, no LDS write
+// instructions) through NS stages, NS-1 k-tiles ahead of the multiply; one barrier per
+// k-tile. Rows of A past M read as zeros (out of the buffer's range) and are not stored.
+// GEPI_SWIGLU: the B tile holds W_in rows j0..j0+BN/2-1 (g) and F+j0.. (z); wave (wm, wn)
+// multiplies g rows wn*32.. and z rows BN/2+wn*32.., so g and z of one output share a lane.
+template <int EPI, int WM, int WN, int MI, int NS>
+__global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(GemmArgs g) {
+  constexpr int NW = WM * WN;
+  constexpr int BM = WM * 32 * MI, BN = WN * 64;
+  constexpr int AL = BM / (8 * NW);   // LDS-load instructions per wave per k-tile (A)
+  constexpr int BL = BN / (8 * NW);   // (B)
+  static_assert(AL * 8 * NW == BM && BL * 8 * NW == BN, "tile rows must split over the waves");
+  __shared__ u32x4 As[NS][BM * 8];
+  __shared__ u32x4 Bs[NS][BN * 8];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w % WM, wn = w / WM;
+  const int n_tm = (g.M + BM - 1) / BM;
+  const int n_tn = EPI == GEPI_SWIGLU ? g.F / (BN / 2) : g.N / BN;
   const int tiles = n_tm * n_tn;
 
   // Tile order: workgroup b runs on XCD b mod 8; give each XCD a contiguous range of tiles,
-  // walked in groups of 8 M-tiles per N-tile so concurrent workgroups of an XCD share the
-  // weight tile (and a few activation tiles) in that XCD's L2.
+  // walked in groups of 8 M-tiles per N-tile so concurrent workgroups of an XCD share
+  // weight and activation k-slices in that XCD's L2.
   int b = blockIdx.x;
   if (tiles % 8 == 0) b = (b % 8) * (tiles / 8) + b / 8;
   constexpr int GROUP = 8;
@@ -95,82 +145,93 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
   const int tm = first_m + (b % (GROUP * n_tn)) % gsize;
   const int tn = (b % (GROUP * n_tn)) / gsize;
 
-  const int m0 = tm * GBM;
-  const uint16_t* A = static_cast<const uint16_t*>(g.A);
-  const uint16_t* B = static_cast<const uint16_t*>(g.B);
+  const int m0 = tm * BM;
   const int K = g.K;
   auto brow = [&](int r) -> int {
-    if (EPI == GEPI_SWIGLU) return r < 64 ? tn * 64 + r : g.F + tn * 64 + (r - 64);
-    return tn * GBN + r;
+    if (EPI == GEPI_SWIGLU) return r < BN / 2 ? tn * (BN / 2) + r : g.F + tn * (BN / 2) + (r - BN / 2);
+    return tn * BN + r;
   };
+  const u32x4 ar = rsrc_words(g.A, (uint32_t)((size_t)g.M * K * 2));
+  const u32x4 br = rsrc_words(g.B, (uint32_t)((size_t)(EPI == GEPI_SWIGLU ? 2 * g.F : g.N) * K * 2));
+  // Instruction j of wave w fills rows R0 = (w + NW*j)*8 .. +7 (1 KB of LDS, lane i at
+  // chunk position R0*8 + i): lane i fetches row R0 + i/8, k-chunk (i%8) ^ (i/8), which is
+  // where swz() puts that chunk.
+  const int lrow = lane >> 3, lkc = (lane & 7) ^ (lane >> 3);
+  uint32_t aoff[AL], boff[BL];
+#pragma unroll
+  for (int j = 0; j < AL; ++j) {
+    const int r = (w + NW * j) * 8 + lrow;
+    aoff[j] = (uint32_t)(((size_t)(m0 + r) * K + lkc * 8) * 2);
+  }
+#pragma unroll
+  for (int j = 0; j < BL; ++j) {
+    const int r = (w + NW * j) * 8 + lrow;
+    boff[j] = (uint32_t)(((size_t)brow(r) * K + lkc * 8) * 2);
+  }
+  auto issue = [&](int kt, int st) {
+#pragma unroll
+    for (int j = 0; j < AL; ++j)
+      lds_dma16(ar, aoff[j], kt * GBK * 2, lds_addr(&As[st][(w + NW * j) * 64]));
+#pragma unroll
+    for (int j = 0; j < BL; ++j)
+      lds_dma16(br, boff[j], kt * GBK * 2, lds_addr(&Bs[st][(w + NW * j) * 64]));
+  };
+  auto bcol0 = [&](int j) -> int { return EPI == GEPI_SWIGLU ? j * (BN / 2) + wn * 32 : wn * 64 + j * 32; };
 
-  u32x4 ra[4], rb[4];
-  auto gload = [&](int kt) {
+  f32x16 acc[MI][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + 256 * i, r = id >> 3, kc = id & 7;
-      const int am = m0 + r < g.M ? m0 + r : g.M - 1;
-      ra[i] = *reinterpret_cast<const u32x4*>(A + (size_t)am * K + kt * GBK + kc * 8);
-      rb[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(B + (size_t)brow(r) * K + kt * GBK + kc * 8));
-    }
-  };
-  auto sstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + 256 * i, r = id >> 3, kc = id & 7;
-      *reinterpret_cast<u32x4*>(As + r * GLD + kc * 8) = ra[i];
-      *reinterpret_cast<u32x4*>(Bs + r * GLD + kc * 8) = rb[i];
-    }
-  };
-  auto bcol0 = [&](int j) -> int { return EPI == GEPI_SWIGLU ? j * 64 + wn * 32 : wn * 64 + j * 32; };
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int nk = K / GBK;
-  gload(0);
-  sstore();
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload(kt + 1);
+  auto compute = [&](int st) {
 #pragma unroll
     for (int ks = 0; ks < GBK / 16; ++ks) {
-      bf16x8 av[2], bv[2];
+      const int kc = ks * 2 + (lane >> 5);
+      bf16x8 av[MI], bv[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        av[i] = *reinterpret_cast<const bf16x8*>(As + (wm * 64 + i * 32 + (lane & 31)) * GLD + ks * 16 + 8 * (lane >> 5));
+      for (int i = 0; i < MI; ++i)
+        av[i] = __builtin_bit_cast(bf16x8, As[st][swz(wm * 32 * MI + i * 32 + (lane & 31), kc)]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bv[j] = *reinterpret_cast<const bf16x8*>(Bs + (bcol0(j) + (lane & 31)) * GLD + ks * 16 + 8 * (lane >> 5));
+      for (int j = 0; j < 2; ++j) bv[j] = __builtin_bit_cast(bf16x8, Bs[st][swz(bcol0(j) + (lane & 31), kc)]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
     }
-    __syncthreads();
-    if (kt + 1 < nk) {
-      sstore();
-      __syncthreads();
-    }
+  };
+
+  constexpr int LPT = AL + BL;  // loads per wave per k-tile
+  const int nk = K / GBK;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(s, s);
+  int st = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    // tile kt must have landed; tiles kt+1 .. kt+NS-2 may still be in flight
+    const int ahead = nk - 1 - kt < NS - 2 ? nk - 1 - kt : NS - 2;
+    if (NS >= 4 && ahead >= 2) vm_wait_barrier<(NS >= 4 ? 2 : 0) * LPT>();
+    else if (NS >= 3 && ahead >= 1) vm_wait_barrier<(NS >= 3 ? 1 : 0) * LPT>();
+    else vm_wait_barrier<0>();
+    if (kt + NS - 1 < nk) issue(kt + NS - 1, st == 0 ? NS - 1 : st - 1);
+    compute(st);
+    st = st + 1 == NS ? 0 : st + 1;
   }
 
   // ---- epilogue: acc[i][j][4*jj + ii] is (row 8*jj + 4*(lane/32) + ii, col lane%32) of tile (i, j)
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const int row = m0 + wm * 64 + i * 32 + 8 * jj + 4 * (lane >> 5) + ii;
+        const int row = m0 + wm * 32 * MI + i * 32 + 8 * jj + 4 * (lane >> 5) + ii;
         if (EPI == GEPI_SWIGLU) {
           const float gv = acc[i][0][4 * jj + ii], zv = acc[i][1][4 * jj + ii];
           if (row < g.M) {
-            const int col = tn * 64 + wn * 32 + (lane & 31);
+            const int col = tn * (BN / 2) + wn * 32 + (lane & 31);
             static_cast<uint16_t*>(g.s_out)[(size_t)row * g.F + col] = f32_to_bf16(silu(gv) * zv);
           }
         } else {
@@ -178,11 +239,39 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
           for (int j = 0; j < 2; ++j) {
             const float v = acc[i][j][4 * jj + ii];
             const float partner = dpp_xor1(v);  // column col ^ 1 of the same row
-            const int col = tn * GBN + wn * 64 + j * 32 + (lane & 31);
+            const int col = tn * BN + wn * 64 + j * 32 + (lane & 31);
             if (row < g.M) gemm_store<bf16_t, EPI>(g, row, col, v, partner);
           }
         }
       }
+  // V^T copy for the prefill attention: four consecutive rows (keys) of one column are
+  // four consecutive (permuted) positions, stored as one 8-byte word.
+  if (EPI == GEPI_QKV && g.vt && tn * BN >= 2 * g.D) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int w2 = tn * BN + wn * 64 + j * 32 + (lane & 31) - 2 * g.D;
+      const int head = w2 / g.dh, d = w2 - head * g.dh;
+      uint16_t* vrow = static_cast<uint16_t*>(g.vt) + ((size_t)head * g.dh + d) * g.vt_pitch;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int r0 = m0 + wm * 32 * MI + i * 32 + 8 * jj + 4 * (lane >> 5);
+          const int pos = vt_perm(r0);
+          uint16_t e[4];
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) e[ii] = f32_to_bf16(acc[i][j][4 * jj + ii]);
+          if (r0 + 3 < g.M) {
+            *reinterpret_cast<u32x2*>(vrow + pos) =
+                u32x2{(uint32_t)e[0] | ((uint32_t)e[1] << 16), (uint32_t)e[2] | ((uint32_t)e[3] << 16)};
+          } else {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+              if (r0 + ii < g.M) vrow[pos + ii] = e[ii];
+          }
+        }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- float32 GEMM (FMA)
@@ -247,12 +336,70 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs g) {
   }
 }
 
+// MFMA tile configurations (waves WM x WN, MI 32-row tiles per wave, LDS stages).
+struct GemmCfg {
+  int wm, wn, mi, ns;
+  int bm() const { return wm * 32 * mi; }
+  int bn() const { return wn * 64; }
+};
+static const GemmCfg kGemmCfgs[] = {
+    {2, 4, 3, 2},  // 192 x 256, 8 waves
+    {2, 4, 2, 3},  // 128 x 256, 8 waves
+    {2, 4, 4, 2},  // 256 x 256, 8 waves
+    {2, 2, 3, 3},  // 192 x 128, 4 waves
+    {2, 2, 2, 4},  // 128 x 128, 4 waves
+};
+constexpr int kNumGemmCfgs = sizeof(kGemmCfgs) / sizeof(kGemmCfgs[0]);
+
+static bool cfg_fits(const GemmCfg& c, const GemmArgs& g, int epi) {
+  return epi == GEPI_SWIGLU ? g.F % (c.bn() / 2) == 0 : g.N % c.bn() == 0;
+}
+
+// The configuration with the least work on the busiest CU, ceil(tiles / n_cu) * tile
+// area, scaled by a per-configuration efficiency (wider tiles reuse more per loaded byte).
+static int pick_cfg(const GemmArgs& g, int epi, int n_cu) {
+  static const double eff[kNumGemmCfgs] = {1.0, 0.95, 1.0, 0.85, 0.8};
+  int best = -1;
+  double best_cost = 0;
+  for (int i = 0; i < kNumGemmCfgs; ++i) {
+    const GemmCfg& c = kGemmCfgs[i];
+    if (!cfg_fits(c, g, epi)) continue;
+    const long n_tn = epi == GEPI_SWIGLU ? g.F / (c.bn() / 2) : g.N / c.bn();
+    const long tiles = (long)((g.M + c.bm() - 1) / c.bm()) * n_tn;
+    const double cost = (double)((tiles + n_cu - 1) / n_cu) * c.bm() * c.bn() / eff[i];
+    if (best < 0 || cost < best_cost) {
+      best = i;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+template <int EPI, int WM, int WN, int MI, int NS>
+static void launch_cfg(const GemmArgs& g, hipStream_t s) {
+  constexpr int BM = WM * 32 * MI, BN = WN * 64;
+  const int n_tn = EPI == GEPI_SWIGLU ? g.F / (BN / 2) : g.N / BN;
+  const int n_tm = (g.M + BM - 1) / BM;
+  hipLaunchKernelGGL((k_gemm_bf16<EPI, WM, WN, MI, NS>), dim3(n_tm * n_tn), dim3(WM * WN * 64), 0, s, g);
+}
+
 template <int EPI>
-static hipError_t gemm_dispatch(bool bf16, const GemmArgs& g, hipStream_t s) {
+static hipError_t gemm_dispatch(bool bf16, const GemmArgs& g, int n_cu, hipStream_t s) {
   if (bf16) {
-    const int n_tm = (g.M + GBM - 1) / GBM;
-    const int n_tn = EPI == GEPI_SWIGLU ? g.F / 64 : g.N / GBN;
-    hipLaunchKernelGGL(k_gemm_bf16<EPI>, dim3(n_tm * n_tn), dim3(256), 0, s, g);
+    static const int forced = [] {
+      const char* v = getenv("PP_GEMM_CFG");
+      return v ? atoi(v) : -1;
+    }();
+    int c = forced >= 0 && forced < kNumGemmCfgs && cfg_fits(kGemmCfgs[forced], g, EPI) ? forced
+                                                                                        : pick_cfg(g, EPI, n_cu > 0 ? n_cu : 256);
+    switch (c) {
+      case 0: launch_cfg<EPI, 2, 4, 3, 2>(g, s); break;
+      case 1: launch_cfg<EPI, 2, 4, 2, 3>(g, s); break;
+      case 2: launch_cfg<EPI, 2, 4, 4, 2>(g, s); break;
+      case 3: launch_cfg<EPI, 2, 2, 3, 3>(g, s); break;
+      case 4: launch_cfg<EPI, 2, 2, 2, 4>(g, s); break;
+      default: return hipErrorInvalidValue;
+    }
   } else {
     const int n_tm = (g.M + 63) / 64;
     const int n_tn = EPI == GEPI_SWIGLU ? (g.F + 31) / 32 : (g.N + 63) / 64;
@@ -262,57 +409,90 @@ static hipError_t gemm_dispatch(bool bf16, const GemmArgs& g, hipStream_t s) {
 }
 
 hipError_t launch_gemm(int epi, bool bf16, const GemmArgs& g, int n_cu, hipStream_t s) {
-  (void)n_cu;
   if (g.M <= 0) return hipSuccess;
   if (bf16) {
     // MFMA tiles: K in steps of 64, N in tiles of 128 (SwiGLU: F in tiles of 64)
     if (g.K % GBK) return hipErrorInvalidValue;
-    if (epi == GEPI_SWIGLU ? g.F % 64 : g.N % GBN) return hipErrorInvalidValue;
+    if (epi == GEPI_SWIGLU ? g.F % 64 : g.N % 128) return hipErrorInvalidValue;
+    // buffer loads address A and B with 32-bit byte offsets
+    const size_t b_rows = epi == GEPI_SWIGLU ? 2 * (size_t)g.F : (size_t)g.N;
+    // (rows of the last A tile past M included: they are read as zeros)
+    if (((size_t)g.M + 256) * g.K * 2 > 0xffffffffull || b_rows * g.K * 2 > 0xffffffffull) return hipErrorInvalidValue;
   } else if (epi == GEPI_QKV && (g.dh % 2)) {
     return hipErrorInvalidValue;
   }
   switch (epi) {
-    case GEPI_QKV: return gemm_dispatch<GEPI_QKV>(bf16, g, s);
-    case GEPI_RESID: return gemm_dispatch<GEPI_RESID>(bf16, g, s);
-    case GEPI_SWIGLU: return gemm_dispatch<GEPI_SWIGLU>(bf16, g, s);
+    case GEPI_QKV: return gemm_dispatch<GEPI_QKV>(bf16, g, n_cu, s);
+    case GEPI_RESID: return gemm_dispatch<GEPI_RESID>(bf16, g, n_cu, s);
+    case GEPI_SWIGLU: return gemm_dispatch<GEPI_SWIGLU>(bf16, g, n_cu, s);
   }
   return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------- bf16 flash attention
 
-// Workgroup (query block qb of 128 frames, head h); wave w owns queries qb*128 + 32w ..+31,
-// one per lane column (lane % 32). For each block of 64 keys (up to the causal limit):
-//   S^T = K Q^T   (A = K rows from LDS, B = Q^T kept in registers) -> lane holds the 32
-//                 scores of its query for 32 of the 64 keys; its partner lane (lane ^ 32)
-//                 holds the other 32, so the softmax max/sum need one exchange;
-//   O^T += V^T P^T (A = V^T from LDS, staged transposed; B = P^T straight from the S^T
-//                 registers -- the k index of the product is a fixed permutation of the
-//                 keys, applied identically to V^T).
-// The running max/sum rescale O^T in registers. Causal + window mask per element.
+// Workgroup = 128 queries of one head, 4 waves; wave w owns queries qb*128 + 32w .. +31,
+// one per lane column (lane % 32). Keys go by blocks of 64 through two LDS stages, loaded
+// straight from global memory: K rows from the ring (slot = key, the prefill starts at
+// position 0) and the matching 64 columns of the transposed V copy. Per key block:
+//   S^T = K Q^T   (A = K rows from LDS, B = Q^T kept in registers): lane (q, half) holds
+//                 q's scores for 32 of the 64 keys, its partner lane (lane ^ 32) the other
+//                 32, so the row max and sum need one exchange;
+//   O^T += V^T P^T (A = V^T from LDS, B = P^T straight from the S^T registers: the k index
+//                 of this product runs over the keys in the order the lane holds them,
+//                 which is the column order of the transposed V copy).
+// Softmax in base 2 with the 1/sqrt(d) scale folded into one FMA; the running max/sum
+// rescale O^T in registers only when some lane's max moved. Masks (causal, window, end of
+// sequence) are applied only on key blocks that need them; key blocks entirely in a
+// wave's future are skipped by that wave.
 template <int DH>
-__global__ __launch_bounds__(256) void k_attn_prefill_bf16(AttnPrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a) {
   constexpr int BQ = 128, BKV = 64;
-  constexpr int KLD = DH + 8;    // K tile row pitch (bf16 elements)
-  constexpr int VLD = BKV + 8;   // V^T row pitch (keys)
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BKV * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[DH * VLD];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int h = blockIdx.y;
+  constexpr int KCH = DH / 8;                  // 16-byte chunks per K row
+  constexpr int KRPI = 64 / KCH;               // K rows per LDS-load instruction
+  constexpr int KL = BKV * KCH / 256;          // K loads per wave per key block
+  constexpr int VL = DH * 8 / 256;             // V^T loads per wave per key block
+  __shared__ u32x4 Ks[2][BKV * KCH];
+  __shared__ u32x4 Vs[2][DH * 8];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n_qb = (a.T + BQ - 1) / BQ;
-  const int qb = n_qb - 1 - blockIdx.x;      // longest (latest) query blocks first
+  // longest query blocks first over all heads; head h lands on XCD h mod 8 (H % 8 == 0
+  // keeps a head's keys in one L2)
+  const int qb = n_qb - 1 - (int)blockIdx.x / a.H;
+  const int h = (int)blockIdx.x % a.H;
   const int hi = lane >> 5, ql = lane & 31;
-  const int qi = qb * BQ + w * 32 + ql;      // this lane's query (frame index)
+  const int qw0 = qb * BQ + w * 32;            // first query of this wave
+  const int qi = qw0 + ql;                     // this lane's query
   const int qrow = qi < a.T ? qi : a.T - 1;
-  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
-  const uint16_t* Kg = static_cast<const uint16_t*>(a.k);
-  const uint16_t* Vg = static_cast<const uint16_t*>(a.v);
 
   bf16x8 qr[DH / 16];
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q) + ((size_t)h * a.T + qrow) * DH;
 #pragma unroll
-  for (int ks = 0; ks < DH / 16; ++ks)
-    qr[ks] = *reinterpret_cast<const bf16x8*>(Q + ((size_t)h * a.T + qrow) * DH + ks * 16 + 8 * hi);
+  for (int ks = 0; ks < DH / 16; ++ks) qr[ks] = *reinterpret_cast<const bf16x8*>(Q + ks * 16 + 8 * hi);
 
+  const u32x4 krs = rsrc_words(static_cast<const uint16_t*>(a.k) + (size_t)h * a.C * DH, (uint32_t)((size_t)a.T * DH * 2));
+  const u32x4 vrs = rsrc_words(static_cast<const uint16_t*>(a.vt) + (size_t)h * DH * a.vt_pitch,
+                               (uint32_t)((size_t)DH * a.vt_pitch * 2));
+  uint32_t koff[KL], voff[VL];
+#pragma unroll
+  for (int j = 0; j < KL; ++j) {
+    const int r = (w + 4 * j) * KRPI + lane / KCH, slot = lane % KCH;
+    koff[j] = (uint32_t)(r * DH * 2 + ((slot ^ (r & (KCH - 1))) * 16));
+  }
+#pragma unroll
+  for (int j = 0; j < VL; ++j) {
+    const int d = (w + 4 * j) * 8 + lane / 8, slot = lane % 8;
+    voff[j] = (uint32_t)((size_t)d * a.vt_pitch * 2 + ((slot ^ (d & 7)) * 16));
+  }
+  auto issue = [&](int k0, int st) {
+#pragma unroll
+    for (int j = 0; j < KL; ++j) lds_dma16(krs, koff[j], (uint32_t)(k0 * DH * 2), lds_addr(&Ks[st][(w + 4 * j) * 64]));
+#pragma unroll
+    for (int j = 0; j < VL; ++j) lds_dma16(vrs, voff[j], (uint32_t)(k0 * 2), lds_addr(&Vs[st][(w + 4 * j) * 64]));
+  };
+
+  const float c = a.scale * 1.4426950408889634f;  // scores -> base-2 exponent units
   float m = -INFINITY, l = 0.f;
   f32x16 o[DH / 32];
 #pragma unroll
@@ -321,34 +501,18 @@ __global__ __launch_bounds__(256) void k_attn_prefill_bf16(AttnPrefillArgs a) {
     for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
 
   const int qlast = (qb + 1) * BQ < a.T ? (qb + 1) * BQ - 1 : a.T - 1;
-  const int qfirst = qb * BQ;
-  int kfirst = qfirst - a.C + 1;
+  int kfirst = qb * BQ - a.C + 1;
   kfirst = kfirst > 0 ? kfirst / BKV * BKV : 0;
-  constexpr int CH = DH / 8;  // 16-byte chunks per key row
+  const int nkb = (qlast - kfirst) / BKV + 1;
 
-  for (int k0 = kfirst; k0 <= qlast; k0 += BKV) {
-    // ---- stage K (as is) and V (transposed) of keys k0 .. k0+63
-#pragma unroll
-    for (int i = 0; i < BKV * CH / 256; ++i) {
-      const int id = tid + 256 * i, r = id / CH, c8 = id % CH;
-      const int key = k0 + r;
-      u32x4 kv4 = {0u, 0u, 0u, 0u}, vv4 = {0u, 0u, 0u, 0u};
-      if (key < a.T) {
-        const size_t off = ((size_t)h * a.C + (a.p0 + key) % a.C) * DH + c8 * 8;
-        kv4 = *reinterpret_cast<const u32x4*>(Kg + off);
-        vv4 = *reinterpret_cast<const u32x4*>(Vg + off);
-      }
-      *reinterpret_cast<u32x4*>(Ks + r * KLD + c8 * 8) = kv4;
-      const uint32_t vw[4] = {vv4.x, vv4.y, vv4.z, vv4.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Vt[(c8 * 8 + 2 * e) * VLD + r] = (uint16_t)(vw[e] & 0xffffu);
-        Vt[(c8 * 8 + 2 * e + 1) * VLD + r] = (uint16_t)(vw[e] >> 16);
-      }
-    }
-    __syncthreads();
+  issue(kfirst, 0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int st = kb & 1, k0 = kfirst + kb * BKV;
+    vm_wait_barrier<0>();
+    if (kb + 1 < nkb) issue(k0 + BKV, st ^ 1);
+    if (k0 > qw0 + 31) continue;  // the whole block is in this wave's future
 
-    // ---- S^T for the 64 keys: s[kt][4*jj + ii] is key k0 + 32*kt + 8*jj + 4*hi + ii
+    // ---- S^T: s[kt][4*jj + ii] is key k0 + 32*kt + 8*jj + 4*hi + ii
     f32x16 s[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -356,54 +520,60 @@ __global__ __launch_bounds__(256) void k_attn_prefill_bf16(AttnPrefillArgs a) {
       for (int e = 0; e < 16; ++e) s[kt][e] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < DH / 16; ++ks) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + (kt * 32 + ql) * KLD + ks * 16 + 8 * hi);
+        const int r = kt * 32 + ql, ch = ks * 2 + hi;
+        const bf16x8 ka = __builtin_bit_cast(bf16x8, Ks[st][r * KCH + (ch ^ (r & (KCH - 1)))]);
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qr[ks], s[kt], 0, 0, 0);
       }
     }
-    float mb = -INFINITY;
+    const bool masked = k0 + BKV - 1 > qw0 || k0 < qw0 + 31 - a.C + 1 || k0 + BKV > a.T;
+    if (masked) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + 32 * kt + 8 * (e >> 2) + 4 * hi + (e & 3);
+          const bool ok = key <= qi && qi - key < a.C && key < a.T;
+          s[kt][e] = ok ? s[kt][e] : -INFINITY;
+        }
+    }
+    float mb = s[0][0];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = k0 + 32 * kt + 8 * (e >> 2) + 4 * hi + (e & 3);
-        const bool ok = key <= qi && qi - key < a.C && key < a.T;
-        const float v = ok ? s[kt][e] * a.scale : -INFINITY;
-        s[kt][e] = v;
-        mb = fmaxf(mb, v);
-      }
+      for (int e = 0; e < 16; ++e) mb = fmaxf(mb, s[kt][e]);
     mb = fmaxf(mb, __shfl_xor(mb, 32, kWave));
     const float mn = fmaxf(m, mb);
-    const float sc = mn == -INFINITY ? 1.f : expf(m - mn);
-    l *= sc;
+    const float mref = mn == -INFINITY ? 0.f : mn;  // rows with nothing visible yet
+    const float sc = __builtin_amdgcn_exp2f((m - mref) * c);
+    if (__ballot(mn != m)) {
+      l *= sc;
 #pragma unroll
-    for (int dt = 0; dt < DH / 32; ++dt)
+      for (int dt = 0; dt < DH / 32; ++dt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[dt][e] *= sc;
+        for (int e = 0; e < 16; ++e) o[dt][e] *= sc;
+    }
     m = mn;
+    const float moff = -mref * c;
 
-    // ---- P^T (bf16) and O^T += V^T P^T over 4 steps of 16 keys
+    // ---- P^T (bf16) and O^T += V^T P^T, 16 keys per step
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int kt = t >> 1, j8 = 8 * (t & 1);
       bf16x8 pb;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float p = s[kt][j8 + i] == -INFINITY ? 0.f : expf(s[kt][j8 + i] - mn);
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][j8 + i], c, moff));
         l += p;
         pb[i] = (__bf16)p;
       }
-      const int kbase = kt * 32 + 16 * (t & 1) + 4 * hi;
+      const int vch = kt * 4 + 2 * (t & 1) + hi;
 #pragma unroll
       for (int dt = 0; dt < DH / 32; ++dt) {
-        const uint16_t* vrow = Vt + (dt * 32 + ql) * VLD;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kbase);
-        const u32x2 hi8 = *reinterpret_cast<const u32x2*>(vrow + kbase + 8);
-        const u32x4 packed = {lo.x, lo.y, hi8.x, hi8.y};
-        const bf16x8 va = __builtin_bit_cast(bf16x8, packed);
+        const int d = dt * 32 + ql;
+        const bf16x8 va = __builtin_bit_cast(bf16x8, Vs[st][d * 8 + (vch ^ (d & 7))]);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
       }
     }
-    __syncthreads();
   }
 
   // ---- normalise and write: o[dt][4*jj + ii] is dim dt*32 + 8*jj + 4*hi + ii of query qi
@@ -457,7 +627,9 @@ __global__ __launch_bounds__(DH) void k_attn_prefill_f32(AttnPrefillArgs a) {
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, bool bf16, int dh, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   if (bf16) {
-    const dim3 grid((a.T + 127) / 128, a.H);
+    // K rows are read from ring slots 0..T-1 and V from its transposed copy
+    if (a.p0 != 0 || !a.vt || a.T > a.C || a.vt_pitch < (a.T + 63) / 64 * 64) return hipErrorInvalidValue;
+    const dim3 grid((a.T + 127) / 128 * a.H);
     if (dh == 128) hipLaunchKernelGGL(k_attn_prefill_bf16<128>, grid, dim3(256), 0, s, a);
     else if (dh == 64) hipLaunchKernelGGL(k_attn_prefill_bf16<64>, grid, dim3(256), 0, s, a);
     else return hipErrorInvalidValue;
