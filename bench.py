@@ -23,6 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "temporal decode ms/frame (B=1, 32 blocks, ctx 3000) + achieved HBM GB/s"
 
 
@@ -145,6 +146,47 @@ def bench_depformer(steps, warmup):
             "workload": "depth transformer, 16 positions greedy, 6 layers x 1024, window 8, bf16"}
 
 
+def prefill_flops(cfg, T):
+    """Algorithmic FLOPs of one T-frame prefill: every linear (2 per weight per frame)
+    plus causal attention (Q K^T and P V over the T (T + 1) / 2 visible pairs per head)."""
+    D, F, L, H, dh = cfg["d_model"], cfg["d_ff"], cfg["n_layers"], cfg["n_heads"], cfg["d_head"]
+    gemm = 2 * T * L * (3 * D * D + D * D + 2 * F * D + D * F)
+    attn = 2 * 2 * dh * H * L * (T * (T + 1) // 2)
+    return gemm, attn
+
+
+def bench_prefill(model, cfg, T, steps, warmup):
+    """Full-sequence prefill of T frames from an empty ring (its own ring), bf16 MFMA path."""
+    import torch
+    from personaplex_temporal_transformer_amd import synth
+    kv = model.kv_alloc()
+    ids = synth.stream_ids(cfg, T, 11)
+    h = torch.empty((T, cfg["d_model"]), device="cuda")
+    for _ in range(warmup):
+        kv.reset()
+        model.prefill(kv, ids, h)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        kv.reset()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        model.prefill(kv, ids, h)
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e))
+    kv.close()
+    ms = float(np.median(times))
+    gemm, attn = prefill_flops(cfg, T)
+    tflops = (gemm + attn) / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 3), "ms_min": round(min(times), 3), "frames": T,
+            "frames_per_s": round(T / (ms * 1e-3), 1), "flop": gemm + attn, "gemm_flop": gemm,
+            "attention_flop": attn, "achieved_TFLOPs": round(tflops, 1), "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+            "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "steps": steps,
+            "workload": "full 32-block temporal prefill, B=1, T=%d frames from position 0, bf16 MFMA, "
+                        "K/V written to ring slots 0..T-1" % T}
+
+
 def fill_ring(kv, cfg, seed):
     import torch
     g = torch.Generator(device="cuda")
@@ -200,6 +242,8 @@ def main():
     ap.add_argument("--graph", type=int, default=0, help="1: time HIP graph replays, 0: direct launches")
     ap.add_argument("--trace-layer", type=int, default=16)
     ap.add_argument("--no-depformer", action="store_true")
+    ap.add_argument("--prefill-T", type=int, default=3000, help="0: skip the prefill line")
+    ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the run, copy 1 GiB device-to-device 3 times (counter calibration)")
     args = ap.parse_args()
@@ -214,7 +258,11 @@ def main():
     cfg = dict(synth.FULL_TEMPORAL)
     t0 = time.time()
     W = make_device_weights(cfg, 8)
-    model = pp.TemporalModel(cfg, W, "bf16")
+    model = pp.TemporalModel(cfg, W, "bf16", max_prefill_T=max(args.prefill_T, 0))
+    prefill = None
+    if args.prefill_T > 0:
+        prefill = bench_prefill(model, cfg, args.prefill_T, args.prefill_steps, 1)
+        print("prefill %s" % json.dumps(prefill), file=sys.stderr, flush=True)
     kv = model.kv_alloc()
     fill_ring(kv, cfg, 9)
     torch.cuda.synchronize()
@@ -284,6 +332,8 @@ def main():
                      "launches_timed": n_tr},
         "final_position": pos,
     }
+    if prefill is not None:
+        out["prefill"] = prefill
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
