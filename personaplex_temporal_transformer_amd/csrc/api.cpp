@@ -104,6 +104,7 @@ extern "C" pp_status pp_temporal_create(const pp_temporal_config* cfg, const pp_
   m->max_T = max_prefill_T;
   m->use_graph = env_int("PP_GRAPH", 1) != 0;
   m->gemv_blocks = env_int("PP_GEMV_BLOCKS_PER_CU", 1) * n_cu;
+  m->wout_rb = env_int("PP_WOUT_ROWS", 2) == 2 && cfg->d_model % 2 == 0 ? 2 : 1;
 
   const int D = cfg->d_model, F = cfg->d_ff, H = cfg->n_heads, dh = cfg->d_head;
   // attention splits: about one block per CU over all heads (at most 64)
@@ -303,7 +304,9 @@ extern "C" pp_status pp_embed_sum(const pp_model* mc, const int32_t* ids_host, i
 
 // ------------------------------------------------------------------ decode step
 
-hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced) {
+// pos_arg: the frame's position, passed by value to the kernels of a direct launch; -1
+// when the launches are captured into a graph, whose kernels read it from `state`.
+hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long long pos_arg) {
   const pp_temporal_config& c = cfg;
   const int D = c.d_model, F = c.d_ff, H = c.n_heads, dh = c.d_head, C = c.context;
   const size_t esz = bf16 ? 2 : 4;
@@ -316,12 +319,12 @@ hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced) {
     GemvArgs g{};
     g.W = w_qkv[l]; g.x = x; g.alpha = norm1[l]; g.eps = (float)c.eps; g.K = D;
     g.n_groups = 3 * D / 2; g.out = q; g.D = D; g.dh = dh; g.C = C; g.kc = kbase; g.vc = vbase;
-    g.state = state; g.rope = rope;
+    g.state = state; g.pos = pos_arg; g.rope = rope;
     e = launch_gemv(PRO_RMSNORM, EPI_QKV, bf16, 2, g, gemv_blocks, s);
     if (e != hipSuccess) break;
 
     AttnDecodeArgs at{};
-    at.q = q; at.k = kbase; at.v = vbase; at.state = state; at.C = C; at.H = H; at.S = S;
+    at.q = q; at.k = kbase; at.v = vbase; at.state = state; at.pos = pos_arg; at.C = C; at.H = H; at.S = S;
     at.scale = 1.0f / std::sqrt((float)dh); at.part_o = part_o; at.part_ml = part_ml; at.out = o;
     const bool merge_in_wo = S <= 8 && D <= 4096;
     at.combine = merge_in_wo ? 0 : 1;
@@ -347,8 +350,8 @@ hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced) {
     if (e != hipSuccess) break;
 
     GemvArgs gw{};
-    gw.W = w_out[l]; gw.x = this->s; gw.K = F; gw.n_groups = D; gw.out = x;
-    e = launch_gemv(PRO_COPY, EPI_RESID, bf16, 1, gw, gemv_blocks, s);
+    gw.W = w_out[l]; gw.x = this->s; gw.K = F; gw.n_groups = D / wout_rb; gw.out = x;
+    e = launch_gemv(PRO_COPY, EPI_RESID, bf16, wout_rb, gw, gemv_blocks, s);
   }
   return e;
 }
@@ -356,7 +359,7 @@ hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced) {
 pp_status pp_model::run_layers(pp_kv* kv, hipStream_t s) {
   const bool traced = trace_layer >= 0;
   if (!use_graph || traced) {
-    hipError_t e = enqueue_layers(kv, s, traced);
+    hipError_t e = enqueue_layers(kv, s, traced, kv->pos);
     if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("decode launch: ") + hipGetErrorString(e));
     return PP_OK;
   }
@@ -370,7 +373,7 @@ pp_status pp_model::run_layers(pp_kv* kv, hipStream_t s) {
       return pp_fail(PP_E_HIP, "hipStreamCreate for graph capture failed");
     hipError_t e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
     if (e == hipSuccess) {
-      hipError_t le = enqueue_layers(kv, cap, false);
+      hipError_t le = enqueue_layers(kv, cap, false, -1);
       e = hipStreamEndCapture(cap, &kv->graph);
       if (le != hipSuccess) e = le;
     }

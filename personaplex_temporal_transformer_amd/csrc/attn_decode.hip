@@ -9,10 +9,14 @@
 //
 // Split-K over keys: block (s, h) handles an equal share of head h's keys, so H x S
 // blocks stream the K and V bytes once, 16 bytes per lane, and each forms a float32
-// partial (o, max, sum). The S partials of a head are merged in split order -- a fixed order, so
+// partial (o, max, sum). Scores are carried in base-2 units (q is pre-scaled by
+// log2(e) / sqrt(d_head)), so every exponential is one exp2 and the partial max is in
+// those units: softmax weights 2^(s - m) equal e^(s' - m') for the natural-unit scores. The S partials of a head are merged in split order -- a fixed order, so
 // results are bit-reproducible -- by a small combine kernel. (Merging inside the split
 // kernel by the last block to finish needs device-scope release/acquire fences, which on
 // this multi-XCD part write back and invalidate L2 and measured slower.)
+#include <stdlib.h>
+
 #include "device.h"
 #include "internal.h"
 
@@ -20,28 +24,30 @@ namespace pp {
 
 constexpr int kMaxSplits = 64;
 
-constexpr int kAttnThreads = 512;
-
 // Block (s, h): one pass over its keys with an online softmax. A group of LPK lanes reads
 // one key row at a time (16 bytes per lane); the KPP groups of the block own contiguous,
 // equal runs of the block's keys. A round loads NB keys' K and V rows per thread with
 // buffer loads (slots past the group's run point out of range and read zeros without
 // memory traffic); the next round is always issued before the current one is consumed.
 // Each group keeps a running max m, sum l and output o (its lanes' EPC dimensions); the
-// groups are merged through LDS at the end.
-template <typename KT, int DH>
-__global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnDecodeArgs a) {
+// groups are merged through LDS at the end, all threads taking part (PARTS partial
+// merges per output dimension, then their sum).
+template <typename KT, int DH, int NB, int NT>
+__global__ __launch_bounds__(NT) void k_attn_decode(AttnDecodeArgs a) {
   constexpr int EPC = Elem<KT>::kPerChunk;  // elements per 16-byte chunk
   constexpr int LPK = DH / EPC;             // lanes per key row
-  constexpr int KPP = kAttnThreads / LPK;   // key groups per block
-  constexpr int NB = 12;                    // keys per group per round
+  constexpr int KPP = NT / LPK;             // key groups per block
   constexpr int ROW = DH * (int)sizeof(KT); // bytes per key row
+  constexpr int PARTS = NT / DH;            // partial merges per output dimension
+  constexpr int GPP = KPP / PARTS;          // groups per partial merge
+  static_assert(PARTS * DH == NT && GPP * PARTS == KPP, "merge layout");
   __shared__ float gm[KPP], gl[KPP];
   __shared__ float go[KPP][DH + 1];
+  __shared__ float po[PARTS][DH], pl[PARTS];
 
   const int s = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int sub = tid % LPK, kg = tid / LPK;
-  const long long pos = a.state[0];
+  const long long pos = a.pos >= 0 ? a.pos : a.state[0];
   const int n = pos + 1 < (long long)a.C ? (int)(pos + 1) : a.C;
   const int j0 = (int)((long long)s * n / a.S), j1 = (int)((long long)(s + 1) * n / a.S);
   const int cnt = j1 - j0;
@@ -52,7 +58,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnDecodeArgs a) 
 
   float qv[EPC];
 #pragma unroll
-  for (int e = 0; e < EPC; ++e) qv[e] = a.q[h * DH + sub * EPC + e] * a.scale;
+  for (int e = 0; e < EPC; ++e) qv[e] = a.q[h * DH + sub * EPC + e] * (a.scale * kLog2e);
   const size_t base = ((size_t)h * a.C + j0) * DH;
   const auto rk = make_rsrc(static_cast<const KT*>(a.k) + base, (uint32_t)cnt * ROW);
   const auto rv = make_rsrc(static_cast<const KT*>(a.v) + base, (uint32_t)cnt * ROW);
@@ -85,13 +91,14 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnDecodeArgs a) 
       mb = fmaxf(mb, sc[b]);
     }
     const float mn = fmaxf(m, mb);
-    const float scale = mn == -INFINITY ? 1.f : expf(m - mn);  // m = -inf -> 0
+    const float mref = mn == -INFINITY ? 0.f : mn;   // nothing visible yet: keep exponents finite
+    const float scale = exp2_fast(m - mref);         // m = -inf -> 0
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] *= scale;
     l *= scale;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const float p = sc[b] == -INFINITY ? 0.f : expf(sc[b] - mn);
+      const float p = exp2_fast(sc[b] - mref);       // masked keys: exp2(-inf) = 0
       l += p;
       float vf[EPC];
       Elem<KT>::widen(cv[b], vf);
@@ -119,17 +126,29 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnDecodeArgs a) 
 #pragma unroll
   for (int e = 0; e < EPC; ++e) go[kg][sub * EPC + e] = acc[e];
   __syncthreads();
+  float M = -INFINITY;
+  for (int g = 0; g < KPP; ++g) M = fmaxf(M, gm[g]);
+  const int d = tid % DH, part = tid / DH;
+  float L = 0.f, o = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < GPP; ++i) {
+      const int g = part * GPP + i;
+      const float w = exp2_fast(gm[g] - M);  // empty group: gm = -inf -> 0 (its o and l are 0)
+      L += w * gl[g];
+      o += w * go[g][d];
+    }
+  }
+  po[part][d] = o;
+  if (d == 0) pl[part] = L;
+  __syncthreads();
   if (tid < DH) {
-    float M = -INFINITY;
-    for (int g = 0; g < KPP; ++g) M = fmaxf(M, gm[g]);
-    float L = 0.f, o = 0.f;
-    if (M != -INFINITY) {
-      for (int g = 0; g < KPP; ++g) {
-        if (gm[g] == -INFINITY) continue;
-        const float w = expf(gm[g] - M);
-        L += w * gl[g];
-        o += w * go[g][tid];
-      }
+    o = 0.f;
+    L = 0.f;
+#pragma unroll
+    for (int i = 0; i < PARTS; ++i) {
+      o += po[i][tid];
+      L += pl[i];
     }
     a.part_o[((size_t)h * a.S + s) * DH + tid] = o;
     if (tid == 0) {
@@ -140,7 +159,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnDecodeArgs a) 
 }
 
 // Merge the S partials (o_s, m_s, l_s) of head h in split order:
-// o = sum_s exp(m_s - M) o_s / sum_s exp(m_s - M) l_s with M = max_s m_s.
+// o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with M = max_s m_s (base-2 units).
 // All partials of the head are first loaded into LDS in one parallel round.
 template <int DH>
 __global__ __launch_bounds__(kBlock) void k_attn_combine(AttnDecodeArgs a) {
@@ -156,7 +175,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(AttnDecodeArgs a) {
   for (int i = 0; i < a.S; ++i) {
     const float mi = pml[2 * i];
     if (mi == -INFINITY) continue;  // empty split
-    const float w = expf(mi - M);
+    const float w = exp2_fast(mi - M);
     L += w * pml[2 * i + 1];
     o += w * po[i * DH + t];
   }
@@ -164,11 +183,23 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(AttnDecodeArgs a) {
 }
 
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, bool bf16, int dh, hipStream_t s) {
-  const dim3 grid(a.S, a.H), block(kAttnThreads);
-  if (bf16 && dh == 128) hipLaunchKernelGGL((k_attn_decode<bf16_t, 128>), grid, block, 0, s, a);
-  else if (bf16 && dh == 64) hipLaunchKernelGGL((k_attn_decode<bf16_t, 64>), grid, block, 0, s, a);
-  else if (!bf16 && dh == 128) hipLaunchKernelGGL((k_attn_decode<float, 128>), grid, block, 0, s, a);
-  else if (!bf16 && dh == 64) hipLaunchKernelGGL((k_attn_decode<float, 64>), grid, block, 0, s, a);
+  const dim3 grid(a.S, a.H);
+  static const int nb_env = [] {
+    const char* v = getenv("PP_ATTN_NB");
+    return v ? atoi(v) : 6;
+  }();
+  static const int nt_env = [] {
+    const char* v = getenv("PP_ATTN_THREADS");
+    return v ? atoi(v) : 512;
+  }();
+  if (bf16 && dh == 128) {
+    if (nt_env == 1024 && nb_env == 3) hipLaunchKernelGGL((k_attn_decode<bf16_t, 128, 3, 1024>), grid, dim3(1024), 0, s, a);
+    else if (nt_env == 1024) hipLaunchKernelGGL((k_attn_decode<bf16_t, 128, 4, 1024>), grid, dim3(1024), 0, s, a);
+    else if (nb_env == 4) hipLaunchKernelGGL((k_attn_decode<bf16_t, 128, 4, 512>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_decode<bf16_t, 128, 6, 512>), grid, dim3(512), 0, s, a);
+  } else if (bf16 && dh == 64) hipLaunchKernelGGL((k_attn_decode<bf16_t, 64, 6, 512>), grid, dim3(512), 0, s, a);
+  else if (!bf16 && dh == 128) hipLaunchKernelGGL((k_attn_decode<float, 128, 6, 512>), grid, dim3(512), 0, s, a);
+  else if (!bf16 && dh == 64) hipLaunchKernelGGL((k_attn_decode<float, 64, 6, 512>), grid, dim3(512), 0, s, a);
   else return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.combine) return e;

@@ -123,4 +123,8 @@ __device__ __forceinline__ float block_sum_256(float v, float* scratch) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
+// 2^x with the hardware exponential (exp2(-inf) = 0); used where x <= 0 (softmax weights).
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 }  // namespace pp

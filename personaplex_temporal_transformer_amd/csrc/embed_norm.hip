@@ -10,50 +10,59 @@
 
 namespace pp {
 
-// One thread owns 4 consecutive features of one frame; it adds the streams' rows in
-// stream order 0..n-1 in float32 (a fixed order, so the result is reproducible). All
-// rows are loaded first (row 0 stands in for ID -1 and contributes +0.0, which leaves
-// the sum's bits unchanged: the running sum starts at +0.0 and can never become -0.0).
+// One thread owns one 16-byte chunk of the output row's table rows (8 bfloat16 or 4
+// float32 features) of one frame; blocks of 64 threads, so a decode frame spreads over
+// D / 512 (bfloat16) workgroups. It loads the chunk of every stream's row first (all in
+// flight together), then adds them in stream order 0..n-1 in float32 -- a fixed order,
+// so the result is reproducible. Row 0 stands in for ID -1 and contributes +0.0, which
+// leaves the sum's bits unchanged (the running sum starts at +0.0 and cannot become -0.0).
+constexpr int kEmbedThreads = 64;
+
 template <typename WT>
-__global__ __launch_bounds__(kBlock) void k_embed_sum(EmbedArgs a) {
+__global__ __launch_bounds__(kEmbedThreads) void k_embed_sum(EmbedArgs a) {
+  constexpr int EPC = Elem<WT>::kPerChunk;
   const int row = blockIdx.y;
-  const int d = (blockIdx.x * kBlock + threadIdx.x) * 4;
+  const int d = (blockIdx.x * kEmbedThreads + threadIdx.x) * EPC;
   if (a.state && row == 0 && blockIdx.x == 0) {
     if (threadIdx.x == 0) a.state[0] = a.pos;
-    if (a.rope && threadIdx.x < a.dh) a.rope[threadIdx.x] = a.rope_cs[threadIdx.x];
+    for (int i = threadIdx.x; a.rope && i < a.dh; i += kEmbedThreads) a.rope[i] = a.rope_cs[i];
   }
   if (d >= a.D) return;
-  float v[kMaxStreams][4];
+  u32x4 raw[kMaxStreams];
+  float keep[kMaxStreams];
 #pragma unroll
   for (int k = 0; k < kMaxStreams; ++k) {
     if (k < a.n_streams) {
       const int id = a.ids_dev ? a.ids_dev[(size_t)row * a.n_streams + k] : a.ids_arg[k];
-      const WT* r = static_cast<const WT*>(a.tables[k]) + (size_t)(id < 0 ? 0 : id) * a.D + d;
-      const float keep = id < 0 ? 0.f : 1.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[k][e] = keep * Elem<WT>::load1(r + e);
+      raw[k] = load16(static_cast<const WT*>(a.tables[k]) + (size_t)(id < 0 ? 0 : id) * a.D + d);
+      keep[k] = id < 0 ? 0.f : 1.f;
     }
   }
-  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+  float acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
 #pragma unroll
   for (int k = 0; k < kMaxStreams; ++k) {
     if (k < a.n_streams) {
-      acc0 += v[k][0];
-      acc1 += v[k][1];
-      acc2 += v[k][2];
-      acc3 += v[k][3];
+      float v[EPC];
+      Elem<WT>::widen(raw[k], v);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[e] += keep[k] * v[e];
     }
   }
-  f32x4 out = {acc0, acc1, acc2, acc3};
-  *reinterpret_cast<f32x4*>(a.out + (size_t)row * a.D + d) = out;
+  float* o = a.out + (size_t)row * a.D + d;
+#pragma unroll
+  for (int e = 0; e < EPC; e += 4) *reinterpret_cast<f32x4*>(o + e) = f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
 }
 
 hipError_t launch_embed(const EmbedArgs& a, bool bf16, hipStream_t s) {
-  dim3 grid((a.D / 4 + kBlock - 1) / kBlock, a.rows);
+  const int epc = bf16 ? 8 : 4;
+  if (a.D % epc) return hipErrorInvalidValue;
+  dim3 grid((a.D / epc + kEmbedThreads - 1) / kEmbedThreads, a.rows);
   if (bf16)
-    hipLaunchKernelGGL(k_embed_sum<bf16_t>, grid, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(k_embed_sum<bf16_t>, grid, dim3(kEmbedThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(k_embed_sum<float>, grid, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(k_embed_sum<float>, grid, dim3(kEmbedThreads), 0, s, a);
   return hipGetLastError();
 }
 

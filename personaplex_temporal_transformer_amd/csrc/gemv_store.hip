@@ -1,0 +1,6 @@
+// GEMV instantiation: PRO_COPY prologue, EPI_STORE epilogue.
+#include "gemv_kernel.h"
+
+namespace pp {
+template hipError_t launch_gemv_kind<PRO_COPY, EPI_STORE>(int, bool, const GemvArgs&, int, hipStream_t);
+}  // namespace pp

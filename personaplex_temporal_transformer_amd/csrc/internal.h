@@ -55,6 +55,7 @@ struct GemvArgs {
   void* kc;             // K ring of this layer, batch 0: [H][C][dh]   (depth: [H][C][dh] fp32)
   void* vc;
   const long long* state;  // state[0] = position of this frame (slot = pos mod C)
+  long long pos;           // >= 0: the position itself (direct launches); -1: read state[0]
   const float* rope;       // [dh] cos/sin pairs of this frame's position
   int slot_override;    // depth: >= 0 gives the cache row directly
   // EPI_SWIGLU
@@ -87,10 +88,11 @@ struct AttnDecodeArgs {
   const void* k;        // ring of this layer, batch 0: [H][C][dh]
   const void* v;
   const long long* state;
+  long long pos;        // >= 0: the position itself (direct launches); -1: read state[0]
   int C, H, S;          // S = splits of the key range per head
   float scale;
   float* part_o;        // [H][S][dh] partial outputs (unnormalised)
-  float* part_ml;       // [H][S][2] partial (max, sum)
+  float* part_ml;       // [H][S][2] partial (max in base-2 units, sum)
   float* out;           // [H * dh], written by the combine kernel
   int combine;          // 1: launch the combine kernel; 0: the consumer merges
 };

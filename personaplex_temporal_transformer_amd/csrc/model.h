@@ -41,6 +41,7 @@ struct pp_model {
   float* rope = nullptr;       // [dh] cos/sin table of that position
   int S = 16;                // attention splits per head
   int gemv_blocks = 256;     // workgroups per GEMV launch (one per CU)
+  int wout_rb = 1;           // rows per group of the W_out GEMV
 
   // prefill workspace (one hipMalloc, sized by max_T)
   void* pws = nullptr;
@@ -72,7 +73,7 @@ struct pp_model {
   pp_status check_ids(const int32_t* ids, size_t frames) const;
   void embed_tables(pp::EmbedArgs& a) const;
   pp_status stage_ids(const int32_t* ids_host, size_t n, hipStream_t s);
-  hipError_t enqueue_layers(pp_kv* kv, hipStream_t s, bool traced);
+  hipError_t enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long long pos_arg);
   pp_status run_layers(pp_kv* kv, hipStream_t s);
 };
 
