@@ -70,10 +70,13 @@ __device__ __forceinline__ void gemm_store(const GemmArgs& g, int row, int col, 
 
 constexpr int GBK = 64;
 
-// LDS tiles are rows of 64 bf16 (8 chunks of 16 bytes) without padding; chunk kc of row r
-// sits at r*8 + (kc ^ (r & 7)), so the 32 rows read by one MFMA fragment load spread over
-// all banks.
-__device__ __forceinline__ int swz(int r, int kc) { return r * 8 + (kc ^ (r & 7)); }
+// LDS tiles are rows of 64 bf16 (8 chunks of 16 bytes = 128 B) without padding. The LDS
+// serves a 16-byte-per-lane read for 16 lanes at a time from a 256-byte bank window, i.e.
+// from two consecutive 128-byte rows; chunk kc of row r therefore sits at slot
+// kc ^ ((r >> 1) & 7), so 16 consecutive rows read at one chunk index hit 16 distinct
+// 16-byte bank groups (rows r and r+1 share a slot but sit in different halves).
+__device__ __forceinline__ int swz_slot(int r, int kc) { return kc ^ ((r >> 1) & 7); }
+__device__ __forceinline__ int swz(int r, int kc) { return r * 8 + swz_slot(r, kc); }
 
 // Column of key t in the transposed V copy: bits 2 and 3 of t swapped, so that within
 // each group of 16 keys the order is 0-3, 8-11, 4-7, 12-15 -- the order in which one
@@ -110,22 +113,28 @@ __device__ __forceinline__ void vm_wait_barrier() {
 }
 
 // C[M][N] = A[M][K] B[N][K]^T. Workgroup = WM x WN waves, tile BM x BN with BM = WM*32*MI,
-// BN = WN*64; wave (wm, wn) owns rows wm*32*MI.. and 64 columns as MI x 2 tiles of 32 x 32
-// (v_mfma_f32_32x32x16_bf16, fp32 accumulation). A and B k-tiles (64 wide) go from global
-// memory straight into LDS (buffer loads with the LDS flag: no registers, no LDS write
-// instructions) through NS stages, NS-1 k-tiles ahead of the multiply; one barrier per
-// k-tile. Rows of A past M read as zeros (out of the buffer's range) and are not stored.
+// BN = WN*32*NI; wave (wm, wn) owns rows wm*32*MI.. and 32*NI columns as MI x NI tiles of
+// 32 x 32 (v_mfma_f32_32x32x16_bf16, fp32 accumulation). A and B k-tiles (64 wide) go from
+// global memory straight into LDS (buffer loads with the LDS flag: no registers, no LDS
+// write instructions) through NS stages, NS-1 k-tiles ahead of the multiply; one barrier
+// per k-tile. Rows of A past M read as zeros (out of the buffer's range) and are not stored.
 // GEPI_SWIGLU: the B tile holds W_in rows j0..j0+BN/2-1 (g) and F+j0.. (z); wave (wm, wn)
-// multiplies g rows wn*32.. and z rows BN/2+wn*32.., so g and z of one output share a lane.
-template <int EPI, int WM, int WN, int MI, int NS>
+// multiplies g rows wn*16*NI.. (NI/2 tiles) and the z rows BN/2 + wn*16*NI.., so g and z
+// of one output share a lane.
+template <int EPI, int WM, int WN, int MI, int NI, int NS>
 __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(GemmArgs g) {
   constexpr int NW = WM * WN;
-  constexpr int BM = WM * 32 * MI, BN = WN * 64;
+  constexpr int BM = WM * 32 * MI, BN = WN * 32 * NI;
   constexpr int AL = BM / (8 * NW);   // LDS-load instructions per wave per k-tile (A)
   constexpr int BL = BN / (8 * NW);   // (B)
   static_assert(AL * 8 * NW == BM && BL * 8 * NW == BN, "tile rows must split over the waves");
-  __shared__ u32x4 As[NS][BM * 8];
-  __shared__ u32x4 Bs[NS][BN * 8];
+  static_assert(EPI != GEPI_SWIGLU || NI % 2 == 0, "SwiGLU pairs g and z tiles");
+  // pipeline stages; GEPI_QKV reuses the same LDS for its output tile (bf16, row pitch TP)
+  constexpr int TP = BN + 8;
+  constexpr int STAGE_CH = NS * (BM + BN) * 8, TILE_CH = EPI == GEPI_QKV ? BM * TP * 2 / 16 : 0;
+  __shared__ u32x4 lds[STAGE_CH > TILE_CH ? STAGE_CH : TILE_CH];
+  u32x4 (*As)[BM * 8] = reinterpret_cast<u32x4 (*)[BM * 8]>(lds);
+  u32x4 (*Bs)[BN * 8] = reinterpret_cast<u32x4 (*)[BN * 8]>(lds + NS * BM * 8);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w % WM, wn = w / WM;
@@ -154,19 +163,19 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(GemmArgs g) {
   const u32x4 ar = rsrc_words(g.A, (uint32_t)((size_t)g.M * K * 2));
   const u32x4 br = rsrc_words(g.B, (uint32_t)((size_t)(EPI == GEPI_SWIGLU ? 2 * g.F : g.N) * K * 2));
   // Instruction j of wave w fills rows R0 = (w + NW*j)*8 .. +7 (1 KB of LDS, lane i at
-  // chunk position R0*8 + i): lane i fetches row R0 + i/8, k-chunk (i%8) ^ (i/8), which is
-  // where swz() puts that chunk.
-  const int lrow = lane >> 3, lkc = (lane & 7) ^ (lane >> 3);
+  // chunk position R0*8 + i): lane i fetches row r = R0 + i/8, and the k-chunk that swz()
+  // puts at slot i%8 of that row (the XOR is its own inverse).
+  const int lrow = lane >> 3;
   uint32_t aoff[AL], boff[BL];
 #pragma unroll
   for (int j = 0; j < AL; ++j) {
     const int r = (w + NW * j) * 8 + lrow;
-    aoff[j] = (uint32_t)(((size_t)(m0 + r) * K + lkc * 8) * 2);
+    aoff[j] = (uint32_t)(((size_t)(m0 + r) * K + swz_slot(r, lane & 7) * 8) * 2);
   }
 #pragma unroll
   for (int j = 0; j < BL; ++j) {
     const int r = (w + NW * j) * 8 + lrow;
-    boff[j] = (uint32_t)(((size_t)brow(r) * K + lkc * 8) * 2);
+    boff[j] = (uint32_t)(((size_t)brow(r) * K + swz_slot(r, lane & 7) * 8) * 2);
   }
   auto issue = [&](int kt, int st) {
 #pragma unroll
@@ -176,31 +185,63 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(GemmArgs g) {
     for (int j = 0; j < BL; ++j)
       lds_dma16(br, boff[j], kt * GBK * 2, lds_addr(&Bs[st][(w + NW * j) * 64]));
   };
-  auto bcol0 = [&](int j) -> int { return EPI == GEPI_SWIGLU ? j * (BN / 2) + wn * 32 : wn * 64 + j * 32; };
+  // first LDS row (B tile) of the wave's column tile j
+  auto bcol0 = [&](int j) -> int {
+    if (EPI == GEPI_SWIGLU) return (j < NI / 2 ? 0 : BN / 2) + wn * 16 * NI + (j % (NI / 2)) * 32;
+    return wn * 32 * NI + j * 32;
+  };
 
-  f32x16 acc[MI][2];
+  f32x16 acc[MI][NI];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NI; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  auto compute = [&](int st) {
+  // Fragments of k-step ks of stage st (lane: row/col lane%32, k-chunk 2*ks + lane/32).
+  auto load_frags = [&](int st, int ks, bf16x8 (&av)[MI], bf16x8 (&bv)[NI]) {
+    const int kc = ks * 2 + (lane >> 5);
 #pragma unroll
-    for (int ks = 0; ks < GBK / 16; ++ks) {
-      const int kc = ks * 2 + (lane >> 5);
-      bf16x8 av[MI], bv[2];
+    for (int i = 0; i < MI; ++i)
+      av[i] = __builtin_bit_cast(bf16x8, As[st][swz(wm * 32 * MI + i * 32 + (lane & 31), kc)]);
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
-        av[i] = __builtin_bit_cast(bf16x8, As[st][swz(wm * 32 * MI + i * 32 + (lane & 31), kc)]);
+    for (int j = 0; j < NI; ++j) bv[j] = __builtin_bit_cast(bf16x8, Bs[st][swz(bcol0(j) + (lane & 31), kc)]);
+  };
+  auto mfmas = [&](const bf16x8 (&av)[MI], const bf16x8 (&bv)[NI]) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bv[j] = __builtin_bit_cast(bf16x8, Bs[st][swz(bcol0(j) + (lane & 31), kc)]);
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+      for (int j = 0; j < NI; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+  };
+  // One k-tile: the fragments of the next k-step are read while the current one's MFMAs
+  // run (two register sets); `after_first` runs once the first k-step's reads are issued
+  // (the next tile's global loads go out behind them).
+  // The schedule is pinned with scheduling-group barriers: each k-step's MI*NI MFMAs
+  // alternate with the next k-step's MI+NI fragment reads (masks: 0x008 MFMA, 0x100 LDS
+  // read), so LDS latency hides under the matrix-core work of the same wave.
+  auto compute = [&](int st, auto&& after_first) {
+    static_assert(GBK / 16 == 4, "four k-steps per tile");
+    bf16x8 a0[MI], b0[NI], a1[MI], b1[NI];
+    load_frags(st, 0, a0, b0);
+    after_first();
+    load_frags(st, 1, a1, b1);
+    mfmas(a0, b0);
+    load_frags(st, 2, a0, b0);
+    mfmas(a1, b1);
+    load_frags(st, 3, a1, b1);
+    mfmas(a0, b0);
+    mfmas(a1, b1);
+    constexpr int NF = MI + NI, NM = MI * NI;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+    for (int ks = 0; ks < 3; ++ks) {
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
   };
 
   constexpr int LPT = AL + BL;  // loads per wave per k-tile
@@ -215,12 +256,77 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(GemmArgs g) {
     if (NS >= 4 && ahead >= 2) vm_wait_barrier<(NS >= 4 ? 2 : 0) * LPT>();
     else if (NS >= 3 && ahead >= 1) vm_wait_barrier<(NS >= 3 ? 1 : 0) * LPT>();
     else vm_wait_barrier<0>();
-    if (kt + NS - 1 < nk) issue(kt + NS - 1, st == 0 ? NS - 1 : st - 1);
-    compute(st);
+    const int nst = st == 0 ? NS - 1 : st - 1;
+    compute(st, [&] {
+      if (kt + NS - 1 < nk) issue(kt + NS - 1, nst);
+    });
     st = st + 1 == NS ? 0 : st + 1;
   }
 
   // ---- epilogue: acc[i][j][4*jj + ii] is (row 8*jj + 4*(lane/32) + ii, col lane%32) of tile (i, j)
+  if constexpr (EPI == GEPI_QKV) {
+    // RoPE in registers (pair partner = neighbouring lane), bf16 tile into LDS, then
+    // 16-byte stores: Q rows to q_out, K / V rows to their ring slots, and (V tiles) the
+    // transposed copy along keys. The tile lies in one of the Q / K / V sections.
+    const int sec = tn * BN / g.D;
+    uint16_t* T = reinterpret_cast<uint16_t*>(lds);
+    __syncthreads();  // every wave is done reading the pipeline stages
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int rl = wm * 32 * MI + i * 32 + 8 * jj + 4 * (lane >> 5) + ii;
+          const int row = m0 + rl < g.M ? m0 + rl : g.M - 1;  // rows past M hold zeros
+#pragma unroll
+          for (int j = 0; j < NI; ++j) {
+            const int cl = wn * 32 * NI + j * 32 + (lane & 31);
+            const float v = acc[i][j][4 * jj + ii];
+            const float partner = dpp_xor1(v);  // column cl ^ 1 of the same row
+            float y = v;
+            if (sec < 2) {
+              const int d = (tn * BN + cl - sec * g.D) % g.dh;
+              const float2 cs = *reinterpret_cast<const float2*>(g.rope + (size_t)row * g.dh + (d & ~1));
+              y = (d & 1) ? partner * cs.y + v * cs.x : v * cs.x - partner * cs.y;
+            }
+            T[rl * TP + cl] = f32_to_bf16(y);
+          }
+        }
+    __syncthreads();
+    constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
+    for (int idx = tid; idx < BM * CPR; idx += NW * 64) {
+      const int rl = idx / CPR, c = idx - rl * CPR;
+      const int row = m0 + rl;
+      if (row >= g.M) continue;
+      const int wcol = tn * BN + c * 8 - sec * g.D;
+      const int head = wcol / g.dh, d = wcol - head * g.dh;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(T + rl * TP + c * 8);
+      uint16_t* dst;
+      if (sec == 0) dst = static_cast<uint16_t*>(g.q_out) + ((size_t)head * g.M + row) * g.dh + d;
+      else dst = static_cast<uint16_t*>(sec == 1 ? g.kc : g.vc) + ((size_t)head * g.C + (g.p0 + row) % g.C) * g.dh + d;
+      *reinterpret_cast<u32x4*>(dst) = v;
+    }
+    if (sec == 2 && g.vt) {
+      // key t of the tile sits in column vt_perm(t); 8 consecutive columns from 8 rows
+      const int pend = m0 + BM < g.vt_pitch ? m0 + BM : g.vt_pitch;
+      for (int idx = tid; idx < BN * (BM / 8); idx += NW * 64) {
+        const int cl = idx / (BM / 8), pg = idx - cl * (BM / 8);
+        const int p = m0 + pg * 8;
+        if (p >= pend) continue;
+        const int wcol = tn * BN + cl - 2 * g.D;
+        const int head = wcol / g.dh, d = wcol - head * g.dh;
+        uint32_t wv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r0 = vt_perm(p + 2 * e) - m0, r1 = vt_perm(p + 2 * e + 1) - m0;
+          wv[e] = (uint32_t)T[r0 * TP + cl] | ((uint32_t)T[r1 * TP + cl] << 16);
+        }
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.vt) + ((size_t)head * g.dh + d) * g.vt_pitch + p) =
+            u32x4{wv[0], wv[1], wv[2], wv[3]};
+      }
+    }
+  } else {
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -229,48 +335,22 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(GemmArgs g) {
       for (int ii = 0; ii < 4; ++ii) {
         const int row = m0 + wm * 32 * MI + i * 32 + 8 * jj + 4 * (lane >> 5) + ii;
         if (EPI == GEPI_SWIGLU) {
-          const float gv = acc[i][0][4 * jj + ii], zv = acc[i][1][4 * jj + ii];
-          if (row < g.M) {
-            const int col = tn * (BN / 2) + wn * 32 + (lane & 31);
-            static_cast<uint16_t*>(g.s_out)[(size_t)row * g.F + col] = f32_to_bf16(silu(gv) * zv);
+#pragma unroll
+          for (int j = 0; j < NI / 2; ++j) {
+            const float gv = acc[i][j][4 * jj + ii], zv = acc[i][j + NI / 2][4 * jj + ii];
+            if (row < g.M) {
+              const int col = tn * (BN / 2) + wn * 16 * NI + j * 32 + (lane & 31);
+              static_cast<uint16_t*>(g.s_out)[(size_t)row * g.F + col] = f32_to_bf16(silu(gv) * zv);
+            }
           }
         } else {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const float v = acc[i][j][4 * jj + ii];
-            const float partner = dpp_xor1(v);  // column col ^ 1 of the same row
-            const int col = tn * BN + wn * 64 + j * 32 + (lane & 31);
-            if (row < g.M) gemm_store<bf16_t, EPI>(g, row, col, v, partner);
+          for (int j = 0; j < NI; ++j) {
+            const int col = tn * BN + wn * 32 * NI + j * 32 + (lane & 31);
+            if (row < g.M) gemm_store<bf16_t, EPI>(g, row, col, acc[i][j][4 * jj + ii], 0.f);
           }
         }
       }
-  // V^T copy for the prefill attention: four consecutive rows (keys) of one column are
-  // four consecutive (permuted) positions, stored as one 8-byte word.
-  if (EPI == GEPI_QKV && g.vt && tn * BN >= 2 * g.D) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int w2 = tn * BN + wn * 64 + j * 32 + (lane & 31) - 2 * g.D;
-      const int head = w2 / g.dh, d = w2 - head * g.dh;
-      uint16_t* vrow = static_cast<uint16_t*>(g.vt) + ((size_t)head * g.dh + d) * g.vt_pitch;
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int r0 = m0 + wm * 32 * MI + i * 32 + 8 * jj + 4 * (lane >> 5);
-          const int pos = vt_perm(r0);
-          uint16_t e[4];
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) e[ii] = f32_to_bf16(acc[i][j][4 * jj + ii]);
-          if (r0 + 3 < g.M) {
-            *reinterpret_cast<u32x2*>(vrow + pos) =
-                u32x2{(uint32_t)e[0] | ((uint32_t)e[1] << 16), (uint32_t)e[2] | ((uint32_t)e[3] << 16)};
-          } else {
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-              if (r0 + ii < g.M) vrow[pos + ii] = e[ii];
-          }
-        }
-    }
   }
 }
 
@@ -336,29 +416,40 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs g) {
   }
 }
 
-// MFMA tile configurations (waves WM x WN, MI 32-row tiles per wave, LDS stages).
+// MFMA tile configurations (waves WM x WN, MI x NI 32 x 32 tiles per wave, LDS stages).
 struct GemmCfg {
-  int wm, wn, mi, ns;
+  int wm, wn, mi, ni, ns;
   int bm() const { return wm * 32 * mi; }
-  int bn() const { return wn * 64; }
+  int bn() const { return wn * 32 * ni; }
 };
+#define PP_GEMM_CFGS(X)   \
+  X(0, 2, 4, 3, 2, 2)     \
+  X(1, 2, 4, 2, 2, 3)     \
+  X(2, 2, 4, 4, 2, 2)     \
+  X(3, 2, 2, 3, 2, 3)     \
+  X(4, 2, 2, 2, 2, 4)
 static const GemmCfg kGemmCfgs[] = {
-    {2, 4, 3, 2},  // 192 x 256, 8 waves
-    {2, 4, 2, 3},  // 128 x 256, 8 waves
-    {2, 4, 4, 2},  // 256 x 256, 8 waves
-    {2, 2, 3, 3},  // 192 x 128, 4 waves
-    {2, 2, 2, 4},  // 128 x 128, 4 waves
+#define PP_CFG_ROW(id, wm, wn, mi, ni, ns) {wm, wn, mi, ni, ns},
+    PP_GEMM_CFGS(PP_CFG_ROW)
+#undef PP_CFG_ROW
 };
 constexpr int kNumGemmCfgs = sizeof(kGemmCfgs) / sizeof(kGemmCfgs[0]);
+// per-configuration efficiency (wider wave tiles reuse more of each LDS fragment read).
+// Four-wave tiles of 128 x 128 per wave measured slower than these eight-wave ones: with
+// one wave per SIMD nothing hides the LDS fragment reads, and their two-stage pipeline
+// does not cover the global-load latency.
+static const double kGemmEff[kNumGemmCfgs] = {1.0, 0.95, 1.0, 0.85, 0.8};
 
 static bool cfg_fits(const GemmCfg& c, const GemmArgs& g, int epi) {
-  return epi == GEPI_SWIGLU ? g.F % (c.bn() / 2) == 0 : g.N % c.bn() == 0;
+  if (epi == GEPI_SWIGLU) return c.ni % 2 == 0 && g.F % (c.bn() / 2) == 0;
+  // QKV tiles must not straddle the Q / K / V sections (their 16-byte stores stay in one head)
+  if (epi == GEPI_QKV) return g.N % c.bn() == 0 && g.D % c.bn() == 0 && g.dh % 8 == 0;
+  return g.N % c.bn() == 0;
 }
 
 // The configuration with the least work on the busiest CU, ceil(tiles / n_cu) * tile
-// area, scaled by a per-configuration efficiency (wider tiles reuse more per loaded byte).
+// area, scaled by its efficiency.
 static int pick_cfg(const GemmArgs& g, int epi, int n_cu) {
-  static const double eff[kNumGemmCfgs] = {1.0, 0.95, 1.0, 0.85, 0.8};
   int best = -1;
   double best_cost = 0;
   for (int i = 0; i < kNumGemmCfgs; ++i) {
@@ -366,7 +457,7 @@ static int pick_cfg(const GemmArgs& g, int epi, int n_cu) {
     if (!cfg_fits(c, g, epi)) continue;
     const long n_tn = epi == GEPI_SWIGLU ? g.F / (c.bn() / 2) : g.N / c.bn();
     const long tiles = (long)((g.M + c.bm() - 1) / c.bm()) * n_tn;
-    const double cost = (double)((tiles + n_cu - 1) / n_cu) * c.bm() * c.bn() / eff[i];
+    const double cost = (double)((tiles + n_cu - 1) / n_cu) * c.bm() * c.bn() / kGemmEff[i];
     if (best < 0 || cost < best_cost) {
       best = i;
       best_cost = cost;
@@ -375,12 +466,12 @@ static int pick_cfg(const GemmArgs& g, int epi, int n_cu) {
   return best;
 }
 
-template <int EPI, int WM, int WN, int MI, int NS>
+template <int EPI, int WM, int WN, int MI, int NI, int NS>
 static void launch_cfg(const GemmArgs& g, hipStream_t s) {
-  constexpr int BM = WM * 32 * MI, BN = WN * 64;
+  constexpr int BM = WM * 32 * MI, BN = WN * 32 * NI;
   const int n_tn = EPI == GEPI_SWIGLU ? g.F / (BN / 2) : g.N / BN;
   const int n_tm = (g.M + BM - 1) / BM;
-  hipLaunchKernelGGL((k_gemm_bf16<EPI, WM, WN, MI, NS>), dim3(n_tm * n_tn), dim3(WM * WN * 64), 0, s, g);
+  hipLaunchKernelGGL((k_gemm_bf16<EPI, WM, WN, MI, NI, NS>), dim3(n_tm * n_tn), dim3(WM * WN * 64), 0, s, g);
 }
 
 template <int EPI>
@@ -393,11 +484,12 @@ static hipError_t gemm_dispatch(bool bf16, const GemmArgs& g, int n_cu, hipStrea
     int c = forced >= 0 && forced < kNumGemmCfgs && cfg_fits(kGemmCfgs[forced], g, EPI) ? forced
                                                                                         : pick_cfg(g, EPI, n_cu > 0 ? n_cu : 256);
     switch (c) {
-      case 0: launch_cfg<EPI, 2, 4, 3, 2>(g, s); break;
-      case 1: launch_cfg<EPI, 2, 4, 2, 3>(g, s); break;
-      case 2: launch_cfg<EPI, 2, 4, 4, 2>(g, s); break;
-      case 3: launch_cfg<EPI, 2, 2, 3, 3>(g, s); break;
-      case 4: launch_cfg<EPI, 2, 2, 2, 4>(g, s); break;
+#define PP_CFG_CASE(id, wm, wn, mi, ni, ns) \
+  case id:                                  \
+    if constexpr (EPI != GEPI_SWIGLU || ni % 2 == 0) launch_cfg<EPI, wm, wn, mi, ni, ns>(g, s); \
+    break;
+      PP_GEMM_CFGS(PP_CFG_CASE)
+#undef PP_CFG_CASE
       default: return hipErrorInvalidValue;
     }
   } else {
@@ -411,9 +503,11 @@ static hipError_t gemm_dispatch(bool bf16, const GemmArgs& g, int n_cu, hipStrea
 hipError_t launch_gemm(int epi, bool bf16, const GemmArgs& g, int n_cu, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
   if (bf16) {
-    // MFMA tiles: K in steps of 64, N in tiles of 128 (SwiGLU: F in tiles of 64)
+    // MFMA tiles: K in steps of 64, and N (SwiGLU: F) must split into some configuration's tiles
     if (g.K % GBK) return hipErrorInvalidValue;
-    if (epi == GEPI_SWIGLU ? g.F % 64 : g.N % 128) return hipErrorInvalidValue;
+    bool any = false;
+    for (int i = 0; i < kNumGemmCfgs; ++i) any = any || cfg_fits(kGemmCfgs[i], g, epi);
+    if (!any) return hipErrorInvalidValue;
     // buffer loads address A and B with 32-bit byte offsets
     const size_t b_rows = epi == GEPI_SWIGLU ? 2 * (size_t)g.F : (size_t)g.N;
     // (rows of the last A tile past M included: they are read as zeros)
@@ -449,6 +543,9 @@ template <int DH>
 __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a) {
   constexpr int BQ = 128, BKV = 64;
   constexpr int KCH = DH / 8;                  // 16-byte chunks per K row
+  // slot of chunk c of K row r: 256-byte rows (d_head 128) span the bank window, so XOR
+  // with r & 15 spreads 16 rows; 128-byte rows (d_head 64) use the GEMM tiles' swizzle
+  auto kslot = [](int r, int c) { return KCH == 16 ? c ^ (r & 15) : swz_slot(r, c); };
   constexpr int KRPI = 64 / KCH;               // K rows per LDS-load instruction
   constexpr int KL = BKV * KCH / 256;          // K loads per wave per key block
   constexpr int VL = DH * 8 / 256;             // V^T loads per wave per key block
@@ -478,12 +575,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a)
 #pragma unroll
   for (int j = 0; j < KL; ++j) {
     const int r = (w + 4 * j) * KRPI + lane / KCH, slot = lane % KCH;
-    koff[j] = (uint32_t)(r * DH * 2 + ((slot ^ (r & (KCH - 1))) * 16));
+    koff[j] = (uint32_t)(r * DH * 2 + (kslot(r, slot) * 16));
   }
 #pragma unroll
   for (int j = 0; j < VL; ++j) {
     const int d = (w + 4 * j) * 8 + lane / 8, slot = lane % 8;
-    voff[j] = (uint32_t)((size_t)d * a.vt_pitch * 2 + ((slot ^ (d & 7)) * 16));
+    voff[j] = (uint32_t)((size_t)d * a.vt_pitch * 2 + (swz_slot(d, slot) * 16));
   }
   auto issue = [&](int k0, int st) {
 #pragma unroll
@@ -521,7 +618,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a)
 #pragma unroll
       for (int ks = 0; ks < DH / 16; ++ks) {
         const int r = kt * 32 + ql, ch = ks * 2 + hi;
-        const bf16x8 ka = __builtin_bit_cast(bf16x8, Ks[st][r * KCH + (ch ^ (r & (KCH - 1)))]);
+        const bf16x8 ka = __builtin_bit_cast(bf16x8, Ks[st][r * KCH + kslot(r, ch)]);
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qr[ks], s[kt], 0, 0, 0);
       }
     }
@@ -570,7 +667,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a)
 #pragma unroll
       for (int dt = 0; dt < DH / 32; ++dt) {
         const int d = dt * 32 + ql;
-        const bf16x8 va = __builtin_bit_cast(bf16x8, Vs[st][d * 8 + (vch ^ (d & 7))]);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, Vs[st][swz(d, vch)]);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
       }
     }
