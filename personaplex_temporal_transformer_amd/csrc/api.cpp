@@ -112,6 +112,8 @@ extern "C" pp_status pp_temporal_create(const pp_temporal_config* cfg, const pp_
   S = env_int("PP_ATTN_SPLITS", S);
   m->S = S < 1 ? 1 : (S > 64 ? 64 : S);
 
+  m->fuse_qkv_attn = env_int("PP_FUSE_QKV_ATTN", 1) != 0 && m->gemv_blocks == n_cu &&
+                     qkv_attn_supported(m->bf16, D, dh, H, m->S, n_cu);
   st = m->alloc_decode(D, F, H, dh);
   if (!st) st = m->alloc_prefill();
   if (st) {
@@ -129,6 +131,7 @@ pp_status pp_model::alloc_decode(int D, int F, int H, int dh) {
   const size_t os = take(sizeof(float) * F), op = take(sizeof(float) * (size_t)H * S * dh);
   const size_t oml = take(sizeof(float) * (size_t)H * S * 2);
   const size_t ost = take(sizeof(long long) * 4);
+  const size_t ocnt = take(sizeof(unsigned long long) * (size_t)cfg.n_layers * H);
   const size_t orp = take(sizeof(float) * dh);
   if (hipMalloc(&ws, bytes) != hipSuccess) return pp_fail(PP_E_HIP, "hipMalloc of decode workspace failed");
   if (hipMemset(ws, 0, bytes) != hipSuccess) return pp_fail(PP_E_HIP, "hipMemset of decode workspace failed");
@@ -140,6 +143,10 @@ pp_status pp_model::alloc_decode(int D, int F, int H, int dh) {
   part_o = reinterpret_cast<float*>(b + op);
   part_ml = reinterpret_cast<float*>(b + oml);
   state = reinterpret_cast<long long*>(b + ost);
+  head_cnt = reinterpret_cast<unsigned long long*>(b + ocnt);
+  if (hipHostMalloc(reinterpret_cast<void**>(&fuse_err), sizeof(int)) != hipSuccess)
+    return pp_fail(PP_E_HIP, "hipHostMalloc of the fused-wait status word failed");
+  *fuse_err = 0;
   rope = reinterpret_cast<float*>(b + orp);
   return PP_OK;
 }
@@ -149,6 +156,7 @@ pp_model::~pp_model() {
   free_prefill();
   if (ws) (void)hipFree(ws);
   if (ids_pinned) (void)hipHostFree(ids_pinned);
+  if (fuse_err) (void)hipHostFree(fuse_err);
   if (ids_event) (void)hipEventDestroy(ids_event);
 }
 
@@ -306,7 +314,7 @@ extern "C" pp_status pp_embed_sum(const pp_model* mc, const int32_t* ids_host, i
 
 // pos_arg: the frame's position, passed by value to the kernels of a direct launch; -1
 // when the launches are captured into a graph, whose kernels read it from `state`.
-hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long long pos_arg) {
+hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long long pos_arg, long long seq_arg) {
   const pp_temporal_config& c = cfg;
   const int D = c.d_model, F = c.d_ff, H = c.n_heads, dh = c.d_head, C = c.context;
   const size_t esz = bf16 ? 2 : 4;
@@ -320,15 +328,18 @@ hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long 
     g.W = w_qkv[l]; g.x = x; g.alpha = norm1[l]; g.eps = (float)c.eps; g.K = D;
     g.n_groups = 3 * D / 2; g.out = q; g.D = D; g.dh = dh; g.C = C; g.kc = kbase; g.vc = vbase;
     g.state = state; g.pos = pos_arg; g.rope = rope;
-    e = launch_gemv(PRO_RMSNORM, EPI_QKV, bf16, 2, g, gemv_blocks, s);
-    if (e != hipSuccess) break;
-
     AttnDecodeArgs at{};
     at.q = q; at.k = kbase; at.v = vbase; at.state = state; at.pos = pos_arg; at.C = C; at.H = H; at.S = S;
     at.scale = 1.0f / std::sqrt((float)dh); at.part_o = part_o; at.part_ml = part_ml; at.out = o;
     const bool merge_in_wo = S <= 8 && D <= 4096;
     at.combine = merge_in_wo ? 0 : 1;
-    e = launch_attn_decode(at, bf16, dh, s);
+    if (fuse_qkv_attn && merge_in_wo) {
+      QkvAttnFuse f{head_cnt + (size_t)l * H, seq_arg, fuse_err};
+      e = launch_qkv_attn(g, at, f, s);
+    } else {
+      e = launch_gemv(PRO_RMSNORM, EPI_QKV, bf16, 2, g, gemv_blocks, s);
+      if (e == hipSuccess) e = launch_attn_decode(at, bf16, dh, s);
+    }
     if (e != hipSuccess) break;
 
     GemvArgs go{};
@@ -359,7 +370,7 @@ hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long 
 pp_status pp_model::run_layers(pp_kv* kv, hipStream_t s) {
   const bool traced = trace_layer >= 0;
   if (!use_graph || traced) {
-    hipError_t e = enqueue_layers(kv, s, traced, kv->pos);
+    hipError_t e = enqueue_layers(kv, s, traced, kv->pos, fused_seq);
     if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("decode launch: ") + hipGetErrorString(e));
     return PP_OK;
   }
@@ -373,7 +384,7 @@ pp_status pp_model::run_layers(pp_kv* kv, hipStream_t s) {
       return pp_fail(PP_E_HIP, "hipStreamCreate for graph capture failed");
     hipError_t e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
     if (e == hipSuccess) {
-      hipError_t le = enqueue_layers(kv, cap, false, -1);
+      hipError_t le = enqueue_layers(kv, cap, false, -1, -1);
       e = hipStreamEndCapture(cap, &kv->graph);
       if (le != hipSuccess) e = le;
     }
@@ -394,8 +405,13 @@ extern "C" pp_status pp_temporal_decode_step(pp_model* m, pp_kv* kv, const int32
   if (text_logits_dev && !m->text_head) return pp_fail(PP_E_ARG, "text logits requested but the model has no text head");
   pp_status st = m->check_ids(ids_host, (size_t)kv->B);
   if (st) return st;
+  if (m->fuse_err && __atomic_load_n(m->fuse_err, __ATOMIC_ACQUIRE)) {
+    *m->fuse_err = 0;
+    return pp_fail(PP_E_HIP, "an earlier decode step's cross-workgroup wait timed out (its output is invalid)");
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const pp_temporal_config& c = m->cfg;
+  if (m->fuse_qkv_attn) ++m->fused_seq;
 
   EmbedArgs a{};
   m->embed_tables(a);
@@ -404,6 +420,7 @@ extern "C" pp_status pp_temporal_decode_step(pp_model* m, pp_kv* kv, const int32
   a.rows = 1;
   a.state = m->state;
   a.pos = kv->pos;
+  a.seq = m->fused_seq;
   a.rope = m->rope;
   a.dh = c.d_head;
   // RoPE angles pos * theta^(-2j/d_head) formed in float64 on the host

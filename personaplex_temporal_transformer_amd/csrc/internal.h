@@ -15,8 +15,8 @@ struct EmbedArgs {
   int32_t ids_arg[kMaxStreams];     // one frame's IDs when ids_dev == nullptr
   const int32_t* ids_dev;           // [rows][n_streams] device IDs (prefill) or nullptr
   float* out;                       // [rows][D]
-  long long* state;                 // if non-null, state[0] := pos (decode position)
-  long long pos;
+  long long* state;                 // if non-null, state[0] := pos, state[1] := seq
+  long long pos, seq;
   int n_streams, D, rows;
   // RoPE table of this position (decode), computed on the host in float64 and rounded:
   // rope_cs[2j] = cos(pos * omega_j), rope_cs[2j+1] = sin(pos * omega_j), with
@@ -54,7 +54,7 @@ struct GemvArgs {
   int D, dh, C;         // model width, head width, ring capacity (slots)
   void* kc;             // K ring of this layer, batch 0: [H][C][dh]   (depth: [H][C][dh] fp32)
   void* vc;
-  const long long* state;  // state[0] = position of this frame (slot = pos mod C)
+  const long long* state;  // state[0] = position of this frame (slot = pos mod C), state[1] = fused frame count
   long long pos;           // >= 0: the position itself (direct launches); -1: read state[0]
   const float* rope;       // [dh] cos/sin pairs of this frame's position
   int slot_override;    // depth: >= 0 gives the cache row directly
@@ -97,6 +97,16 @@ struct AttnDecodeArgs {
   int combine;          // 1: launch the combine kernel; 0: the consumer merges
 };
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, bool bf16, int dh, hipStream_t s);
+
+// ---------------------------------------------------------------- fused QKV + attention (decode)
+struct QkvAttnFuse {
+  unsigned long long* cnt;  // [H] rows published per head for this layer (monotonic, zeroed at creation)
+  long long seq;            // >= 1: fused frames so far including this one; -1: read state[1]
+  int* err;                 // host-visible word set when a wait times out
+};
+bool qkv_attn_supported(bool bf16, int D, int dh, int H, int S, int n_cu);
+// grid H*S workgroups: QKV rows (g, published) then attention split (blk % S, head blk / S)
+hipError_t launch_qkv_attn(const GemvArgs& g, const AttnDecodeArgs& at, const QkvAttnFuse& f, hipStream_t s);
 
 // ---------------------------------------------------------------- row RMSNorm
 hipError_t launch_rmsnorm_rows(const float* x, const float* alpha, float eps, int D, int rows,

@@ -37,7 +37,11 @@ struct pp_model {
   float* s = nullptr;        // SiLU(g) * z [F]
   float* part_o = nullptr;   // attention partial outputs [H][S][dh]
   float* part_ml = nullptr;  // attention partial (max, sum) [H][S][2]
-  long long* state = nullptr;  // [0] = position of the frame being decoded
+  long long* state = nullptr;  // [0] = position of the frame being decoded, [1] = fused frame count
+  unsigned long long* head_cnt = nullptr;  // [L][H] rows published per head (fused QKV + attention)
+  bool fuse_qkv_attn = false;  // decode runs QKV and attention as one launch
+  long long fused_seq = 0;     // frames decoded with the fused launch
+  int* fuse_err = nullptr;     // pinned host word: a fused wait timed out
   float* rope = nullptr;       // [dh] cos/sin table of that position
   int S = 16;                // attention splits per head
   int gemv_blocks = 256;     // workgroups per GEMV launch (one per CU)
@@ -73,7 +77,7 @@ struct pp_model {
   pp_status check_ids(const int32_t* ids, size_t frames) const;
   void embed_tables(pp::EmbedArgs& a) const;
   pp_status stage_ids(const int32_t* ids_host, size_t n, hipStream_t s);
-  hipError_t enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long long pos_arg);
+  hipError_t enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long long pos_arg, long long seq_arg);
   pp_status run_layers(pp_kv* kv, hipStream_t s);
 };
 

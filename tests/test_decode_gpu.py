@@ -191,3 +191,36 @@ def test_two_runs_are_bit_identical():
     model.decode_step(kv, ids[0], h2)
     torch.cuda.synchronize()
     assert torch.equal(h1, h2)
+
+
+def test_fused_qkv_attention_matches_separate_launches(monkeypatch):
+    """QKV + attention as one launch (rows published across workgroups, per-head waits)
+    against the two-launch path, over 12 frames that wrap a 256-slot ring, so the frame's
+    own slot falls in different splits; and the fused launch replayed from a graph
+    (position and frame count read from device memory) against direct launches."""
+    import torch
+    cfg = synth.with_(synth.FULL_TEMPORAL, n_layers=2, context=256)
+    W = synth.temporal_weights(cfg, 31, "bf16", with_text_head=False, shared_layer=True)
+    frames = synth.cache_frames(cfg, 250, 32)
+    ids = synth.stream_ids(cfg, 12, 33)
+    dW = to_device(W)
+    src = torch.from_numpy(frames.view(np.int16)).cuda()
+    outs = {}
+    for mode, fuse in (("separate", "0"), ("fused", "1"), ("fused_graph", "1")):
+        monkeypatch.setenv("PP_FUSE_QKV_ATTN", fuse)
+        model = pp.TemporalModel(cfg, dW, "bf16")
+        model.set_graph(mode == "fused_graph")
+        kv = model.kv_alloc()
+        kv.load(src, 250)
+        h = torch.empty((12, cfg["d_model"]), device="cuda")
+        for t in range(12):
+            model.decode_step(kv, ids[t], h[t])
+        torch.cuda.synchronize()
+        outs[mode] = h.cpu().numpy()
+        assert kv.info()[0] == 262
+        kv.close()
+        model.close()
+    err = norm_max_err(outs["fused"], outs["separate"])
+    print("fused vs separate QKV/attention launches: %.3g" % err)
+    assert err <= 1e-4
+    assert np.array_equal(outs["fused"], outs["fused_graph"])
