@@ -45,16 +45,27 @@ def w_in_bytes(cfg):
     return 2 * F * D * 2 + D * 4 + D * 4 + F * 4
 
 
+GEMV_SOURCES = ("device.h", "gemv_kernel.h", "gemv_swiglu.hip")
+
+
+def gemv_source_hash():
+    """SHA-256 over the sources the W_in kernel is compiled from."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in GEMV_SOURCES:
+        h.update(open(os.path.join(ROOT, "personaplex_temporal_transformer_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic():
     """HBM bytes per launch of the W_in kernel from the committed counter runs
-    (profiles/decode_w_in_traffic.json), or None once the GEMV source has changed since."""
-    import hashlib
+    (profiles/decode_w_in_traffic.json), or None once the GEMV sources have changed since."""
     try:
         rec = json.load(open(os.path.join(ROOT, "profiles", "decode_w_in_traffic.json")))
-        src = open(os.path.join(ROOT, "personaplex_temporal_transformer_amd", "csrc", "gemv.hip"), "rb").read()
+        digest = gemv_source_hash()
     except (OSError, ValueError):
         return None
-    if rec.get("gemv_source_sha256") != hashlib.sha256(src).hexdigest():
+    if rec.get("gemv_source_sha256") != digest:
         return None
     return rec.get("traffic_bytes_per_launch")
 

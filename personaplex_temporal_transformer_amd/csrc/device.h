@@ -67,6 +67,26 @@ __device__ __forceinline__ u32x4 buffer_load16_stream(__amdgpu_buffer_rsrc_t r, 
   return __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 2 /* non-temporal */);
 }
 
+// 16 bytes per lane from a buffer into LDS: lane i's bytes land at LDS byte address
+// lds_base + 16*i (lds_base is wave-uniform, passed through M0). Issued from inline
+// assembly so that the compiler does not add a wait on these loads before every LDS read
+// (it cannot tell the pipeline stages apart); the kernel waits for them explicitly with
+// an explicit s_waitcnt. No other instruction in these kernels uses M0.
+__device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_base) : "memory");
+}
+
+// Buffer resource words for [base, base + bytes): raw addressing, no stride, reads past
+// the end return zero.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// LDS byte address of a __shared__ object (the low half of its generic address).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
 // DPP lane moves inside a row of 16 lanes (no LDS traffic).
 __device__ __forceinline__ float dpp_xor1(float v) {  // quad_perm [1,0,3,2]
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));

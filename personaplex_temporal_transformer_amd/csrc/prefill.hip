@@ -83,26 +83,6 @@ __device__ __forceinline__ int swz(int r, int kc) { return r * 8 + swz_slot(r, k
 // lane holds probabilities after the S^T product (see k_attn_prefill_bf16).
 __device__ __forceinline__ int vt_perm(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
 
-// 16 bytes per lane from a buffer into LDS: lane i's bytes land at LDS byte address
-// lds_base + 16*i (lds_base is wave-uniform, passed through M0). Issued from inline
-// assembly so that the compiler does not add a wait on these loads before every LDS read
-// (it cannot tell the pipeline stages apart); the kernel waits for them explicitly with
-// vm_wait_barrier. No other instruction in these kernels uses M0.
-__device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_base) : "memory");
-}
-
-// Buffer resource words for [base, base + bytes): raw addressing, no stride, reads past
-// the end return zero.
-__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)base;
-  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
-}
-
-// LDS byte address of a __shared__ object (the low half of its generic address).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
-
 // Wait until at most N vector-memory operations of this wave are outstanding and all its
 // LDS operations are done, then synchronise the workgroup. Loads into LDS complete in
 // issue order, so N = the loads issued after the ones that must have landed.
