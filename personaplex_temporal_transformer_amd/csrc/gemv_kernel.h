@@ -112,42 +112,65 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, int g, const float (
 
 // Depth attention for every head into x (element i stored at xpos(i)): scores
 // q.k * scale over the keys of positions [aq_pos - awin + 1, aq_pos] (clipped at 0),
-// softmax with max subtraction, then the weighted sum of values. `sc` holds aH x 32
-// floats of scratch LDS.
+// softmax with max subtraction, then the weighted sum of values. Wave w takes heads w,
+// w + nw, ...; lane l holds head dimensions l and l + 64 (d_head <= 128), so every q, K
+// and V read is a coalesced row segment. Keys go in batches of 8 (one batch for the usual
+// window of 8) whose K and V reads are all issued together; each score is a wave-wide sum
+// (every lane gets the same bits) and the softmax runs online across batches.
 template <class XPos>
-__device__ void depth_attention(const GemvArgs& a, float* x, float* sc, XPos xpos) {
-  const int tid = threadIdx.x;
+__device__ void depth_attention(const GemvArgs& a, float* x, XPos xpos) {
+  constexpr int KB = 8;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int k0 = a.aq_pos - a.awin + 1 > 0 ? a.aq_pos - a.awin + 1 : 0;
   const int nk = a.aq_pos - k0 + 1;
-  const int nt = blockDim.x;
-  for (int i = tid; i < a.aH * nk; i += nt) {
-    const int h = i / nk, j = i - h * nk;
-    const float* qh = a.aq + h * a.adh;
-    const float* kh = a.ak + ((size_t)h * a.acap + k0 + j) * a.adh;
-    float d = 0.f;
-    for (int e = 0; e < a.adh; ++e) d += qh[e] * kh[e];
-    sc[h * 32 + j] = d * a.ascale;
-  }
-  __syncthreads();
-  for (int h = tid; h < a.aH; h += nt) {
-    float m = -INFINITY;
-    for (int j = 0; j < nk; ++j) m = fmaxf(m, sc[h * 32 + j]);
-    float l = 0.f;
-    for (int j = 0; j < nk; ++j) {
-      const float p = expf(sc[h * 32 + j] - m);
-      sc[h * 32 + j] = p;
-      l += p;
+  const int dh = a.adh;
+  const bool on0 = lane < dh, on1 = lane + 64 < dh;
+  for (int h = w; h < a.aH; h += nw) {
+    const float* qh = a.aq + h * dh;
+    const float* kh = a.ak + ((size_t)h * a.acap + k0) * dh;
+    const float* vh = a.av + ((size_t)h * a.acap + k0) * dh;
+    const float q0 = on0 ? qh[lane] : 0.f, q1 = on1 ? qh[lane + 64] : 0.f;
+    float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int jb = 0; jb < nk; jb += KB) {
+      float kv0[KB], kv1[KB], vv0[KB], vv1[KB];
+#pragma unroll
+      for (int b = 0; b < KB; ++b) {
+        const int j = jb + b;
+        const bool ok = j < nk;
+        kv0[b] = ok && on0 ? kh[j * dh + lane] : 0.f;
+        kv1[b] = ok && on1 ? kh[j * dh + lane + 64] : 0.f;
+        vv0[b] = ok && on0 ? vh[j * dh + lane] : 0.f;
+        vv1[b] = ok && on1 ? vh[j * dh + lane + 64] : 0.f;
+      }
+      float sc[KB];
+      float mb = -INFINITY;
+#pragma unroll
+      for (int b = 0; b < KB; ++b) {
+        sc[b] = -INFINITY;
+        if (jb + b < nk) {
+          sc[b] = wave_sum(q0 * kv0[b] + q1 * kv1[b]) * a.ascale;
+          mb = fmaxf(mb, sc[b]);
+        }
+      }
+      const float mn = fmaxf(m, mb);                       // finite: the batch has >= 1 key
+      const float r = m == -INFINITY ? 0.f : expf(m - mn);  // rescale of the earlier batches
+      l *= r;
+      o0 *= r;
+      o1 *= r;
+#pragma unroll
+      for (int b = 0; b < KB; ++b) {
+        if (jb + b < nk) {
+          const float p = expf(sc[b] - mn);
+          l += p;
+          o0 += p * vv0[b];
+          o1 += p * vv1[b];
+        }
+      }
+      m = mn;
     }
     const float inv = 1.0f / l;
-    for (int j = 0; j < nk; ++j) sc[h * 32 + j] *= inv;
-  }
-  __syncthreads();
-  for (int i = tid; i < a.aH * a.adh; i += nt) {
-    const int h = i / a.adh, d = i - h * a.adh;
-    const float* vh = a.av + ((size_t)h * a.acap + k0) * a.adh + d;
-    float o = 0.f;
-    for (int j = 0; j < nk; ++j) o += sc[h * 32 + j] * vh[(size_t)j * a.adh];
-    x[xpos(i)] = o;
+    if (on0) x[xpos(h * dh + lane)] = o0 * inv;
+    if (on1) x[xpos(h * dh + lane + 64)] = o1 * inv;
   }
 }
 
@@ -312,12 +335,12 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a, float* xs, int blk,
     if (ga >= gb1) return;
     if (gb < gb1) issue(wb, rb, gb, pb);
   } else {
-    depth_attention(a, xs, xs + XR * NT * 4,
-                    [&](int i) { return xq_index(i / EPC, (i % EPC) / 4) + (i % 4); });
+    // the first weights do not depend on the attention: request them first
+    if (ga < gb1) issue(wa, ra, ga, pa);
+    if (gb < gb1) issue(wb, rb, gb, pb);
+    depth_attention(a, xs, [&](int i) { return xq_index(i / EPC, (i % EPC) / 4) + (i % 4); });
     __syncthreads();
     if (ga >= gb1) return;
-    issue(wa, ra, ga, pa);
-    if (gb < gb1) issue(wb, rb, gb, pb);
   }
   if constexpr (ONEPASS) {
 #pragma unroll
@@ -412,15 +435,14 @@ static void launch_x(const GemvArgs& a, dim3 grid, dim3 block, size_t lds, hipSt
   else hipLaunchKernelGGL((k_gemv<WT, RB, U, OP, PRO, EPI, false, false, XR>), grid, block, lds, s, a);
 }
 
-// XR: float4 of x per thread in the prologue; the LDS copy of x is padded to XR*NT*4
-// floats (plus the depth-attention scratch).
+// XR: float4 of x per thread in the prologue; the LDS copy of x is padded to XR*NT*4 floats.
 constexpr int kXPer = kGemvWaves * 64 * 4;
 static int x_regs(int K) { return K <= kXPer ? 1 : (K <= 2 * kXPer ? 2 : 6); }
 
 template <typename WT, int RB, int U, bool OP, int PRO, int EPI>
 static void launch_u(const GemvArgs& a, dim3 grid, dim3 block, hipStream_t s) {
   const int xr = x_regs(a.K);
-  const size_t lds = ((size_t)xr * kXPer + (PRO == PRO_DEPTH_ATTN ? 32 * 32 : 0)) * sizeof(float);
+  const size_t lds = (size_t)xr * kXPer * sizeof(float);
   if (xr == 1) launch_x<WT, RB, U, OP, PRO, EPI, 1>(a, grid, block, lds, s);
   else if (xr == 2) launch_x<WT, RB, U, OP, PRO, EPI, 2>(a, grid, block, lds, s);
   else launch_x<WT, RB, U, OP, PRO, EPI, 6>(a, grid, block, lds, s);
