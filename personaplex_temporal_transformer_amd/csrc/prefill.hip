@@ -109,9 +109,10 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(GemmArgs g) {
   constexpr int BL = BN / (8 * NW);   // (B)
   static_assert(AL * 8 * NW == BM && BL * 8 * NW == BN, "tile rows must split over the waves");
   static_assert(EPI != GEPI_SWIGLU || NI % 2 == 0, "SwiGLU pairs g and z tiles");
-  // pipeline stages; GEPI_QKV reuses the same LDS for its output tile (bf16, row pitch TP)
-  constexpr int TP = BN + 8;
-  constexpr int STAGE_CH = NS * (BM + BN) * 8, TILE_CH = EPI == GEPI_QKV ? BM * TP * 2 / 16 : 0;
+  // pipeline stages; GEPI_QKV reuses the same LDS for half of its output tile (fp32, row
+  // pitch TPF floats)
+  constexpr int TPF = BN / 2 + 4;
+  constexpr int STAGE_CH = NS * (BM + BN) * 8, TILE_CH = EPI == GEPI_QKV ? BM * TPF * 4 / 16 : 0;
   __shared__ u32x4 lds[STAGE_CH > TILE_CH ? STAGE_CH : TILE_CH];
   u32x4 (*As)[BM * 8] = reinterpret_cast<u32x4 (*)[BM * 8]>(lds);
   u32x4 (*Bs)[BN * 8] = reinterpret_cast<u32x4 (*)[BN * 8]>(lds + NS * BM * 8);
@@ -245,65 +246,78 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(GemmArgs g) {
 
   // ---- epilogue: acc[i][j][4*jj + ii] is (row 8*jj + 4*(lane/32) + ii, col lane%32) of tile (i, j)
   if constexpr (EPI == GEPI_QKV) {
-    // RoPE in registers (pair partner = neighbouring lane), bf16 tile into LDS, then
-    // 16-byte stores: Q rows to q_out, K / V rows to their ring slots, and (V tiles) the
-    // transposed copy along keys. The tile lies in one of the Q / K / V sections.
+    // Half a tile at a time (128-byte-aligned column halves): the waves holding those
+    // columns write their fp32 values into LDS, then every thread takes 8 consecutive
+    // columns of a row -- 4 RoPE pairs, whose cos/sin are 8 consecutive floats of the
+    // table (two 16-byte loads) -- rotates them, and stores them as one 16-byte bf16 word:
+    // Q rows to q_out, K / V rows to their ring slots; V tiles also fill the transposed
+    // copy along keys. The tile lies in one of the Q / K / V sections.
     const int sec = tn * BN / g.D;
-    uint16_t* T = reinterpret_cast<uint16_t*>(lds);
-    __syncthreads();  // every wave is done reading the pipeline stages
+    float* T = reinterpret_cast<float*>(lds);
+    constexpr int HALF = BN / 2, CPR = HALF / 8;  // columns per half, 8-column chunks per row
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int half = 0; half < 2; ++half) {
+      __syncthreads();  // the pipeline stages (first half) / the previous half are no longer read
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int rl = wm * 32 * MI + i * 32 + 8 * jj + 4 * (lane >> 5) + ii;
-          const int row = m0 + rl < g.M ? m0 + rl : g.M - 1;  // rows past M hold zeros
+        for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-          for (int j = 0; j < NI; ++j) {
-            const int cl = wn * 32 * NI + j * 32 + (lane & 31);
-            const float v = acc[i][j][4 * jj + ii];
-            const float partner = dpp_xor1(v);  // column cl ^ 1 of the same row
-            float y = v;
-            if (sec < 2) {
-              const int d = (tn * BN + cl - sec * g.D) % g.dh;
-              const float2 cs = *reinterpret_cast<const float2*>(g.rope + (size_t)row * g.dh + (d & ~1));
-              y = (d & 1) ? partner * cs.y + v * cs.x : v * cs.x - partner * cs.y;
+          for (int ii = 0; ii < 4; ++ii) {
+            const int rl = wm * 32 * MI + i * 32 + 8 * jj + 4 * (lane >> 5) + ii;
+#pragma unroll
+            for (int j = 0; j < NI; ++j) {
+              const int cl = wn * 32 * NI + j * 32 + (lane & 31) - half * HALF;
+              if (cl >= 0 && cl < HALF) T[rl * TPF + cl] = acc[i][j][4 * jj + ii];
             }
-            T[rl * TP + cl] = f32_to_bf16(y);
+          }
+      __syncthreads();
+      for (int idx = tid; idx < BM * CPR; idx += NW * 64) {
+        const int rl = idx / CPR, c = idx - rl * CPR;
+        const int row = m0 + rl;
+        if (row >= g.M) continue;
+        const int wcol = tn * BN + half * HALF + c * 8 - sec * g.D;
+        const int head = wcol / g.dh, d = wcol - head * g.dh;
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(T + rl * TPF + c * 8);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(T + rl * TPF + c * 8 + 4);
+        float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        if (sec < 2) {
+          const f32x4 c0 = *reinterpret_cast<const f32x4*>(g.rope + (size_t)row * g.dh + d);
+          const f32x4 c1 = *reinterpret_cast<const f32x4*>(g.rope + (size_t)row * g.dh + d + 4);
+          const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float e = v[2 * k], o = v[2 * k + 1], cc = cs[2 * k], sn = cs[2 * k + 1];
+            v[2 * k] = e * cc - o * sn;
+            v[2 * k + 1] = e * sn + o * cc;
           }
         }
-    __syncthreads();
-    constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
-    for (int idx = tid; idx < BM * CPR; idx += NW * 64) {
-      const int rl = idx / CPR, c = idx - rl * CPR;
-      const int row = m0 + rl;
-      if (row >= g.M) continue;
-      const int wcol = tn * BN + c * 8 - sec * g.D;
-      const int head = wcol / g.dh, d = wcol - head * g.dh;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(T + rl * TP + c * 8);
-      uint16_t* dst;
-      if (sec == 0) dst = static_cast<uint16_t*>(g.q_out) + ((size_t)head * g.M + row) * g.dh + d;
-      else dst = static_cast<uint16_t*>(sec == 1 ? g.kc : g.vc) + ((size_t)head * g.C + (g.p0 + row) % g.C) * g.dh + d;
-      *reinterpret_cast<u32x4*>(dst) = v;
-    }
-    if (sec == 2 && g.vt) {
-      // key t of the tile sits in column vt_perm(t); 8 consecutive columns from 8 rows
-      const int pend = m0 + BM < g.vt_pitch ? m0 + BM : g.vt_pitch;
-      for (int idx = tid; idx < BN * (BM / 8); idx += NW * 64) {
-        const int cl = idx / (BM / 8), pg = idx - cl * (BM / 8);
-        const int p = m0 + pg * 8;
-        if (p >= pend) continue;
-        const int wcol = tn * BN + cl - 2 * g.D;
-        const int head = wcol / g.dh, d = wcol - head * g.dh;
-        uint32_t wv[4];
+        uint32_t pk[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r0 = vt_perm(p + 2 * e) - m0, r1 = vt_perm(p + 2 * e + 1) - m0;
-          wv[e] = (uint32_t)T[r0 * TP + cl] | ((uint32_t)T[r1 * TP + cl] << 16);
+        for (int k = 0; k < 4; ++k) pk[k] = (uint32_t)f32_to_bf16(v[2 * k]) | ((uint32_t)f32_to_bf16(v[2 * k + 1]) << 16);
+        uint16_t* dst;
+        if (sec == 0) dst = static_cast<uint16_t*>(g.q_out) + ((size_t)head * g.M + row) * g.dh + d;
+        else dst = static_cast<uint16_t*>(sec == 1 ? g.kc : g.vc) + ((size_t)head * g.C + (g.p0 + row) % g.C) * g.dh + d;
+        *reinterpret_cast<u32x4*>(dst) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+      }
+      if (sec == 2 && g.vt) {
+        // key t of the tile sits in column vt_perm(t); 8 consecutive columns from 8 rows
+        const int pend = m0 + BM < g.vt_pitch ? m0 + BM : g.vt_pitch;
+        for (int idx = tid; idx < HALF * (BM / 8); idx += NW * 64) {
+          const int cl = idx / (BM / 8), pg = idx - cl * (BM / 8);
+          const int p = m0 + pg * 8;
+          if (p >= pend) continue;
+          const int wcol = tn * BN + half * HALF + cl - 2 * g.D;
+          const int head = wcol / g.dh, d = wcol - head * g.dh;
+          uint32_t wv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r0 = vt_perm(p + 2 * e) - m0, r1 = vt_perm(p + 2 * e + 1) - m0;
+            wv[e] = (uint32_t)f32_to_bf16(T[r0 * TPF + cl]) | ((uint32_t)f32_to_bf16(T[r1 * TPF + cl]) << 16);
+          }
+          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.vt) + ((size_t)head * g.dh + d) * g.vt_pitch + p) =
+              u32x4{wv[0], wv[1], wv[2], wv[3]};
         }
-        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.vt) + ((size_t)head * g.dh + d) * g.vt_pitch + p) =
-            u32x4{wv[0], wv[1], wv[2], wv[3]};
       }
     }
   } else {
