@@ -45,7 +45,7 @@ def w_in_bytes(cfg):
     return 2 * F * D * 2 + D * 4 + D * 4 + F * 4
 
 
-GEMV_SOURCES = ("device.h", "gemv_kernel.h", "gemv_swiglu.hip")
+GEMV_SOURCES = ("device.h", "gemv_kernel.h", "gemv_swiglu.hip")  # the W_in kernel's sources
 
 
 def gemv_source_hash():
@@ -211,37 +211,74 @@ def fill_ring(kv, cfg, seed):
     del buf
 
 
-def cpu_baseline(cfg, seconds_budget=25.0):
-    """The oracle (fp64 NumPy) on a bounded sample: one decode frame through 2 of the 32
-    full-width blocks at 3000 visible keys, scaled x16 to a 32-block ms/frame."""
-    from oracle import temporal as O
-    from personaplex_temporal_transformer_amd import synth
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        cores = os.cpu_count() or 1
+        return os.cpu_count() or 1
+
+
+def _best_of(fn, n=3):
+    times = []
+    for _ in range(n):
+        t0 = time.time()
+        fn()
+        times.append(time.time() - t0)
+    return min(times), len(times)
+
+
+def cpu_baselines(cfg, want_prefill=True, want_depth=True):
+    """The oracle (fp64 NumPy) on bounded samples of each workload, on this host's cores:
+    decode -- one frame through 2 of the 32 full-width blocks at 3000 visible keys, x16;
+    prefill -- one full-width block over T = 256 frames, scaled by the FLOP ratio of the
+    32-block T = 3000 prefill; depth -- 2 of the 16 positions of a depth frame (weights of a
+    2-position depth stack), x8. Each is the best of 3."""
+    from oracle import depformer as OD
+    from oracle import temporal as O
+    from personaplex_temporal_transformer_amd import synth
+    cores = int(_blas_threads())
+    out = {}
     n_l = 2
     sc = synth.with_(cfg, n_layers=n_l)
     W = synth.temporal_weights(sc, 8, "bf16", with_text_head=False)
     frames = synth.cache_frames(sc, cfg["context"], 9)
     ks = [frames[l, 0, 0].transpose(1, 0, 2) for l in range(n_l)]
     vs = [frames[l, 1, 0].transpose(1, 0, 2) for l in range(n_l)]
-    ids = synth.stream_ids(sc, 1, 10)
-    times = []
-    t_end = time.time() + seconds_budget
-    while time.time() < t_end or not times:
+    ids = synth.stream_ids(sc, 256, 10)
+
+    def decode_frame():
         cache = O.cache_from_blocks(ks, vs, np.arange(cfg["context"]), n_l)
-        t0 = time.time()
-        x = O.decode_step(O.embed(ids[0], W, sc), cfg["context"], cache, W, sc)
-        O.final(x, W, sc)
-        times.append(time.time() - t0)
-        if len(times) >= 3:
-            break
-    ms = min(times) * 1000.0 * cfg["n_layers"] / n_l
-    return {"value": ms, "unit": "ms/frame", "cores": int(cores), "kind": "oracle",
-            "sample": "one decode frame through 2 of 32 full-width blocks at 3000 visible keys "
-                      "(fp64 NumPy), best of %d, scaled x16 to 32 blocks" % len(times)}
+        O.final(O.decode_step(O.embed(ids[0], W, sc), cfg["context"], cache, W, sc), W, sc)
+
+    t, n = _best_of(decode_frame)
+    out["decode"] = {"value": t * 1000.0 * cfg["n_layers"] / n_l, "unit": "ms/frame", "cores": cores,
+                     "kind": "oracle",
+                     "sample": "one decode frame through 2 of 32 full-width blocks at 3000 visible keys "
+                               "(fp64 NumPy), best of %d, scaled x16 to 32 blocks" % n}
+    del frames, ks, vs
+    if want_prefill:
+        T = 256
+        X = np.stack([O.embed(ids[t], W, sc) for t in range(T)])
+        t, n = _best_of(lambda: O.block_full(X, np.arange(T), 0, W, sc))
+        g_s, a_s = prefill_flops(synth.with_(cfg, n_layers=1), T)
+        g_f, a_f = prefill_flops(cfg, cfg["context"])
+        scale = (g_f + a_f) / (g_s + a_s)
+        out["prefill"] = {"value": t * 1000.0 * scale, "unit": "ms per %d-frame prefill" % cfg["context"],
+                          "cores": cores, "kind": "oracle",
+                          "sample": "one full-width block over T=%d frames (fp64 NumPy, %.2f s), best of %d, "
+                                    "scaled x%.1f by the FLOP ratio to 32 blocks at T=%d" % (T, t, n, scale, cfg["context"])}
+    del W
+    if want_depth:
+        dc = synth.with_(synth.FULL_DEPTH, n_steps=2)
+        DW = synth.depth_weights(dc, 5, "bf16")
+        h = synth.hidden(dc["d_temporal"], 6)
+        t, n = _best_of(lambda: OD.step_logits(h, 7, None, DW, dc))
+        out["depth"] = {"value": t * 1000.0 * synth.FULL_DEPTH["n_steps"] / 2, "unit": "ms/frame", "cores": cores,
+                        "kind": "oracle",
+                        "sample": "2 of the 16 positions of a depth frame (fp64 NumPy, a 2-position depth stack "
+                                  "of full width), best of %d, scaled x8" % n}
+    return out
 
 
 def main():
@@ -353,13 +390,17 @@ def main():
         del a, b
     if not args.no_depformer:
         model.close()
-        if args.prefill_T <= 0:
-            kv.close()
+        kv.close()
         del W
         torch.cuda.empty_cache()
         out["depformer"] = bench_depformer(max(10, args.steps // 2), 3)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg)
+        cb = cpu_baselines(cfg, want_prefill="prefill" in out, want_depth="depformer" in out)
+        out["cpu_baseline"] = cb["decode"]
+        if "prefill" in cb:
+            out["prefill"]["cpu_baseline"] = cb["prefill"]
+        if "depth" in cb:
+            out["depformer"]["cpu_baseline"] = cb["depth"]
     print(json.dumps(out), flush=True)
 
 

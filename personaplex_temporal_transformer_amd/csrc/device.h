@@ -27,6 +27,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return uint16_t(u >> 16);
 }
 
+// float32 -> float16 bits, round to nearest even (the hardware conversion).
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
 // Storage-type helpers for weights / cache elements (float or bfloat16).
 template <typename T> struct Elem;
 template <> struct Elem<float> {

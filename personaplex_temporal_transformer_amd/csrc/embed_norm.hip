@@ -69,11 +69,12 @@ hipError_t launch_embed(const EmbedArgs& a, bool bf16, hipStream_t s) {
   return hipGetLastError();
 }
 
-// One block per row; float32 statistics; writes float32 and/or bfloat16 output.
+// One block per row; float32 statistics; writes float32 and/or float16 output (the
+// float16 rows are the activation operand of the prefill's matrix products).
 __global__ __launch_bounds__(kBlock) void k_rmsnorm_rows(const float* __restrict__ x,
                                                          const float* __restrict__ alpha, float eps,
                                                          int D, float* __restrict__ out_f32,
-                                                         uint16_t* __restrict__ out_bf16) {
+                                                         uint16_t* __restrict__ out_f16) {
   __shared__ float red[4];
   const float* xr = x + (size_t)blockIdx.x * D;
   float ss = 0.f;
@@ -87,18 +88,18 @@ __global__ __launch_bounds__(kBlock) void k_rmsnorm_rows(const float* __restrict
     f32x4 al = *reinterpret_cast<const f32x4*>(alpha + i);
     f32x4 y = (v * r) * al;
     if (out_f32) *reinterpret_cast<f32x4*>(out_f32 + (size_t)blockIdx.x * D + i) = y;
-    if (out_bf16) {
-      uint16_t* o = out_bf16 + (size_t)blockIdx.x * D + i;
-      o[0] = f32_to_bf16(y.x); o[1] = f32_to_bf16(y.y);
-      o[2] = f32_to_bf16(y.z); o[3] = f32_to_bf16(y.w);
+    if (out_f16) {
+      const uint32_t lo = (uint32_t)f32_to_f16(y.x) | ((uint32_t)f32_to_f16(y.y) << 16);
+      const uint32_t hi = (uint32_t)f32_to_f16(y.z) | ((uint32_t)f32_to_f16(y.w) << 16);
+      *reinterpret_cast<uint2*>(out_f16 + (size_t)blockIdx.x * D + i) = make_uint2(lo, hi);
     }
   }
 }
 
 hipError_t launch_rmsnorm_rows(const float* x, const float* alpha, float eps, int D, int rows,
-                               float* out_f32, void* out_bf16, hipStream_t s) {
+                               float* out_f32, void* out_f16, hipStream_t s) {
   hipLaunchKernelGGL(k_rmsnorm_rows, dim3(rows), dim3(kBlock), 0, s, x, alpha, eps, D, out_f32,
-                     static_cast<uint16_t*>(out_bf16));
+                     static_cast<uint16_t*>(out_f16));
   return hipGetLastError();
 }
 

@@ -110,7 +110,7 @@ hipError_t launch_qkv_attn(const GemvArgs& g, const AttnDecodeArgs& at, const Qk
 
 // ---------------------------------------------------------------- row RMSNorm
 hipError_t launch_rmsnorm_rows(const float* x, const float* alpha, float eps, int D, int rows,
-                               float* out_f32, void* out_bf16, hipStream_t s);
+                               float* out_f32, void* out_f16, hipStream_t s);
 
 }  // namespace pp
 
@@ -145,7 +145,7 @@ namespace pp {
 enum GemmEpi { GEPI_QKV = 0, GEPI_RESID = 1, GEPI_SWIGLU = 2 };
 
 struct GemmArgs {
-  const void* A;        // [M][K] activations, row-major (bf16 or float32)
+  const void* A;        // [M][K] activations, row-major (float16 on the bf16-weight path, or float32)
   const void* B;        // weights, row-major [rows][K]
   int M, N, K;          // N = output columns (GEPI_SWIGLU: N = F, B has 2F rows)
   // GEPI_QKV: columns Q|K|V; RoPE on Q and K with rope[row][d] (cos, sin pairs);
@@ -156,9 +156,10 @@ struct GemmArgs {
   const float* rope;
   int D, dh, C, p0;
   float* x;             // GEPI_RESID: x[row][col] += (A W^T)[row][col], float32 [M][N]
-  void* s_out;          // GEPI_SWIGLU: [M][F] = SiLU(g) * z
+  void* s_out;          // GEPI_SWIGLU: [M][F] = SiLU(g) * z (float16 on the bf16-weight path)
   int F;
-  // GEPI_QKV, bf16 only: if non-null, V is also written transposed, vt[H][dh][vt_pitch],
+  // GEPI_QKV, bf16 only: Q goes to q_out as bfloat16; if non-null, V is also written
+  // transposed as float16, vt[H][dh][vt_pitch],
   // key t in column vt_perm(t) (bits 2 and 3 of t swapped), for the prefill attention
   void* vt;
   int vt_pitch;
@@ -166,12 +167,12 @@ struct GemmArgs {
 hipError_t launch_gemm(int epi, bool bf16, const GemmArgs& g, int n_cu, hipStream_t s);
 
 struct AttnPrefillArgs {
-  const void* q;        // [H][T][dh] rotated queries (positions p0..p0+T-1)
+  const void* q;        // [H][T][dh] rotated queries (positions p0..p0+T-1; bfloat16 on the bf16 path)
   const void* k;        // ring of this layer [H][C][dh]; key of position p in slot p mod C
   const void* v;
-  const void* vt;       // bf16: V transposed as written by the QKV GEMM (p0 must be 0)
+  const void* vt;       // bf16 path: V transposed (float16) as written by the QKV GEMM (p0 must be 0)
   int vt_pitch;
-  void* out;            // [T][H*dh]
+  void* out;            // [T][H*dh] (float16 on the bf16 path)
   int T, H, C, p0;
   float scale;
 };

@@ -51,12 +51,12 @@ struct pp_model {
   void* pws = nullptr;
   int32_t* ids_dev = nullptr;  // [max_T][n_streams]
   float* px = nullptr;         // residual stream [T][D] float32
-  void* pu = nullptr;          // normalised rows, bf16 [T][D] (f32 path: float32)
-  void* pq = nullptr;          // rotated Q [H][T][dh]
-  void* pa = nullptr;          // attention output [T][D]
-  void* pg = nullptr;          // SiLU(g)*z [T][F]
+  void* pu = nullptr;          // normalised rows [T][D]: float16 (bf16-weight path) or float32
+  void* pq = nullptr;          // rotated Q [H][T][dh]: bfloat16 (bf16-weight path) or float32
+  void* pa = nullptr;          // attention output [T][D], same element type
+  void* pg = nullptr;          // SiLU(g)*z [T][F], same element type
   float* prope = nullptr;      // RoPE table [T][dh] (cos, sin pairs)
-  void* pvt = nullptr;         // bf16: V transposed [H][dh][vt_pitch] (zero past T)
+  void* pvt = nullptr;         // bf16-weight path: V transposed, float16 [H][dh][vt_pitch] (zero past T)
   int vt_pitch = 0;            // max_T rounded up to 64
 
   int32_t* ids_pinned = nullptr;

@@ -5,8 +5,13 @@
 // -> W_O + residual -> RMSNorm -> W_in -> SiLU(g) * z -> W_out + residual.
 //
 // bf16 path: the matrix products are dense, so they run on the CDNA4 matrix cores
-// (v_mfma_f32_32x32x16_bf16, fp32 accumulation); operands are bf16 (activations are
-// rounded to bf16 once per product), statistics and the residual stream stay fp32.
+// (fp32 accumulation). The weights are bfloat16; the activations of the four projections
+// enter as float16 (11-bit significand: eight times less rounding than bfloat16, at the
+// same matrix-core rate; v_mfma_f32_32x32x16_f16), and the bfloat16 weight fragments are
+// widened to float16 in registers -- exact for bfloat16 values in float16's normal range,
+// which covers weights of this scale. In attention, Q K^T is a bfloat16 product (keys are
+// bfloat16 in the ring, shared with decode) and P V a float16 one (P and the transposed V
+// copy in float16). Statistics and the residual stream stay fp32.
 // float32 path (small shapes, fp32 parity): plain FMA kernels with the same epilogues.
 #include <stdlib.h>
 
@@ -15,7 +20,21 @@
 
 namespace pp {
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// 8 bfloat16 values (one 16-byte chunk) as float16: each bfloat16 is the top half of a
+// float32; the packed conversion is exact for values inside float16's normal range.
+__device__ __forceinline__ f16x8 bf16x8_to_f16(u32x4 w) {
+  f16x8 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const auto p = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w[k] << 16), __uint_as_float(w[k] & 0xffff0000u));
+    r[2 * k] = (_Float16)p[0];
+    r[2 * k + 1] = (_Float16)p[1];
+  }
+  return r;
+}
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -181,19 +200,24 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(GemmArgs g) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   // Fragments of k-step ks of stage st (lane: row/col lane%32, k-chunk 2*ks + lane/32).
-  auto load_frags = [&](int st, int ks, bf16x8 (&av)[MI], bf16x8 (&bv)[NI]) {
+  // (B first: its bfloat16 -> float16 conversion then has the A reads and two MFMAs to
+  // hide the LDS latency behind)
+  auto load_frags = [&](int st, int ks, f16x8 (&av)[MI], f16x8 (&bv)[NI]) {
     const int kc = ks * 2 + (lane >> 5);
+    u32x4 braw[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) braw[j] = Bs[st][swz(bcol0(j) + (lane & 31), kc)];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
-      av[i] = __builtin_bit_cast(bf16x8, As[st][swz(wm * 32 * MI + i * 32 + (lane & 31), kc)]);
+      av[i] = __builtin_bit_cast(f16x8, As[st][swz(wm * 32 * MI + i * 32 + (lane & 31), kc)]);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) bv[j] = __builtin_bit_cast(bf16x8, Bs[st][swz(bcol0(j) + (lane & 31), kc)]);
+    for (int j = 0; j < NI; ++j) bv[j] = bf16x8_to_f16(braw[j]);
   };
-  auto mfmas = [&](const bf16x8 (&av)[MI], const bf16x8 (&bv)[NI]) {
+  auto mfmas = [&](const f16x8 (&av)[MI], const f16x8 (&bv)[NI]) {
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < NI; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < NI; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
   };
   // One k-tile: the fragments of the next k-step are read while the current one's MFMAs
   // run (two register sets); `after_first` runs once the first k-step's reads are issued
@@ -203,7 +227,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(GemmArgs g) {
   // read), so LDS latency hides under the matrix-core work of the same wave.
   auto compute = [&](int st, auto&& after_first) {
     static_assert(GBK / 16 == 4, "four k-steps per tile");
-    bf16x8 a0[MI], b0[NI], a1[MI], b1[NI];
+    f16x8 a0[MI], b0[NI], a1[MI], b1[NI];
     load_frags(st, 0, a0, b0);
     after_first();
     load_frags(st, 1, a1, b1);
@@ -213,6 +237,9 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(GemmArgs g) {
     load_frags(st, 3, a1, b1);
     mfmas(a0, b0);
     mfmas(a1, b1);
+    // per k-step with a successor: MFMAs alternate with the next k-step's fragment reads
+    // (B first), and each B fragment's conversion (12 VALU: 0x002) follows two MFMAs after
+    // its read
     constexpr int NF = MI + NI, NM = MI * NI;
 #pragma unroll
     for (int ks = 0; ks < 3; ++ks) {
@@ -220,6 +247,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(GemmArgs g) {
       for (int i = 0; i < NM; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (i < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (i >= 2 && i - 2 < NI) __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
       }
     }
     __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
@@ -292,6 +320,8 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(GemmArgs g) {
             v[2 * k + 1] = e * sn + o * cc;
           }
         }
+        // Q, K and V are bfloat16 (K and V in the ring, as in decode; Q meets K in a
+        // bfloat16 product)
         uint32_t pk[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) pk[k] = (uint32_t)f32_to_bf16(v[2 * k]) | ((uint32_t)f32_to_bf16(v[2 * k + 1]) << 16);
@@ -313,7 +343,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(GemmArgs g) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r0 = vt_perm(p + 2 * e) - m0, r1 = vt_perm(p + 2 * e + 1) - m0;
-            wv[e] = (uint32_t)f32_to_bf16(T[r0 * TPF + cl]) | ((uint32_t)f32_to_bf16(T[r1 * TPF + cl]) << 16);
+            wv[e] = (uint32_t)f32_to_f16(T[r0 * TPF + cl]) | ((uint32_t)f32_to_f16(T[r1 * TPF + cl]) << 16);
           }
           *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.vt) + ((size_t)head * g.dh + d) * g.vt_pitch + p) =
               u32x4{wv[0], wv[1], wv[2], wv[3]};
@@ -334,7 +364,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(GemmArgs g) {
             const float gv = acc[i][j][4 * jj + ii], zv = acc[i][j + NI / 2][4 * jj + ii];
             if (row < g.M) {
               const int col = tn * (BN / 2) + wn * 16 * NI + j * 32 + (lane & 31);
-              static_cast<uint16_t*>(g.s_out)[(size_t)row * g.F + col] = f32_to_bf16(silu(gv) * zv);
+              static_cast<uint16_t*>(g.s_out)[(size_t)row * g.F + col] = f32_to_f16(silu(gv) * zv);
             }
           }
         } else {
@@ -650,19 +680,19 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a)
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int kt = t >> 1, j8 = 8 * (t & 1);
-      bf16x8 pb;
+      f16x8 pb;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][j8 + i], c, moff));
         l += p;
-        pb[i] = (__bf16)p;
+        pb[i] = (_Float16)p;
       }
       const int vch = kt * 4 + 2 * (t & 1) + hi;
 #pragma unroll
       for (int dt = 0; dt < DH / 32; ++dt) {
         const int d = dt * 32 + ql;
-        const bf16x8 va = __builtin_bit_cast(bf16x8, Vs[st][swz(d, vch)]);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
+        const f16x8 va = __builtin_bit_cast(f16x8, Vs[st][swz(d, vch)]);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb, o[dt], 0, 0, 0);
       }
     }
   }
@@ -677,8 +707,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int d = dt * 32 + 8 * jj + 4 * hi;
-        const uint32_t w0 = (uint32_t)f32_to_bf16(o[dt][4 * jj] * inv) | ((uint32_t)f32_to_bf16(o[dt][4 * jj + 1] * inv) << 16);
-        const uint32_t w1 = (uint32_t)f32_to_bf16(o[dt][4 * jj + 2] * inv) | ((uint32_t)f32_to_bf16(o[dt][4 * jj + 3] * inv) << 16);
+        const uint32_t w0 = (uint32_t)f32_to_f16(o[dt][4 * jj] * inv) | ((uint32_t)f32_to_f16(o[dt][4 * jj + 1] * inv) << 16);
+        const uint32_t w1 = (uint32_t)f32_to_f16(o[dt][4 * jj + 2] * inv) | ((uint32_t)f32_to_f16(o[dt][4 * jj + 3] * inv) << 16);
         *reinterpret_cast<u32x2*>(out + d) = u32x2{w0, w1};
       }
   }
