@@ -13,6 +13,8 @@ Modules
   depformer  -- the 16-position depth transformer with per-position weights
   inventory  -- tensor shapes and parameter / cache byte arithmetic of the constructor
   ring       -- the integer slot/position arithmetic of a ring KV cache
+  sampling   -- temperature / top-k sampling with caller-supplied uniform draws
+  generator  -- one generator frame: delayed-code ring, text and depth sampling
 
 Every function is pinned by tests/test_oracle_*.py against facts the pages fix
 (printed counts, integer examples, closed forms, invariants, brute force). The one
@@ -20,4 +22,4 @@ part that stays "parity unpinned" is agreement with the released PersonaPlex
 checkpoint's numerics: the pages publish no weights or reference outputs.
 """
 
-from . import temporal, depformer, inventory, ring  # noqa: F401
+from . import temporal, depformer, inventory, ring, sampling, generator  # noqa: F401

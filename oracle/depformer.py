@@ -41,6 +41,18 @@ def step_logits(h, text_token, forced, W, cfg):
 
     The depth KV history starts empty for every call; position q attends to the
     positions q' of this frame with 0 <= q - q' < window."""
+    def select(q, lg):
+        if forced is not None and int(forced[q]) >= 0:
+            return int(forced[q])
+        return int(np.argmax(lg))      # first maximum = lowest index on ties
+    return step_select(h, text_token, select, W, cfg)
+
+
+def step_select(h, text_token, select, W, cfg):
+    """The depth loop of one frame with a caller-chosen selection rule: after position q's
+    logits are formed, select(q, logits_q) returns the code that position q emits, which
+    is also the input of position q + 1 (the generator samples, or uses a supplied code
+    where one is provided). Returns (codes [n_steps] int64, logits [n_steps, n_out])."""
     D, H, dh, F = cfg["d_model"], cfg["n_heads"], cfg["d_head"], cfg["d_ff"]
     S, L, eps, win = cfg["n_steps"], cfg["n_layers"], cfg["eps"], cfg["window"]
     h = np.asarray(h, np.float64)
@@ -74,9 +86,8 @@ def step_logits(h, text_token, forced, W, cfg):
             gz = f64(W[pre + "gating.%d.linear_in.weight" % q]) @ rmsnorm(z, W[pre + "norm2.alpha"], eps)
             z = z + f64(W[pre + "gating.%d.linear_out.weight" % q]) @ (silu(gz[:F]) * gz[F:])
         logits[q] = f64(W["linears.%d.weight" % q]) @ z
-        if forced is not None and int(forced[q]) >= 0:
-            prev = int(forced[q])
-        else:
-            prev = int(np.argmax(logits[q]))      # first maximum = lowest index on ties
+        prev = int(select(q, logits[q]))
+        if not 0 <= prev < cfg["audio_vocab"]:
+            raise ValueError("position %d selected code %d outside the audio table" % (q, prev))
         codes[q] = prev
     return codes, logits
