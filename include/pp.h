@@ -208,6 +208,75 @@ pp_status pp_depformer_step(pp_depformer* d, const float* h_dev, const int32_t* 
 /* Depth-step launch mode: 0 = launch each kernel, 1 = replay a captured HIP graph (default). */
 pp_status pp_depformer_set_graph(pp_depformer* d, int32_t enable);
 
+/* ------------------------------------------------------------------ sampling and the generator frame */
+
+/* Temperature / top-k sampling of `rows` independent logit rows ("PersonaPlex native LM
+ * audit", section 7 "One exact generator step" and the sampling defaults after it; the
+ * page names the parameters, the procedure below is the plain reading of them):
+ * the candidates are the top_k largest logits of the row, ordered by value (larger
+ * first; equal values by lower index); weights w_i = exp((l_i - l_0) / temperature) in
+ * float64 with the float32 temperature widened; with the row's draw u, the result is
+ * the first candidate whose running sum w_0 + .. + w_i (added in candidate order)
+ * exceeds u * (w_0 + .. + w_{k-1}), or the last candidate if none does.
+ * top_k <= 1 or temperature <= 0 selects the largest logit (lowest index on ties).
+ * logits_dev [rows][n] float32, finite; uniforms_dev [rows] float64 in [0, 1), or NULL
+ * for all zeros (the largest logit); out_dev [rows] int32. 1 <= n <= 32768,
+ * top_k <= 1024 (values above n act as n), else PP_E_ARG. */
+pp_status pp_sample_top_k(const float* logits_dev, int32_t rows, int32_t n, float temperature,
+                          int32_t top_k, const double* uniforms_dev, int32_t* out_dev, void* stream);
+
+/* Generator parameters (audit section 7 and "Generator delayed-code cache"). Stream k
+ * of the ring is stream k of the temporal embedding sum: 0 = agent text, 1..8 = agent
+ * codebooks 0..7, 9..16 = user codebooks 0..7; depth position q selects stream q + 1.
+ * Defaults of the released path: delays {0, 0, 1 x 7, 0, 1 x 7}, initial tokens 32000
+ * (text) and 2048 (audio), text temperature 0.7 / top-k 25, audio temperature 0.8 /
+ * top-k 250. Requirements: n_streams == n_audio + 1 of the model == n_steps + 1 of the
+ * depformer; 0 <= delay <= 5 (the ring has max delay + 3 slots); initial tokens are rows
+ * of their tables; top-k <= 1024; sampled audio needs n_out <= 2048 and the text head
+ * at most 32768 classes. */
+typedef struct {
+  int32_t n_streams;
+  int32_t delays[32];
+  int32_t text_initial, audio_initial;
+  float text_temperature;
+  int32_t text_top_k;
+  float audio_temperature;
+  int32_t audio_top_k;
+} pp_generator_config;
+
+typedef struct pp_generator pp_generator;
+
+/* A generator session over a temporal model with its KV ring (batch 1) and a
+ * depformer, none of which it owns; they must outlive it and must not be used by other
+ * calls while it runs. The temporal position continues from the ring's current position
+ * (0 after pp_kv_reset, or past a prefilled prompt). The code ring starts empty at
+ * cursor 0. */
+pp_status pp_generator_create(pp_model* m, pp_kv* kv, pp_depformer* d, const pp_generator_config* cfg,
+                              pp_generator** out);
+pp_status pp_generator_destroy(pp_generator* g);
+
+/* One generator call at cursor s (audit section 7, steps 1-7), all on the device:
+ * supplied codes go to ring slot (s + delay_k) mod C, marked provided; at s = 0 slot 0
+ * receives the initial tokens where nothing was supplied and the call ends; otherwise
+ * the temporal step reads slot (s - 1) mod C, the text is drawn from its logits with
+ * uniforms[0] (a supplied text of slot s mod C replaces it), depth position q draws with
+ * uniforms[1 + q] (a supplied code replaces it and feeds position q + 1), selections fill
+ * the unsupplied entries of slot s mod C, the flags of slot (s - 1) mod C are cleared, and
+ * when s > max delay the aligned output of stream k is slot (s - max_delay + delay_k) mod C.
+ * provided_host [n_streams] int32 (-1 = not supplied; text in [0, text_vocab), audio in
+ * [0, n_out)) or NULL; uniforms_host [n_streams] float64 in [0, 1) or NULL (all zero);
+ * out_dev [n_streams] int32 written when *has_output_host is set to 1 (NULL: not written).
+ * The cursor advances by one per call. */
+pp_status pp_generator_step(pp_generator* g, const int32_t* provided_host, const double* uniforms_host,
+                            int32_t* out_dev, int32_t* has_output_host, void* stream);
+
+/* Copies of the last model step's intermediate values (any pointer may be NULL):
+ * inputs_dev [n_streams] the temporal input IDs; chosen_dev [n_streams] the selection per
+ * stream (supplied or drawn); text_logits_dev [text_vocab - 1]; depth_logits_dev
+ * [n_steps][n_out]. Valid after the last pp_generator_step that ran the model. */
+pp_status pp_generator_inspect(const pp_generator* g, int32_t* inputs_dev, int32_t* chosen_dev,
+                               float* text_logits_dev, float* depth_logits_dev, void* stream);
+
 /* ------------------------------------------------------------------ diagnostics */
 
 /* Message of the last error on the calling thread ("" if none). */

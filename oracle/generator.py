@@ -61,6 +61,7 @@ class Generator:
         self.last_chosen = None          # the 17 selections of the last model step
         self.last_h = None               # its final-normed temporal hidden
         self.last_text_logits = None     # and its text logits
+        self.last_depth_logits = None    # [n_steps, n_out] depth logits of the last model step
 
     def step(self, provided=None, uniforms=None):
         """One call. provided: length-17 codes (-1 = not supplied); user audio is streams
@@ -98,7 +99,7 @@ class Generator:
                 return int(self.tok[k, tgt])
             return sample_top_k(lg, self.at, self.ak, u[k])
 
-        codes, _ = OD.step_select(h, text, select, self.W_d, self.cfg_d)
+        codes, self.last_depth_logits = OD.step_select(h, text, select, self.W_d, self.cfg_d)
         chosen = [text] + [int(c) for c in codes]
         self.last_chosen = np.array(chosen, np.int64)
         for k in range(N_STREAMS):

@@ -406,26 +406,36 @@ extern "C" pp_status pp_temporal_decode_step(pp_model* m, pp_kv* kv, const int32
                                              float* h_out_dev, float* text_logits_dev, void* stream) {
   if (!m || !kv || !ids_host || !h_out_dev) return pp_fail(PP_E_ARG, "NULL argument");
   if (kv->m != m) return pp_fail(PP_E_ARG, "kv ring belongs to another model");
-  if (text_logits_dev && !m->text_head) return pp_fail(PP_E_ARG, "text logits requested but the model has no text head");
   pp_status st = m->check_ids(ids_host, (size_t)kv->B);
   if (st) return st;
-  if (m->fuse_err && __atomic_load_n(m->fuse_err, __ATOMIC_ACQUIRE)) {
-    *m->fuse_err = 0;
+  return m->decode(kv, ids_host, nullptr, h_out_dev, text_logits_dev, static_cast<hipStream_t>(stream));
+}
+
+// One decode frame. The IDs come from the host (ids_host, already validated) or from
+// device memory (ids_dev: the generator's ring, whose entries are valid by construction).
+pp_status pp_model::decode(pp_kv* kv, const int32_t* ids_host, const int32_t* ids_dev, float* h_out_dev,
+                           float* text_logits_dev, hipStream_t s) {
+  if (text_logits_dev && !text_head) return pp_fail(PP_E_ARG, "text logits requested but the model has no text head");
+  if (fuse_err && __atomic_load_n(fuse_err, __ATOMIC_ACQUIRE)) {
+    *fuse_err = 0;
     return pp_fail(PP_E_HIP, "an earlier decode step's cross-workgroup wait timed out (its output is invalid)");
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const pp_temporal_config& c = m->cfg;
-  if (m->fuse_qkv_attn) ++m->fused_seq;
+  const pp_temporal_config& c = cfg;
+  if (fuse_qkv_attn) ++fused_seq;
 
   EmbedArgs a{};
-  m->embed_tables(a);
-  for (int k = 0; k < a.n_streams; ++k) a.ids_arg[k] = ids_host[k];
-  a.out = m->x;
+  embed_tables(a);
+  if (ids_dev) {
+    a.ids_dev = ids_dev;
+  } else {
+    for (int k = 0; k < a.n_streams; ++k) a.ids_arg[k] = ids_host[k];
+  }
+  a.out = x;
   a.rows = 1;
-  a.state = m->state;
+  a.state = state;
   a.pos = kv->pos;
-  a.seq = m->fused_seq;
-  a.rope = m->rope;
+  a.seq = fused_seq;
+  a.rope = rope;
   a.dh = c.d_head;
   // RoPE angles pos * theta^(-2j/d_head) formed in float64 on the host
   for (int j = 0; j < c.d_head / 2; ++j) {
@@ -433,18 +443,19 @@ extern "C" pp_status pp_temporal_decode_step(pp_model* m, pp_kv* kv, const int32
     a.rope_cs[2 * j] = (float)std::cos(ang);
     a.rope_cs[2 * j + 1] = (float)std::sin(ang);
   }
-  hipError_t e = launch_embed(a, m->bf16, s);
+  hipError_t e = launch_embed(a, bf16, s);
   if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("embed: ") + hipGetErrorString(e));
 
-  if ((st = m->run_layers(kv, s))) return st;
+  pp_status st = run_layers(kv, s);
+  if (st) return st;
 
-  e = launch_rmsnorm_rows(m->x, m->out_norm, (float)c.eps, c.d_model, 1, h_out_dev, nullptr, s);
+  e = launch_rmsnorm_rows(x, out_norm, (float)c.eps, c.d_model, 1, h_out_dev, nullptr, s);
   if (e == hipSuccess && text_logits_dev) {
     GemvArgs g{};
-    g.W = m->text_head; g.x = m->x; g.alpha = m->out_norm; g.eps = (float)c.eps; g.K = c.d_model;
+    g.W = text_head; g.x = x; g.alpha = out_norm; g.eps = (float)c.eps; g.K = c.d_model;
     g.n_groups = (c.text_vocab - 1) / 2; g.out = text_logits_dev;
     if ((c.text_vocab - 1) % 2 == 0) {
-      e = launch_gemv(PRO_RMSNORM, EPI_STORE, m->bf16, 2, g, m->gemv_blocks, s);
+      e = launch_gemv(PRO_RMSNORM, EPI_STORE, bf16, 2, g, gemv_blocks, s);
     } else {
       return pp_fail(PP_E_ARG, "text head rows must be even");
     }

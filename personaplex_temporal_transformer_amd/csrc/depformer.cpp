@@ -22,31 +22,6 @@
 
 using namespace pp;
 
-struct pp_depformer {
-  pp_depth_config cfg{};
-  bool bf16 = true;
-  int n_cu = 0;
-  std::vector<const void*> in_proj, audio_emb, w_qkv, w_o, w_in, w_out, head;
-  std::vector<const float*> norm1, norm2;
-  const void* text_emb = nullptr;
-
-  void* ws = nullptr;
-  float *h = nullptr, *c_all = nullptr, *z = nullptr, *q = nullptr, *s = nullptr, *kv = nullptr,
-        *logits = nullptr;
-  int32_t *codes = nullptr, *ctrl = nullptr;
-  int gemv_blocks = 256;
-  bool use_graph = true;
-  hipGraph_t graph = nullptr;
-  hipGraphExec_t exec = nullptr;
-
-  ~pp_depformer() {
-    if (exec) (void)hipGraphExecDestroy(exec);
-    if (graph) (void)hipGraphDestroy(graph);
-    if (ws) (void)hipFree(ws);
-  }
-  hipError_t enqueue(hipStream_t st);
-};
-
 static pp_status validate_depth_config(const pp_depth_config* c) {
   if (!c) return pp_fail(PP_E_ARG, "config is NULL");
   if (c->wdtype != PP_F32 && c->wdtype != PP_BF16) return pp_fail(PP_E_DTYPE, "wdtype must be PP_F32 or PP_BF16");
@@ -109,7 +84,7 @@ extern "C" pp_status pp_depformer_create(const pp_depth_config* cfg, const pp_de
   auto take = [&](size_t n) { size_t off = bytes; bytes += (n + 255) / 256 * 256; return off; };
   const size_t oh = take(4 * (size_t)cfg->d_temporal), oc = take(4 * (size_t)S * D), oz = take(4 * (size_t)D);
   const size_t oq = take(4 * (size_t)D), os = take(4 * (size_t)F), okv = take(4 * (size_t)L * 2 * H * S * dh);
-  const size_t ol = take(4 * (size_t)S * cfg->n_out), ocd = take(4 * (size_t)S), oct = take(4 * (size_t)(S + 1));
+  const size_t ol = take(4 * (size_t)S * cfg->n_out), ocd = take(4 * (size_t)S), oct = take(sizeof(DepthCtrl));
   if (hipMalloc(&d->ws, bytes) != hipSuccess || hipMemset(d->ws, 0, bytes) != hipSuccess) {
     delete d;
     return pp_fail(PP_E_HIP, "hipMalloc of the depformer workspace failed");
@@ -123,7 +98,7 @@ extern "C" pp_status pp_depformer_create(const pp_depth_config* cfg, const pp_de
   d->kv = reinterpret_cast<float*>(b + okv);
   d->logits = reinterpret_cast<float*>(b + ol);
   d->codes = reinterpret_cast<int32_t*>(b + ocd);
-  d->ctrl = reinterpret_cast<int32_t*>(b + oct);
+  d->ctrl = reinterpret_cast<DepthCtrl*>(b + oct);
   *out = d;
   return PP_OK;
 }
@@ -223,35 +198,45 @@ extern "C" pp_status pp_depformer_step(pp_depformer* d, const float* h_dev, cons
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = launch_depth_setup(sa, st);
   if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("depth setup: ") + hipGetErrorString(e));
-  if (!d->use_graph) {
-    e = d->enqueue(st);
+  pp_status ps = d->run(st);
+  if (ps) return ps;
+  e = hipMemcpyAsync(codes_dev, d->codes, sizeof(int32_t) * c.n_steps, hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess && logits_dev)
+    e = hipMemcpyAsync(logits_dev, d->logits, sizeof(float) * c.n_steps * c.n_out, hipMemcpyDeviceToDevice, st);
+  if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("depformer step: ") + hipGetErrorString(e));
+  return PP_OK;
+}
+
+// The frame's launches after the control words and h are in place: directly, or as one
+// graph captured on first use and replayed (its kernels read everything per-frame from
+// device memory).
+pp_status pp_depformer::run(hipStream_t st) {
+  hipError_t e;
+  if (!use_graph) {
+    e = enqueue(st);
   } else {
-    if (!d->exec) {
+    if (!exec) {
       hipStream_t cap;
       if (hipStreamCreateWithFlags(&cap, hipStreamNonBlocking) != hipSuccess)
         return pp_fail(PP_E_HIP, "hipStreamCreate for graph capture failed");
       e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
       if (e == hipSuccess) {
-        hipError_t le = d->enqueue(cap);
-        e = hipStreamEndCapture(cap, &d->graph);
+        hipError_t le = enqueue(cap);
+        e = hipStreamEndCapture(cap, &graph);
         if (le != hipSuccess) e = le;
       }
-      if (e == hipSuccess) e = hipGraphInstantiate(&d->exec, d->graph, nullptr, nullptr, 0);
+      if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
       (void)hipStreamDestroy(cap);
       if (e != hipSuccess) {
-        if (d->graph) (void)hipGraphDestroy(d->graph);
-        d->graph = nullptr;
-        d->exec = nullptr;
+        if (graph) (void)hipGraphDestroy(graph);
+        graph = nullptr;
+        exec = nullptr;
         return pp_fail(PP_E_HIP, std::string("depformer graph capture: ") + hipGetErrorString(e));
       }
     }
-    e = hipGraphLaunch(d->exec, st);
+    e = hipGraphLaunch(exec, st);
   }
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(codes_dev, d->codes, sizeof(int32_t) * c.n_steps, hipMemcpyDeviceToDevice, st);
-  if (e == hipSuccess && logits_dev)
-    e = hipMemcpyAsync(logits_dev, d->logits, sizeof(float) * c.n_steps * c.n_out, hipMemcpyDeviceToDevice, st);
-  if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("depformer step: ") + hipGetErrorString(e));
+  if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("depformer launch: ") + hipGetErrorString(e));
   return PP_OK;
 }
 

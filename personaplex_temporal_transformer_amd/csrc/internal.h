@@ -116,11 +116,22 @@ hipError_t launch_rmsnorm_rows(const float* x, const float* alpha, float eps, in
 
 namespace pp {
 // ---------------------------------------------------------------- depth transformer
+// Per-frame control words of the depth loop, in device memory so that a captured graph
+// reads them at replay time.
+struct DepthCtrl {
+  int32_t text;          // text token that conditions position 0
+  int32_t forced[32];    // forced[q] >= 0: the code of position q; -1: selected by the model
+  float temperature;     // selection rule: top_k <= 1 or temperature <= 0 -> argmax,
+  int32_t top_k;         //   else temperature / top-k sampling with draw u[q]
+  int32_t pad;
+  double u[32];
+};
+
 struct DepthSetupArgs {
   const float* h_src;   // caller's temporal hidden [d_temporal]
   float* h_dst;         // library copy
   int d_temporal;
-  int32_t* ctrl;        // [0] = text token, [1 + q] = forced code of position q (-1: select)
+  DepthCtrl* ctrl;
   int32_t text_token;
   int32_t forced[32];
   int n_steps;
@@ -131,12 +142,13 @@ struct DepthSelectArgs {
   const float* c_all;        // [n_steps][D] temporal-to-depth projections
   const void* text_emb;      // [text_vocab][D]
   const void* audio_emb[32]; // position q > 0 reads table q-1
-  const int32_t* ctrl;
+  const DepthCtrl* ctrl;
   const float* logits;       // [n_steps][n_out]
   int32_t* codes;            // [n_steps]
   float* z;                  // [D] residual of position q
   int q, D, n_out, n_steps;
 };
+constexpr int kDepthSampleMaxOut = 2048;   // sampled depth selection: n_out <= this
 hipError_t launch_depth_select(const DepthSelectArgs& a, bool bf16, hipStream_t s);
 }  // namespace pp
 
@@ -180,4 +192,59 @@ hipError_t launch_attn_prefill(const AttnPrefillArgs& a, bool bf16, int dh, hipS
 
 // rope[t][2j] = cos((p0 + t) * omega_j), rope[t][2j+1] = sin(...), angles in float64
 hipError_t launch_rope_rows(float* rope, int T, int p0, int dh, double log_theta, hipStream_t s);
+}  // namespace pp
+
+namespace pp {
+// ---------------------------------------------------------------- generator frame
+constexpr int kGenMaxRing = 8;   // code-ring slots (maximum delay + 3)
+constexpr int kMaxTopK = 1024;   // sampling candidates at most
+
+// The generator's device state: the delayed-code ring with its provided flags, and the
+// current frame's temporal input, selections and text control.
+struct GenState {
+  int32_t tok[kMaxStreams][kGenMaxRing];
+  int32_t prov[kMaxStreams][kGenMaxRing];
+  int32_t ids[kMaxStreams];      // temporal input of the frame (ring slot s-1)
+  int32_t chosen[kMaxStreams];   // the frame's selection per stream (supplied or sampled)
+  int32_t text_forced;           // supplied text of the target slot, -1 if none
+  int32_t pad;
+  double u_text;                 // the text draw
+};
+
+struct GenPrepArgs {
+  GenState* g;
+  DepthCtrl* dctrl;
+  int32_t provided[kMaxStreams];   // -1: not supplied
+  int32_t delays[kMaxStreams];
+  int32_t initial[kMaxStreams];
+  double u[kMaxStreams];           // [0] text, [1 + q] depth position q
+  long long s;                     // cursor at entry
+  int n, C;
+  float audio_temperature;
+  int audio_top_k;
+};
+struct GenTextArgs {
+  GenState* g;
+  DepthCtrl* dctrl;
+  const float* logits;   // [n] text logits of the frame
+  int n;
+  float temperature;
+  int top_k;
+};
+struct GenFinishArgs {
+  GenState* g;
+  const int32_t* codes;   // [n_streams - 1] depth selections
+  int32_t* out;           // [n_streams] aligned output, or nullptr
+  int32_t delays[kMaxStreams];
+  long long s;
+  int n, C, max_delay;
+};
+constexpr int kGenTextThreads = 1024, kGenTextPer = 32;   // text rows up to 32768 logits
+hipError_t launch_gen_prepare(const GenPrepArgs& a, hipStream_t s);
+hipError_t launch_gen_text(const GenTextArgs& a, hipStream_t s);
+hipError_t launch_gen_finish(const GenFinishArgs& a, hipStream_t s);
+
+// rows independent draws: out[r] = sample of logits[r*n .. r*n+n) with u[r]; n <= 32768
+hipError_t launch_sample_rows(const float* logits, int rows, int n, float temperature, int top_k,
+                              const double* u, int32_t* out, hipStream_t s);
 }  // namespace pp

@@ -79,6 +79,8 @@ struct pp_model {
   pp_status stage_ids(const int32_t* ids_host, size_t n, hipStream_t s);
   hipError_t enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long long pos_arg, long long seq_arg);
   pp_status run_layers(pp_kv* kv, hipStream_t s);
+  pp_status decode(pp_kv* kv, const int32_t* ids_host, const int32_t* ids_dev, float* h_out_dev,
+                   float* text_logits_dev, hipStream_t s);
 };
 
 struct pp_kv {
@@ -92,3 +94,32 @@ struct pp_kv {
   int exec_model_gen = -1;
   ~pp_kv();
 };
+
+// Depth transformer handle (depformer.cpp); its workspace holds the per-frame state.
+struct pp_depformer {
+  pp_depth_config cfg{};
+  bool bf16 = true;
+  int n_cu = 0;
+  std::vector<const void*> in_proj, audio_emb, w_qkv, w_o, w_in, w_out, head;
+  std::vector<const float*> norm1, norm2;
+  const void* text_emb = nullptr;
+
+  void* ws = nullptr;
+  float *h = nullptr, *c_all = nullptr, *z = nullptr, *q = nullptr, *s = nullptr, *kv = nullptr,
+        *logits = nullptr;
+  int32_t* codes = nullptr;
+  pp::DepthCtrl* ctrl = nullptr;
+  int gemv_blocks = 256;
+  bool use_graph = true;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+
+  ~pp_depformer() {
+    if (exec) (void)hipGraphExecDestroy(exec);
+    if (graph) (void)hipGraphDestroy(graph);
+    if (ws) (void)hipFree(ws);
+  }
+  hipError_t enqueue(hipStream_t st);
+  pp_status run(hipStream_t st);
+};
+

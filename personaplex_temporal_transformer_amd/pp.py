@@ -23,7 +23,8 @@ EXPORTS = ["pp_temporal_create", "pp_temporal_destroy", "pp_kv_alloc", "pp_kv_fr
            "pp_kv_info", "pp_kv_load", "pp_kv_store", "pp_embed_sum", "pp_temporal_decode_step",
            "pp_temporal_prefill", "pp_depformer_create", "pp_depformer_destroy", "pp_depformer_step",
            "pp_last_error", "pp_temporal_set_graph", "pp_temporal_trace", "pp_temporal_trace_read",
-           "pp_depformer_set_graph"]
+           "pp_depformer_set_graph", "pp_sample_top_k", "pp_generator_create", "pp_generator_destroy",
+           "pp_generator_step", "pp_generator_inspect"]
 
 
 class PPError(RuntimeError):
@@ -63,6 +64,13 @@ class DepthWeights(ctypes.Structure):
                 ("norm2", ctypes.POINTER(ctypes.c_void_p)), ("head", ctypes.POINTER(ctypes.c_void_p))]
 
 
+class GeneratorConfig(ctypes.Structure):
+    _fields_ = [("n_streams", ctypes.c_int32), ("delays", ctypes.c_int32 * 32), ("text_initial", ctypes.c_int32),
+                ("audio_initial", ctypes.c_int32), ("text_temperature", ctypes.c_float),
+                ("text_top_k", ctypes.c_int32), ("audio_temperature", ctypes.c_float),
+                ("audio_top_k", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -95,6 +103,11 @@ def load():
         "pp_depformer_set_graph": [VP, I32],
         "pp_temporal_trace": [VP, I32],
         "pp_temporal_trace_read": [VP, P(I64), P(ctypes.c_double)],
+        "pp_sample_top_k": [VP, I32, I32, ctypes.c_float, I32, VP, VP, VP],
+        "pp_generator_create": [VP, VP, VP, P(GeneratorConfig), P(VP)],
+        "pp_generator_destroy": [VP],
+        "pp_generator_step": [VP, P(I32), P(ctypes.c_double), VP, P(I32), VP],
+        "pp_generator_inspect": [VP, VP, VP, VP, VP, VP],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -306,3 +319,66 @@ class Depformer:
             fp = None
         _check(load().pp_depformer_step(self.handle, _ptr(h), tp, fp, 1, _ptr(codes_out), _ptr(logits_out),
                                         _stream(stream)))
+
+
+# ----------------------------------------------------------------------------- sampling / generator
+
+def sample_top_k(logits, temperature, top_k, uniforms, out, stream=None):
+    """pp_sample_top_k over a [rows, n] float32 CUDA tensor; uniforms: float64 CUDA tensor
+    [rows] or None; out: int32 CUDA tensor [rows]."""
+    rows, n = (1, logits.shape[0]) if logits.dim() == 1 else tuple(logits.shape)
+    _check(load().pp_sample_top_k(_ptr(logits), int(rows), int(n), float(temperature), int(top_k),
+                                  _ptr(uniforms), _ptr(out), _stream(stream)))
+
+
+# Released-path generator defaults: delays per stream (text, agent codebooks 0..7, user
+# codebooks 0..7), initial tokens, text and audio sampling.
+GENERATOR_DEFAULTS = dict(delays=(0, 0, 1, 1, 1, 1, 1, 1, 1, 0, 1, 1, 1, 1, 1, 1, 1), text_initial=32000,
+                          audio_initial=2048, text_temperature=0.7, text_top_k=25, audio_temperature=0.8,
+                          audio_top_k=250)
+
+
+class Generator:
+    """pp_generator_create over a TemporalModel, its KV ring and a Depformer (kept alive)."""
+
+    def __init__(self, model, kv, depformer, **overrides):
+        p = dict(GENERATOR_DEFAULTS)
+        p.update(overrides)
+        self._keep = (model, kv, depformer)
+        d = list(p["delays"])
+        c = GeneratorConfig(len(d), (ctypes.c_int32 * 32)(*d), p["text_initial"], p["audio_initial"],
+                            p["text_temperature"], p["text_top_k"], p["audio_temperature"], p["audio_top_k"])
+        self.n = len(d)
+        h = ctypes.c_void_p()
+        _check(load().pp_generator_create(model.handle, kv.handle, depformer.handle, ctypes.byref(c),
+                                          ctypes.byref(h)))
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None):
+            _check(load().pp_generator_destroy(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def step(self, provided=None, uniforms=None, out=None, stream=None):
+        """Returns True when `out` (int32 CUDA tensor [n_streams]) received an aligned frame."""
+        pp_ = None
+        if provided is not None:
+            pa, pp_ = _ids(np.asarray(provided, np.int32))
+        up = None
+        if uniforms is not None:
+            ua = np.ascontiguousarray(uniforms, np.float64)
+            up = ua.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+        has = ctypes.c_int32()
+        _check(load().pp_generator_step(self.handle, pp_, up, _ptr(out), ctypes.byref(has), _stream(stream)))
+        return bool(has.value)
+
+    def inspect(self, inputs=None, chosen=None, text_logits=None, depth_logits=None, stream=None):
+        _check(load().pp_generator_inspect(self.handle, _ptr(inputs), _ptr(chosen), _ptr(text_logits),
+                                           _ptr(depth_logits), _stream(stream)))
+
