@@ -98,6 +98,7 @@ def make_device_weights(cfg, seed):
         W[p + "norm1.alpha"] = norm(D)
         W[p + "norm2.alpha"] = norm(D)
     W["out_norm.alpha"] = norm(D)
+    W["text_linear.weight"] = mat(cfg["text_vocab"] - 1, D)
     return W
 
 
@@ -109,13 +110,10 @@ def depth_frame_bytes(dc):
     return S * per_step * 2
 
 
-def bench_depformer(steps, warmup):
-    """Depth transformer frames (16 positions, greedy selection) at full size, bf16."""
+def make_depth_weights(dc, seed):
     import torch
-    from personaplex_temporal_transformer_amd import pp, synth
-    dc = dict(synth.FULL_DEPTH)
     g = torch.Generator(device="cuda")
-    g.manual_seed(5)
+    g.manual_seed(seed)
     D, F, S, L = dc["d_model"], dc["d_ff"], dc["n_steps"], dc["n_layers"]
 
     def mat(r, c):
@@ -136,7 +134,15 @@ def bench_depformer(steps, warmup):
             W[p + "gating.%d.linear_out.weight" % q] = mat(D, F)
         W[p + "norm1.alpha"] = 1.0 + 0.02 * torch.randn(D, generator=g, device="cuda")
         W[p + "norm2.alpha"] = 1.0 + 0.02 * torch.randn(D, generator=g, device="cuda")
-    d = pp.Depformer(dc, W, "bf16")
+    return W
+
+
+def bench_depformer(d, dc, steps, warmup):
+    """Depth transformer frames (16 positions, greedy selection) at full size, bf16."""
+    import torch
+    S = dc["n_steps"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(6)
     h = torch.randn(dc["d_temporal"], generator=g, device="cuda")
     codes = torch.empty(S, dtype=torch.int32, device="cuda")
     for i in range(warmup):
@@ -150,11 +156,48 @@ def bench_depformer(steps, warmup):
     torch.cuda.synchronize()
     ms = s.elapsed_time(e) / steps
     nb = depth_frame_bytes(dc)
-    d.close()
-    del W
     return {"ms_per_frame": round(ms, 4), "frame_bytes": nb, "achieved_GBps": round(nb / (ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "steps": steps,
             "workload": "depth transformer, 16 positions greedy, 6 layers x 1024, window 8, bf16"}
+
+
+FRAME_BUDGET_MS = 80.0   # one 12.5 Hz audio frame
+
+
+def bench_generator(model, kv, d, cfg, dc, steps, warmup):
+    """Whole generator frames at full size: the code ring, the 32-block temporal step with
+    the ring of keys full, the text head and a text draw (top 25, temperature 0.7), and the
+    16-position depth loop drawing each code (top 250, temperature 0.8); user audio codes
+    supplied every call, uniforms drawn on the host."""
+    import torch
+    from personaplex_temporal_transformer_amd import pp
+    gen = pp.Generator(model, kv, d)
+    rng = np.random.default_rng(12)
+    n = warmup + steps + 1
+    prov = np.full((n, 17), -1, np.int32)
+    prov[:, 9:] = rng.integers(0, dc["n_out"], (n, 8))
+    U = rng.random((n, 17))
+    out = torch.empty(17, dtype=torch.int32, device="cuda")
+    for i in range(warmup + 1):
+        gen.step(prov[i], U[i], out)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(warmup + 1, n):
+        gen.step(prov[i], U[i], out)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    pos, _ = kv.info()
+    nb = frame_bytes(cfg, cfg["context"]) + depth_frame_bytes(dc) + (cfg["text_vocab"] - 1) * cfg["d_model"] * 2
+    gen.close()
+    return {"ms_per_frame": round(ms, 4), "frames_per_s": round(1000.0 / ms, 2),
+            "realtime_factor": round(FRAME_BUDGET_MS / ms, 2), "frame_budget_ms": FRAME_BUDGET_MS,
+            "frame_bytes": nb, "achieved_GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "steps": steps,
+            "final_position": pos,
+            "workload": "generator frame: code ring + 32-block temporal step (3000 visible keys) + text head "
+                        "+ text draw (top 25, T 0.7) + 16-position depth loop with draws (top 250, T 0.8), bf16"}
 
 
 def prefill_flops(cfg, T):
@@ -278,6 +321,24 @@ def cpu_baselines(cfg, want_prefill=True, want_depth=True):
                         "kind": "oracle",
                         "sample": "2 of the 16 positions of a depth frame (fp64 NumPy, a 2-position depth stack "
                                   "of full width), best of %d, scaled x8" % n}
+        from oracle.sampling import sample_top_k
+        rng = np.random.default_rng(3)
+        tl = rng.normal(size=cfg["text_vocab"] - 1).astype(np.float32)
+        dl = rng.normal(size=(16, dc["n_out"])).astype(np.float32)
+        u = rng.random(17)
+
+        def draws():
+            sample_top_k(tl, 0.7, 25, u[0])
+            for q in range(16):
+                sample_top_k(dl[q], 0.8, 250, u[q + 1])
+
+        t, n = _best_of(draws)
+        out["draws"] = {"value": t * 1000.0, "unit": "ms/frame"}
+        Wh = synth.weight(8, "text_linear.weight", (cfg["text_vocab"] - 1, cfg["d_model"]), "bf16")
+        Wf = {"out_norm.alpha": synth.norm_scale(8, "out_norm.alpha", cfg["d_model"]), "text_linear.weight": Wh}
+        xv = synth.hidden(cfg["d_model"], 4)
+        t, n = _best_of(lambda: O.final(xv, Wf, cfg, with_logits=True))
+        out["text_head"] = {"value": t * 1000.0, "unit": "ms/frame"}
     return out
 
 
@@ -378,6 +439,12 @@ def main():
     }
     # the extra workloads run after the headline decode timing (a prefill burst at full
     # matrix-core load leaves the clocks lower for a while)
+    dc = dict(synth.FULL_DEPTH)
+    dep = None
+    if not args.no_depformer:
+        DW = make_depth_weights(dc, 5)
+        dep = pp.Depformer(dc, DW, "bf16")
+        out["generator"] = bench_generator(model, kv, dep, cfg, dc, max(10, args.steps // 2), 3)
     if args.prefill_T > 0:
         kv.close()
         out["prefill"] = bench_prefill(model, cfg, args.prefill_T, args.prefill_steps, 1)
@@ -388,12 +455,9 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         del a, b
-    if not args.no_depformer:
-        model.close()
-        kv.close()
-        del W
-        torch.cuda.empty_cache()
-        out["depformer"] = bench_depformer(max(10, args.steps // 2), 3)
+    if dep is not None:
+        out["depformer"] = bench_depformer(dep, dc, max(10, args.steps // 2), 3)
+        dep.close()
     if not args.no_cpu_baseline:
         cb = cpu_baselines(cfg, want_prefill="prefill" in out, want_depth="depformer" in out)
         out["cpu_baseline"] = cb["decode"]
@@ -401,6 +465,13 @@ def main():
             out["prefill"]["cpu_baseline"] = cb["prefill"]
         if "depth" in cb:
             out["depformer"]["cpu_baseline"] = cb["depth"]
+            g = cb["draws"]
+            out["generator"]["cpu_baseline"] = {
+                "value": cb["decode"]["value"] + cb["depth"]["value"] + g["value"] + cb["text_head"]["value"],
+                "unit": "ms/frame", "cores": cb["decode"]["cores"], "kind": "oracle",
+                "sample": "sum of the oracle's decode-frame and depth-frame samples above, the text head "
+                          "(%.1f ms) and one frame's 17 draws at full vocab sizes (%.1f ms)"
+                          % (cb["text_head"]["value"], g["value"])}
     print(json.dumps(out), flush=True)
 
 

@@ -77,6 +77,9 @@ extern "C" pp_status pp_depformer_create(const pp_depth_config* cfg, const pp_de
   d->norm2.assign(w->norm2, w->norm2 + L);
   d->text_emb = w->text_emb;
   d->gemv_blocks = env_int("PP_GEMV_BLOCKS_PER_CU", 1) * n_cu;
+  d->qkv_blocks = env_int("PP_DEPTH_QKV_BLOCKS", d->gemv_blocks);
+  d->attn_blocks = env_int("PP_DEPTH_ATTN_BLOCKS", d->gemv_blocks);
+  d->ffn_blocks = env_int("PP_DEPTH_FFN_BLOCKS", d->gemv_blocks);
   d->use_graph = env_int("PP_GRAPH", 1) != 0;
 
   const int D = cfg->d_model, F = cfg->d_ff, H = cfg->n_heads, dh = cfg->d_head;
@@ -147,23 +150,23 @@ hipError_t pp_depformer::enqueue(hipStream_t st) {
       g.W = static_cast<const char*>(w_qkv[m]) + (size_t)qs * 3 * D * D * esz;
       g.x = z; g.alpha = norm1[m]; g.eps = (float)c.eps; g.K = D; g.n_groups = 3 * D / 2;
       g.out = q; g.D = D; g.dh = dh; g.C = S; g.kc = kc; g.vc = vc; g.slot_override = qs;
-      if ((e = launch_gemv(PRO_RMSNORM, EPI_DEPTH_QKV, bf16, 2, g, gemv_blocks, st)) != hipSuccess) return e;
+      if ((e = launch_gemv(PRO_RMSNORM, EPI_DEPTH_QKV, bf16, 2, g, qkv_blocks, st)) != hipSuccess) return e;
 
       GemvArgs go{};
       go.W = static_cast<const char*>(w_o[m]) + (size_t)qs * D * D * esz;
       go.K = D; go.n_groups = D / 2; go.out = z;
       go.aq = q; go.ak = kc; go.av = vc; go.aH = H; go.adh = dh; go.acap = S; go.aq_pos = qs;
       go.awin = c.window; go.ascale = 1.0f / std::sqrt((float)dh);
-      if ((e = launch_gemv(PRO_DEPTH_ATTN, EPI_RESID, bf16, 2, go, gemv_blocks, st)) != hipSuccess) return e;
+      if ((e = launch_gemv(PRO_DEPTH_ATTN, EPI_RESID, bf16, 2, go, attn_blocks, st)) != hipSuccess) return e;
 
       GemvArgs gi{};
       gi.W = w_in[m * S + qs]; gi.x = z; gi.alpha = norm2[m]; gi.eps = (float)c.eps; gi.K = D;
       gi.n_groups = F; gi.out = s; gi.F = F;
-      if ((e = launch_gemv(PRO_RMSNORM, EPI_SWIGLU, bf16, 2, gi, gemv_blocks, st)) != hipSuccess) return e;
+      if ((e = launch_gemv(PRO_RMSNORM, EPI_SWIGLU, bf16, 2, gi, ffn_blocks, st)) != hipSuccess) return e;
 
       GemvArgs gw{};
       gw.W = w_out[m * S + qs]; gw.x = s; gw.K = F; gw.n_groups = D / 2; gw.out = z;
-      if ((e = launch_gemv(PRO_COPY, EPI_RESID, bf16, 2, gw, gemv_blocks, st)) != hipSuccess) return e;
+      if ((e = launch_gemv(PRO_COPY, EPI_RESID, bf16, 2, gw, ffn_blocks, st)) != hipSuccess) return e;
     }
     GemvArgs gh{};
     gh.W = head[qs]; gh.x = z; gh.K = D; gh.n_groups = c.n_out / 2; gh.out = logits + (size_t)qs * c.n_out;

@@ -110,6 +110,7 @@ struct pp_depformer {
   int32_t* codes = nullptr;
   pp::DepthCtrl* ctrl = nullptr;
   int gemv_blocks = 256;
+  int qkv_blocks = 256, attn_blocks = 256, ffn_blocks = 256;   // per-launch workgroups of the depth GEMVs
   bool use_graph = true;
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;

@@ -107,3 +107,75 @@ def test_full_prefill_32_blocks_T3000():
             e = norm_max_err(O.f64(ap[l, kvi, 0][:, rows]), O.f64(ad[l, kvi, 0][:, rows]))
             print("ring layer %d %s: err %.3g" % (l, "KV"[kvi], e))
             assert e <= 2 * BF16_TOL
+
+
+def test_full_generator_frames_ctx3000():
+    """Generator frames at full size with the ring of keys full, as the benchmark runs them:
+    every drawn code equals the oracle sampler's draw on the GPU's own logits, supplied codes
+    win, the temporal input of call s is the ring slot that call s - 1 filled, and the
+    aligned output takes delay-0 streams from call s - 1 and delay-1 streams from call s."""
+    import torch
+    from oracle import generator as OG
+    from oracle.sampling import sample_top_k
+    cfg, dc = dict(synth.FULL_TEMPORAL), dict(synth.FULL_DEPTH)
+    C, D = cfg["context"], cfg["d_model"]
+    W = synth.temporal_weights(cfg, 46, "bf16", with_text_head=True, shared_layer=True)
+    model = _model(cfg, W)
+    kv = model.kv_alloc()
+    frames = synth.cache_frames(cfg, C, 47)
+    kv.load(torch.from_numpy(frames.view(np.int16)).cuda(), C)
+    del frames
+    g = torch.Generator(device="cuda")
+    g.manual_seed(48)
+    Dd, F, S, Ld = dc["d_model"], dc["d_ff"], dc["n_steps"], dc["n_layers"]
+    mat = lambda r, c: (0.02 * torch.randn((r, c), generator=g, device="cuda")).to(torch.bfloat16)
+    DW = {"depformer_text_emb.weight": mat(dc["text_vocab"], Dd)}
+    for q in range(S):
+        DW["depformer_in.%d.weight" % q] = mat(Dd, D)
+        DW["linears.%d.weight" % q] = mat(dc["n_out"], Dd)
+        if q < S - 1:
+            DW["depformer_emb.%d.weight" % q] = mat(dc["audio_vocab"], Dd)
+    for m in range(Ld):
+        p = "depformer.layers.%d." % m
+        DW[p + "self_attn.in_proj_weight"] = mat(S * 3 * Dd, Dd)
+        DW[p + "self_attn.out_proj.weight"] = mat(S * Dd, Dd)
+        for q in range(S):
+            DW[p + "gating.%d.linear_in.weight" % q] = mat(2 * F, Dd)
+            DW[p + "gating.%d.linear_out.weight" % q] = mat(Dd, F)
+        DW[p + "norm1.alpha"] = torch.ones(Dd, device="cuda")
+        DW[p + "norm2.alpha"] = torch.ones(Dd, device="cuda")
+    dep = pp.Depformer(dc, DW, "bf16")
+    gen = pp.Generator(model, kv, dep)
+    rng = np.random.default_rng(49)
+    n = 6
+    prov = np.full((n, 17), -1, np.int32)
+    prov[:, 9:] = rng.integers(0, dc["n_out"], (n, 8))
+    U = rng.random((n, 17))
+    dly = np.array(OG.DELAYS)
+    out = torch.empty(17, dtype=torch.int32, device="cuda")
+    ins = torch.empty(17, dtype=torch.int32, device="cuda")
+    cho = torch.empty(17, dtype=torch.int32, device="cuda")
+    tl = torch.empty(cfg["text_vocab"] - 1, device="cuda")
+    dl = torch.empty((S, dc["n_out"]), device="cuda")
+    chosen = {}
+    for s in range(n):
+        has = gen.step(prov[s], U[s], out)
+        if s == 0:
+            assert not has
+            continue
+        gen.inspect(ins, cho, tl, dl)
+        torch.cuda.synchronize()
+        c, i, t_l, d_l = cho.cpu().numpy(), ins.cpu().numpy(), tl.cpu().numpy(), dl.cpu().numpy()
+        chosen[s] = c
+        assert c[0] == sample_top_k(t_l, 0.7, 25, U[s][0]), s
+        for k in range(1, 9):
+            assert c[k] == sample_top_k(d_l[k - 1], 0.8, 250, U[s][k]), (s, k)
+        assert c[9] == prov[s][9] and np.array_equal(c[10:], prov[s - 1][10:]), s
+        if s >= 2:
+            assert np.array_equal(i, chosen[s - 1]), s      # the input slot is the last call's target
+        assert has == (s >= 2), s
+        if has:
+            want = np.where(dly == 0, chosen[s - 1], c)
+            assert np.array_equal(out.cpu().numpy(), want), s
+    assert kv.info()[0] == C + n - 1
+    print("full generator: %d calls, drawn codes equal the oracle sampler on the GPU logits" % n)

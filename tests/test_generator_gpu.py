@@ -40,7 +40,8 @@ def _check_rows(logits, temperature, top_k, u, label):
 
 
 @pytest.mark.parametrize("n,k,t", [(2048, 250, 0.8), (32000, 25, 0.7), (1000, 250, 0.8), (5000, 40, 1.3),
-                                   (2049, 1024, 0.5), (32768, 1024, 2.0), (100, 250, 0.8), (1, 25, 0.7)])
+                                   (2049, 1024, 0.5), (32768, 1024, 2.0), (2048, 1024, 1.0), (100, 250, 0.8),
+                                   (1, 25, 0.7)])
 def test_sampler_random_rows(n, k, t):
     g = np.random.default_rng(n + k)
     rows = 48
