@@ -241,6 +241,39 @@ def bench_prefill(model, cfg, T, steps, warmup):
                         "K/V written to ring slots 0..T-1" % T}
 
 
+def bench_chunk(model, kv, cfg, T, steps, warmup):
+    """Prefill chunks of T frames into the live, full ring (prompt replay at position > 0):
+    each chunk's queries see the 3000-key window of history plus the chunk."""
+    import torch
+    n = warmup + steps
+    ids = synth_ids(cfg, n * T, 13)
+    h = torch.empty((T, cfg["d_model"]), device="cuda")
+    for i in range(warmup):
+        model.prefill(kv, ids[i * T:(i + 1) * T], h)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(warmup, n):
+        model.prefill(kv, ids[i * T:(i + 1) * T], h)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    D, F, L, H, dh, C = cfg["d_model"], cfg["d_ff"], cfg["n_layers"], cfg["n_heads"], cfg["d_head"], cfg["context"]
+    gemm = 2.0 * T * L * (3 * D * D + D * D + 2 * F * D + D * F)
+    attn = 2.0 * 2 * dh * H * L * T * C          # every query sees a full window of C keys
+    tf = (gemm + attn) / (ms * 1e-3) / 1e12
+    pos, _ = kv.info()
+    return {"ms": round(ms, 3), "T": T, "TFLOPs": round(tf, 1), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "frames_per_s": round(T * 1000.0 / ms, 1), "flop": gemm + attn, "steps": steps, "final_position": pos,
+            "workload": "prefill chunk of %d frames into the full ring (history window 3000 keys, ring wraps), "
+                        "32 blocks, bf16" % T}
+
+
+def synth_ids(cfg, n, seed):
+    from personaplex_temporal_transformer_amd import synth
+    return synth.stream_ids(cfg, n, seed)
+
+
 def fill_ring(kv, cfg, seed):
     import torch
     g = torch.Generator(device="cuda")
@@ -353,6 +386,7 @@ def main():
     ap.add_argument("--no-depformer", action="store_true")
     ap.add_argument("--prefill-T", type=int, default=3000, help="0: skip the prefill line")
     ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--chunk-T", type=int, default=256, help="0: skip the prefill-chunk line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the run, copy 1 GiB device-to-device 3 times (counter calibration)")
     args = ap.parse_args()
@@ -445,6 +479,8 @@ def main():
         DW = make_depth_weights(dc, 5)
         dep = pp.Depformer(dc, DW, "bf16")
         out["generator"] = bench_generator(model, kv, dep, cfg, dc, max(10, args.steps // 2), 3)
+    if args.chunk_T > 0 and args.prefill_T >= args.chunk_T:
+        out["prefill_chunk"] = bench_chunk(model, kv, cfg, args.chunk_T, 5, 1)
     if args.prefill_T > 0:
         kv.close()
         out["prefill"] = bench_prefill(model, cfg, args.prefill_T, args.prefill_steps, 1)

@@ -40,7 +40,7 @@ typedef enum {
   PP_OK = 0,
   PP_E_ARG = 1,       /* bad pointer, size, config or handle */
   PP_E_ID = 2,        /* a stream ID outside [-1, vocab) (includes -2) */
-  PP_E_CAPACITY = 3,  /* prefill longer than the ring or the workspace, or not at position 0 */
+  PP_E_CAPACITY = 3,  /* prefill longer than the ring or the workspace */
   PP_E_DEVICE = 4,    /* no gfx950 device current */
   PP_E_HIP = 5,       /* HIP runtime error */
   PP_E_DTYPE = 6      /* unsupported weight dtype */
@@ -118,6 +118,10 @@ pp_status pp_kv_info(const pp_kv* kv, int64_t* position, uint64_t* bytes);
 pp_status pp_kv_load(pp_kv* kv, const void* src_dev, int32_t n_frames, void* stream);
 /* Copy the whole ring [n_layers][2][batch][n_heads][context][d_head] to dst_dev. */
 pp_status pp_kv_store(const pp_kv* kv, void* dst_dev, void* stream);
+/* Snapshot restore (audit section 9, cached voice prompts restored before live audio):
+ * copy a whole ring written by pp_kv_store (same model and batch) from src_dev and set
+ * position := the position the ring had when it was stored (position >= 0). */
+pp_status pp_kv_restore(pp_kv* kv, const void* src_dev, int64_t position, void* stream);
 
 /* Embedding sum (audit section 3, 'Input embedding sum'): for each of batch*T frames,
  * x = sum over the n_audio+1 streams of that stream's table row, in stream order,
@@ -138,10 +142,13 @@ pp_status pp_embed_sum(const pp_model* m, const int32_t* ids_host, int32_t batch
 pp_status pp_temporal_decode_step(pp_model* m, pp_kv* kv, const int32_t* ids_host,
                                   float* h_out_dev, float* text_logits_dev, void* stream);
 
-/* Full-sequence forward of T frames at positions 0..T-1 into an empty ring (position
- * must be 0, 1 <= T <= min(context, max_prefill_T)), causal attention over the frames,
- * K/V written to slots 0..T-1; position := T afterwards, so decode continues at T.
- * ids_host [batch][T][n_audio+1]; h_out_dev [batch][T][d_model] float32 final-norm hidden. */
+/* Full-sequence forward of T frames at positions p..p+T-1, p = the ring's position
+ * (audit section 3; section 9 for prompts replayed into a live ring): causal attention
+ * among the frames and, when p > 0, over the keys of the ring still inside each frame's
+ * context window (0 <= position - key_position < context); K/V of the frames written to
+ * slots (p+t) mod context; position := p+T afterwards, so decode continues there.
+ * 1 <= T <= min(context, max_prefill_T), batch 1. ids_host [batch][T][n_audio+1];
+ * h_out_dev [batch][T][d_model] float32 final-norm hidden. */
 pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* ids_host, int32_t T,
                               float* h_out_dev, void* stream);
 

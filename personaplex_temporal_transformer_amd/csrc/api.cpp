@@ -244,6 +244,15 @@ extern "C" pp_status pp_kv_store(const pp_kv* kv, void* dst_dev, void* stream) {
   return PP_OK;
 }
 
+extern "C" pp_status pp_kv_restore(pp_kv* kv, const void* src_dev, int64_t position, void* stream) {
+  if (!kv || !src_dev) return pp_fail(PP_E_ARG, "NULL argument");
+  if (position < 0) return pp_fail(PP_E_ARG, "negative position");
+  hipError_t e = hipMemcpyAsync(kv->ring, src_dev, kv->bytes, hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("pp_kv_restore: ") + hipGetErrorString(e));
+  kv->pos = position;
+  return PP_OK;
+}
+
 // ------------------------------------------------------------------ embedding
 
 pp_status pp_model::check_ids(const int32_t* ids, size_t frames) const {

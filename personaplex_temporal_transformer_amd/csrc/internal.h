@@ -171,27 +171,53 @@ struct GemmArgs {
   void* s_out;          // GEPI_SWIGLU: [M][F] = SiLU(g) * z (float16 on the bf16-weight path)
   int F;
   // GEPI_QKV, bf16 only: Q goes to q_out as bfloat16; if non-null, V is also written
-  // transposed as float16, vt[H][dh][vt_pitch],
-  // key t in column vt_perm(t) (bits 2 and 3 of t swapped), for the prefill attention
+  // transposed as float16, vt[H][dh][vt_pitch]: key index j in column vt_perm(j) (bits 2
+  // and 3 of j swapped), for the prefill attention; row `row` is key index xoff + row
   void* vt;
   int vt_pitch;
+  // GEPI_QKV, a chunk that starts past position 0: K (and on the float32 path V) are also
+  // written to the chunk's contiguous key space kx / vx [H][x_pitch][dh] at key index
+  // xoff + row (xoff a multiple of 16), where the attention reads them
+  void* kx;
+  void* vx;
+  int x_pitch, xoff;
 };
 hipError_t launch_gemm(int epi, bool bf16, const GemmArgs& g, int n_cu, hipStream_t s);
 
+// The attention of a chunk of T frames at positions p0..p0+T-1 runs in a contiguous key
+// space: key index j is position p0 - koff + j, query i is key index koff + i. Keys
+// [jlo, koff) are the history gathered from the ring, [koff, koff + T) the chunk's own.
 struct AttnPrefillArgs {
-  const void* q;        // [H][T][dh] rotated queries (positions p0..p0+T-1; bfloat16 on the bf16 path)
-  const void* k;        // ring of this layer [H][C][dh]; key of position p in slot p mod C
-  const void* v;
-  const void* vt;       // bf16 path: V transposed (float16) as written by the QKV GEMM (p0 must be 0)
-  int vt_pitch;
+  const void* q;        // [H][T][dh] rotated queries (bfloat16 on the bf16 path)
+  const void* k;        // keys [H][k_pitch][dh] (the ring itself when koff == 0)
+  const void* v;        // float32 path: values, same layout as k
+  const void* vt;       // bf16 path: V transposed, float16 [H][dh][vt_pitch], key j in column vt_perm(j)
+  int vt_pitch, k_pitch;
   void* out;            // [T][H*dh] (float16 on the bf16 path)
-  int T, H, C, p0;
+  int T, H, C;
+  int koff;             // key index of query 0, a multiple of 16
+  int jlo;              // first key index that exists and is inside some query's window
   float scale;
 };
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, bool bf16, int dh, hipStream_t s);
 
+// History of a chunk at p0 > 0: keys [jlo, jhi) of its key space (positions q0 + j) are
+// copied from their ring slots (q0 + j) mod C -- K to kx, V to vt (bf16 path, transposed
+// float16) or vx (float32 path) -- and keys [0, jlo) are zero-filled. jhi is a multiple of 16.
+struct GatherArgs {
+  const void* kring;
+  const void* vring;    // this layer's ring [H][C][dh]
+  void* kx;
+  void* vx;
+  void* vt;
+  int x_pitch, vt_pitch, C, H, dh;
+  long long q0;
+  int jlo, jhi;
+};
+hipError_t launch_gather_history(const GatherArgs& a, bool bf16, hipStream_t s);
+
 // rope[t][2j] = cos((p0 + t) * omega_j), rope[t][2j+1] = sin(...), angles in float64
-hipError_t launch_rope_rows(float* rope, int T, int p0, int dh, double log_theta, hipStream_t s);
+hipError_t launch_rope_rows(float* rope, int T, long long p0, int dh, double log_theta, hipStream_t s);
 }  // namespace pp
 
 namespace pp {

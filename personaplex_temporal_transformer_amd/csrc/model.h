@@ -56,8 +56,10 @@ struct pp_model {
   void* pa = nullptr;          // attention output [T][D], same element type
   void* pg = nullptr;          // SiLU(g)*z [T][F], same element type
   float* prope = nullptr;      // RoPE table [T][dh] (cos, sin pairs)
-  void* pvt = nullptr;         // bf16-weight path: V transposed, float16 [H][dh][vt_pitch] (zero past T)
-  int vt_pitch = 0;            // max_T rounded up to 64
+  void* pvt = nullptr;         // bf16-weight path: V transposed, float16 [H][dh][vt_pitch] of a chunk's key space
+  void* pkx = nullptr;         // a chunk's key space: K [H][x_pitch][dh] (wdtype)
+  void* pvx = nullptr;         // float32 path: V [H][x_pitch][dh]
+  int vt_pitch = 0, x_pitch = 0;   // keys of the key space: max_T + context + 16, rounded up to 64
 
   int32_t* ids_pinned = nullptr;
   size_t ids_cap = 0;

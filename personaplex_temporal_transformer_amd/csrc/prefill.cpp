@@ -1,8 +1,14 @@
 // Full-sequence (prefill) path of the temporal model: workspace and launch order.
 //
 // "PersonaPlex native LM audit", section 3: every block of the temporal transformer
-// applied to T frames at positions 0..T-1 at once, causal attention among them, K and V
-// of every frame left in the ring so that decoding continues at position T.
+// applied to T frames at positions p0..p0+T-1 at once, K and V of every frame left in the
+// ring so that decoding continues at position p0+T. From position 0 the frames attend
+// among themselves (keys read from the ring); a chunk at p0 > 0 (prompt replay into a
+// live ring, section 9 'Startup prompt and clock facts') also attends to the history
+// still inside each query's context window. Its keys could be overwritten by the chunk's
+// own ring writes, so per layer the history is first gathered from the ring into a
+// contiguous key space, the chunk's K and V are written there as well as to the ring, and
+// the attention runs over that key space.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -22,8 +28,11 @@ pp_status pp_model::alloc_prefill() {
   size_t bytes = 0;
   auto take = [&](size_t n) { size_t off = bytes; bytes += (n + 255) / 256 * 256; return off; };
   const size_t oid = take(sizeof(int32_t) * T * ns);
-  size_t ox = 0, ou = 0, oq = 0, oa = 0, og = 0, orope = 0, ovt = 0;
-  vt_pitch = (int)((T + 63) / 64 * 64);
+  size_t ox = 0, ou = 0, oq = 0, oa = 0, og = 0, orope = 0, ovt = 0, okx = 0, ovx = 0;
+  // key space of a chunk: up to context + 15 history keys (start rounded to 16) + T
+  x_pitch = (int)((T + cfg.context + 16 + 63) / 64 * 64);
+  vt_pitch = x_pitch;
+  const size_t H = cfg.n_heads;
   if (max_T > 0) {
     ox = take(sizeof(float) * T * D);
     ou = take(esz * T * D);
@@ -31,7 +40,9 @@ pp_status pp_model::alloc_prefill() {
     oa = take(esz * T * D);
     og = take(esz * T * F);
     orope = take(sizeof(float) * T * dh);
-    if (bf16) ovt = take(2 * (size_t)cfg.n_heads * dh * vt_pitch);
+    okx = take(esz * H * x_pitch * dh);
+    if (bf16) ovt = take(2 * H * dh * vt_pitch);
+    else ovx = take(esz * H * x_pitch * dh);
   }
   if (hipMalloc(&pws, bytes) != hipSuccess) return pp_fail(PP_E_HIP, "hipMalloc of prefill workspace failed");
   char* b = static_cast<char*>(pws);
@@ -43,11 +54,15 @@ pp_status pp_model::alloc_prefill() {
     pa = b + oa;
     pg = b + og;
     prope = reinterpret_cast<float*>(b + orope);
+    pkx = b + okx;
     if (bf16) {
       pvt = b + ovt;
-      // columns past T are read by the attention (as zero-weighted values): keep them finite
-      if (hipMemset(pvt, 0, 2 * (size_t)cfg.n_heads * dh * vt_pitch) != hipSuccess)
+      // columns outside a chunk's keys are read by the attention (as zero-weighted
+      // values): keep them finite
+      if (hipMemset(pvt, 0, 2 * H * dh * vt_pitch) != hipSuccess)
         return pp_fail(PP_E_HIP, "hipMemset of the prefill V copy failed");
+    } else {
+      pvx = b + ovx;
     }
   }
   return PP_OK;
@@ -66,7 +81,7 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
                                          float* h_out_dev, void* stream) {
   if (!m || !kv || !ids_host || !h_out_dev) return pp_fail(PP_E_ARG, "NULL argument");
   if (kv->m != m) return pp_fail(PP_E_ARG, "kv ring belongs to another model");
-  if (kv->pos != 0) return pp_fail(PP_E_ARG, "prefill needs an empty ring (position 0); call pp_kv_reset");
+  if (kv->B != 1) return pp_fail(PP_E_ARG, "prefill needs a batch-1 ring");
   const pp_temporal_config& c = m->cfg;
   if (T < 1 || T > c.context || T > m->max_T)
     return pp_fail(PP_E_CAPACITY, "T must be in [1, min(context, max_prefill_T)]");
@@ -81,6 +96,12 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
   if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = m->bf16;
+  const long long p0 = kv->pos;
+  // key space of the chunk: key index j is position q0 + j; the queries start at koff
+  const int koff = p0 == 0 ? 0 : (int)(((p0 < C - 1 ? p0 : C - 1) + 15) / 16 * 16);
+  const long long q0 = p0 - koff;
+  int jlo = koff - (int)(p0 < (long long)C - 1 ? p0 : (long long)C - 1);   // the oldest key some query sees
+  if (jlo < 0) jlo = 0;
 
   EmbedArgs a{};
   m->embed_tables(a);
@@ -90,7 +111,7 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
   a.ids_dev = m->ids_dev;
   hipError_t e = launch_embed(a, bf, s);
   if (e != hipSuccess) return hip_fail("prefill embed", e);
-  e = launch_rope_rows(m->prope, T, 0, dh, std::log(c.rope_theta), s);
+  e = launch_rope_rows(m->prope, T, p0, dh, std::log(c.rope_theta), s);
   if (e != hipSuccess) return hip_fail("prefill rope table", e);
 
   const size_t esz = bf ? 2 : 4;
@@ -100,20 +121,36 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
   for (int l = 0; l < c.n_layers; ++l) {
     char* kbase = static_cast<char*>(kv->ring) + (size_t)(2 * l) * per_kv;
     char* vbase = kbase + per_kv;
+    if (koff > 0) {
+      GatherArgs ga{};
+      ga.kring = kbase; ga.vring = vbase; ga.kx = m->pkx; ga.vx = m->pvx; ga.vt = m->pvt;
+      ga.x_pitch = m->x_pitch; ga.vt_pitch = m->vt_pitch; ga.C = C; ga.H = H; ga.dh = dh;
+      ga.q0 = q0; ga.jlo = jlo; ga.jhi = koff;
+      e = launch_gather_history(ga, bf, s);
+      if (e != hipSuccess) return hip_fail("prefill history gather", e);
+    }
     e = launch_rmsnorm_rows(m->px, m->norm1[l], (float)c.eps, D, T, u32, u16, s);
     if (e != hipSuccess) return hip_fail("prefill norm1", e);
 
     GemmArgs g{};
     g.A = m->pu; g.B = m->w_qkv[l]; g.M = T; g.N = 3 * D; g.K = D;
     g.q_out = m->pq; g.kc = kbase; g.vc = vbase; g.rope = m->prope;
-    g.D = D; g.dh = dh; g.C = C; g.p0 = 0;
+    g.D = D; g.dh = dh; g.C = C; g.p0 = (int)(p0 % C);
     g.vt = m->pvt; g.vt_pitch = m->vt_pitch;
+    if (koff > 0) {
+      g.kx = m->pkx; g.vx = bf ? nullptr : m->pvx; g.x_pitch = m->x_pitch; g.xoff = koff;
+    }
     e = launch_gemm(GEPI_QKV, bf, g, m->n_cu, s);
     if (e != hipSuccess) return hip_fail("prefill QKV", e);
 
     AttnPrefillArgs at{};
-    at.q = m->pq; at.k = kbase; at.v = vbase; at.vt = m->pvt; at.vt_pitch = m->vt_pitch; at.out = m->pa;
-    at.T = T; at.H = H; at.C = C; at.p0 = 0; at.scale = 1.0f / std::sqrt((float)dh);
+    at.q = m->pq; at.vt = m->pvt; at.vt_pitch = m->vt_pitch; at.out = m->pa;
+    if (koff > 0) {
+      at.k = m->pkx; at.v = m->pvx; at.k_pitch = m->x_pitch;
+    } else {
+      at.k = kbase; at.v = vbase; at.k_pitch = C;
+    }
+    at.T = T; at.H = H; at.C = C; at.koff = koff; at.jlo = jlo; at.scale = 1.0f / std::sqrt((float)dh);
     e = launch_attn_prefill(at, bf, dh, s);
     if (e != hipSuccess) return hip_fail("prefill attention", e);
 
@@ -137,6 +174,6 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
   }
   e = launch_rmsnorm_rows(m->px, m->out_norm, (float)c.eps, D, T, h_out_dev, nullptr, s);
   if (e != hipSuccess) return hip_fail("prefill final norm", e);
-  kv->pos = T;
+  kv->pos = p0 + T;
   return PP_OK;
 }

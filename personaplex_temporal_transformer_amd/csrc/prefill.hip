@@ -40,7 +40,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- RoPE table
 
-__global__ __launch_bounds__(kBlock) void k_rope_rows(float* rope, int T, int p0, int dh, double log_theta) {
+__global__ __launch_bounds__(kBlock) void k_rope_rows(float* rope, int T, long long p0, int dh, double log_theta) {
   const int i = blockIdx.x * kBlock + threadIdx.x;   // (t, j)
   const int half = dh / 2;
   if (i >= T * half) return;
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kBlock) void k_rope_rows(float* rope, int T, int p0
   rope[(size_t)t * dh + 2 * j + 1] = (float)sn;
 }
 
-hipError_t launch_rope_rows(float* rope, int T, int p0, int dh, double log_theta, hipStream_t s) {
+hipError_t launch_rope_rows(float* rope, int T, long long p0, int dh, double log_theta, hipStream_t s) {
   const int n = T * (dh / 2);
   hipLaunchKernelGGL(k_rope_rows, dim3((n + kBlock - 1) / kBlock), dim3(kBlock), 0, s, rope, T, p0, dh, log_theta);
   return hipGetLastError();
@@ -79,6 +79,8 @@ __device__ __forceinline__ void gemm_store(const GemmArgs& g, int row, int col, 
       const int slot = (g.p0 + row) % g.C;
       OT* base = static_cast<OT*>(sec == 1 ? g.kc : g.vc);
       Elem<OT>::store1(base + ((size_t)head * g.C + slot) * g.dh + d, y);
+      OT* xb = static_cast<OT*>(sec == 1 ? g.kx : g.vx);
+      if (xb) Elem<OT>::store1(xb + ((size_t)head * g.x_pitch + g.xoff + row) * g.dh + d, y);
     }
   } else if (EPI == GEPI_RESID) {
     g.x[(size_t)row * g.N + col] += v;
@@ -329,10 +331,14 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(GemmArgs g) {
         if (sec == 0) dst = static_cast<uint16_t*>(g.q_out) + ((size_t)head * g.M + row) * g.dh + d;
         else dst = static_cast<uint16_t*>(sec == 1 ? g.kc : g.vc) + ((size_t)head * g.C + (g.p0 + row) % g.C) * g.dh + d;
         *reinterpret_cast<u32x4*>(dst) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+        if (sec == 1 && g.kx)
+          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.kx) + ((size_t)head * g.x_pitch + g.xoff + row) * g.dh + d) =
+              u32x4{pk[0], pk[1], pk[2], pk[3]};
       }
       if (sec == 2 && g.vt) {
-        // key t of the tile sits in column vt_perm(t); 8 consecutive columns from 8 rows
-        const int pend = m0 + BM < g.vt_pitch ? m0 + BM : g.vt_pitch;
+        // key t of the tile sits in column xoff + vt_perm(t) (xoff is a multiple of 16);
+        // 8 consecutive columns from 8 rows
+        const int pend = m0 + BM < g.vt_pitch - g.xoff ? m0 + BM : g.vt_pitch - g.xoff;
         for (int idx = tid; idx < HALF * (BM / 8); idx += NW * 64) {
           const int cl = idx / (BM / 8), pg = idx - cl * (BM / 8);
           const int p = m0 + pg * 8;
@@ -345,7 +351,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(GemmArgs g) {
             const int r0 = vt_perm(p + 2 * e) - m0, r1 = vt_perm(p + 2 * e + 1) - m0;
             wv[e] = (uint32_t)f32_to_f16(T[r0 * TPF + cl]) | ((uint32_t)f32_to_f16(T[r1 * TPF + cl]) << 16);
           }
-          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.vt) + ((size_t)head * g.dh + d) * g.vt_pitch + p) =
+          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.vt) + ((size_t)head * g.dh + d) * g.vt_pitch + g.xoff + p) =
               u32x4{wv[0], wv[1], wv[2], wv[3]};
         }
       }
@@ -551,8 +557,9 @@ hipError_t launch_gemm(int epi, bool bf16, const GemmArgs& g, int n_cu, hipStrea
 
 // Workgroup = 128 queries of one head, 4 waves; wave w owns queries qb*128 + 32w .. +31,
 // one per lane column (lane % 32). Keys go by blocks of 64 through two LDS stages, loaded
-// straight from global memory: K rows from the ring (slot = key, the prefill starts at
-// position 0) and the matching 64 columns of the transposed V copy. Per key block:
+// straight from global memory: K rows of the chunk's key space (the ring itself for a
+// prefill from position 0) and the matching 64 columns of the transposed V copy. Query i
+// is key index koff + i. Per key block:
 //   S^T = K Q^T   (A = K rows from LDS, B = Q^T kept in registers): lane (q, half) holds
 //                 q's scores for 32 of the 64 keys, its partner lane (lane ^ 32) the other
 //                 32, so the row max and sum need one exchange;
@@ -592,7 +599,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a)
 #pragma unroll
   for (int ks = 0; ks < DH / 16; ++ks) qr[ks] = *reinterpret_cast<const bf16x8*>(Q + ks * 16 + 8 * hi);
 
-  const u32x4 krs = rsrc_words(static_cast<const uint16_t*>(a.k) + (size_t)h * a.C * DH, (uint32_t)((size_t)a.T * DH * 2));
+  const int ko = a.koff, nk = a.koff + a.T;
+  const u32x4 krs = rsrc_words(static_cast<const uint16_t*>(a.k) + (size_t)h * a.k_pitch * DH, (uint32_t)((size_t)nk * DH * 2));
   const u32x4 vrs = rsrc_words(static_cast<const uint16_t*>(a.vt) + (size_t)h * DH * a.vt_pitch,
                                (uint32_t)((size_t)DH * a.vt_pitch * 2));
   uint32_t koff[KL], voff[VL];
@@ -622,16 +630,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a)
     for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
 
   const int qlast = (qb + 1) * BQ < a.T ? (qb + 1) * BQ - 1 : a.T - 1;
-  int kfirst = qb * BQ - a.C + 1;
-  kfirst = kfirst > 0 ? kfirst / BKV * BKV : 0;
-  const int nkb = (qlast - kfirst) / BKV + 1;
+  int kfirst = ko + qb * BQ - a.C + 1;
+  kfirst = (kfirst > a.jlo ? kfirst : a.jlo) / BKV * BKV;
+  const int nkb = (ko + qlast - kfirst) / BKV + 1;
 
   issue(kfirst, 0);
   for (int kb = 0; kb < nkb; ++kb) {
     const int st = kb & 1, k0 = kfirst + kb * BKV;
     vm_wait_barrier<0>();
     if (kb + 1 < nkb) issue(k0 + BKV, st ^ 1);
-    if (k0 > qw0 + 31) continue;  // the whole block is in this wave's future
+    if (k0 > ko + qw0 + 31) continue;  // the whole block is in this wave's future
 
     // ---- S^T: s[kt][4*jj + ii] is key k0 + 32*kt + 8*jj + 4*hi + ii
     f32x16 s[2];
@@ -646,14 +654,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a)
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qr[ks], s[kt], 0, 0, 0);
       }
     }
-    const bool masked = k0 + BKV - 1 > qw0 || k0 < qw0 + 31 - a.C + 1 || k0 + BKV > a.T;
+    const bool masked = k0 + BKV - 1 > ko + qw0 || k0 < ko + qw0 + 31 - a.C + 1 || k0 + BKV > nk || k0 < a.jlo;
     if (masked) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = k0 + 32 * kt + 8 * (e >> 2) + 4 * hi + (e & 3);
-          const bool ok = key <= qi && qi - key < a.C && key < a.T;
+          const bool ok = key <= ko + qi && ko + qi - key < a.C && key < nk && key >= a.jlo;
           s[kt][e] = ok ? s[kt][e] : -INFINITY;
         }
     }
@@ -716,8 +724,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a)
 
 // ---------------------------------------------------------------- float32 attention
 
-// One workgroup of d_head threads per (query, head): online softmax over the visible keys,
-// one key at a time (scores reduced through LDS). For the small fp32 shapes only.
+// One workgroup of d_head threads per (query, head): online softmax over the visible keys
+// of the chunk's key space, one key at a time (scores reduced through LDS). For the small
+// fp32 shapes only.
 template <int DH>
 __global__ __launch_bounds__(DH) void k_attn_prefill_f32(AttnPrefillArgs a) {
   __shared__ float red[DH / 64 > 0 ? DH / 64 : 1];
@@ -727,9 +736,10 @@ __global__ __launch_bounds__(DH) void k_attn_prefill_f32(AttnPrefillArgs a) {
   const float* Vg = static_cast<const float*>(a.v);
   const float qd = Q[((size_t)h * a.T + t) * DH + d] * a.scale;
   float m = -INFINITY, l = 0.f, o = 0.f;
-  const int kfirst = t - a.C + 1 > 0 ? t - a.C + 1 : 0;
-  for (int key = kfirst; key <= t; ++key) {
-    const size_t off = ((size_t)h * a.C + (a.p0 + key) % a.C) * DH + d;
+  const int qk = a.koff + t;
+  const int kfirst = qk - a.C + 1 > a.jlo ? qk - a.C + 1 : a.jlo;
+  for (int key = kfirst; key <= qk; ++key) {
+    const size_t off = ((size_t)h * a.k_pitch + key) * DH + d;
     float part = wave_sum(qd * Kg[off]);
     if ((d & 63) == 0) red[d >> 6] = part;
     __syncthreads();
@@ -748,17 +758,88 @@ __global__ __launch_bounds__(DH) void k_attn_prefill_f32(AttnPrefillArgs a) {
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, bool bf16, int dh, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   if (bf16) {
-    // K rows are read from ring slots 0..T-1 and V from its transposed copy
-    if (a.p0 != 0 || !a.vt || a.T > a.C || a.vt_pitch < (a.T + 63) / 64 * 64) return hipErrorInvalidValue;
+    // K rows of the key space and V from its transposed copy; 64-key blocks of V^T
+    if (!a.vt || a.T > a.C || a.koff % 16 || a.jlo < 0 || a.jlo > a.koff || a.k_pitch < a.koff + a.T ||
+        a.vt_pitch < (a.koff + a.T + 63) / 64 * 64)
+      return hipErrorInvalidValue;
     const dim3 grid((a.T + 127) / 128 * a.H);
     if (dh == 128) hipLaunchKernelGGL(k_attn_prefill_bf16<128>, grid, dim3(256), 0, s, a);
     else if (dh == 64) hipLaunchKernelGGL(k_attn_prefill_bf16<64>, grid, dim3(256), 0, s, a);
     else return hipErrorInvalidValue;
   } else {
+    if (a.T > a.C || a.jlo < 0 || a.jlo > a.koff || a.k_pitch < a.koff + a.T || !a.v) return hipErrorInvalidValue;
     const dim3 grid(a.T, a.H);
     if (dh == 128) hipLaunchKernelGGL(k_attn_prefill_f32<128>, grid, dim3(128), 0, s, a);
     else if (dh == 64) hipLaunchKernelGGL(k_attn_prefill_f32<64>, grid, dim3(64), 0, s, a);
     else return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- chunk history
+
+// K rows (and float32 V rows): one thread per 16-byte chunk of a row.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_gather_rows(GatherArgs a, const void* ring, void* dst) {
+  constexpr int EPC = 16 / sizeof(T);
+  const int cpr = a.dh / EPC;
+  const long long n = (long long)a.H * a.jhi * cpr;
+  const long long i = (long long)blockIdx.x * kBlock + threadIdx.x;
+  if (i >= n) return;
+  const int c = (int)(i % cpr);
+  const long long hj = i / cpr;
+  const int j = (int)(hj % a.jhi), h = (int)(hj / a.jhi);
+  u32x4 v = u32x4{0u, 0u, 0u, 0u};
+  if (j >= a.jlo) {
+    const long long pos = a.q0 + j;   // >= 0 for j >= jlo
+    v = *reinterpret_cast<const u32x4*>(static_cast<const T*>(ring) + ((size_t)h * a.C + pos % a.C) * a.dh + c * EPC);
+  }
+  *reinterpret_cast<u32x4*>(static_cast<T*>(dst) + ((size_t)h * a.x_pitch + j) * a.dh + c * EPC) = v;
+}
+
+// bf16 path, V transposed to float16: one thread per (head, dim, group of 8 columns);
+// column c holds key vt_perm(c), so the group's keys lie in one aligned group of 16.
+__global__ __launch_bounds__(kBlock) void k_gather_vt(GatherArgs a) {
+  const long long n = (long long)a.H * a.dh * (a.jhi / 8);
+  const long long i = (long long)blockIdx.x * kBlock + threadIdx.x;
+  if (i >= n) return;
+  const int d = (int)(i % a.dh);
+  const long long r = i / a.dh;
+  const int g = (int)(r % (a.jhi / 8)), h = (int)(r / (a.jhi / 8));
+  const uint16_t* V = static_cast<const uint16_t*>(a.vring) + (size_t)h * a.C * a.dh + d;
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t half[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int key = vt_perm(g * 8 + 2 * e + x);
+      float f = 0.f;
+      if (key >= a.jlo) f = bf16_to_f32(V[(size_t)((a.q0 + key) % a.C) * a.dh]);
+      half[x] = f32_to_f16(f);
+    }
+    w[e] = half[0] | (half[1] << 16);
+  }
+  *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.vt) + ((size_t)h * a.dh + d) * a.vt_pitch + g * 8) =
+      u32x4{w[0], w[1], w[2], w[3]};
+}
+
+hipError_t launch_gather_history(const GatherArgs& a, bool bf16, hipStream_t s) {
+  if (a.jhi <= 0) return hipSuccess;
+  if (a.jhi % 16 || a.jlo < 0 || a.jlo > a.jhi || a.q0 + a.jlo < 0 || a.x_pitch < a.jhi || a.dh % 8)
+    return hipErrorInvalidValue;
+  const int epc = bf16 ? 8 : 4;
+  const long long nr = (long long)a.H * a.jhi * (a.dh / epc);
+  const dim3 gr((unsigned)((nr + kBlock - 1) / kBlock));
+  if (bf16) {
+    if (!a.vt || a.vt_pitch < a.jhi) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_gather_rows<uint16_t>, gr, dim3(kBlock), 0, s, a, a.kring, a.kx);
+    const long long nv = (long long)a.H * a.dh * (a.jhi / 8);
+    hipLaunchKernelGGL(k_gather_vt, dim3((unsigned)((nv + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, a);
+  } else {
+    if (!a.vx) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_gather_rows<float>, gr, dim3(kBlock), 0, s, a, a.kring, a.kx);
+    hipLaunchKernelGGL(k_gather_rows<float>, gr, dim3(kBlock), 0, s, a, a.vring, a.vx);
   }
   return hipGetLastError();
 }

@@ -23,7 +23,7 @@ EXPORTS = ["pp_temporal_create", "pp_temporal_destroy", "pp_kv_alloc", "pp_kv_fr
            "pp_kv_info", "pp_kv_load", "pp_kv_store", "pp_embed_sum", "pp_temporal_decode_step",
            "pp_temporal_prefill", "pp_depformer_create", "pp_depformer_destroy", "pp_depformer_step",
            "pp_last_error", "pp_temporal_set_graph", "pp_temporal_trace", "pp_temporal_trace_read",
-           "pp_depformer_set_graph", "pp_sample_top_k", "pp_generator_create", "pp_generator_destroy",
+           "pp_depformer_set_graph", "pp_kv_restore", "pp_sample_top_k", "pp_generator_create", "pp_generator_destroy",
            "pp_generator_step", "pp_generator_inspect"]
 
 
@@ -93,6 +93,7 @@ def load():
         "pp_kv_info": [VP, P(I64), P(ctypes.c_uint64)],
         "pp_kv_load": [VP, VP, I32, VP],
         "pp_kv_store": [VP, VP, VP],
+        "pp_kv_restore": [VP, VP, I64, VP],
         "pp_embed_sum": [VP, P(I32), I32, I32, VP, VP],
         "pp_temporal_decode_step": [VP, VP, P(I32), VP, VP, VP],
         "pp_temporal_prefill": [VP, VP, P(I32), I32, VP, VP],
@@ -260,6 +261,9 @@ class KV:
 
     def store(self, dst, stream=None):
         _check(load().pp_kv_store(self.handle, _ptr(dst), _stream(stream)))
+
+    def restore(self, src, position, stream=None):
+        _check(load().pp_kv_restore(self.handle, _ptr(src), int(position), _stream(stream)))
 
 
 # ----------------------------------------------------------------------------- depth
