@@ -32,6 +32,8 @@ def frame_bytes(cfg, n_keys):
     once, one new K/V slot, 17 embedding rows (bf16)."""
     D, F, L, H, dh = cfg["d_model"], cfg["d_ff"], cfg["n_layers"], cfg["n_heads"], cfg["d_head"]
     weights = L * (3 * D * D + D * D + 2 * F * D + D * F) * 2
+    if cfg.get("_no_kv"):
+        return weights
     kv_read = L * 2 * H * n_keys * dh * 2
     kv_write = L * 2 * D * 2
     emb = 17 * D * 2
@@ -269,6 +271,50 @@ def bench_chunk(model, kv, cfg, T, steps, warmup):
                         "32 blocks, bf16" % T}
 
 
+def bench_batched(model, cfg, batches, steps, warmup):
+    """Batched decode: B sessions at one position share every weight byte of the step;
+    each session's ring is full (3000 frames, zero-filled keys/values -- the timing does
+    not depend on their values), positions 3000+."""
+    import torch
+    out = []
+    C = cfg["context"]
+    for B in batches:
+        kv = model.kv_alloc(B)
+        buf = torch.zeros(kv.info()[1] // 2, dtype=torch.bfloat16, device="cuda")
+        kv.load(buf, C)
+        del buf
+        ids = synth_ids(cfg, warmup + steps, 14 + B)
+        h = torch.empty((B, cfg["d_model"]), device="cuda")
+        rows = [np.ascontiguousarray(np.broadcast_to(ids[i], (B, ids.shape[1]))) for i in range(warmup + steps)]
+        for i in range(warmup):
+            model.decode_step(kv, rows[i], h)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for i in range(warmup, warmup + steps):
+            model.decode_step(kv, rows[i], h)
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / steps
+        nb = frame_bytes(cfg, C) + (B - 1) * (frame_bytes(cfg, C) - frame_bytes(synth_cfg_no_weights(cfg), 0))
+        out.append({"B": B, "ms_per_step": round(ms, 4), "frames_per_s": round(B * 1000.0 / ms, 1),
+                    "step_bytes": nb, "achieved_GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)})
+        kv.close()
+        torch.cuda.empty_cache()
+    return {"workload": "batched decode, B sessions at one position, each ring full at 3000 frames, 32 blocks, "
+                        "bf16 weights, float16 activations into v_mfma_f32_16x16x32_f16", "steps": steps,
+            "points": out}
+
+
+def synth_cfg_no_weights(cfg):
+    """The decode-frame byte formula with the weights taken out: frame_bytes(cfg, C) minus
+    frame_bytes(this, 0) is one session's K/V read, K/V write and embedding rows."""
+    c = dict(cfg)
+    c["_no_kv"] = True
+    return c
+
+
 def synth_ids(cfg, n, seed):
     from personaplex_temporal_transformer_amd import synth
     return synth.stream_ids(cfg, n, seed)
@@ -387,6 +433,7 @@ def main():
     ap.add_argument("--prefill-T", type=int, default=3000, help="0: skip the prefill line")
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--chunk-T", type=int, default=256, help="0: skip the prefill-chunk line")
+    ap.add_argument("--batches", default="4,16,32", help="batched-decode sizes ('' to skip)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the run, copy 1 GiB device-to-device 3 times (counter calibration)")
     args = ap.parse_args()
@@ -401,7 +448,9 @@ def main():
     cfg = dict(synth.FULL_TEMPORAL)
     t0 = time.time()
     W = make_device_weights(cfg, 8)
-    model = pp.TemporalModel(cfg, W, "bf16", max_prefill_T=max(args.prefill_T, 0))
+    batches = [int(b) for b in args.batches.split(",") if b.strip()]
+    model = pp.TemporalModel(cfg, W, "bf16", max_prefill_T=max(args.prefill_T, 0),
+                             max_batch=max(batches + [1]))
     kv = model.kv_alloc()
     fill_ring(kv, cfg, 9)
     torch.cuda.synchronize()
@@ -479,6 +528,8 @@ def main():
         DW = make_depth_weights(dc, 5)
         dep = pp.Depformer(dc, DW, "bf16")
         out["generator"] = bench_generator(model, kv, dep, cfg, dc, max(10, args.steps // 2), 3)
+    if batches:
+        out["batched"] = bench_batched(model, cfg, batches, max(10, args.steps // 5), 3)
     if args.chunk_T > 0 and args.prefill_T >= args.chunk_T:
         out["prefill_chunk"] = bench_chunk(model, kv, cfg, args.chunk_T, 5, 1)
     if args.prefill_T > 0:

@@ -93,10 +93,13 @@ typedef struct {
 typedef struct pp_model pp_model;
 typedef struct pp_kv pp_kv;
 
-/* Create a temporal model on the current device. max_batch must be 1 in this version
- * (the pages' server runs B = 1). max_prefill_T (0..context) sizes the prefill
- * workspace. The library allocates its workspace here (hipMalloc); weights are not
- * copied. */
+/* Create a temporal model on the current device. max_batch (1..64) bounds the sessions a
+ * KV ring may hold for batched decode (B is the tensors' leading axis, audit section 3;
+ * the pages' server runs B = 1); max_batch > 1 needs bf16 weights, d_model % 16 == 0,
+ * d_ff % 32 == 0 and text-head rows % 16 == 0. max_prefill_T (0..context) sizes the
+ * prefill workspace. The library allocates its workspace here (hipMalloc); weights are
+ * not copied, except that max_batch > 1 keeps one copy of every matrix (and the text
+ * head) rearranged for the batched products (13.4 GB at full size), made here. */
 pp_status pp_temporal_create(const pp_temporal_config* cfg, const pp_temporal_weights* w,
                              int32_t max_batch, int32_t max_prefill_T, pp_model** out);
 pp_status pp_temporal_destroy(pp_model* m);
@@ -138,7 +141,10 @@ pp_status pp_embed_sum(const pp_model* m, const int32_t* ids_host, int32_t batch
  * ids_host [batch][n_audio+1]. h_out_dev [batch][d_model] float32 receives the final-norm
  * hidden state; text_logits_dev [batch][text_vocab-1] float32, if not NULL, the text-head
  * logits (needs a text_head weight). The position then advances by one; past `context`
- * frames the ring wraps and positions keep counting. */
+ * frames the ring wraps and positions keep counting. A ring with batch B > 1 holds B
+ * sessions at one shared position, each attending only to its own keys; their step
+ * streams every weight once for all B sessions (float16 activations into the matrix
+ * cores, float32 accumulation, residual stream and norms in float32). */
 pp_status pp_temporal_decode_step(pp_model* m, pp_kv* kv, const int32_t* ids_host,
                                   float* h_out_dev, float* text_logits_dev, void* stream);
 

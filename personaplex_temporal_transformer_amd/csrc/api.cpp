@@ -70,7 +70,11 @@ extern "C" pp_status pp_temporal_create(const pp_temporal_config* cfg, const pp_
   pp_status st = validate_temporal_config(cfg);
   if (st) return st;
   if (!w) return pp_fail(PP_E_ARG, "weights are NULL");
-  if (max_batch != 1) return pp_fail(PP_E_ARG, "max_batch must be 1 in this version");
+  if (max_batch < 1 || max_batch > kSgemmMaxBatch) return pp_fail(PP_E_ARG, "max_batch must be in [1, 64]");
+  if (max_batch > 1 && cfg->wdtype != PP_BF16)
+    return pp_fail(PP_E_ARG, "batched decode (max_batch > 1) needs bf16 weights");
+  if (max_batch > 1 && (cfg->d_model % 16 || cfg->d_ff % 32 || (cfg->text_vocab - 1) % 16))
+    return pp_fail(PP_E_ARG, "batched decode needs d_model % 16, d_ff % 32 and the text head rows % 16 == 0");
   if (max_prefill_T < 0 || max_prefill_T > cfg->context)
     return pp_fail(PP_E_CAPACITY, "max_prefill_T must be in [0, context]");
   int n_cu = 0;
@@ -120,6 +124,7 @@ extern "C" pp_status pp_temporal_create(const pp_temporal_config* cfg, const pp_
                      qkv_attn_supported(m->bf16, D, dh, H, m->S, n_cu);
   st = m->alloc_decode(D, F, H, dh);
   if (!st) st = m->alloc_prefill();
+  if (!st && max_batch > 1) st = m->pack_batched();
   if (st) {
     delete m;
     return st;
@@ -137,6 +142,11 @@ pp_status pp_model::alloc_decode(int D, int F, int H, int dh) {
   const size_t ost = take(sizeof(long long) * 4);
   const size_t ocnt = take(sizeof(unsigned long long) * (size_t)cfg.n_layers * H);
   const size_t orp = take(sizeof(float) * dh);
+  // batched decode: per-session residuals, queries, float16 activations, attention partials
+  const size_t nb = max_batch > 1 ? (size_t)max_batch : 0;
+  const size_t obx = take(sizeof(float) * nb * D), obq = take(sizeof(float) * nb * D);
+  const size_t obu = take(2 * nb * D), obo = take(2 * nb * D), obs = take(2 * nb * F);
+  const size_t obp = take(sizeof(float) * nb * H * S * dh), obm = take(sizeof(float) * nb * H * S * 2);
   if (hipMalloc(&ws, bytes) != hipSuccess) return pp_fail(PP_E_HIP, "hipMalloc of decode workspace failed");
   if (hipMemset(ws, 0, bytes) != hipSuccess) return pp_fail(PP_E_HIP, "hipMemset of decode workspace failed");
   char* b = static_cast<char*>(ws);
@@ -152,6 +162,49 @@ pp_status pp_model::alloc_decode(int D, int F, int H, int dh) {
     return pp_fail(PP_E_HIP, "hipHostMalloc of the fused-wait status word failed");
   *fuse_err = 0;
   rope = reinterpret_cast<float*>(b + orp);
+  if (nb) {
+    bx = reinterpret_cast<float*>(b + obx);
+    bq = reinterpret_cast<float*>(b + obq);
+    bu16 = reinterpret_cast<uint16_t*>(b + obu);
+    bo16 = reinterpret_cast<uint16_t*>(b + obo);
+    bs16 = reinterpret_cast<uint16_t*>(b + obs);
+    bpart_o = reinterpret_cast<float*>(b + obp);
+    bpart_ml = reinterpret_cast<float*>(b + obm);
+  }
+  return PP_OK;
+}
+
+// Batched decode reads every matrix from a copy in the skinny products' fragment order
+// (csrc/sgemm.hip): one allocation holding all layers' W_QKV, W_O, W_in, W_out and the
+// text head, packed once here.
+pp_status pp_model::pack_batched() {
+  const pp_temporal_config& c = cfg;
+  const size_t D = c.d_model, F = c.d_ff, L = c.n_layers, V = c.text_vocab - 1;
+  const size_t per_layer = (3 * D * D + D * D + 2 * F * D + D * F) * 2;
+  const size_t bytes = L * per_layer + (text_head ? V * D * 2 : 0);
+  if (hipMalloc(&pk_ws, bytes) != hipSuccess) return pp_fail(PP_E_HIP, "hipMalloc of the packed weights failed");
+  char* p = static_cast<char*>(pk_ws);
+  hipError_t e = hipSuccess;
+  for (size_t l = 0; l < L && e == hipSuccess; ++l) {
+    pk_qkv.push_back(p);
+    e = launch_sgemm_pack(w_qkv[l], p, (int)(3 * D), (int)D, 0, false, nullptr);
+    p += 3 * D * D * 2;
+    pk_o.push_back(p);
+    if (e == hipSuccess) e = launch_sgemm_pack(w_o[l], p, (int)D, (int)D, 0, false, nullptr);
+    p += D * D * 2;
+    pk_in.push_back(p);
+    if (e == hipSuccess) e = launch_sgemm_pack(w_in[l], p, (int)F, (int)D, (int)F, true, nullptr);
+    p += 2 * F * D * 2;
+    pk_out.push_back(p);
+    if (e == hipSuccess) e = launch_sgemm_pack(w_out[l], p, (int)D, (int)F, 0, false, nullptr);
+    p += D * F * 2;
+  }
+  if (e == hipSuccess && text_head) {
+    pk_head = p;
+    e = launch_sgemm_pack(text_head, p, (int)V, (int)D, 0, false, nullptr);
+  }
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("packing weights for batched decode: ") + hipGetErrorString(e));
   return PP_OK;
 }
 
@@ -159,6 +212,7 @@ pp_model::~pp_model() {
   for (hipEvent_t e : trace_ev) (void)hipEventDestroy(e);
   free_prefill();
   if (ws) (void)hipFree(ws);
+  if (pk_ws) (void)hipFree(pk_ws);
   if (ids_pinned) (void)hipHostFree(ids_pinned);
   if (fuse_err) (void)hipHostFree(fuse_err);
   if (ids_event) (void)hipEventDestroy(ids_event);
@@ -383,7 +437,7 @@ hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long 
 pp_status pp_model::run_layers(pp_kv* kv, hipStream_t s) {
   const bool traced = trace_layer >= 0;
   if (!use_graph || traced) {
-    hipError_t e = enqueue_layers(kv, s, traced, kv->pos, fused_seq);
+    hipError_t e = kv->B > 1 ? enqueue_layers_batched(kv, s, kv->pos) : enqueue_layers(kv, s, traced, kv->pos, fused_seq);
     if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("decode launch: ") + hipGetErrorString(e));
     return PP_OK;
   }
@@ -397,7 +451,7 @@ pp_status pp_model::run_layers(pp_kv* kv, hipStream_t s) {
       return pp_fail(PP_E_HIP, "hipStreamCreate for graph capture failed");
     hipError_t e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
     if (e == hipSuccess) {
-      hipError_t le = enqueue_layers(kv, cap, false, -1, -1);
+      hipError_t le = kv->B > 1 ? enqueue_layers_batched(kv, cap, -1) : enqueue_layers(kv, cap, false, -1, -1);
       e = hipStreamEndCapture(cap, &kv->graph);
       if (le != hipSuccess) e = le;
     }
@@ -429,6 +483,7 @@ pp_status pp_model::decode(pp_kv* kv, const int32_t* ids_host, const int32_t* id
     *fuse_err = 0;
     return pp_fail(PP_E_HIP, "an earlier decode step's cross-workgroup wait timed out (its output is invalid)");
   }
+  if (kv->B > 1) return decode_batched(kv, ids_host, h_out_dev, text_logits_dev, s);
   const pp_temporal_config& c = cfg;
   if (fuse_qkv_attn) ++fused_seq;
 
@@ -468,6 +523,80 @@ pp_status pp_model::decode(pp_kv* kv, const int32_t* ids_host, const int32_t* id
     } else {
       return pp_fail(PP_E_ARG, "text head rows must be even");
     }
+  }
+  if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("final norm / text head: ") + hipGetErrorString(e));
+  kv->pos += 1;
+  return PP_OK;
+}
+
+// ------------------------------------------------------------------ batched decode
+
+// B sessions at one position: every weight byte streamed once per step serves all of
+// them (skinny float16 matrix-core products, csrc/sgemm.hip); attention runs per session
+// over its own ring. pos_arg as in enqueue_layers.
+hipError_t pp_model::enqueue_layers_batched(pp_kv* kv, hipStream_t s, long long pos_arg) {
+  const pp_temporal_config& c = cfg;
+  const int D = c.d_model, F = c.d_ff, H = c.n_heads, dh = c.d_head, C = c.context, B = kv->B;
+  const size_t per_kv = (size_t)B * H * C * dh * 2;
+  const long long bstride = (long long)H * C * dh;
+  hipError_t e = hipSuccess;
+  for (int l = 0; l < c.n_layers && e == hipSuccess; ++l) {
+    char* kbase = static_cast<char*>(kv->ring) + (size_t)(2 * l) * per_kv;
+    char* vbase = kbase + per_kv;
+    if ((e = launch_rmsnorm_rows(bx, norm1[l], (float)c.eps, D, B, nullptr, bu16, s)) != hipSuccess) break;
+    SgemmArgs g{};
+    g.act = bu16; g.W = pk_qkv[l]; g.B = B; g.K = D; g.N = 3 * D;
+    g.q_out = bq; g.kc = kbase; g.vc = vbase; g.kv_bstride = bstride; g.rope = rope; g.state = state;
+    g.pos = pos_arg; g.D = D; g.dh = dh; g.C = C;
+    if ((e = launch_sgemm(SEPI_QKV, g, s)) != hipSuccess) break;
+    AttnDecodeArgs at{};
+    at.q = bq; at.k = kbase; at.v = vbase; at.state = state; at.pos = pos_arg; at.C = C; at.H = H; at.S = S;
+    at.scale = 1.0f / std::sqrt((float)dh); at.part_o = bpart_o; at.part_ml = bpart_ml; at.combine = 1;
+    at.batch = B; at.kv_bstride = bstride; at.out16 = bo16;
+    if ((e = launch_attn_decode(at, true, dh, s)) != hipSuccess) break;
+    SgemmArgs go{};
+    go.act = bo16; go.W = pk_o[l]; go.B = B; go.K = D; go.N = D; go.x = bx;
+    if ((e = launch_sgemm(SEPI_RESID, go, s)) != hipSuccess) break;
+    if ((e = launch_rmsnorm_rows(bx, norm2[l], (float)c.eps, D, B, nullptr, bu16, s)) != hipSuccess) break;
+    SgemmArgs gi{};
+    gi.act = bu16; gi.W = pk_in[l]; gi.B = B; gi.K = D; gi.N = F; gi.F = F; gi.s_out = bs16;
+    if ((e = launch_sgemm(SEPI_SWIGLU, gi, s)) != hipSuccess) break;
+    SgemmArgs gw{};
+    gw.act = bs16; gw.W = pk_out[l]; gw.B = B; gw.K = F; gw.N = D; gw.x = bx;
+    e = launch_sgemm(SEPI_RESID, gw, s);
+  }
+  return e;
+}
+
+pp_status pp_model::decode_batched(pp_kv* kv, const int32_t* ids_host, float* h_out_dev, float* text_logits_dev,
+                                   hipStream_t s) {
+  const pp_temporal_config& c = cfg;
+  const int B = kv->B, D = c.d_model;
+  if (!ids_host) return pp_fail(PP_E_ARG, "batched decode takes host IDs");
+  EmbedArgs a{};
+  embed_tables(a);
+  pp_status st = stage_ids(ids_host, (size_t)B * a.n_streams, s);
+  if (st) return st;
+  a.ids_dev = ids_dev;
+  a.out = bx;
+  a.rows = B;
+  a.state = state;
+  a.pos = kv->pos;
+  a.rope = rope;
+  a.dh = c.d_head;
+  for (int j = 0; j < c.d_head / 2; ++j) {
+    const double ang = (double)kv->pos * std::exp(-std::log(c.rope_theta) * (2.0 * j) / (double)c.d_head);
+    a.rope_cs[2 * j] = (float)std::cos(ang);
+    a.rope_cs[2 * j + 1] = (float)std::sin(ang);
+  }
+  hipError_t e = launch_embed(a, bf16, s);
+  if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("embed: ") + hipGetErrorString(e));
+  if ((st = run_layers(kv, s))) return st;
+  e = launch_rmsnorm_rows(bx, out_norm, (float)c.eps, D, B, h_out_dev, text_logits_dev ? bu16 : nullptr, s);
+  if (e == hipSuccess && text_logits_dev) {
+    SgemmArgs g{};
+    g.act = bu16; g.W = pk_head; g.B = B; g.K = D; g.N = c.text_vocab - 1; g.out = text_logits_dev;
+    e = launch_sgemm(SEPI_STORE, g, s);
   }
   if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("final norm / text head: ") + hipGetErrorString(e));
   kv->pos += 1;

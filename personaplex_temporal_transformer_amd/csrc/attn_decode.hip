@@ -26,6 +26,14 @@ constexpr int kMaxSplits = 64;
 // Block (s, h) of the split-K decode attention (see attn_body.h).
 template <typename KT, int DH, int NB, int NT>
 __global__ __launch_bounds__(NT) void k_attn_decode(AttnDecodeArgs a) {
+  if (blockIdx.z > 0) {  // session b of a batched step
+    const size_t b = blockIdx.z;
+    a.q += b * a.H * DH;
+    a.k = static_cast<const KT*>(a.k) + b * a.kv_bstride;
+    a.v = static_cast<const KT*>(a.v) + b * a.kv_bstride;
+    a.part_o += b * a.H * a.S * DH;
+    a.part_ml += b * a.H * a.S * 2;
+  }
   attn_body<KT, DH, NB, NT, false>(a, blockIdx.x, blockIdx.y, AttnFuse{});
 }
 
@@ -36,8 +44,11 @@ template <int DH>
 __global__ __launch_bounds__(kBlock) void k_attn_combine(AttnDecodeArgs a) {
   __shared__ float po[kMaxSplits * DH], pml[kMaxSplits * 2];
   const int h = blockIdx.x, t = threadIdx.x;
-  for (int i = t; i < a.S * DH; i += kBlock) po[i] = a.part_o[(size_t)h * a.S * DH + i];
-  for (int i = t; i < a.S * 2; i += kBlock) pml[i] = a.part_ml[(size_t)h * a.S * 2 + i];
+  const size_t b = blockIdx.y;   // session (batched step)
+  const float* part_o = a.part_o + b * a.H * a.S * DH;
+  const float* part_ml = a.part_ml + b * a.H * a.S * 2;
+  for (int i = t; i < a.S * DH; i += kBlock) po[i] = part_o[(size_t)h * a.S * DH + i];
+  for (int i = t; i < a.S * 2; i += kBlock) pml[i] = part_ml[(size_t)h * a.S * 2 + i];
   __syncthreads();
   if (t >= DH) return;
   float M = -INFINITY;
@@ -50,11 +61,15 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(AttnDecodeArgs a) {
     L += w * pml[2 * i + 1];
     o += w * po[i * DH + t];
   }
-  a.out[h * DH + t] = o / L;
+  const size_t oi = b * a.H * DH + h * DH + t;
+  if (a.out16) a.out16[oi] = f32_to_f16(o / L);
+  else a.out[oi] = o / L;
 }
 
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, bool bf16, int dh, hipStream_t s) {
-  const dim3 grid(a.S, a.H);
+  const int nb = a.batch > 1 ? a.batch : 1;
+  if (a.S < 1 || a.S > kMaxSplits) return hipErrorInvalidValue;
+  const dim3 grid(a.S, a.H, nb);
   static const int nb_env = [] {
     const char* v = getenv("PP_ATTN_NB");
     return v ? atoi(v) : 6;
@@ -74,8 +89,8 @@ hipError_t launch_attn_decode(const AttnDecodeArgs& a, bool bf16, int dh, hipStr
   else return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.combine) return e;
-  if (dh == 128) hipLaunchKernelGGL((k_attn_combine<128>), dim3(a.H), dim3(kBlock), 0, s, a);
-  else hipLaunchKernelGGL((k_attn_combine<64>), dim3(a.H), dim3(kBlock), 0, s, a);
+  if (dh == 128) hipLaunchKernelGGL((k_attn_combine<128>), dim3(a.H, nb), dim3(kBlock), 0, s, a);
+  else hipLaunchKernelGGL((k_attn_combine<64>), dim3(a.H, nb), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 

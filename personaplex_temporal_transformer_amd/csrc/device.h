@@ -8,6 +8,22 @@ namespace pp {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// 8 bfloat16 values (one 16-byte chunk) as float16: each bfloat16 is the top half of a
+// float32; the packed conversion is exact for values inside float16's normal range
+// (bfloat16 has the shorter significand).
+__device__ __forceinline__ f16x8 bf16x8_to_f16(u32x4 w) {
+  f16x8 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const auto p = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w[k] << 16), __uint_as_float(w[k] & 0xffff0000u));
+    r[2 * k] = (_Float16)p[0];
+    r[2 * k + 1] = (_Float16)p[1];
+  }
+  return r;
+}
 
 constexpr int kWave = 64;
 

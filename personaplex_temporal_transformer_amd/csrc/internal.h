@@ -95,6 +95,13 @@ struct AttnDecodeArgs {
   float* part_ml;       // [H][S][2] partial (max in base-2 units, sum)
   float* out;           // [H * dh], written by the combine kernel
   int combine;          // 1: launch the combine kernel; 0: the consumer merges
+  // several sessions at one position (batched decode): session b's query, ring and
+  // partials follow at b * H*dh floats, b * kv_bstride elements and b * H*S*(dh | 2)
+  // floats; the combine kernel writes session b's output at b * H*dh (float16 to out16
+  // when it is set)
+  int batch;
+  long long kv_bstride;
+  uint16_t* out16;
 };
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, bool bf16, int dh, hipStream_t s);
 
@@ -274,3 +281,37 @@ hipError_t launch_gen_finish(const GenFinishArgs& a, hipStream_t s);
 hipError_t launch_sample_rows(const float* logits, int rows, int n, float temperature, int top_k,
                               const double* u, int32_t* out, hipStream_t s);
 }  // namespace pp
+
+namespace pp {
+// ---------------------------------------------------------------- batched decode (skinny products)
+enum SgemmEpi { SEPI_STORE = 0, SEPI_RESID = 1, SEPI_QKV = 2, SEPI_SWIGLU = 3 };
+
+// out[b][n] = sum_k act[b][k] W[n][k] for the B sessions of a batched decode step:
+// float16 activations, bf16 weights widened to float16, float32 accumulation.
+struct SgemmArgs {
+  const uint16_t* act;   // [B][K] float16 (rows >= B are not read)
+  const void* W;         // bfloat16 weights packed by launch_sgemm_pack (rows = N, or 2F g|z rows)
+  int B, K, N;           // N = output columns (SEPI_SWIGLU: F)
+  float* out;            // SEPI_STORE: [B][N] float32
+  float* x;              // SEPI_RESID: [B][N] float32, += product
+  uint16_t* s_out;       // SEPI_SWIGLU: [B][F] float16 SiLU(g) * z
+  int F;
+  // SEPI_QKV: columns Q | K | V of width D; RoPE on Q and K with rope[dh] (cos, sin pairs of
+  // this position); Q -> q_out [B][D] float32; K, V -> slot pos mod C of session b's ring
+  // (kc / vc + b * kv_bstride elements, [H][C][dh] bfloat16)
+  float* q_out;
+  void* kc;
+  void* vc;
+  long long kv_bstride;
+  const float* rope;
+  const long long* state;
+  long long pos;         // >= 0: the position; -1: read state[0]
+  int D, dh, C;
+};
+constexpr int kSgemmMaxBatch = 64;
+hipError_t launch_sgemm(int epi, const SgemmArgs& a, hipStream_t s);
+// Copy of a row-major [rows][K] bf16 matrix in the fragment order the skinny products
+// read (same byte count); rows_out = N (or F for the SiLU-gated W_in with 2F rows).
+hipError_t launch_sgemm_pack(const void* W, void* packed, int rows_out, int K, int F, bool swiglu, hipStream_t s);
+}  // namespace pp
+

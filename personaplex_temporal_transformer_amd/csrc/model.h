@@ -43,6 +43,19 @@ struct pp_model {
   long long fused_seq = 0;     // frames decoded with the fused launch
   int* fuse_err = nullptr;     // pinned host word: a fused wait timed out
   float* rope = nullptr;       // [dh] cos/sin table of that position
+  // batched decode (max_batch > 1): residuals [B][D], queries [B][D] float32; float16
+  // normalised rows [B][D], attention outputs [B][D], SiLU products [B][F]; partials
+  float* bx = nullptr;
+  float* bq = nullptr;
+  uint16_t* bu16 = nullptr;
+  uint16_t* bo16 = nullptr;
+  uint16_t* bs16 = nullptr;
+  float* bpart_o = nullptr;
+  float* bpart_ml = nullptr;
+  // batched decode: the matrices in the skinny products' fragment order (one allocation)
+  void* pk_ws = nullptr;
+  std::vector<const void*> pk_qkv, pk_o, pk_in, pk_out;
+  const void* pk_head = nullptr;
   int S = 16;                // attention splits per head
   int gemv_blocks = 256;     // workgroups per GEMV launch (one per CU)
   int wout_rb = 1;           // rows per group of the W_out GEMV
@@ -83,6 +96,10 @@ struct pp_model {
   pp_status run_layers(pp_kv* kv, hipStream_t s);
   pp_status decode(pp_kv* kv, const int32_t* ids_host, const int32_t* ids_dev, float* h_out_dev,
                    float* text_logits_dev, hipStream_t s);
+  hipError_t enqueue_layers_batched(pp_kv* kv, hipStream_t s, long long pos_arg);
+  pp_status pack_batched();
+  pp_status decode_batched(pp_kv* kv, const int32_t* ids_host, float* h_out_dev, float* text_logits_dev,
+                           hipStream_t s);
 };
 
 struct pp_kv {

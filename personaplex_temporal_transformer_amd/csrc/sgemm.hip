@@ -1,0 +1,185 @@
+// Skinny matrix products for batched decode: B sessions (B <= 64) at one position share
+// every weight byte the step streams ("PersonaPlex native LM audit", section 3: the
+// per-block linears of the temporal step, with the batch as the tensors' leading axis).
+//
+// out[b][n] = sum_k act[b][k] W[n][k]. A workgroup owns 16 output columns (for SiLU-gated
+// rows: 8 g rows and their 8 z rows) over all of K; its 8 waves split K into equal runs of
+// 32-element steps, taken in groups of U steps with the next group's loads in flight
+// while the current one is multiplied. Per step a lane takes 8 weights of one row (bf16,
+// widened to float16 in registers) and 8 activations of one session per 16-session tile,
+// and issues one v_mfma_f32_16x16x32_f16 per tile: A = activations (row = session
+// lane % 16, k = 8 * (lane / 16) + e), B = weights (column = lane % 16, same k), so the
+// lane holds D[session 4 * (lane / 16) + i][column lane % 16]. The weights are read from a
+// copy packed once per model in exactly that fragment order -- tile, 32-element step,
+// lane, 8 elements -- so each load instruction of a wave reads 1 KB of contiguous memory
+// (the row-major matrix would give 16 rows x 64 bytes per instruction). The waves' partial tiles
+// are summed in LDS in wave order (fixed order: reproducible), then the epilogue applies
+// RoPE / ring append, the residual add, the SiLU product or a plain store.
+#include "device.h"
+#include "internal.h"
+
+namespace pp {
+
+constexpr int kSgWaves = 8;
+
+template <int EPI, int NBT>
+__global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
+  __shared__ float red[kSgWaves][NBT][64][4];
+  __shared__ float tile[NBT * 16][17];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int nsteps = a.K / 32;
+  // packed fragments of this workgroup's tile: [step][lane][8]
+  const uint16_t* Wr = static_cast<const uint16_t*>(a.W) + ((size_t)blockIdx.x * nsteps * 64 + lane) * 8;
+  const int s0 = w * nsteps / kSgWaves, s1 = (w + 1) * nsteps / kSgWaves;
+  // this lane's session row in each tile (rows past B contribute zeros)
+  const uint16_t* Ar[NBT];
+  bool live[NBT];
+#pragma unroll
+  for (int t = 0; t < NBT; ++t) {
+    const int b = t * 16 + n;
+    live[t] = b < a.B;
+    Ar[t] = a.act + (size_t)(live[t] ? b : 0) * a.K + 8 * g;
+  }
+  f32x4 acc[NBT];
+#pragma unroll
+  for (int t = 0; t < NBT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // groups of U steps, the next group's loads issued before the current group is
+  // multiplied (loads complete in issue order, so the wait for a group is exact)
+  constexpr int U = NBT == 1 ? 8 : (NBT == 2 ? 4 : 2);
+  u32x4 wv[2][U], av[2][U][NBT];
+  auto load_group = [&](int buf, int st0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      wv[buf][u] = load_stream(Wr + (size_t)(st0 + u) * 512);
+#pragma unroll
+      for (int t = 0; t < NBT; ++t)
+        av[buf][u][t] = live[t] ? *reinterpret_cast<const u32x4*>(Ar[t] + (size_t)(st0 + u) * 32) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto mul_group = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const f16x8 wf = bf16x8_to_f16(wv[buf][u]);
+#pragma unroll
+      for (int t = 0; t < NBT; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av[buf][u][t]), wf, acc[t], 0, 0, 0);
+    }
+  };
+  const int ng = (s1 - s0) / U;
+  if (ng > 0) load_group(0, s0);
+  for (int gi = 0; gi < ng; gi += 2) {
+    if (gi + 1 < ng) load_group(1, s0 + (gi + 1) * U);
+    mul_group(0);
+    if (gi + 1 < ng) {
+      if (gi + 2 < ng) load_group(0, s0 + (gi + 2) * U);
+      mul_group(1);
+    }
+  }
+  for (int st = s0 + ng * U; st < s1; ++st) {
+    const f16x8 wf = bf16x8_to_f16(load_stream(Wr + (size_t)st * 512));
+#pragma unroll
+    for (int t = 0; t < NBT; ++t) {
+      const u32x4 a1 = live[t] ? *reinterpret_cast<const u32x4*>(Ar[t] + (size_t)st * 32) : u32x4{0u, 0u, 0u, 0u};
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a1), wf, acc[t], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NBT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[w][t][lane][i] = acc[t][i];
+  __syncthreads();
+  for (int o = tid; o < NBT * 256; o += kSgWaves * 64) {
+    const int t = o >> 8, l = (o >> 2) & 63, i = o & 3;
+    float v = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kSgWaves; ++ww) v += red[ww][t][l][i];
+    tile[t * 16 + 4 * (l >> 4) + i][l & 15] = v;
+  }
+  __syncthreads();
+
+  // epilogue: thread -> (session b, column c)
+  for (int o = tid; o < NBT * 256; o += kSgWaves * 64) {
+    const int b = o >> 4, c = o & 15;
+    if (b >= a.B) continue;
+    const float v = tile[b][c];
+    if constexpr (EPI == SEPI_STORE) {
+      a.out[(size_t)b * a.N + blockIdx.x * 16 + c] = v;
+    } else if constexpr (EPI == SEPI_RESID) {
+      a.x[(size_t)b * a.N + blockIdx.x * 16 + c] += v;
+    } else if constexpr (EPI == SEPI_SWIGLU) {
+      if (c < 8) a.s_out[(size_t)b * a.F + blockIdx.x * 8 + c] = f32_to_f16(silu(v) * tile[b][c + 8]);
+    } else {
+      const int col = blockIdx.x * 16 + c;
+      const int sec = col / a.D, wcol = col - sec * a.D;
+      const int head = wcol / a.dh, d = wcol - head * a.dh;
+      float y = v;
+      if (sec < 2) {
+        const float partner = tile[b][c ^ 1];
+        const float cs = a.rope[d & ~1], sn = a.rope[d | 1];
+        y = (d & 1) ? partner * sn + v * cs : v * cs - partner * sn;
+      }
+      if (sec == 0) {
+        a.q_out[(size_t)b * a.D + wcol] = y;
+      } else {
+        const long long pos = a.pos >= 0 ? a.pos : a.state[0];
+        uint16_t* ring = static_cast<uint16_t*>(sec == 1 ? a.kc : a.vc) + (size_t)b * a.kv_bstride;
+        ring[((size_t)head * a.C + (size_t)(pos % a.C)) * a.dh + d] = f32_to_bf16(y);
+      }
+    }
+  }
+}
+
+// Packs W [rows][K] (row-major bf16) into the fragment order above: tile t (16 output
+// columns; SiLU-gated: g rows 8t.. and z rows F+8t..), step s, lane l, element e holds
+// W[row(t, l % 16)][32 s + 8 (l / 16) + e]. One thread per 16-byte fragment.
+__global__ __launch_bounds__(kBlock) void k_sgemm_pack(const uint16_t* __restrict__ W, uint16_t* __restrict__ P,
+                                                       int tiles, int K, int F, int swiglu) {
+  const int nsteps = K / 32;
+  const long long i = (long long)blockIdx.x * kBlock + threadIdx.x;
+  if (i >= (long long)tiles * nsteps * 64) return;
+  const int l = (int)(i % 64);
+  const long long ts = i / 64;
+  const int st = (int)(ts % nsteps), t = (int)(ts / nsteps);
+  const int n = l & 15, g = l >> 4;
+  const int row = swiglu ? (n < 8 ? t * 8 + n : F + t * 8 + (n - 8)) : t * 16 + n;
+  *reinterpret_cast<u32x4*>(P + (size_t)i * 8) = *reinterpret_cast<const u32x4*>(W + (size_t)row * K + st * 32 + 8 * g);
+}
+
+hipError_t launch_sgemm_pack(const void* W, void* packed, int rows_out, int K, int F, bool swiglu, hipStream_t s) {
+  if (K % 32 || (swiglu ? F % 8 : rows_out % 16)) return hipErrorInvalidValue;
+  const int tiles = swiglu ? F / 8 : rows_out / 16;
+  const long long n = (long long)tiles * (K / 32) * 64;
+  hipLaunchKernelGGL(k_sgemm_pack, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, s,
+                     static_cast<const uint16_t*>(W), static_cast<uint16_t*>(packed), tiles, K, F, swiglu ? 1 : 0);
+  return hipGetLastError();
+}
+
+template <int EPI>
+static hipError_t launch_epi(const SgemmArgs& a, hipStream_t s) {
+  const int tiles = EPI == SEPI_SWIGLU ? a.F / 8 : a.N / 16;
+  const dim3 grid(tiles), block(kSgWaves * 64);
+  const int nbt = (a.B + 15) / 16;
+  if (nbt == 1) hipLaunchKernelGGL((k_sgemm<EPI, 1>), grid, block, 0, s, a);
+  else if (nbt == 2) hipLaunchKernelGGL((k_sgemm<EPI, 2>), grid, block, 0, s, a);
+  else if (nbt == 3) hipLaunchKernelGGL((k_sgemm<EPI, 3>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((k_sgemm<EPI, 4>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sgemm(int epi, const SgemmArgs& a, hipStream_t s) {
+  if (a.B < 1 || a.B > kSgemmMaxBatch || a.K % 32 || a.K <= 0) return hipErrorInvalidValue;
+  if (epi == SEPI_SWIGLU ? (a.F <= 0 || a.F % 8) : (a.N <= 0 || a.N % 16)) return hipErrorInvalidValue;
+  if (epi == SEPI_QKV && (a.N != 3 * a.D || a.dh % 2 || a.D % a.dh)) return hipErrorInvalidValue;
+  switch (epi) {
+    case SEPI_STORE: return launch_epi<SEPI_STORE>(a, s);
+    case SEPI_RESID: return launch_epi<SEPI_RESID>(a, s);
+    case SEPI_QKV: return launch_epi<SEPI_QKV>(a, s);
+    case SEPI_SWIGLU: return launch_epi<SEPI_SWIGLU>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pp

@@ -158,7 +158,7 @@ class TemporalModel:
     text_linear.weight). `weights` maps those names to CUDA tensors (bf16 or fp32
     matrices, fp32 norm scales); references are kept for the model's lifetime."""
 
-    def __init__(self, cfg, weights, wdtype, max_prefill_T=0):
+    def __init__(self, cfg, weights, wdtype, max_prefill_T=0, max_batch=1):
         lib = load()
         self.cfg = dict(cfg)
         self._w = weights
@@ -182,7 +182,8 @@ class TemporalModel:
                             weights["out_norm.alpha"].data_ptr(),
                             weights["text_linear.weight"].data_ptr() if "text_linear.weight" in weights else None)
         h = ctypes.c_void_p()
-        _check(lib.pp_temporal_create(ctypes.byref(c), ctypes.byref(w), 1, int(max_prefill_T), ctypes.byref(h)))
+        _check(lib.pp_temporal_create(ctypes.byref(c), ctypes.byref(w), int(max_batch), int(max_prefill_T),
+                                      ctypes.byref(h)))
         self.handle = h
 
     def close(self):

@@ -222,3 +222,37 @@ def test_full_prefill_chunk_after_full_ring():
     print("full chunk at 3000: rows vs decode %s, ring %s" % (["%.3g" % e for e in errs], ["%.3g" % e for e in ring_errs]))
     assert max(errs) <= 2 * BF16_TOL and max(ring_errs) <= 2 * BF16_TOL
     assert np.array_equal(rc[:, :, :, :, 256:], rd[:, :, :, :, 256:])   # untouched slots agree bit for bit
+
+
+def test_full_batched_decode_ctx3000_matches_single_sessions():
+    """4 sessions decoded together (every weight byte shared, float16 activations into the
+    matrix cores) against the same 4 sessions decoded one at a time, rings full at 3000
+    random frames, 2 frames at positions 3000 and 3001 (keys wrap): 2 x 2e-2."""
+    import torch
+    cfg = dict(synth.FULL_TEMPORAL)
+    C, L, D, H, dh = cfg["context"], cfg["n_layers"], cfg["d_model"], cfg["n_heads"], cfg["d_head"]
+    W = synth.temporal_weights(cfg, 70, "bf16", with_text_head=False, shared_layer=True)
+    require_gpu()
+    B = 4
+    model = pp.TemporalModel(cfg, to_device(W), "bf16", max_batch=B)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(71)
+    frames = torch.randn((L, 2, B, H, C, dh), generator=g, device="cuda").to(torch.bfloat16)
+    ids = synth.stream_ids(cfg, 2, 72, batch=B)
+    kv = model.kv_alloc(B)
+    kv.load(frames, C)
+    hb = torch.empty((2, B, D), device="cuda")
+    for t in range(2):
+        model.decode_step(kv, ids[:, t], hb[t])
+    errs = []
+    for b in range(B):
+        kv1 = model.kv_alloc(1)
+        kv1.load(frames[:, :, b:b + 1].contiguous(), C)
+        h1 = torch.empty((2, D), device="cuda")
+        for t in range(2):
+            model.decode_step(kv1, ids[b, t], h1[t])
+        torch.cuda.synchronize()
+        errs.append(norm_max_err(hb[:, b].cpu().numpy(), h1.cpu().numpy()))
+        kv1.close()
+    print("full batched decode B=4 vs single sessions: errs %s" % ["%.3g" % e for e in errs])
+    assert max(errs) <= 2 * BF16_TOL
