@@ -15,6 +15,8 @@
 // (the row-major matrix would give 16 rows x 64 bytes per instruction). The waves' partial tiles
 // are summed in LDS in wave order (fixed order: reproducible), then the epilogue applies
 // RoPE / ring append, the residual add, the SiLU product or a plain store.
+#include <stdlib.h>
+
 #include "device.h"
 #include "internal.h"
 
@@ -22,18 +24,20 @@ namespace pp {
 
 constexpr int kSgWaves = 8;
 
-template <int EPI, int NBT>
+template <int EPI, int NBT, int NT>
 __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
-  __shared__ float red[kSgWaves][NBT][64][4];
-  __shared__ float tile[NBT * 16][17];
+  __shared__ float red[kSgWaves][NT * NBT][64][4];
+  __shared__ float tile[NBT * 16][NT * 16 + 1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int nsteps = a.K / 32;
-  // packed fragments of this workgroup's tile: [step][lane][8]
-  const uint16_t* Wr = static_cast<const uint16_t*>(a.W) + ((size_t)blockIdx.x * nsteps * 64 + lane) * 8;
+  const int tile0 = blockIdx.x * NT;
+  // packed fragments of this workgroup's tiles: [tile][step][lane][8]
+  const uint16_t* Wr = static_cast<const uint16_t*>(a.W) + ((size_t)tile0 * nsteps * 64 + lane) * 8;
+  const size_t tstride = (size_t)nsteps * 512;
   const int s0 = w * nsteps / kSgWaves, s1 = (w + 1) * nsteps / kSgWaves;
-  // this lane's session row in each tile (rows past B contribute zeros)
+  // this lane's session row in each session tile (rows past B contribute zeros)
   const uint16_t* Ar[NBT];
   bool live[NBT];
 #pragma unroll
@@ -42,18 +46,21 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
     live[t] = b < a.B;
     Ar[t] = a.act + (size_t)(live[t] ? b : 0) * a.K + 8 * g;
   }
-  f32x4 acc[NBT];
+  f32x4 acc[NT][NBT];
 #pragma unroll
-  for (int t = 0; t < NBT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int t = 0; t < NBT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // groups of U steps, the next group's loads issued before the current group is
   // multiplied (loads complete in issue order, so the wait for a group is exact)
-  constexpr int U = NBT == 1 ? 8 : (NBT == 2 ? 4 : 2);
-  u32x4 wv[2][U], av[2][U][NBT];
+  constexpr int U = NT * NBT == 1 ? 8 : (NT * NBT == 2 ? 4 : 2);
+  u32x4 wv[2][U][NT], av[2][U][NBT];
   auto load_group = [&](int buf, int st0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      wv[buf][u] = load_stream(Wr + (size_t)(st0 + u) * 512);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) wv[buf][u][j] = load_stream(Wr + j * tstride + (size_t)(st0 + u) * 512);
 #pragma unroll
       for (int t = 0; t < NBT; ++t)
         av[buf][u][t] = live[t] ? *reinterpret_cast<const u32x4*>(Ar[t] + (size_t)(st0 + u) * 32) : u32x4{0u, 0u, 0u, 0u};
@@ -61,12 +68,14 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
   };
   auto mul_group = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const f16x8 wf = bf16x8_to_f16(wv[buf][u]);
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int t = 0; t < NBT; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av[buf][u][t]), wf, acc[t], 0, 0, 0);
-    }
+      for (int j = 0; j < NT; ++j) {
+        const f16x8 wf = bf16x8_to_f16(wv[buf][u][j]);
+#pragma unroll
+        for (int t = 0; t < NBT; ++t)
+          acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av[buf][u][t]), wf, acc[j][t], 0, 0, 0);
+      }
   };
   const int ng = (s1 - s0) / U;
   if (ng > 0) load_group(0, s0);
@@ -79,45 +88,55 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
     }
   }
   for (int st = s0 + ng * U; st < s1; ++st) {
-    const f16x8 wf = bf16x8_to_f16(load_stream(Wr + (size_t)st * 512));
+    u32x4 a1[NBT];
 #pragma unroll
-    for (int t = 0; t < NBT; ++t) {
-      const u32x4 a1 = live[t] ? *reinterpret_cast<const u32x4*>(Ar[t] + (size_t)st * 32) : u32x4{0u, 0u, 0u, 0u};
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a1), wf, acc[t], 0, 0, 0);
+    for (int t = 0; t < NBT; ++t)
+      a1[t] = live[t] ? *reinterpret_cast<const u32x4*>(Ar[t] + (size_t)st * 32) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const f16x8 wf = bf16x8_to_f16(load_stream(Wr + j * tstride + (size_t)st * 512));
+#pragma unroll
+      for (int t = 0; t < NBT; ++t)
+        acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a1[t]), wf, acc[j][t], 0, 0, 0);
     }
   }
 #pragma unroll
-  for (int t = 0; t < NBT; ++t)
+  for (int j = 0; j < NT; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[w][t][lane][i] = acc[t][i];
+    for (int t = 0; t < NBT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[w][j * NBT + t][lane][i] = acc[j][t][i];
   __syncthreads();
-  for (int o = tid; o < NBT * 256; o += kSgWaves * 64) {
-    const int t = o >> 8, l = (o >> 2) & 63, i = o & 3;
+  for (int o = tid; o < NT * NBT * 256; o += kSgWaves * 64) {
+    const int jt = o >> 8, l = (o >> 2) & 63, i = o & 3;
+    const int j = jt / NBT, t = jt - j * NBT;
     float v = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kSgWaves; ++ww) v += red[ww][t][l][i];
-    tile[t * 16 + 4 * (l >> 4) + i][l & 15] = v;
+    for (int ww = 0; ww < kSgWaves; ++ww) v += red[ww][jt][l][i];
+    tile[t * 16 + 4 * (l >> 4) + i][j * 16 + (l & 15)] = v;
   }
   __syncthreads();
 
-  // epilogue: thread -> (session b, column c)
-  for (int o = tid; o < NBT * 256; o += kSgWaves * 64) {
-    const int b = o >> 4, c = o & 15;
+  // epilogue: thread -> (session b, column c of the workgroup's NT * 16)
+  for (int o = tid; o < NBT * 16 * NT * 16; o += kSgWaves * 64) {
+    const int b = o / (NT * 16), cc = o - b * (NT * 16);
     if (b >= a.B) continue;
-    const float v = tile[b][c];
+    const int j = cc >> 4, c = cc & 15;
+    const int tl = tile0 + j;     // this column's 16-column tile
+    const float v = tile[b][cc];
     if constexpr (EPI == SEPI_STORE) {
-      a.out[(size_t)b * a.N + blockIdx.x * 16 + c] = v;
+      a.out[(size_t)b * a.N + tl * 16 + c] = v;
     } else if constexpr (EPI == SEPI_RESID) {
-      a.x[(size_t)b * a.N + blockIdx.x * 16 + c] += v;
+      a.x[(size_t)b * a.N + tl * 16 + c] += v;
     } else if constexpr (EPI == SEPI_SWIGLU) {
-      if (c < 8) a.s_out[(size_t)b * a.F + blockIdx.x * 8 + c] = f32_to_f16(silu(v) * tile[b][c + 8]);
+      if (c < 8) a.s_out[(size_t)b * a.F + tl * 8 + c] = f32_to_f16(silu(v) * tile[b][cc + 8]);
     } else {
-      const int col = blockIdx.x * 16 + c;
+      const int col = tl * 16 + c;
       const int sec = col / a.D, wcol = col - sec * a.D;
       const int head = wcol / a.dh, d = wcol - head * a.dh;
       float y = v;
       if (sec < 2) {
-        const float partner = tile[b][c ^ 1];
+        const float partner = tile[b][cc ^ 1];
         const float cs = a.rope[d & ~1], sn = a.rope[d | 1];
         y = (d & 1) ? partner * sn + v * cs : v * cs - partner * sn;
       }
@@ -160,12 +179,26 @@ hipError_t launch_sgemm_pack(const void* W, void* packed, int rows_out, int K, i
 template <int EPI>
 static hipError_t launch_epi(const SgemmArgs& a, hipStream_t s) {
   const int tiles = EPI == SEPI_SWIGLU ? a.F / 8 : a.N / 16;
-  const dim3 grid(tiles), block(kSgWaves * 64);
+  const dim3 block(kSgWaves * 64);
   const int nbt = (a.B + 15) / 16;
-  if (nbt == 1) hipLaunchKernelGGL((k_sgemm<EPI, 1>), grid, block, 0, s, a);
-  else if (nbt == 2) hipLaunchKernelGGL((k_sgemm<EPI, 2>), grid, block, 0, s, a);
-  else if (nbt == 3) hipLaunchKernelGGL((k_sgemm<EPI, 3>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((k_sgemm<EPI, 4>), grid, block, 0, s, a);
+  // two column tiles per workgroup (each activation fragment feeds two products) when
+  // there are enough tiles to keep every CU busy
+  static const int nt_env = [] {
+    const char* v = getenv("PP_SGEMM_NT");
+    return v ? atoi(v) : 2;
+  }();
+  const bool two = nt_env == 2 && tiles % 2 == 0 && tiles >= 512 && nbt <= 2;
+  if (two) {
+    const dim3 grid(tiles / 2);
+    if (nbt == 1) hipLaunchKernelGGL((k_sgemm<EPI, 1, 2>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_sgemm<EPI, 2, 2>), grid, block, 0, s, a);
+    return hipGetLastError();
+  }
+  const dim3 grid(tiles);
+  if (nbt == 1) hipLaunchKernelGGL((k_sgemm<EPI, 1, 1>), grid, block, 0, s, a);
+  else if (nbt == 2) hipLaunchKernelGGL((k_sgemm<EPI, 2, 1>), grid, block, 0, s, a);
+  else if (nbt == 3) hipLaunchKernelGGL((k_sgemm<EPI, 3, 1>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((k_sgemm<EPI, 4, 1>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
