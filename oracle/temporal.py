@@ -165,16 +165,19 @@ def block_full(X, pos, l, W, cfg):
     return y + swiglu(gz, F) @ f64(_lw(W, l, "gating.linear_out.weight")).T
 
 
-def forward_full(ids, W, cfg, p0=0, with_logits=False):
+def forward_full(ids, W, cfg, p0=0, with_logits=False, after_block=None):
     """h = final RMSNorm of the 32-block stack over frames ids [T, n_audio+1] placed at
     positions p0 .. p0+T-1 (audit section 3). Returns h [T, D] (and logits [T, V_text-1]
-    from the untied text head when with_logits)."""
+    from the untied text head when with_logits). after_block: optional {l: f} applied to
+    every row of the residual stream after block l (a memory reader)."""
     ids = np.asarray(ids)
     T = ids.shape[0]
     pos = np.arange(p0, p0 + T)
     X = np.stack([embed(ids[t], W, cfg) for t in range(T)])
     for l in range(cfg["n_layers"]):
         X = block_full(X, pos, l, W, cfg)
+        if after_block and l in after_block:
+            X = np.stack([after_block[l](X[t]) for t in range(T)])
     h = rmsnorm(X, W["out_norm.alpha"], cfg["eps"])
     if with_logits:
         return h, h @ f64(W["text_linear.weight"]).T
@@ -207,10 +210,11 @@ class Cache:
         return np.concatenate(ps), np.concatenate(ks), np.concatenate(vs)
 
 
-def decode_step(x, pos, cache, W, cfg):
+def decode_step(x, pos, cache, W, cfg, after_block=None):
     """One new frame with embedding sum x [D] at absolute position pos, attending over the
     cached keys/values; appends this frame's post-RoPE key and raw value to the cache.
-    Returns the residual stream after the last block (before the final norm)."""
+    Returns the residual stream after the last block (before the final norm).
+    after_block: optional {l: f} applied to the residual stream after block l."""
     D, H, dh, F = cfg["d_model"], cfg["n_heads"], cfg["d_head"], cfg["d_ff"]
     eps, theta, C = cfg["eps"], cfg["rope_theta"], cfg["context"]
     x = np.asarray(x, np.float64)
@@ -227,6 +231,8 @@ def decode_step(x, pos, cache, W, cfg):
         y = x + f64(_lw(W, l, "self_attn.out_proj.weight")) @ a.reshape(D)
         gz = f64(_lw(W, l, "gating.linear_in.weight")) @ rmsnorm(y, _lw(W, l, "norm2.alpha"), eps)
         x = y + f64(_lw(W, l, "gating.linear_out.weight")) @ swiglu(gz, F)
+        if after_block and l in after_block:
+            x = after_block[l](x)
     return x
 
 
@@ -237,14 +243,14 @@ def final(x, W, cfg, with_logits=False):
     return h
 
 
-def decode_incremental(ids, W, cfg, p0=0, cache=None, with_logits=False):
+def decode_incremental(ids, W, cfg, p0=0, cache=None, with_logits=False, after_block=None):
     """Frame-by-frame decode of ids [T, n_audio+1] from position p0, with a KV cache
     (a separate code path from forward_full; the two must agree)."""
     ids = np.asarray(ids)
     cache = cache if cache is not None else Cache(cfg["n_layers"])
     hs, logits = [], []
     for t in range(ids.shape[0]):
-        x = decode_step(embed(ids[t], W, cfg), p0 + t, cache, W, cfg)
+        x = decode_step(embed(ids[t], W, cfg), p0 + t, cache, W, cfg, after_block)
         out = final(x, W, cfg, with_logits)
         if with_logits:
             hs.append(out[0])

@@ -193,3 +193,34 @@ def hidden(n, seed, name="h"):
 def depth_codes(cfg, seed):
     g = np.random.Generator(np.random.PCG64(_seed_for(seed, "codes")))
     return g.integers(0, cfg["n_out"], size=cfg["n_steps"]).astype(np.int32)
+
+
+def reader_weights(cfg, n_readers, mem_dim, seed, wdtype="bf16", scale=0.02, zero_out=False):
+    """Memory-reader weights (readers.{i}.norm / q_proj / k_proj / v_proj / out_proj):
+    matrices scale * N(0, 1) (bfloat16 bits or float32), biases scale * N(0, 1) float32,
+    LayerNorm weight 1 + 0.02 N(0, 1) and bias 0.02 N(0, 1); zero_out makes the output
+    projection's weight and bias zero (the readers' initial state)."""
+    D = cfg["d_model"]
+    R = {}
+    for i in range(n_readers):
+        p = "readers.%d." % i
+        R[p + "norm.weight"] = norm_scale(seed, p + "norm.weight", D)
+        R[p + "norm.bias"] = 0.02 * normal_f32(seed, p + "norm.bias", (D,))
+        for name, shape in (("q_proj", (D, D)), ("k_proj", (D, mem_dim)), ("v_proj", (D, mem_dim)),
+                            ("out_proj", (D, D))):
+            a = scale * normal_f32(seed, p + name + ".weight", shape)
+            b = scale * normal_f32(seed, p + name + ".bias", (D,))
+            if zero_out and name == "out_proj":
+                a = np.zeros_like(a)
+                b = np.zeros_like(b)
+            R[p + name + ".weight"] = to_bf16_bits(a) if wdtype == "bf16" else a.astype(np.float32)
+            R[p + name + ".bias"] = b.astype(np.float32)
+    return R
+
+
+def memory_bank(n, mem_dim, seed, wdtype="bf16"):
+    """A memory bank [n, mem_dim] of N(0, 1) rows (the writer's output is LayerNorm-ed, so
+    rows have unit scale), bfloat16 bits or float32."""
+    a = normal_f32(seed, "memory", (n, mem_dim))
+    return to_bf16_bits(a) if wdtype == "bf16" else a
+
