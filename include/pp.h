@@ -290,6 +290,51 @@ pp_status pp_generator_step(pp_generator* g, const int32_t* provided_host, const
 pp_status pp_generator_inspect(const pp_generator* g, int32_t* inputs_dev, int32_t* chosen_dev,
                                float* text_logits_dev, float* depth_logits_dev, void* stream);
 
+/* ------------------------------------------------------------------ memory readers */
+
+/* Memory readers inserted after temporal blocks ("Current sequence memory: one writer,
+ * four readers" on the PersonaPlex + Inkling page, sections 1 and 6; the released
+ * configuration has 4 readers after zero-based blocks 7, 15, 23, 31, 32 heads of 128, a
+ * 1024-wide memory). A reader after block l adds, to the residual stream z,
+ *   r = W_O concat_h(softmax_v(Q_h . K_h,v / sqrt(d_head)) V_h,v) + b_O,
+ *   Q = W_Q LayerNorm(z) + b_Q (affine, eps ln_eps),  K_v = W_K m_v + b_K,  V_v = W_V m_v + b_V
+ * over the visible memory rows m_v; no visible row adds nothing. Heads as the model's.
+ * Weights (device pointers, kept until the model is destroyed): ln_w, ln_b [d_model]
+ * float32; w_q, w_o [d_model][d_model], w_k, w_v [d_model][mem_dim] in wdtype; biases
+ * [d_model] float32. Requirements: 1..8 readers on distinct blocks, mem_dim % 16 == 0,
+ * d_model % 64 == 0. Readers act in batch-1 decode (and the generator); a prefill or a
+ * batched step with visible memory gives PP_E_ARG. */
+typedef struct {
+  int32_t n_readers;
+  int32_t blocks[8];
+  int32_t mem_dim;
+  int32_t max_slots;   /* memory rows the library keeps keys/values for */
+  double ln_eps;       /* 1e-5 */
+} pp_reader_config;
+
+typedef struct {
+  const float* ln_w;
+  const float* ln_b;
+  const void* w_q;
+  const float* b_q;
+  const void* w_k;
+  const float* b_k;
+  const void* w_v;
+  const float* b_v;
+  const void* w_o;
+  const float* b_o;
+} pp_reader_weights;
+
+/* Attach readers (w: n_readers entries); allocates 2 x n_readers x n_heads x max_slots x
+ * d_head keys/values (wdtype). Once per model. */
+pp_status pp_readers_attach(pp_model* m, const pp_reader_config* cfg, const pp_reader_weights* w);
+/* Write memory rows slot0 .. slot0+n-1 from mem_dev [n][mem_dim] (wdtype): every reader's
+ * keys and values of those rows are formed now. slot0 + n <= max_slots, else PP_E_CAPACITY. */
+pp_status pp_readers_write(pp_model* m, const void* mem_dev, int32_t slot0, int32_t n, void* stream);
+/* Rows 0 .. n_visible-1 are visible to every reader from the next decode step on
+ * (0 = empty memory: readers add nothing). 0 <= n_visible <= max_slots. */
+pp_status pp_readers_set_visible(pp_model* m, int32_t n_visible);
+
 /* ------------------------------------------------------------------ diagnostics */
 
 /* Message of the last error on the calling thread ("" if none). */

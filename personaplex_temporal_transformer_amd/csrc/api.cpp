@@ -430,6 +430,7 @@ hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long 
     GemvArgs gw{};
     gw.W = w_out[l]; gw.x = this->s; gw.K = F; gw.n_groups = D / wout_rb; gw.out = x;
     e = launch_gemv(PRO_COPY, EPI_RESID, bf16, wout_rb, gw, gemv_blocks, s);
+    if (e == hipSuccess) e = enqueue_reader(l, s);
   }
   return e;
 }
@@ -483,7 +484,10 @@ pp_status pp_model::decode(pp_kv* kv, const int32_t* ids_host, const int32_t* id
     *fuse_err = 0;
     return pp_fail(PP_E_HIP, "an earlier decode step's cross-workgroup wait timed out (its output is invalid)");
   }
-  if (kv->B > 1) return decode_batched(kv, ids_host, h_out_dev, text_logits_dev, s);
+  if (kv->B > 1) {
+    if (readers.visible > 0) return pp_fail(PP_E_ARG, "memory readers run in batch-1 decode only");
+    return decode_batched(kv, ids_host, h_out_dev, text_logits_dev, s);
+  }
   const pp_temporal_config& c = cfg;
   if (fuse_qkv_attn) ++fused_seq;
 

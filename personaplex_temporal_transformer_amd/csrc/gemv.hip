@@ -21,6 +21,7 @@ hipError_t launch_gemv(int pro, int epi, bool bf16, int rows_per_group, const Ge
   if (pro == PRO_RMSNORM && epi == EPI_DEPTH_QKV) return launch_gemv_kind<PRO_RMSNORM, EPI_DEPTH_QKV>(rb, bf16, a, blocks, s);
   if (pro == PRO_DEPTH_ATTN && epi == EPI_RESID) return launch_gemv_kind<PRO_DEPTH_ATTN, EPI_RESID>(rb, bf16, a, blocks, s);
   if (pro == PRO_ATTN_MERGE && epi == EPI_RESID) return launch_gemv_kind<PRO_ATTN_MERGE, EPI_RESID>(rb, bf16, a, blocks, s);
+  if (pro == PRO_LAYERNORM && epi == EPI_STORE) return launch_gemv_kind<PRO_LAYERNORM, EPI_STORE>(rb, bf16, a, blocks, s);
   return hipErrorInvalidValue;
 }
 

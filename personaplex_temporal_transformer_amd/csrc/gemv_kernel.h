@@ -10,6 +10,9 @@
 // Fused prologue / epilogues follow "PersonaPlex native LM audit", section 3 ('One of
 // the 32 temporal blocks', 'Positions, attention mask and final text head'):
 //   PRO_RMSNORM  x <- alpha * x / sqrt(mean(x^2) + eps) in float32
+//   PRO_LAYERNORM  x <- alpha * (x - mean(x)) / sqrt(mean((x - mean(x))^2) + eps) + beta
+//                (the memory readers' query norm, "Current sequence memory: one writer,
+//                four readers", section 6; two workgroup reductions, mean first)
 //   PRO_ATTN_MERGE  x <- merge of the decode-attention split partials (online-softmax
 //                rescaling by 2^(m_s - max m), the maxima being in base-2 units, divided
 //                by the merged sum)
@@ -53,7 +56,7 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, int g, const float (
     }
   } else if (EPI == EPI_RESID) {
 #pragma unroll
-    for (int r = 0; r < RB; ++r) a.out[g * RB + r] = res[r] + acc[r];
+    for (int r = 0; r < RB; ++r) a.out[g * RB + r] = res[r] + (acc[r] + (a.add ? a.add[g * RB + r] : 0.f));
   } else if (EPI == EPI_SWIGLU) {
     constexpr int P = RB / 2;
 #pragma unroll
@@ -198,6 +201,7 @@ template <typename WT, int RB, int U, bool ONEPASS, int PRO, int EPI, bool MM, b
 __device__ __forceinline__ void gemv_body(const GemvArgs& a, float* xs, int blk, int nblk) {
   constexpr int NW = kGemvWaves, NT = NW * 64;
   __shared__ float red[NW];
+  __shared__ float red2[PRO == PRO_LAYERNORM ? NW : 1];
   __shared__ float ropes[EPI == EPI_QKV ? 256 : 1];
   constexpr int EPC = Elem<WT>::kPerChunk;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -293,13 +297,15 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a, float* xs, int blk,
     // unconditional; then the first item's weights; then x is staged in LDS (padded to
     // XR*NT*4 floats, so the stores are unconditional too). Straight-line code lets the
     // compiler wait for x alone, and lds_barrier() leaves the weight loads in flight.
-    f32x4 xv[XR], av[PRO == PRO_RMSNORM ? XR : 1];
+    constexpr bool NORM = PRO == PRO_RMSNORM || PRO == PRO_LAYERNORM;
+    f32x4 xv[XR], av[NORM ? XR : 1], bv[PRO == PRO_LAYERNORM ? XR : 1];
 #pragma unroll
     for (int i = 0; i < XR; ++i) {
       const int k = (i * NT + tid) * 4;
       const int kc = k < K ? k : K - 4;
       xv[i] = *reinterpret_cast<const f32x4*>(a.x + kc);
-      if (PRO == PRO_RMSNORM) av[i] = *reinterpret_cast<const f32x4*>(a.alpha + kc);
+      if (NORM) av[i] = *reinterpret_cast<const f32x4*>(a.alpha + kc);
+      if (PRO == PRO_LAYERNORM) bv[i] = *reinterpret_cast<const f32x4*>(a.beta + kc);
     }
     float rope_v = 0.f;
     if constexpr (EPI == EPI_QKV) {
@@ -323,10 +329,41 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a, float* xs, int blk,
       for (int w = 0; w < NW; ++w) tot += red[w];
       r = 1.0f / sqrtf(tot / (float)K + a.eps);
     }
+    float mean = 0.f;
+    if (PRO == PRO_LAYERNORM) {
+      float sm = 0.f;
+#pragma unroll
+      for (int i = 0; i < XR; ++i) {
+        const float q = (xv[i].x + xv[i].y) + (xv[i].z + xv[i].w);
+        sm += (i * NT + tid) * 4 < K ? q : 0.f;
+      }
+      sm = wave_sum(sm);
+      if (lane == 0) red[wid] = sm;
+      lds_barrier();
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) tot += red[w];
+      mean = tot / (float)K;
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < XR; ++i) {
+        const f32x4 d = xv[i] - mean;
+        const float q = d.x * d.x + d.y * d.y + d.z * d.z + d.w * d.w;
+        ss += (i * NT + tid) * 4 < K ? q : 0.f;
+      }
+      ss = wave_sum(ss);
+      if (lane == 0) red2[wid] = ss;
+      lds_barrier();
+      float var = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) var += red2[w];
+      r = 1.0f / sqrtf(var / (float)K + a.eps);
+    }
 #pragma unroll
     for (int i = 0; i < XR; ++i) {
       f32x4 v = xv[i];
       if (PRO == PRO_RMSNORM) v = (v * r) * av[i];
+      if (PRO == PRO_LAYERNORM) v = ((v - mean) * r) * av[i] + bv[PRO == PRO_LAYERNORM ? i : 0];
       const int k = (i * NT + tid) * 4;  // float index; chunk k / EPC, quarter (k % EPC) / 4
       *reinterpret_cast<f32x4*>(xs + xq_index(k / EPC, (k % EPC) / 4)) = v;
     }

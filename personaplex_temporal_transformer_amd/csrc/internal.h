@@ -33,6 +33,7 @@ enum GemvPro {
   PRO_RMSNORM = 1,     // alpha * x / sqrt(mean(x^2) + eps)
   PRO_DEPTH_ATTN = 2,  // x = depth attention output computed from q and the depth cache
   PRO_ATTN_MERGE = 3,  // x = merge of the decode-attention split partials (<= 8 splits)
+  PRO_LAYERNORM = 4,   // alpha * (x - mean(x)) / sqrt(var(x) + eps) + beta
 };
 enum GemvEpi {
   EPI_STORE = 0,   // out[row] = W x
@@ -45,7 +46,8 @@ enum GemvEpi {
 struct GemvArgs {
   const void* W;        // [rows][K] row-major
   const float* x;       // [K] input vector
-  const float* alpha;   // [K] RMSNorm scale (PRO_RMSNORM)
+  const float* alpha;   // [K] RMSNorm / LayerNorm scale (PRO_RMSNORM, PRO_LAYERNORM)
+  const float* beta;    // [K] LayerNorm shift (PRO_LAYERNORM)
   float eps;
   int K;
   int n_groups;         // row groups; a group is rows_per_group rows
@@ -60,7 +62,7 @@ struct GemvArgs {
   int slot_override;    // depth: >= 0 gives the cache row directly
   // EPI_SWIGLU
   int F;
-  // a second input added to the output (EPI_STORE), or null
+  // a second input added to the output (EPI_STORE, EPI_RESID: a bias), or null
   const float* add;
   // rows spread over several matrices: row r is row (r % rows_per_mat) of mats[r / rows_per_mat]
   // (rows_per_mat = 0: one matrix W)
@@ -313,5 +315,19 @@ hipError_t launch_sgemm(int epi, const SgemmArgs& a, hipStream_t s);
 // Copy of a row-major [rows][K] bf16 matrix in the fragment order the skinny products
 // read (same byte count); rows_out = N (or F for the SiLU-gated W_in with 2F rows).
 hipError_t launch_sgemm_pack(const void* W, void* packed, int rows_out, int K, int F, bool swiglu, hipStream_t s);
+}  // namespace pp
+
+namespace pp {
+// ---------------------------------------------------------------- memory readers
+// Keys (or values) of memory rows for one reader: out[h][slot][d] = (W m_slot + b)[h*dh + d]
+// for slots slot0 .. slot0+n-1, stored in the weight type (float32 products).
+struct ReaderKvArgs {
+  const void* mem;      // [n][mem_dim] rows (weight type)
+  const void* W;        // [D][mem_dim]
+  const float* bias;    // [D]
+  void* out;            // [H][max_slots][dh]
+  int n, slot0, mem_dim, D, dh, max_slots;
+};
+hipError_t launch_reader_kv(const ReaderKvArgs& a, bool bf16, hipStream_t s);
 }  // namespace pp
 

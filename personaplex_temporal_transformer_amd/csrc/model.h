@@ -78,6 +78,22 @@ struct pp_model {
   size_t ids_cap = 0;
   hipEvent_t ids_event = nullptr;
 
+  // memory readers (csrc/reader.cpp)
+  struct Reader {
+    int block = 0;
+    pp_reader_weights w{};
+    void* K = nullptr;   // [H][max_slots][dh], weight type
+    void* V = nullptr;
+  };
+  struct ReaderSet {
+    int n = 0, mem_dim = 0, max_slots = 0, visible = 0;
+    double eps = 1e-5;
+    std::vector<Reader> r;
+    void* ws = nullptr;
+    ~ReaderSet();
+  } readers;
+  hipError_t enqueue_reader(int l, hipStream_t s);
+
   // launch mode and timing
   bool use_graph = true;
   int graph_gen = 0;

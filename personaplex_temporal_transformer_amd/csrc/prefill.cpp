@@ -82,6 +82,7 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
   if (!m || !kv || !ids_host || !h_out_dev) return pp_fail(PP_E_ARG, "NULL argument");
   if (kv->m != m) return pp_fail(PP_E_ARG, "kv ring belongs to another model");
   if (kv->B != 1) return pp_fail(PP_E_ARG, "prefill needs a batch-1 ring");
+  if (m->readers.visible > 0) return pp_fail(PP_E_ARG, "memory readers run in batch-1 decode only");
   const pp_temporal_config& c = m->cfg;
   if (T < 1 || T > c.context || T > m->max_T)
     return pp_fail(PP_E_CAPACITY, "T must be in [1, min(context, max_prefill_T)]");

@@ -24,7 +24,8 @@ EXPORTS = ["pp_temporal_create", "pp_temporal_destroy", "pp_kv_alloc", "pp_kv_fr
            "pp_temporal_prefill", "pp_depformer_create", "pp_depformer_destroy", "pp_depformer_step",
            "pp_last_error", "pp_temporal_set_graph", "pp_temporal_trace", "pp_temporal_trace_read",
            "pp_depformer_set_graph", "pp_kv_restore", "pp_sample_top_k", "pp_generator_create", "pp_generator_destroy",
-           "pp_generator_step", "pp_generator_inspect"]
+           "pp_generator_step", "pp_generator_inspect", "pp_readers_attach", "pp_readers_write",
+           "pp_readers_set_visible"]
 
 
 class PPError(RuntimeError):
@@ -71,6 +72,15 @@ class GeneratorConfig(ctypes.Structure):
                 ("audio_top_k", ctypes.c_int32)]
 
 
+class ReaderConfig(ctypes.Structure):
+    _fields_ = [("n_readers", ctypes.c_int32), ("blocks", ctypes.c_int32 * 8), ("mem_dim", ctypes.c_int32),
+                ("max_slots", ctypes.c_int32), ("ln_eps", ctypes.c_double)]
+
+
+class ReaderWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("ln_w", "ln_b", "w_q", "b_q", "w_k", "b_k", "w_v", "b_v", "w_o", "b_o")]
+
+
 _lib = None
 
 
@@ -109,6 +119,9 @@ def load():
         "pp_generator_destroy": [VP],
         "pp_generator_step": [VP, P(I32), P(ctypes.c_double), VP, P(I32), VP],
         "pp_generator_inspect": [VP, VP, VP, VP, VP, VP],
+        "pp_readers_attach": [VP, P(ReaderConfig), P(ReaderWeights)],
+        "pp_readers_write": [VP, VP, I32, I32, VP],
+        "pp_readers_set_visible": [VP, I32],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -219,6 +232,28 @@ class TemporalModel:
 
     def set_graph(self, enable):
         _check(load().pp_temporal_set_graph(self.handle, 1 if enable else 0))
+
+    def attach_readers(self, blocks, weights, mem_dim, max_slots, ln_eps=1e-5):
+        """pp_readers_attach: reader i after block blocks[i], weights named readers.{i}.norm /
+        q_proj / k_proj / v_proj / out_proj (.weight, .bias) as CUDA tensors (kept alive)."""
+        self._readers = weights
+        n = len(blocks)
+        cfg = ReaderConfig(n, (ctypes.c_int32 * 8)(*blocks), int(mem_dim), int(max_slots), float(ln_eps))
+        arr = (ReaderWeights * n)()
+        for i in range(n):
+            p = "readers.%d." % i
+            t = lambda k: weights[p + k].data_ptr()
+            arr[i] = ReaderWeights(t("norm.weight"), t("norm.bias"), t("q_proj.weight"), t("q_proj.bias"),
+                                   t("k_proj.weight"), t("k_proj.bias"), t("v_proj.weight"), t("v_proj.bias"),
+                                   t("out_proj.weight"), t("out_proj.bias"))
+        _check(load().pp_readers_attach(self.handle, ctypes.byref(cfg), arr))
+
+    def write_memory(self, rows, slot0=0, stream=None):
+        n = rows.shape[0]
+        _check(load().pp_readers_write(self.handle, _ptr(rows), int(slot0), int(n), _stream(stream)))
+
+    def set_visible(self, n_visible):
+        _check(load().pp_readers_set_visible(self.handle, int(n_visible)))
 
     def trace(self, layer):
         _check(load().pp_temporal_trace(self.handle, int(layer)))
