@@ -307,6 +307,49 @@ def bench_batched(model, cfg, batches, steps, warmup):
             "points": out}
 
 
+def bench_readers(model, kv, cfg, slots_list, steps, warmup):
+    """Decode frames with the 4 memory readers of the released configuration (after blocks
+    7, 15, 23, 31; 1024-wide memory; weights drawn on the device) at several visible-memory
+    sizes, on the live full ring."""
+    import torch
+    D, mem = cfg["d_model"], 1024
+    g = torch.Generator(device="cuda")
+    g.manual_seed(15)
+    R = {}
+    for i in range(4):
+        p = "readers.%d." % i
+        R[p + "norm.weight"] = 1.0 + 0.02 * torch.randn(D, generator=g, device="cuda")
+        R[p + "norm.bias"] = 0.02 * torch.randn(D, generator=g, device="cuda")
+        for name, k in (("q_proj", D), ("k_proj", mem), ("v_proj", mem), ("out_proj", D)):
+            R[p + name + ".weight"] = (0.02 * torch.randn((D, k), generator=g, device="cuda")).to(torch.bfloat16)
+            R[p + name + ".bias"] = 0.02 * torch.randn(D, generator=g, device="cuda")
+    top = max(slots_list)
+    model.attach_readers([7, 15, 23, 31], R, mem, top)
+    model.write_memory(torch.randn((top, mem), generator=g, device="cuda").to(torch.bfloat16))
+    ids = synth_ids(cfg, warmup + steps, 16)
+    h = torch.empty(D, device="cuda")
+    pts = []
+    for n in slots_list:
+        model.set_visible(n)
+        for i in range(warmup):
+            model.decode_step(kv, ids[i], h)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for i in range(warmup, warmup + steps):
+            model.decode_step(kv, ids[i], h)
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / steps
+        extra = 4 * (2 * D * D * 2 + 2 * n * D * 2)
+        nb = frame_bytes(cfg, cfg["context"]) + extra
+        pts.append({"visible_rows": n, "ms_per_frame": round(ms, 4), "frame_bytes": nb,
+                    "reader_bytes": extra, "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)})
+    model.set_visible(0)
+    return {"workload": "decode frame (32 blocks, ring full) with 4 memory readers after blocks 7/15/23/31, "
+                        "32 heads x 128, 1024-wide memory", "steps": steps, "points": pts}
+
+
 def synth_cfg_no_weights(cfg):
     """The decode-frame byte formula with the weights taken out: frame_bytes(cfg, C) minus
     frame_bytes(this, 0) is one session's K/V read, K/V write and embedding rows."""
@@ -434,6 +477,7 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--chunk-T", type=int, default=256, help="0: skip the prefill-chunk line")
     ap.add_argument("--batches", default="4,16,32", help="batched-decode sizes ('' to skip)")
+    ap.add_argument("--reader-slots", default="1024,8192", help="visible memory rows for the reader line ('' to skip)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the run, copy 1 GiB device-to-device 3 times (counter calibration)")
     args = ap.parse_args()
@@ -528,6 +572,9 @@ def main():
         DW = make_depth_weights(dc, 5)
         dep = pp.Depformer(dc, DW, "bf16")
         out["generator"] = bench_generator(model, kv, dep, cfg, dc, max(10, args.steps // 2), 3)
+    slots = [int(v) for v in args.reader_slots.split(",") if v.strip()]
+    if slots:
+        out["readers"] = bench_readers(model, kv, cfg, slots, max(10, args.steps // 5), 3)
     if batches:
         out["batched"] = bench_batched(model, cfg, batches, max(10, args.steps // 5), 3)
     if args.chunk_T > 0 and args.prefill_T >= args.chunk_T:

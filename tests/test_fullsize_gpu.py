@@ -256,3 +256,35 @@ def test_full_batched_decode_ctx3000_matches_single_sessions():
         kv1.close()
     print("full batched decode B=4 vs single sessions: errs %s" % ["%.3g" % e for e in errs])
     assert max(errs) <= 2 * BF16_TOL
+
+
+def test_full_decode_with_four_readers_matches_oracle():
+    """The released reader configuration: 4 readers after zero-based blocks 7, 15, 23, 31
+    of the 32-block stack, 32 heads x 128, 1024-wide memory with 1024 visible rows; one
+    decode frame at position 3000 on a full ring, against the oracle (2e-2)."""
+    import torch
+    from oracle import reader as ORD
+    cfg = dict(synth.FULL_TEMPORAL)
+    C, L, D = cfg["context"], cfg["n_layers"], cfg["d_model"]
+    W = synth.temporal_weights(cfg, 100, "bf16", with_text_head=False, shared_layer=True)
+    R = synth.reader_weights(cfg, 4, 1024, 101, "bf16", scale=0.05)
+    M = synth.memory_bank(1024, 1024, 102, "bf16")
+    frames = synth.cache_frames(cfg, C, 103)
+    ids = synth.stream_ids(cfg, 1, 104)
+    model = _model(cfg, W)
+    model.attach_readers([7, 15, 23, 31], to_device(R), 1024, 1024)
+    model.write_memory(torch.from_numpy(M.view(np.int16)).cuda().view(torch.bfloat16))
+    model.set_visible(1024)
+    kv = model.kv_alloc()
+    kv.load(torch.from_numpy(frames.view(np.int16)).cuda(), C)
+    h = torch.empty(D, device="cuda")
+    model.decode_step(kv, ids[0], h)
+    torch.cuda.synchronize()
+    ks = [frames[l, 0, 0].transpose(1, 0, 2) for l in range(L)]
+    vs = [frames[l, 1, 0].transpose(1, 0, 2) for l in range(L)]
+    cache = O.cache_from_blocks(ks, vs, np.arange(C), L)
+    x = O.decode_step(O.embed(ids[0], W, cfg), C, cache, W, cfg,
+                      after_block=ORD.hooks([7, 15, 23, 31], M, 1024, R, cfg["n_heads"]))
+    err = norm_max_err(h.cpu().numpy(), O.final(x, W, cfg))
+    print("full decode with 4 readers (1024 visible rows): err %.3g" % err)
+    assert err <= BF16_TOL
