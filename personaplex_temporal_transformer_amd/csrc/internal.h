@@ -167,7 +167,7 @@ enum GemmEpi { GEPI_QKV = 0, GEPI_RESID = 1, GEPI_SWIGLU = 2 };
 
 struct GemmArgs {
   const void* A;        // [M][K] activations, row-major (float16 on the bf16-weight path, or float32)
-  const void* B;        // weights, row-major [rows][K]
+  const void* B;        // weights, row-major [rows][K] (float16 copy on the bf16-weight path, or float32)
   int M, N, K;          // N = output columns (GEPI_SWIGLU: N = F, B has 2F rows)
   // GEPI_QKV: columns Q|K|V; RoPE on Q and K with rope[row][d] (cos, sin pairs);
   // Q -> q_out [H][M][dh]; K, V -> ring slots (p0 + row) mod C of [H][C][dh]
@@ -192,6 +192,8 @@ struct GemmArgs {
   int x_pitch, xoff;
 };
 hipError_t launch_gemm(int epi, bool bf16, const GemmArgs& g, int n_cu, hipStream_t s);
+// float16 copy of n_elems bfloat16 values (n_elems % 8 == 0), exact
+hipError_t launch_bf16_to_f16(const void* src, void* dst, size_t n_elems, hipStream_t s);
 
 // The attention of a chunk of T frames at positions p0..p0+T-1 runs in a contiguous key
 // space: key index j is position p0 - koff + j, query i is key index koff + i. Keys

@@ -72,7 +72,9 @@ struct pp_model {
   void* pvt = nullptr;         // bf16-weight path: V transposed, float16 [H][dh][vt_pitch] of a chunk's key space
   void* pkx = nullptr;         // a chunk's key space: K [H][x_pitch][dh] (wdtype)
   void* pvx = nullptr;         // float32 path: V [H][x_pitch][dh]
-  int vt_pitch = 0, x_pitch = 0;   // keys of the key space: max_T + context + 16, rounded up to 64
+  int vt_pitch = 0, x_pitch = 0;
+  void* pf16_ws = nullptr;     // bf16-weight path: float16 copies of the block matrices (one allocation)
+  std::vector<const void*> f16_qkv, f16_o, f16_in, f16_out;   // keys of the key space: max_T + context + 16, rounded up to 64
 
   int32_t* ids_pinned = nullptr;
   size_t ids_cap = 0;

@@ -13,6 +13,7 @@
 
 #include <cmath>
 #include <string>
+#include <vector>
 
 #include "internal.h"
 #include "model.h"
@@ -45,6 +46,29 @@ pp_status pp_model::alloc_prefill() {
     else ovx = take(esz * H * x_pitch * dh);
   }
   if (hipMalloc(&pws, bytes) != hipSuccess) return pp_fail(PP_E_HIP, "hipMalloc of prefill workspace failed");
+  if (max_T > 0 && bf16) {
+    // the matrix-core products take float16 operands: one float16 copy of every matrix,
+    // converted once here (13.15 GB at full size)
+    const size_t L = cfg.n_layers;
+    const size_t per_layer = (3 * D * D + D * D + 2 * F * D + D * F) * 2;
+    if (hipMalloc(&pf16_ws, L * per_layer) != hipSuccess)
+      return pp_fail(PP_E_HIP, "hipMalloc of the prefill float16 weights failed");
+    char* p = static_cast<char*>(pf16_ws);
+    hipError_t e = hipSuccess;
+    auto conv = [&](const void* src, size_t n, std::vector<const void*>& dst) {
+      dst.push_back(p);
+      if (e == hipSuccess) e = launch_bf16_to_f16(src, p, n, nullptr);
+      p += n * 2;
+    };
+    for (size_t l = 0; l < L; ++l) {
+      conv(w_qkv[l], 3 * D * D, f16_qkv);
+      conv(w_o[l], D * D, f16_o);
+      conv(w_in[l], 2 * F * D, f16_in);
+      conv(w_out[l], D * F, f16_out);
+    }
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("converting prefill weights: ") + hipGetErrorString(e));
+  }
   char* b = static_cast<char*>(pws);
   ids_dev = reinterpret_cast<int32_t*>(b + oid);
   if (max_T > 0) {
@@ -71,6 +95,8 @@ pp_status pp_model::alloc_prefill() {
 void pp_model::free_prefill() {
   if (pws) (void)hipFree(pws);
   pws = nullptr;
+  if (pf16_ws) (void)hipFree(pf16_ws);
+  pf16_ws = nullptr;
 }
 
 static pp_status hip_fail(const char* what, hipError_t e) {
@@ -134,7 +160,7 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
     if (e != hipSuccess) return hip_fail("prefill norm1", e);
 
     GemmArgs g{};
-    g.A = m->pu; g.B = m->w_qkv[l]; g.M = T; g.N = 3 * D; g.K = D;
+    g.A = m->pu; g.B = bf ? m->f16_qkv[l] : m->w_qkv[l]; g.M = T; g.N = 3 * D; g.K = D;
     g.q_out = m->pq; g.kc = kbase; g.vc = vbase; g.rope = m->prope;
     g.D = D; g.dh = dh; g.C = C; g.p0 = (int)(p0 % C);
     g.vt = m->pvt; g.vt_pitch = m->vt_pitch;
@@ -156,7 +182,7 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
     if (e != hipSuccess) return hip_fail("prefill attention", e);
 
     GemmArgs go{};
-    go.A = m->pa; go.B = m->w_o[l]; go.M = T; go.N = D; go.K = D; go.x = m->px;
+    go.A = m->pa; go.B = bf ? m->f16_o[l] : m->w_o[l]; go.M = T; go.N = D; go.K = D; go.x = m->px;
     e = launch_gemm(GEPI_RESID, bf, go, m->n_cu, s);
     if (e != hipSuccess) return hip_fail("prefill W_O", e);
 
@@ -164,12 +190,12 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
     if (e != hipSuccess) return hip_fail("prefill norm2", e);
 
     GemmArgs gi{};
-    gi.A = m->pu; gi.B = m->w_in[l]; gi.M = T; gi.N = F; gi.K = D; gi.F = F; gi.s_out = m->pg;
+    gi.A = m->pu; gi.B = bf ? m->f16_in[l] : m->w_in[l]; gi.M = T; gi.N = F; gi.K = D; gi.F = F; gi.s_out = m->pg;
     e = launch_gemm(GEPI_SWIGLU, bf, gi, m->n_cu, s);
     if (e != hipSuccess) return hip_fail("prefill W_in", e);
 
     GemmArgs gw{};
-    gw.A = m->pg; gw.B = m->w_out[l]; gw.M = T; gw.N = D; gw.K = F; gw.x = m->px;
+    gw.A = m->pg; gw.B = bf ? m->f16_out[l] : m->w_out[l]; gw.M = T; gw.N = D; gw.K = F; gw.x = m->px;
     e = launch_gemm(GEPI_RESID, bf, gw, m->n_cu, s);
     if (e != hipSuccess) return hip_fail("prefill W_out", e);
   }

@@ -98,9 +98,11 @@ __device__ __forceinline__ void vm_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// C[M][N] = A[M][K] B[N][K]^T. Workgroup = WM x WN waves, tile BM x BN with BM = WM*32*MI,
+// C[M][N] = A[M][K] B[N][K]^T with float16 A (activations) and B (the model's float16
+// weight copy, converted once from bf16 -- exactly, so the products equal those of the
+// bf16 weights). Workgroup = WM x WN waves, tile BM x BN with BM = WM*32*MI,
 // BN = WN*32*NI; wave (wm, wn) owns rows wm*32*MI.. and 32*NI columns as MI x NI tiles of
-// 32 x 32 (v_mfma_f32_32x32x16_bf16, fp32 accumulation). A and B k-tiles (64 wide) go from
+// 32 x 32 (v_mfma_f32_32x32x16_f16, fp32 accumulation). A and B k-tiles (64 wide) go from
 // global memory straight into LDS (buffer loads with the LDS flag: no registers, no LDS
 // write instructions) through NS stages, NS-1 k-tiles ahead of the multiply; one barrier
 // per k-tile. Rows of A past M read as zeros (out of the buffer's range) and are not stored.
@@ -108,7 +110,7 @@ __device__ __forceinline__ void vm_wait_barrier() {
 // multiplies g rows wn*16*NI.. (NI/2 tiles) and the z rows BN/2 + wn*16*NI.., so g and z
 // of one output share a lane.
 template <int EPI, int WM, int WN, int MI, int NI, int NS>
-__global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(GemmArgs g) {
+__global__ __launch_bounds__(WM * WN * 64) void k_gemm_f16(GemmArgs g) {
   constexpr int NW = WM * WN;
   constexpr int BM = WM * 32 * MI, BN = WN * 32 * NI;
   constexpr int AL = BM / (8 * NW);   // LDS-load instructions per wave per k-tile (A)
@@ -187,18 +189,13 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(GemmArgs g) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   // Fragments of k-step ks of stage st (lane: row/col lane%32, k-chunk 2*ks + lane/32).
-  // (B first: its bfloat16 -> float16 conversion then has the A reads and two MFMAs to
-  // hide the LDS latency behind)
   auto load_frags = [&](int st, int ks, f16x8 (&av)[MI], f16x8 (&bv)[NI]) {
     const int kc = ks * 2 + (lane >> 5);
-    u32x4 braw[NI];
 #pragma unroll
-    for (int j = 0; j < NI; ++j) braw[j] = Bs[st][swz(bcol0(j) + (lane & 31), kc)];
+    for (int j = 0; j < NI; ++j) bv[j] = __builtin_bit_cast(f16x8, Bs[st][swz(bcol0(j) + (lane & 31), kc)]);
 #pragma unroll
     for (int i = 0; i < MI; ++i)
       av[i] = __builtin_bit_cast(f16x8, As[st][swz(wm * 32 * MI + i * 32 + (lane & 31), kc)]);
-#pragma unroll
-    for (int j = 0; j < NI; ++j) bv[j] = bf16x8_to_f16(braw[j]);
   };
   auto mfmas = [&](const f16x8 (&av)[MI], const f16x8 (&bv)[NI]) {
 #pragma unroll
@@ -225,8 +222,6 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(GemmArgs g) {
     mfmas(a0, b0);
     mfmas(a1, b1);
     // per k-step with a successor: MFMAs alternate with the next k-step's fragment reads
-    // (B first), and each B fragment's conversion (12 VALU: 0x002) follows two MFMAs after
-    // its read
     constexpr int NF = MI + NI, NM = MI * NI;
 #pragma unroll
     for (int ks = 0; ks < 3; ++ks) {
@@ -234,7 +229,6 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(GemmArgs g) {
       for (int i = 0; i < NM; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (i < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (i >= 2 && i - 2 < NI) __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
       }
     }
     __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
@@ -486,7 +480,7 @@ static void launch_cfg(const GemmArgs& g, hipStream_t s) {
   constexpr int BM = WM * 32 * MI, BN = WN * 32 * NI;
   const int n_tn = EPI == GEPI_SWIGLU ? g.F / (BN / 2) : g.N / BN;
   const int n_tm = (g.M + BM - 1) / BM;
-  hipLaunchKernelGGL((k_gemm_bf16<EPI, WM, WN, MI, NI, NS>), dim3(n_tm * n_tn), dim3(WM * WN * 64), 0, s, g);
+  hipLaunchKernelGGL((k_gemm_f16<EPI, WM, WN, MI, NI, NS>), dim3(n_tm * n_tn), dim3(WM * WN * 64), 0, s, g);
 }
 
 template <int EPI>
@@ -512,6 +506,23 @@ static hipError_t gemm_dispatch(bool bf16, const GemmArgs& g, int n_cu, hipStrea
     const int n_tn = EPI == GEPI_SWIGLU ? (g.F + 31) / 32 : (g.N + 63) / 64;
     hipLaunchKernelGGL(k_gemm_f32<EPI>, dim3(n_tm * n_tn), dim3(256), 0, s, g);
   }
+  return hipGetLastError();
+}
+
+// The prefill's float16 copy of a bf16 matrix: one 16-byte word (8 values) per thread,
+// widened exactly (bfloat16's significand is the shorter; values below float16's range
+// flush toward zero).
+__global__ __launch_bounds__(kBlock) void k_bf16_to_f16(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                        long long n16) {
+  const long long i = (long long)blockIdx.x * kBlock + threadIdx.x;
+  if (i < n16) dst[i] = __builtin_bit_cast(u32x4, bf16x8_to_f16(src[i]));
+}
+
+hipError_t launch_bf16_to_f16(const void* src, void* dst, size_t n_elems, hipStream_t s) {
+  if (n_elems % 8) return hipErrorInvalidValue;
+  const long long n16 = (long long)(n_elems / 8);
+  hipLaunchKernelGGL(k_bf16_to_f16, dim3((unsigned)((n16 + kBlock - 1) / kBlock)), dim3(kBlock), 0, s,
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
   return hipGetLastError();
 }
 
