@@ -239,7 +239,8 @@ def bench_prefill(model, cfg, T, steps, warmup):
             "frames_per_s": round(T / (ms * 1e-3), 1), "flop": gemm + attn, "gemm_flop": gemm,
             "attention_flop": attn, "achieved_TFLOPs": round(tflops, 1), "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
             "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "steps": steps,
-            "workload": "full 32-block temporal prefill, B=1, T=%d frames from position 0, bf16 MFMA, "
+            "workload": "full 32-block temporal prefill, B=1, T=%d frames from position 0, float16 matrix "
+                        "cores (float16 copy of the bf16 weights; peak = the 2.5 PFLOP/s dense bf16/fp16 figure), "
                         "K/V written to ring slots 0..T-1" % T}
 
 

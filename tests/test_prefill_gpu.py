@@ -81,7 +81,9 @@ def test_tiny_fp32_prefill_then_decode_continues():
     L, H, C, dh = cfg["n_layers"], cfg["n_heads"], cfg["context"], cfg["d_head"]
     b = before.reshape(L, 2, 1, H, C, dh)
     a = after.reshape(L, 2, 1, H, C, dh)
-    assert np.array_equal(a[..., 50:, :], b[..., 50:, :])     # slots >= T untouched
+    # slots >= T untouched, bit for bit (the fresh ring holds whatever the allocation held,
+    # NaN patterns included, so the bits are compared, not the values)
+    assert np.array_equal(a[..., 50:, :].view(np.uint32), b[..., 50:, :].view(np.uint32))
     # decoded frame by frame from an empty ring, the same 50 frames fill the same slots
     kv2 = model.kv_alloc()
     for t in range(50):
