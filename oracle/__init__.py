@@ -15,6 +15,8 @@ Modules
   ring       -- the integer slot/position arithmetic of a ring KV cache
   sampling   -- temperature / top-k sampling with caller-supplied uniform draws
   generator  -- one generator frame: delayed-code ring, text and depth sampling
+  reader     -- memory readers: LayerNorm query, attention over visible memory rows,
+                output projection added to the residual
 
 Every function is pinned by tests/test_oracle_*.py against facts the pages fix
 (printed counts, integer examples, closed forms, invariants, brute force). The one
@@ -22,4 +24,4 @@ part that stays "parity unpinned" is agreement with the released PersonaPlex
 checkpoint's numerics: the pages publish no weights or reference outputs.
 """
 
-from . import temporal, depformer, inventory, ring, sampling, generator  # noqa: F401
+from . import temporal, depformer, inventory, ring, sampling, generator, reader  # noqa: F401
