@@ -15,6 +15,8 @@
 // float32 path (small shapes, fp32 parity): plain FMA kernels with the same epilogues.
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
@@ -98,32 +100,70 @@ __device__ __forceinline__ void vm_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// GEMM stage rows hold KB/8 chunks of 16 bytes. Rows of 8 chunks (KB = 64) use swz_slot;
+// rows of 4 chunks (KB = 32) XOR the chunk index with bits 2..3 of the row, so that 16
+// consecutive rows read at one chunk index again fall into 16 distinct 16-byte bank groups
+// of a 256-byte window (bits 2..3 of the row pick the 64-byte quarter, the XOR the chunk).
+template <int CPRL>
+__device__ __forceinline__ int gswz_slot(int r, int kc) {
+  static_assert(CPRL == 4 || CPRL == 8, "row width");
+  return CPRL == 8 ? kc ^ ((r >> 1) & 7) : kc ^ ((r >> 2) & 3);
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Wait until at most a * L loads of this wave are outstanding (0 <= a; a above A counts as A).
+template <int L, int A>
+__device__ __forceinline__ void vm_wait_tiles(int a) {
+  if constexpr (A == 0) {
+    vm_wait<0>();
+  } else {
+    if (a >= A) vm_wait<A * L>();
+    else vm_wait_tiles<L, A - 1>(a);
+  }
+}
+__device__ __forceinline__ void lds_wait_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // C[M][N] = A[M][K] B[N][K]^T with float16 A (activations) and B (the model's float16
 // weight copy, converted once from bf16 -- exactly, so the products equal those of the
 // bf16 weights). Workgroup = WM x WN waves, tile BM x BN with BM = WM*32*MI,
 // BN = WN*32*NI; wave (wm, wn) owns rows wm*32*MI.. and 32*NI columns as MI x NI tiles of
-// 32 x 32 (v_mfma_f32_32x32x16_f16, fp32 accumulation). A and B k-tiles (64 wide) go from
-// global memory straight into LDS (buffer loads with the LDS flag: no registers, no LDS
-// write instructions) through NS stages, NS-1 k-tiles ahead of the multiply; one barrier
-// per k-tile. Rows of A past M read as zeros (out of the buffer's range) and are not stored.
+// 32 x 32 (v_mfma_f32_32x32x16_f16, fp32 accumulation).
+// k-tiles of KB columns go from global memory straight into LDS (buffer loads with the LDS
+// flag: no registers, no LDS write instructions). Stage st holds one k-tile: rows 0..BM-1
+// of A, then rows BM..BM+BN-1 of B. One barrier per k-tile, in one of two schedules:
+//   early (LATE = false): NS-1 tiles ahead; the barrier opens tile kt, whose first
+//     fragments are read before the stage of tile kt-1 is refilled with tile kt+NS-1;
+//   late (LATE = true): all NS stages in use; the barrier sits before tile kt's last
+//     k-step: once every wave has read all of tile kt's fragments its stage is refilled
+//     with tile kt+NS, and tile kt+1's first fragments are read under the last k-step's
+//     matrix products.
+// Rows of A past M read as zeros (out of the buffer's range) and are not stored.
 // GEPI_SWIGLU: the B tile holds W_in rows j0..j0+BN/2-1 (g) and F+j0.. (z); wave (wm, wn)
 // multiplies g rows wn*16*NI.. (NI/2 tiles) and the z rows BN/2 + wn*16*NI.., so g and z
 // of one output share a lane.
-template <int EPI, int WM, int WN, int MI, int NI, int NS>
+template <int EPI, int WM, int WN, int MI, int NI, int NS, int KB, bool LATE>
 __global__ __launch_bounds__(WM * WN * 64) void k_gemm_f16(GemmArgs g) {
   constexpr int NW = WM * WN;
   constexpr int BM = WM * 32 * MI, BN = WN * 32 * NI;
-  constexpr int AL = BM / (8 * NW);   // LDS-load instructions per wave per k-tile (A)
-  constexpr int BL = BN / (8 * NW);   // (B)
-  static_assert(AL * 8 * NW == BM && BL * 8 * NW == BN, "tile rows must split over the waves");
+  constexpr int CPRL = KB / 8;            // 16-byte chunks per LDS row
+  constexpr int RPI = 64 / CPRL;          // LDS rows one load instruction fills (1 KB)
+  constexpr int NQ = (BM + BN) / RPI;     // load instructions per k-tile
+  constexpr int LW = (NQ + NW - 1) / NW;  // per wave: LW for waves w < NQ - NW*(LW-1), else LW-1
+  constexpr int KS = KB / 16;             // k-steps (of 16) per tile
+  static_assert(KB == 32 || KB == 64, "k-tile width");
+  static_assert(BM % RPI == 0 && NQ >= NW, "load instructions cover whole A / B rows");
+  static_assert(KS % 2 == 0, "the two fragment register sets alternate per k-step");
+  static_assert(NS >= 2 && (NS - 1) * LW < 64, "stages");
   static_assert(EPI != GEPI_SWIGLU || NI % 2 == 0, "SwiGLU pairs g and z tiles");
-  // pipeline stages; GEPI_QKV reuses the same LDS for half of its output tile (fp32, row
-  // pitch TPF floats)
+  // GEPI_QKV reuses the LDS for half of its output tile (fp32, row pitch TPF floats)
   constexpr int TPF = BN / 2 + 4;
-  constexpr int STAGE_CH = NS * (BM + BN) * 8, TILE_CH = EPI == GEPI_QKV ? BM * TPF * 4 / 16 : 0;
+  constexpr int STAGE = (BM + BN) * CPRL;
+  constexpr int STAGE_CH = NS * STAGE, TILE_CH = EPI == GEPI_QKV ? BM * TPF * 4 / 16 : 0;
   __shared__ u32x4 lds[STAGE_CH > TILE_CH ? STAGE_CH : TILE_CH];
-  u32x4 (*As)[BM * 8] = reinterpret_cast<u32x4 (*)[BM * 8]>(lds);
-  u32x4 (*Bs)[BN * 8] = reinterpret_cast<u32x4 (*)[BN * 8]>(lds + NS * BM * 8);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w % WM, wn = w / WM;
@@ -151,33 +191,36 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_f16(GemmArgs g) {
   };
   const u32x4 ar = rsrc_words(g.A, (uint32_t)((size_t)g.M * K * 2));
   const u32x4 br = rsrc_words(g.B, (uint32_t)((size_t)(EPI == GEPI_SWIGLU ? 2 * g.F : g.N) * K * 2));
-  // Instruction j of wave w fills rows R0 = (w + NW*j)*8 .. +7 (1 KB of LDS, lane i at
-  // chunk position R0*8 + i): lane i fetches row r = R0 + i/8, and the k-chunk that swz()
-  // puts at slot i%8 of that row (the XOR is its own inverse).
-  const int lrow = lane >> 3;
-  uint32_t aoff[AL], boff[BL];
+  // Instruction q = w + NW*j fills stage rows q*RPI .. q*RPI + RPI-1 (1 KB, lane i at chunk
+  // position q*64 + i): lane i fetches row q*RPI + i/CPRL and the k-chunk that gswz_slot
+  // puts at slot i%CPRL of that row (the XOR is its own inverse).
+  const bool full = w + NW * (LW - 1) < NQ;  // this wave issues LW loads per k-tile
+  uint32_t voff[LW];
 #pragma unroll
-  for (int j = 0; j < AL; ++j) {
-    const int r = (w + NW * j) * 8 + lrow;
-    aoff[j] = (uint32_t)(((size_t)(m0 + r) * K + swz_slot(r, lane & 7) * 8) * 2);
+  for (int j = 0; j < LW; ++j) {
+    const int q = w + NW * j;
+    const int r = q * RPI + lane / CPRL;
+    const int chunk = gswz_slot<CPRL>(r, lane % CPRL);
+    const size_t grow = r < BM ? (size_t)(m0 + r) : (size_t)brow(r - BM);
+    voff[j] = (uint32_t)((grow * K + chunk * 8) * 2);
   }
-#pragma unroll
-  for (int j = 0; j < BL; ++j) {
-    const int r = (w + NW * j) * 8 + lrow;
-    boff[j] = (uint32_t)(((size_t)brow(r) * K + swz_slot(r, lane & 7) * 8) * 2);
-  }
+  auto issue_one = [&](int kt, int st, int j) {
+    const int q = w + NW * j;
+    if (j < LW - 1 || full)
+      lds_dma16(q * RPI < BM ? ar : br, voff[j], (uint32_t)(kt * KB * 2), lds_addr(lds + st * STAGE + q * 64));
+  };
   auto issue = [&](int kt, int st) {
 #pragma unroll
-    for (int j = 0; j < AL; ++j)
-      lds_dma16(ar, aoff[j], kt * GBK * 2, lds_addr(&As[st][(w + NW * j) * 64]));
-#pragma unroll
-    for (int j = 0; j < BL; ++j)
-      lds_dma16(br, boff[j], kt * GBK * 2, lds_addr(&Bs[st][(w + NW * j) * 64]));
+    for (int j = 0; j < LW; ++j) issue_one(kt, st, j);
   };
-  // first LDS row (B tile) of the wave's column tile j
+  auto wait_tiles = [&](int a, auto amax) {  // at most a of this wave's k-tiles still loading
+    if (full) vm_wait_tiles<LW, decltype(amax)::value>(a);
+    else vm_wait_tiles<LW - 1, decltype(amax)::value>(a);
+  };
+  // first stage row (B part) of the wave's column tile j
   auto bcol0 = [&](int j) -> int {
-    if (EPI == GEPI_SWIGLU) return (j < NI / 2 ? 0 : BN / 2) + wn * 16 * NI + (j % (NI / 2)) * 32;
-    return wn * 32 * NI + j * 32;
+    if (EPI == GEPI_SWIGLU) return BM + (j < NI / 2 ? 0 : BN / 2) + wn * 16 * NI + (j % (NI / 2)) * 32;
+    return BM + wn * 32 * NI + j * 32;
   };
 
   f32x16 acc[MI][NI];
@@ -188,14 +231,17 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_f16(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+  // One fragment: stage row r, k-chunk kc.
+  auto frag = [&](int st, int r, int kc) -> f16x8 {
+    return __builtin_bit_cast(f16x8, lds[st * STAGE + r * CPRL + gswz_slot<CPRL>(r, kc)]);
+  };
   // Fragments of k-step ks of stage st (lane: row/col lane%32, k-chunk 2*ks + lane/32).
   auto load_frags = [&](int st, int ks, f16x8 (&av)[MI], f16x8 (&bv)[NI]) {
     const int kc = ks * 2 + (lane >> 5);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) bv[j] = __builtin_bit_cast(f16x8, Bs[st][swz(bcol0(j) + (lane & 31), kc)]);
+    for (int j = 0; j < NI; ++j) bv[j] = frag(st, bcol0(j) + (lane & 31), kc);
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
-      av[i] = __builtin_bit_cast(f16x8, As[st][swz(wm * 32 * MI + i * 32 + (lane & 31), kc)]);
+    for (int i = 0; i < MI; ++i) av[i] = frag(st, wm * 32 * MI + i * 32 + (lane & 31), kc);
   };
   auto mfmas = [&](const f16x8 (&av)[MI], const f16x8 (&bv)[NI]) {
 #pragma unroll
@@ -203,54 +249,104 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_f16(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < NI; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
   };
-  // One k-tile: the fragments of the next k-step are read while the current one's MFMAs
-  // run (two register sets); `after_first` runs once the first k-step's reads are issued
-  // (the next tile's global loads go out behind them).
-  // The schedule is pinned with scheduling-group barriers: each k-step's MI*NI MFMAs
-  // alternate with the next k-step's MI+NI fragment reads (masks: 0x008 MFMA, 0x100 LDS
-  // read), so LDS latency hides under the matrix-core work of the same wave.
-  auto compute = [&](int st, auto&& after_first) {
-    static_assert(GBK / 16 == 4, "four k-steps per tile");
-    f16x8 a0[MI], b0[NI], a1[MI], b1[NI];
-    load_frags(st, 0, a0, b0);
-    after_first();
-    load_frags(st, 1, a1, b1);
-    mfmas(a0, b0);
-    load_frags(st, 2, a0, b0);
-    mfmas(a1, b1);
-    load_frags(st, 3, a1, b1);
-    mfmas(a0, b0);
-    mfmas(a1, b1);
-    // per k-step with a successor: MFMAs alternate with the next k-step's fragment reads
-    constexpr int NF = MI + NI, NM = MI * NI;
+  // Pin the schedule of n k-steps whose MFMAs each alternate with the next k-step's
+  // fragment reads (masks: 0x008 MFMA, 0x100 LDS read), so LDS latency hides under the
+  // matrix-core work of the same wave.
+  constexpr int NF = MI + NI, NM = MI * NI;
+  auto interleave = [&](auto n) {
 #pragma unroll
-    for (int ks = 0; ks < 3; ++ks) {
+    for (int ks = 0; ks < decltype(n)::value; ++ks)
 #pragma unroll
       for (int i = 0; i < NM; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (i < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
   };
 
-  constexpr int LPT = AL + BL;  // loads per wave per k-tile
-  const int nk = K / GBK;
+  const int nk = K / KB;
+  f16x8 a0[MI], b0[NI], a1[MI], b1[NI];
+  if constexpr (LATE) {
+    // All NS stages in use; the barrier sits before each tile's last k-step.
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) issue(s, s);
-  int st = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    // tile kt must have landed; tiles kt+1 .. kt+NS-2 may still be in flight
-    const int ahead = nk - 1 - kt < NS - 2 ? nk - 1 - kt : NS - 2;
-    if (NS >= 4 && ahead >= 2) vm_wait_barrier<(NS >= 4 ? 2 : 0) * LPT>();
-    else if (NS >= 3 && ahead >= 1) vm_wait_barrier<(NS >= 3 ? 1 : 0) * LPT>();
-    else vm_wait_barrier<0>();
-    const int nst = st == 0 ? NS - 1 : st - 1;
-    compute(st, [&] {
+    for (int s = 0; s < NS; ++s)
+      if (s < nk) issue(s, s);
+    wait_tiles(nk - 1, std::integral_constant<int, NS - 1>{});  // tile 0 has landed
+    lds_wait_barrier();
+    load_frags(0, 0, a0, b0);
+    int st = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      // k-steps 0 .. KS-2, each with the next k-step's fragment reads
+#pragma unroll
+      for (int ks = 0; ks + 1 < KS; ++ks) {
+        if (ks % 2 == 0) {
+          load_frags(st, ks + 1, a1, b1);
+          mfmas(a0, b0);
+        } else {
+          load_frags(st, ks + 1, a0, b0);
+          mfmas(a1, b1);
+        }
+      }
+      interleave(std::integral_constant<int, KS - 1>{});
+      // The last k-step's fragments are in set 1. Tile kt+1 landed (tiles kt+2 .. kt+NS-1
+      // may still be loading) and every wave is done reading tile kt. After the last tile
+      // the wait, the barrier and the reads of the next stage are harmless (in-bounds LDS,
+      // nothing loading), which keeps the loop body free of branches around the MFMAs.
+      wait_tiles(nk - 2 - kt, std::integral_constant<int, NS - 2>{});
+      lds_wait_barrier();
+      // The last k-step's MFMAs, the next stage's first fragment reads and this wave's
+      // loads of tile kt+NS, interleaved in program order (each load is an asm statement
+      // the scheduler does not move anything across): a burst of loads would hold up
+      // the in-order issue of the MFMAs behind it.
+      const int sn = st + 1 == NS ? 0 : st + 1;
+      const bool more = kt + NS < nk;
+#pragma unroll
+      for (int t = 0; t < NM; ++t) {
+        const int i = t / NI, j = t % NI;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[i], b1[j], acc[i][j], 0, 0, 0);
+        if (t < NI) b0[t] = frag(sn, bcol0(t) + (lane & 31), lane >> 5);
+        else if (t < NF) a0[t - NI] = frag(sn, wm * 32 * MI + (t - NI) * 32 + (lane & 31), lane >> 5);
+#pragma unroll
+        for (int r = t * LW / NM; r < (t + 1) * LW / NM; ++r)
+          if (more) issue_one(kt + NS, st, r);
+      }
+      if constexpr (NM < NF) {
+#pragma unroll
+        for (int t = NM; t < NF; ++t) {
+          if (t < NI) b0[t] = frag(sn, bcol0(t) + (lane & 31), lane >> 5);
+          else a0[t - NI] = frag(sn, wm * 32 * MI + (t - NI) * 32 + (lane & 31), lane >> 5);
+        }
+      }
+      st = sn;
+    }
+  } else {
+    // NS-1 tiles ahead; the barrier opens each tile, the stage read by the previous tile is
+    // refilled once this tile's first fragments are read.
+#pragma unroll
+    for (int s = 0; s + 1 < NS; ++s)
+      if (s < nk) issue(s, s);
+    int st = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      // tile kt landed; tiles kt+1 .. kt+NS-2 may still be loading
+      wait_tiles(nk - 1 - kt, std::integral_constant<int, NS - 2>{});
+      lds_wait_barrier();
+      const int nst = st == 0 ? NS - 1 : st - 1;
+      load_frags(st, 0, a0, b0);
       if (kt + NS - 1 < nk) issue(kt + NS - 1, nst);
-    });
-    st = st + 1 == NS ? 0 : st + 1;
+#pragma unroll
+      for (int ks = 0; ks + 1 < KS; ++ks) {
+        if (ks % 2 == 0) {
+          load_frags(st, ks + 1, a1, b1);
+          mfmas(a0, b0);
+        } else {
+          load_frags(st, ks + 1, a0, b0);
+          mfmas(a1, b1);
+        }
+      }
+      mfmas(a1, b1);
+      interleave(std::integral_constant<int, KS - 1>{});
+      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+      st = st + 1 == NS ? 0 : st + 1;
+    }
   }
 
   // ---- epilogue: acc[i][j][4*jj + ii] is (row 8*jj + 4*(lane/32) + ii, col lane%32) of tile (i, j)
@@ -425,29 +521,34 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs g) {
   }
 }
 
-// MFMA tile configurations (waves WM x WN, MI x NI 32 x 32 tiles per wave, LDS stages).
+// MFMA tile configurations (waves WM x WN, MI x NI 32 x 32 tiles per wave, LDS stages,
+// k-tile width).
 struct GemmCfg {
-  int wm, wn, mi, ni, ns;
+  int wm, wn, mi, ni, ns, kb, late;
   int bm() const { return wm * 32 * mi; }
   int bn() const { return wn * 32 * ni; }
 };
-#define PP_GEMM_CFGS(X)   \
-  X(0, 2, 4, 3, 2, 2)     \
-  X(1, 2, 4, 2, 2, 3)     \
-  X(2, 2, 4, 4, 2, 2)     \
-  X(3, 2, 2, 3, 2, 3)     \
-  X(4, 2, 2, 2, 2, 4)
+#define PP_GEMM_CFGS(X)         \
+  X(0, 2, 4, 3, 2, 2, 64, 1)    \
+  X(1, 2, 4, 2, 2, 3, 64, 0)    \
+  X(2, 2, 2, 3, 2, 3, 64, 0)    \
+  X(3, 2, 2, 2, 2, 4, 64, 0)    \
+  X(4, 2, 4, 3, 2, 2, 64, 0)    \
+  X(5, 2, 2, 3, 4, 2, 64, 1)    \
+  X(6, 2, 2, 2, 2, 4, 64, 1)    \
+  X(7, 2, 4, 2, 2, 3, 64, 1)    \
+  X(8, 2, 2, 3, 2, 3, 64, 1)
 static const GemmCfg kGemmCfgs[] = {
-#define PP_CFG_ROW(id, wm, wn, mi, ni, ns) {wm, wn, mi, ni, ns},
+#define PP_CFG_ROW(id, wm, wn, mi, ni, ns, kb, late) {wm, wn, mi, ni, ns, kb, late},
     PP_GEMM_CFGS(PP_CFG_ROW)
 #undef PP_CFG_ROW
 };
 constexpr int kNumGemmCfgs = sizeof(kGemmCfgs) / sizeof(kGemmCfgs[0]);
-// per-configuration efficiency (wider wave tiles reuse more of each LDS fragment read).
-// Four-wave tiles of 128 x 128 per wave measured slower than these eight-wave ones: with
-// one wave per SIMD nothing hides the LDS fragment reads, and their two-stage pipeline
-// does not cover the global-load latency.
-static const double kGemmEff[kNumGemmCfgs] = {1.0, 0.95, 1.0, 0.85, 0.8};
+// Per-configuration efficiency, from whole-prefill timings with one configuration forced:
+// the late-barrier 192 x 256 tile is the fastest at T = 3000 (the early one 4 % slower, the
+// four-wave 96 x 128-per-wave variant 3 %); smaller tiles re-read more weight and activation
+// k-slices per product.
+static const double kGemmEff[kNumGemmCfgs] = {1.0, 0.95, 0.85, 0.8, 0.96, 0.97, 0.8, 0.9, 0.85};
 
 static bool cfg_fits(const GemmCfg& c, const GemmArgs& g, int epi) {
   if (epi == GEPI_SWIGLU) return c.ni % 2 == 0 && g.F % (c.bn() / 2) == 0;
@@ -475,12 +576,12 @@ static int pick_cfg(const GemmArgs& g, int epi, int n_cu) {
   return best;
 }
 
-template <int EPI, int WM, int WN, int MI, int NI, int NS>
+template <int EPI, int WM, int WN, int MI, int NI, int NS, int KB, bool LATE>
 static void launch_cfg(const GemmArgs& g, hipStream_t s) {
   constexpr int BM = WM * 32 * MI, BN = WN * 32 * NI;
   const int n_tn = EPI == GEPI_SWIGLU ? g.F / (BN / 2) : g.N / BN;
   const int n_tm = (g.M + BM - 1) / BM;
-  hipLaunchKernelGGL((k_gemm_f16<EPI, WM, WN, MI, NI, NS>), dim3(n_tm * n_tn), dim3(WM * WN * 64), 0, s, g);
+  hipLaunchKernelGGL((k_gemm_f16<EPI, WM, WN, MI, NI, NS, KB, LATE>), dim3(n_tm * n_tn), dim3(WM * WN * 64), 0, s, g);
 }
 
 template <int EPI>
@@ -493,9 +594,9 @@ static hipError_t gemm_dispatch(bool bf16, const GemmArgs& g, int n_cu, hipStrea
     int c = forced >= 0 && forced < kNumGemmCfgs && cfg_fits(kGemmCfgs[forced], g, EPI) ? forced
                                                                                         : pick_cfg(g, EPI, n_cu > 0 ? n_cu : 256);
     switch (c) {
-#define PP_CFG_CASE(id, wm, wn, mi, ni, ns) \
-  case id:                                  \
-    if constexpr (EPI != GEPI_SWIGLU || ni % 2 == 0) launch_cfg<EPI, wm, wn, mi, ni, ns>(g, s); \
+#define PP_CFG_CASE(id, wm, wn, mi, ni, ns, kb, late) \
+  case id:                                            \
+    if constexpr (EPI != GEPI_SWIGLU || ni % 2 == 0) launch_cfg<EPI, wm, wn, mi, ni, ns, kb, late != 0>(g, s); \
     break;
       PP_GEMM_CFGS(PP_CFG_CASE)
 #undef PP_CFG_CASE
