@@ -190,6 +190,12 @@ struct GemmArgs {
   void* kx;
   void* vx;
   int x_pitch, xoff;
+  // bf16-weight path, GEPI_RESID / GEPI_SWIGLU: workspace for float32 split-K partial sums
+  // (part_bytes bytes); when the product has too few output tiles to fill the GPU, K is
+  // split over several workgroups per tile and the splits are added in order afterwards.
+  // NULL: never split.
+  float* part;
+  size_t part_bytes;
 };
 hipError_t launch_gemm(int epi, bool bf16, const GemmArgs& g, int n_cu, hipStream_t s);
 // float16 copy of n_elems bfloat16 values (n_elems % 8 == 0), exact

@@ -68,6 +68,8 @@ struct pp_model {
   void* pq = nullptr;          // rotated Q [H][T][dh]: bfloat16 (bf16-weight path) or float32
   void* pa = nullptr;          // attention output [T][D], same element type
   void* pg = nullptr;          // SiLU(g)*z [T][F], same element type
+  float* psplit = nullptr;     // bf16-weight path: split-K partial sums of the small-M products
+  size_t psplit_bytes = 0;
   float* prope = nullptr;      // RoPE table [T][dh] (cos, sin pairs)
   void* pvt = nullptr;         // bf16-weight path: V transposed, float16 [H][dh][vt_pitch] of a chunk's key space
   void* pkx = nullptr;         // a chunk's key space: K [H][x_pitch][dh] (wdtype)

@@ -29,7 +29,7 @@ pp_status pp_model::alloc_prefill() {
   size_t bytes = 0;
   auto take = [&](size_t n) { size_t off = bytes; bytes += (n + 255) / 256 * 256; return off; };
   const size_t oid = take(sizeof(int32_t) * (T > (size_t)max_batch ? T : (size_t)max_batch) * ns);
-  size_t ox = 0, ou = 0, oq = 0, oa = 0, og = 0, orope = 0, ovt = 0, okx = 0, ovx = 0;
+  size_t ox = 0, ou = 0, oq = 0, oa = 0, og = 0, orope = 0, ovt = 0, okx = 0, ovx = 0, osplit = 0;
   // key space of a chunk: up to context + 15 history keys (start rounded to 16) + T
   x_pitch = (int)((T + cfg.context + 16 + 63) / 64 * 64);
   vt_pitch = x_pitch;
@@ -44,6 +44,12 @@ pp_status pp_model::alloc_prefill() {
     okx = take(esz * H * x_pitch * dh);
     if (bf16) ovt = take(2 * H * dh * vt_pitch);
     else ovx = take(esz * H * x_pitch * dh);
+    if (bf16) {
+      // split-K partials of the W_O / W_out / W_in products of short chunks: up to 8
+      // splits of 256 x 4096 residual rows, 2 of 256 x 2 d_ff W_in rows at full size
+      psplit_bytes = (size_t)64 << 20;
+      osplit = take(psplit_bytes);
+    }
   }
   if (hipMalloc(&pws, bytes) != hipSuccess) return pp_fail(PP_E_HIP, "hipMalloc of prefill workspace failed");
   if (max_T > 0 && bf16) {
@@ -80,6 +86,7 @@ pp_status pp_model::alloc_prefill() {
     prope = reinterpret_cast<float*>(b + orope);
     pkx = b + okx;
     if (bf16) {
+      psplit = reinterpret_cast<float*>(b + osplit);
       pvt = b + ovt;
       // columns outside a chunk's keys are read by the attention (as zero-weighted
       // values): keep them finite
@@ -183,6 +190,7 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
 
     GemmArgs go{};
     go.A = m->pa; go.B = bf ? m->f16_o[l] : m->w_o[l]; go.M = T; go.N = D; go.K = D; go.x = m->px;
+    go.part = m->psplit; go.part_bytes = m->psplit_bytes;
     e = launch_gemm(GEPI_RESID, bf, go, m->n_cu, s);
     if (e != hipSuccess) return hip_fail("prefill W_O", e);
 
@@ -191,11 +199,13 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
 
     GemmArgs gi{};
     gi.A = m->pu; gi.B = bf ? m->f16_in[l] : m->w_in[l]; gi.M = T; gi.N = F; gi.K = D; gi.F = F; gi.s_out = m->pg;
+    gi.part = m->psplit; gi.part_bytes = m->psplit_bytes;
     e = launch_gemm(GEPI_SWIGLU, bf, gi, m->n_cu, s);
     if (e != hipSuccess) return hip_fail("prefill W_in", e);
 
     GemmArgs gw{};
     gw.A = m->pg; gw.B = bf ? m->f16_out[l] : m->w_out[l]; gw.M = T; gw.N = D; gw.K = F; gw.x = m->px;
+    gw.part = m->psplit; gw.part_bytes = m->psplit_bytes;
     e = launch_gemm(GEPI_RESID, bf, gw, m->n_cu, s);
     if (e != hipSuccess) return hip_fail("prefill W_out", e);
   }

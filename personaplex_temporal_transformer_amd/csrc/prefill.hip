@@ -185,6 +185,10 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_f16(GemmArgs g) {
 
   const int m0 = tm * BM;
   const int K = g.K;
+  // split-K: workgroup row blockIdx.y of gridDim.y takes k-tiles kt0 .. kt0+nk-1
+  const int n_split = gridDim.y, split = blockIdx.y;
+  const int kt0 = split * (K / KB) / n_split;
+  const int nk = (split + 1) * (K / KB) / n_split - kt0;
   auto brow = [&](int r) -> int {
     if (EPI == GEPI_SWIGLU) return r < BN / 2 ? tn * (BN / 2) + r : g.F + tn * (BN / 2) + (r - BN / 2);
     return tn * BN + r;
@@ -207,7 +211,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_f16(GemmArgs g) {
   auto issue_one = [&](int kt, int st, int j) {
     const int q = w + NW * j;
     if (j < LW - 1 || full)
-      lds_dma16(q * RPI < BM ? ar : br, voff[j], (uint32_t)(kt * KB * 2), lds_addr(lds + st * STAGE + q * 64));
+      lds_dma16(q * RPI < BM ? ar : br, voff[j], (uint32_t)((kt0 + kt) * KB * 2), lds_addr(lds + st * STAGE + q * 64));
   };
   auto issue = [&](int kt, int st) {
 #pragma unroll
@@ -263,7 +267,6 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_f16(GemmArgs g) {
       }
   };
 
-  const int nk = K / KB;
   f16x8 a0[MI], b0[NI], a1[MI], b1[NI];
   if constexpr (LATE) {
     // All NS stages in use; the barrier sits before each tile's last k-step.
@@ -350,6 +353,24 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_f16(GemmArgs g) {
   }
 
   // ---- epilogue: acc[i][j][4*jj + ii] is (row 8*jj + 4*(lane/32) + ii, col lane%32) of tile (i, j)
+  if (n_split > 1) {
+    // split-K: float32 partial sums part[split][row][B row]; a separate pass adds the
+    // splits in order and applies the epilogue
+    const int ncol = EPI == GEPI_SWIGLU ? 2 * g.F : g.N;
+    float* pbase = g.part + (size_t)split * g.M * ncol;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int row = m0 + wm * 32 * MI + i * 32 + 8 * jj + 4 * (lane >> 5) + ii;
+          if (row >= g.M) continue;
+#pragma unroll
+          for (int j = 0; j < NI; ++j) pbase[(size_t)row * ncol + brow(bcol0(j) - BM + (lane & 31))] = acc[i][j][4 * jj + ii];
+        }
+    return;
+  }
   if constexpr (EPI == GEPI_QKV) {
     // Half a tile at a time (128-byte-aligned column halves): the waves holding those
     // columns write their fp32 values into LDS, then every thread takes 8 consecutive
@@ -576,12 +597,67 @@ static int pick_cfg(const GemmArgs& g, int epi, int n_cu) {
   return best;
 }
 
+// Split-K sums, added in split order: x[r][c] += part[0][r][c] + part[1][r][c] + ...
+__global__ __launch_bounds__(kBlock) void k_splitk_resid(const float* __restrict__ part, float* __restrict__ x,
+                                                         long long mn, int n_split) {
+  const long long i = ((long long)blockIdx.x * kBlock + threadIdx.x) * 4;
+  if (i >= mn) return;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(part + i);
+  for (int s = 1; s < n_split; ++s) acc += *reinterpret_cast<const f32x4*>(part + (size_t)s * mn + i);
+  f32x4* xp = reinterpret_cast<f32x4*>(x + i);
+  *xp = *xp + acc;
+}
+// s_out[r][j] = SiLU(g) * z as float16, g = the split sums of B row j, z of B row F + j.
+__global__ __launch_bounds__(kBlock) void k_splitk_swiglu(const float* __restrict__ part, uint16_t* __restrict__ s_out,
+                                                          int M, int F, int n_split) {
+  const long long i = ((long long)blockIdx.x * kBlock + threadIdx.x) * 4;  // (r, j), j % 4 == 0
+  if (i >= (long long)M * F) return;
+  const long long r = i / F, j = i - r * F;
+  const size_t ms = (size_t)M * 2 * F;
+  const float* p = part + (size_t)r * 2 * F + j;
+  f32x4 gs = *reinterpret_cast<const f32x4*>(p), zs = *reinterpret_cast<const f32x4*>(p + F);
+  for (int s = 1; s < n_split; ++s) {
+    gs += *reinterpret_cast<const f32x4*>(p + s * ms);
+    zs += *reinterpret_cast<const f32x4*>(p + s * ms + F);
+  }
+  const uint32_t lo = (uint32_t)f32_to_f16(silu(gs.x) * zs.x) | ((uint32_t)f32_to_f16(silu(gs.y) * zs.y) << 16);
+  const uint32_t hi = (uint32_t)f32_to_f16(silu(gs.z) * zs.z) | ((uint32_t)f32_to_f16(silu(gs.w) * zs.w) << 16);
+  *reinterpret_cast<u32x2*>(s_out + i) = u32x2{lo, hi};
+}
+
+// Splits of K for a product with `tiles` output tiles: enough workgroups for every CU, at
+// least 4 k-tiles per split, partial sums within the workspace; 1 = no split (also for the
+// QKV epilogue, which stays fused).
+static int pick_split(int epi, const GemmArgs& g, int tiles, int n_cu) {
+  if (!g.part || epi == GEPI_QKV || tiles * 2 > n_cu) return 1;
+  const size_t ncol = epi == GEPI_SWIGLU ? 2 * (size_t)g.F : (size_t)g.N;
+  const size_t per_split = (size_t)g.M * ncol * sizeof(float);
+  int sp = n_cu / tiles;
+  sp = sp < 8 ? sp : 8;
+  const int nk = g.K / GBK;
+  while (sp > 1 && (nk / sp < 4 || per_split * sp > g.part_bytes)) --sp;
+  return sp;
+}
+
 template <int EPI, int WM, int WN, int MI, int NI, int NS, int KB, bool LATE>
-static void launch_cfg(const GemmArgs& g, hipStream_t s) {
+static hipError_t launch_cfg(const GemmArgs& g, int n_cu, hipStream_t s) {
   constexpr int BM = WM * 32 * MI, BN = WN * 32 * NI;
   const int n_tn = EPI == GEPI_SWIGLU ? g.F / (BN / 2) : g.N / BN;
   const int n_tm = (g.M + BM - 1) / BM;
-  hipLaunchKernelGGL((k_gemm_f16<EPI, WM, WN, MI, NI, NS, KB, LATE>), dim3(n_tm * n_tn), dim3(WM * WN * 64), 0, s, g);
+  const int sp = pick_split(EPI, g, n_tm * n_tn, n_cu);
+  hipLaunchKernelGGL((k_gemm_f16<EPI, WM, WN, MI, NI, NS, KB, LATE>), dim3(n_tm * n_tn, sp), dim3(WM * WN * 64), 0, s, g);
+  if (sp > 1) {
+    if (EPI == GEPI_RESID) {
+      const long long mn = (long long)g.M * g.N;
+      hipLaunchKernelGGL(k_splitk_resid, dim3((unsigned)((mn / 4 + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, g.part, g.x,
+                         mn, sp);
+    } else if (EPI == GEPI_SWIGLU) {
+      const long long mf = (long long)g.M * g.F;
+      hipLaunchKernelGGL(k_splitk_swiglu, dim3((unsigned)((mf / 4 + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, g.part,
+                         static_cast<uint16_t*>(g.s_out), g.M, g.F, sp);
+    }
+  }
+  return hipGetLastError();
 }
 
 template <int EPI>
@@ -596,7 +672,7 @@ static hipError_t gemm_dispatch(bool bf16, const GemmArgs& g, int n_cu, hipStrea
     switch (c) {
 #define PP_CFG_CASE(id, wm, wn, mi, ni, ns, kb, late) \
   case id:                                            \
-    if constexpr (EPI != GEPI_SWIGLU || ni % 2 == 0) launch_cfg<EPI, wm, wn, mi, ni, ns, kb, late != 0>(g, s); \
+    if constexpr (EPI != GEPI_SWIGLU || ni % 2 == 0) return launch_cfg<EPI, wm, wn, mi, ni, ns, kb, late != 0>(g, n_cu > 0 ? n_cu : 256, s); \
     break;
       PP_GEMM_CFGS(PP_CFG_CASE)
 #undef PP_CFG_CASE
