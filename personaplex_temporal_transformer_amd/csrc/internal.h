@@ -215,6 +215,12 @@ struct AttnPrefillArgs {
   int koff;             // key index of query 0, a multiple of 16
   int jlo;              // first key index that exists and is inside some query's window
   float scale;
+  // bf16 path: workspace for key-split partials (part_bytes bytes). When the query blocks
+  // x heads cannot fill the GPU (a short chunk over a long history), each query block's
+  // keys are split over several workgroups and a second pass combines them. NULL: never.
+  float* part;
+  size_t part_bytes;
+  int n_cu;
 };
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, bool bf16, int dh, hipStream_t s);
 

@@ -185,6 +185,7 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
       at.k = kbase; at.v = vbase; at.k_pitch = C;
     }
     at.T = T; at.H = H; at.C = C; at.koff = koff; at.jlo = jlo; at.scale = 1.0f / std::sqrt((float)dh);
+    at.part = m->psplit; at.part_bytes = m->psplit_bytes; at.n_cu = m->n_cu;
     e = launch_attn_prefill(at, bf, dh, s);
     if (e != hipSuccess) return hip_fail("prefill attention", e);
 

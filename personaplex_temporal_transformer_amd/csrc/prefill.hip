@@ -743,6 +743,9 @@ hipError_t launch_gemm(int epi, bool bf16, const GemmArgs& g, int n_cu, hipStrea
 // rescale O^T in registers only when some lane's max moved. Masks (causal, window, end of
 // sequence) are applied only on key blocks that need them; key blocks entirely in a
 // wave's future are skipped by that wave.
+// Key split (gridDim.y > 1): workgroup row y takes its share of the query block's key
+// blocks and writes the unnormalised O, the running max and the sum, float32, for
+// k_attn_combine.
 template <int DH>
 __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a) {
   constexpr int BQ = 128, BKV = 64;
@@ -805,9 +808,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a)
   const int qlast = (qb + 1) * BQ < a.T ? (qb + 1) * BQ - 1 : a.T - 1;
   int kfirst = ko + qb * BQ - a.C + 1;
   kfirst = (kfirst > a.jlo ? kfirst : a.jlo) / BKV * BKV;
-  const int nkb = (ko + qlast - kfirst) / BKV + 1;
+  const int nkb_all = (ko + qlast - kfirst) / BKV + 1;
+  const int n_split = gridDim.y, split = blockIdx.y;
+  const int kb_lo = split * nkb_all / n_split;
+  const int nkb = (split + 1) * nkb_all / n_split - kb_lo;
+  kfirst += kb_lo * BKV;
 
-  issue(kfirst, 0);
+  if (nkb > 0) issue(kfirst, 0);
   for (int kb = 0; kb < nkb; ++kb) {
     const int st = kb & 1, k0 = kfirst + kb * BKV;
     vm_wait_barrier<0>();
@@ -880,6 +887,25 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a)
 
   // ---- normalise and write: o[dt][4*jj + ii] is dim dt*32 + 8*jj + 4*hi + ii of query qi
   const float lt = l + __shfl_xor(l, 32, kWave);
+  if (n_split > 1) {
+    // partials: O [split][h][t][DH], then (max, sum) [split][h][t][2] after all the O
+    if (qi < a.T) {
+      const size_t row = ((size_t)split * a.H + h) * a.T + qi;
+      float* po = a.part + row * DH;
+#pragma unroll
+      for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          *reinterpret_cast<f32x4*>(po + dt * 32 + 8 * jj + 4 * hi) =
+              f32x4{o[dt][4 * jj], o[dt][4 * jj + 1], o[dt][4 * jj + 2], o[dt][4 * jj + 3]};
+      if (hi == 0) {
+        float* pml = a.part + (size_t)n_split * a.H * a.T * DH + row * 2;
+        pml[0] = m;
+        pml[1] = lt;
+      }
+    }
+    return;
+  }
   const float inv = 1.0f / lt;
   if (qi < a.T) {
     uint16_t* out = static_cast<uint16_t*>(a.out) + (size_t)qi * (a.H * DH) + h * DH;
@@ -893,6 +919,28 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a)
         *reinterpret_cast<u32x2*>(out + d) = u32x2{w0, w1};
       }
   }
+}
+
+// Combines the key splits of query t, head h (one thread per dimension): with M the
+// largest split max, weights w_s = 2^((m_s - M) * c), out = sum w_s O_s / sum w_s l_s.
+template <int DH>
+__global__ __launch_bounds__(DH) void k_attn_combine(AttnPrefillArgs a, int n_split) {
+  const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+  const float c = a.scale * 1.4426950408889634f;
+  const size_t plane = (size_t)a.H * a.T;
+  const float* pml = a.part + (size_t)n_split * plane * DH;
+  float mx = -INFINITY;
+  for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, pml[(s * plane + (size_t)h * a.T + t) * 2]);
+  float num = 0.f, den = 0.f;
+  for (int s = 0; s < n_split; ++s) {
+    const size_t row = s * plane + (size_t)h * a.T + t;
+    const float ms = pml[row * 2];
+    if (ms == -INFINITY) continue;  // no visible key in this split
+    const float w = __builtin_amdgcn_exp2f((ms - mx) * c);
+    num += w * a.part[row * DH + d];
+    den += w * pml[row * 2 + 1];
+  }
+  static_cast<uint16_t*>(a.out)[(size_t)t * (a.H * DH) + h * DH + d] = f32_to_f16(num / den);
 }
 
 // ---------------------------------------------------------------- float32 attention
@@ -935,10 +983,25 @@ hipError_t launch_attn_prefill(const AttnPrefillArgs& a, bool bf16, int dh, hipS
     if (!a.vt || a.T > a.C || a.koff % 16 || a.jlo < 0 || a.jlo > a.koff || a.k_pitch < a.koff + a.T ||
         a.vt_pitch < (a.koff + a.T + 63) / 64 * 64)
       return hipErrorInvalidValue;
-    const dim3 grid((a.T + 127) / 128 * a.H);
+    if (dh != 128 && dh != 64) return hipErrorInvalidValue;
+    // key splits: enough workgroups for every CU (two per CU fit), at least 4 key blocks
+    // (of 64) per split for the shortest query block, partials within the workspace
+    const int wgs = (a.T + 127) / 128 * a.H;
+    const int n_cu = a.n_cu > 0 ? a.n_cu : 256;
+    int sp = 1;
+    if (a.part && wgs * 2 <= n_cu) {
+      sp = n_cu / wgs < 8 ? n_cu / wgs : 8;
+      const int keys_min = a.koff - a.jlo + (a.T < 128 ? a.T : 128);  // keys of query block 0 (at most)
+      const size_t per_split = (size_t)a.H * a.T * (dh + 2) * sizeof(float);
+      while (sp > 1 && (keys_min / 64 / sp < 4 || per_split * sp > a.part_bytes)) --sp;
+    }
+    const dim3 grid(wgs, sp);
     if (dh == 128) hipLaunchKernelGGL(k_attn_prefill_bf16<128>, grid, dim3(256), 0, s, a);
-    else if (dh == 64) hipLaunchKernelGGL(k_attn_prefill_bf16<64>, grid, dim3(256), 0, s, a);
-    else return hipErrorInvalidValue;
+    else hipLaunchKernelGGL(k_attn_prefill_bf16<64>, grid, dim3(256), 0, s, a);
+    if (sp > 1) {
+      if (dh == 128) hipLaunchKernelGGL(k_attn_combine<128>, dim3(a.T, a.H), dim3(128), 0, s, a, sp);
+      else hipLaunchKernelGGL(k_attn_combine<64>, dim3(a.T, a.H), dim3(64), 0, s, a, sp);
+    }
   } else {
     if (a.T > a.C || a.jlo < 0 || a.jlo > a.koff || a.k_pitch < a.koff + a.T || !a.v) return hipErrorInvalidValue;
     const dim3 grid(a.T, a.H);

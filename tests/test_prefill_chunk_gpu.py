@@ -109,6 +109,27 @@ def test_tiny_bf16_chunks_match_oracle(context, sizes):
     assert max(errs) <= BF16_TOL
 
 
+def test_tiny_bf16_chunks_after_long_history_split_keys():
+    """Short chunks after a 1200-frame prefill: with few query blocks x heads the attention
+    splits each query block's keys over several workgroups and a second pass combines them
+    (and the small W_out products split K)."""
+    cfg = synth.with_(synth.TINY_TEMPORAL, context=3000)
+    sizes = [1200, 40, 7, 128]
+    W = synth.temporal_weights(cfg, 37, "bf16", with_text_head=False)
+    ids = synth.stream_ids(cfg, sum(sizes), 38)
+    model = _model(cfg, W, "bf16", max(sizes))
+    kv = model.kv_alloc()
+    h, p = _chunks(model, kv, ids, sizes)
+    want = O.forward_full(ids, W, cfg)
+    errs = []
+    q = 0
+    for T in sizes:
+        errs.append(norm_max_err(h[q:q + T], want[q:q + T]))
+        q += T
+    print("tiny bf16 chunks %s after a long history: errs %s" % (sizes, ["%.3g" % e for e in errs]))
+    assert max(errs) <= BF16_TOL
+
+
 def test_snapshot_restore_and_reprime_are_exact():
     """Store the ring after a prompt, decode, restore the snapshot with its position and
     decode the same frames again: identical bits. Reset and prefill the prompt again:
