@@ -558,7 +558,9 @@ struct GemmCfg {
   X(5, 2, 2, 3, 4, 2, 64, 1)    \
   X(6, 2, 2, 2, 2, 4, 64, 1)    \
   X(7, 2, 4, 2, 2, 3, 64, 1)    \
-  X(8, 2, 2, 3, 2, 3, 64, 1)
+  X(8, 2, 2, 3, 2, 3, 64, 1)    \
+  X(9, 1, 4, 7, 2, 2, 64, 1)    \
+  X(10, 1, 4, 7, 2, 2, 64, 0)
 static const GemmCfg kGemmCfgs[] = {
 #define PP_CFG_ROW(id, wm, wn, mi, ni, ns, kb, late) {wm, wn, mi, ni, ns, kb, late},
     PP_GEMM_CFGS(PP_CFG_ROW)
@@ -569,7 +571,7 @@ constexpr int kNumGemmCfgs = sizeof(kGemmCfgs) / sizeof(kGemmCfgs[0]);
 // the late-barrier 192 x 256 tile is the fastest at T = 3000 (the early one 4 % slower, the
 // four-wave 96 x 128-per-wave variant 3 %); smaller tiles re-read more weight and activation
 // k-slices per product.
-static const double kGemmEff[kNumGemmCfgs] = {1.0, 0.95, 0.85, 0.8, 0.96, 0.97, 0.8, 0.9, 0.85};
+static const double kGemmEff[kNumGemmCfgs] = {1.0, 0.95, 0.85, 0.8, 0.96, 0.97, 0.8, 0.9, 0.85, 1.0, 0.96};
 
 static bool cfg_fits(const GemmCfg& c, const GemmArgs& g, int epi) {
   if (epi == GEPI_SWIGLU) return c.ni % 2 == 0 && g.F % (c.bn() / 2) == 0;
