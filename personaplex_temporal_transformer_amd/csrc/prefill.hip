@@ -747,7 +747,7 @@ hipError_t launch_gemm(int epi, bool bf16, const GemmArgs& g, int n_cu, hipStrea
 // wave's future are skipped by that wave.
 // Key split (gridDim.y > 1): workgroup row y takes its share of the query block's key
 // blocks and writes the unnormalised O, the running max and the sum, float32, for
-// k_attn_combine.
+// k_attn_prefill_combine.
 template <int DH>
 __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a) {
   constexpr int BQ = 128, BKV = 64;
@@ -926,7 +926,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a)
 // Combines the key splits of query t, head h (one thread per dimension): with M the
 // largest split max, weights w_s = 2^((m_s - M) * c), out = sum w_s O_s / sum w_s l_s.
 template <int DH>
-__global__ __launch_bounds__(DH) void k_attn_combine(AttnPrefillArgs a, int n_split) {
+__global__ __launch_bounds__(DH) void k_attn_prefill_combine(AttnPrefillArgs a, int n_split) {
   const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
   const float c = a.scale * 1.4426950408889634f;
   const size_t plane = (size_t)a.H * a.T;
@@ -1001,8 +1001,8 @@ hipError_t launch_attn_prefill(const AttnPrefillArgs& a, bool bf16, int dh, hipS
     if (dh == 128) hipLaunchKernelGGL(k_attn_prefill_bf16<128>, grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL(k_attn_prefill_bf16<64>, grid, dim3(256), 0, s, a);
     if (sp > 1) {
-      if (dh == 128) hipLaunchKernelGGL(k_attn_combine<128>, dim3(a.T, a.H), dim3(128), 0, s, a, sp);
-      else hipLaunchKernelGGL(k_attn_combine<64>, dim3(a.T, a.H), dim3(64), 0, s, a, sp);
+      if (dh == 128) hipLaunchKernelGGL(k_attn_prefill_combine<128>, dim3(a.T, a.H), dim3(128), 0, s, a, sp);
+      else hipLaunchKernelGGL(k_attn_prefill_combine<64>, dim3(a.T, a.H), dim3(64), 0, s, a, sp);
     }
   } else {
     if (a.T > a.C || a.jlo < 0 || a.jlo > a.koff || a.k_pitch < a.koff + a.T || !a.v) return hipErrorInvalidValue;
