@@ -923,26 +923,44 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a)
   }
 }
 
-// Combines the key splits of query t, head h (one thread per dimension): with M the
-// largest split max, weights w_s = 2^((m_s - M) * c), out = sum w_s O_s / sum w_s l_s.
+// Combines the key splits of query t, head h: with M the largest split max, weights
+// w_s = 2^((m_s - M) * c), out = sum w_s O_s / sum w_s l_s. DH/4 threads per (head, query)
+// row, 4 dimensions each (16-byte loads); the rows h*T + t of a workgroup are consecutive.
 template <int DH>
-__global__ __launch_bounds__(DH) void k_attn_prefill_combine(AttnPrefillArgs a, int n_split) {
-  const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
-  const float c = a.scale * 1.4426950408889634f;
+__global__ __launch_bounds__(256) void k_attn_prefill_combine(AttnPrefillArgs a, int n_split) {
+  constexpr int TPR = DH / 4, RPB = 256 / TPR, SM = 8;
+  const int row = blockIdx.x * RPB + (int)threadIdx.x / TPR, d = ((int)threadIdx.x % TPR) * 4;
   const size_t plane = (size_t)a.H * a.T;
+  if ((size_t)row >= plane) return;
+  const float c = a.scale * 1.4426950408889634f;
   const float* pml = a.part + (size_t)n_split * plane * DH;
-  float mx = -INFINITY;
-  for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, pml[(s * plane + (size_t)h * a.T + t) * 2]);
-  float num = 0.f, den = 0.f;
-  for (int s = 0; s < n_split; ++s) {
-    const size_t row = s * plane + (size_t)h * a.T + t;
-    const float ms = pml[row * 2];
-    if (ms == -INFINITY) continue;  // no visible key in this split
-    const float w = __builtin_amdgcn_exp2f((ms - mx) * c);
-    num += w * a.part[row * DH + d];
-    den += w * pml[row * 2 + 1];
+  float ms[SM], ls[SM];
+  f32x4 os[SM];
+#pragma unroll
+  for (int s = 0; s < SM; ++s) {
+    const int sc = s < n_split ? s : n_split - 1;  // clamped: every load is unconditional
+    const size_t r = sc * plane + row;
+    ms[s] = pml[r * 2];
+    ls[s] = pml[r * 2 + 1];
+    os[s] = *reinterpret_cast<const f32x4*>(a.part + r * DH + d);
   }
-  static_cast<uint16_t*>(a.out)[(size_t)t * (a.H * DH) + h * DH + d] = f32_to_f16(num / den);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < SM; ++s) mx = s < n_split ? fmaxf(mx, ms[s]) : mx;
+  float den = 0.f;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < SM; ++s) {
+    if (s >= n_split || ms[s] == -INFINITY) continue;  // no visible key in this split
+    const float w = __builtin_amdgcn_exp2f((ms[s] - mx) * c);
+    num += w * os[s];
+    den += w * ls[s];
+  }
+  const float inv = 1.0f / den;
+  const int h = row / a.T, t = row - h * a.T;
+  const uint32_t lo = (uint32_t)f32_to_f16(num.x * inv) | ((uint32_t)f32_to_f16(num.y * inv) << 16);
+  const uint32_t hi = (uint32_t)f32_to_f16(num.z * inv) | ((uint32_t)f32_to_f16(num.w * inv) << 16);
+  *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + (size_t)t * (a.H * DH) + h * DH + d) = u32x2{lo, hi};
 }
 
 // ---------------------------------------------------------------- float32 attention
@@ -1001,8 +1019,9 @@ hipError_t launch_attn_prefill(const AttnPrefillArgs& a, bool bf16, int dh, hipS
     if (dh == 128) hipLaunchKernelGGL(k_attn_prefill_bf16<128>, grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL(k_attn_prefill_bf16<64>, grid, dim3(256), 0, s, a);
     if (sp > 1) {
-      if (dh == 128) hipLaunchKernelGGL(k_attn_prefill_combine<128>, dim3(a.T, a.H), dim3(128), 0, s, a, sp);
-      else hipLaunchKernelGGL(k_attn_prefill_combine<64>, dim3(a.T, a.H), dim3(64), 0, s, a, sp);
+      const long long rows = (long long)a.T * a.H;  // 8 (d_head 128) or 16 (64) rows per workgroup
+      if (dh == 128) hipLaunchKernelGGL(k_attn_prefill_combine<128>, dim3((unsigned)((rows + 7) / 8)), dim3(256), 0, s, a, sp);
+      else hipLaunchKernelGGL(k_attn_prefill_combine<64>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a, sp);
     }
   } else {
     if (a.T > a.C || a.jlo < 0 || a.jlo > a.koff || a.k_pitch < a.koff + a.T || !a.v) return hipErrorInvalidValue;
@@ -1035,31 +1054,36 @@ __global__ __launch_bounds__(kBlock) void k_gather_rows(GatherArgs a, const void
   *reinterpret_cast<u32x4*>(static_cast<T*>(dst) + ((size_t)h * a.x_pitch + j) * a.dh + c * EPC) = v;
 }
 
-// bf16 path, V transposed to float16: one thread per (head, dim, group of 8 columns);
-// column c holds key vt_perm(c), so the group's keys lie in one aligned group of 16.
-__global__ __launch_bounds__(kBlock) void k_gather_vt(GatherArgs a) {
-  const long long n = (long long)a.H * a.dh * (a.jhi / 8);
-  const long long i = (long long)blockIdx.x * kBlock + threadIdx.x;
-  if (i >= n) return;
-  const int d = (int)(i % a.dh);
-  const long long r = i / a.dh;
-  const int g = (int)(r % (a.jhi / 8)), h = (int)(r / (a.jhi / 8));
-  const uint16_t* V = static_cast<const uint16_t*>(a.vring) + (size_t)h * a.C * a.dh + d;
-  uint32_t w[4];
+// bf16 path, V transposed to float16 through LDS: one workgroup per (64 keys, head). The
+// 64 x d_head tile is read as whole key rows (16-byte loads, 16 lanes per 256-byte row) and
+// written as whole 128-byte runs of a transposed row (8 columns per thread); column c of
+// the tile holds key vt_perm(c). Keys below jlo are zero; so are the columns past jhi up to
+// the tile end, which the chunk's own V (written later by the QKV epilogue) covers.
+__global__ __launch_bounds__(256) void k_gather_vt(GatherArgs a) {
+  constexpr int P = 66;                      // LDS row pitch in halves (bank spread)
+  __shared__ uint16_t tile[128 * P];         // [d][key], d_head <= 128
+  const int j0 = blockIdx.x * 64, h = blockIdx.y, dh = a.dh, cpr = dh / 8;
+  const uint16_t* V = static_cast<const uint16_t*>(a.vring) + (size_t)h * a.C * dh;
+  for (int q = threadIdx.x; q < 64 * cpr; q += 256) {
+    const int jr = q / cpr, c = q - jr * cpr, j = j0 + jr;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (j >= a.jlo && j < a.jhi) v = *reinterpret_cast<const u32x4*>(V + (size_t)((a.q0 + j) % a.C) * dh + c * 8);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    uint32_t half[2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int key = vt_perm(g * 8 + 2 * e + x);
-      float f = 0.f;
-      if (key >= a.jlo) f = bf16_to_f32(V[(size_t)((a.q0 + key) % a.C) * a.dh]);
-      half[x] = f32_to_f16(f);
+    for (int e = 0; e < 4; ++e) {
+      tile[(c * 8 + 2 * e) * P + jr] = f32_to_f16(bf16_to_f32((uint16_t)(v[e] & 0xffffu)));
+      tile[(c * 8 + 2 * e + 1) * P + jr] = f32_to_f16(bf16_to_f32((uint16_t)(v[e] >> 16)));
     }
-    w[e] = half[0] | (half[1] << 16);
   }
-  *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.vt) + ((size_t)h * a.dh + d) * a.vt_pitch + g * 8) =
-      u32x4{w[0], w[1], w[2], w[3]};
+  __syncthreads();
+  for (int q = threadIdx.x; q < dh * 8; q += 256) {
+    const int d = q >> 3, cg = q & 7;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)tile[d * P + vt_perm(cg * 8 + 2 * e)] | ((uint32_t)tile[d * P + vt_perm(cg * 8 + 2 * e + 1)] << 16);
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.vt) + ((size_t)h * dh + d) * a.vt_pitch + j0 + cg * 8) =
+        u32x4{w[0], w[1], w[2], w[3]};
+  }
 }
 
 hipError_t launch_gather_history(const GatherArgs& a, bool bf16, hipStream_t s) {
@@ -1070,10 +1094,10 @@ hipError_t launch_gather_history(const GatherArgs& a, bool bf16, hipStream_t s) 
   const long long nr = (long long)a.H * a.jhi * (a.dh / epc);
   const dim3 gr((unsigned)((nr + kBlock - 1) / kBlock));
   if (bf16) {
-    if (!a.vt || a.vt_pitch < a.jhi) return hipErrorInvalidValue;
+    // V^T tiles of 64 columns (the last one up to a multiple of 64) inside the V^T rows
+    if (!a.vt || a.dh > 128 || (a.jhi + 63) / 64 * 64 > a.vt_pitch) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_gather_rows<uint16_t>, gr, dim3(kBlock), 0, s, a, a.kring, a.kx);
-    const long long nv = (long long)a.H * a.dh * (a.jhi / 8);
-    hipLaunchKernelGGL(k_gather_vt, dim3((unsigned)((nv + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(k_gather_vt, dim3((unsigned)((a.jhi + 63) / 64), (unsigned)a.H), dim3(256), 0, s, a);
   } else {
     if (!a.vx) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_gather_rows<float>, gr, dim3(kBlock), 0, s, a, a.kring, a.kx);
