@@ -158,7 +158,8 @@ def bench_depformer(d, dc, steps, warmup):
     torch.cuda.synchronize()
     ms = s.elapsed_time(e) / steps
     nb = depth_frame_bytes(dc)
-    return {"ms_per_frame": round(ms, 4), "frame_bytes": nb, "achieved_GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+    return {"ms_per_frame": round(ms, 4), "us_per_position": round(ms * 1000.0 / S, 2), "frame_bytes": nb,
+            "achieved_GBps": round(nb / (ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "steps": steps,
             "workload": "depth transformer, 16 positions greedy, 6 layers x 1024, window 8, bf16"}
 
@@ -200,6 +201,49 @@ def bench_generator(model, kv, d, cfg, dc, steps, warmup):
             "final_position": pos,
             "workload": "generator frame: code ring + 32-block temporal step (3000 visible keys) + text head "
                         "+ text draw (top 25, T 0.7) + 16-position depth loop with draws (top 250, T 0.8), bf16"}
+
+
+def bench_one_block(W, cfg, steps, warmup):
+    """One full-width block (layer 0's weights) as a 1-block model: ring loaded with 200
+    frames, then `steps` decode steps from position 200 (201 .. 200+steps visible keys),
+    each timed with its own event pair on graph replays. The step also runs the embedding
+    sum and the final norm (two more launches than the block itself)."""
+    import torch
+    from personaplex_temporal_transformer_amd import pp, synth
+    cfg1 = synth.with_(cfg, n_layers=1)
+    W1 = {k: v for k, v in W.items() if not k.startswith("transformer.layers.") or k.startswith("transformer.layers.0.")}
+    m1 = pp.TemporalModel(cfg1, W1, "bf16", max_prefill_T=0, max_batch=1)
+    kv1 = m1.kv_alloc()
+    n0 = 200
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    buf = torch.randn(2 * cfg["n_heads"] * n0 * cfg["d_head"], generator=g, device="cuda").to(torch.bfloat16)
+    ids = synth.stream_ids(cfg1, warmup + steps, 4)
+    h = torch.empty(cfg["d_model"], device="cuda")
+    m1.set_graph(True)
+    kv1.load(buf, n0)
+    for i in range(warmup):
+        m1.decode_step(kv1, ids[i], h)
+    kv1.load(buf, n0)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        evs[i][0].record()
+        m1.decode_step(kv1, ids[warmup + i], h)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1000.0 for a, b in evs)
+    D, F, Hh, dh = cfg["d_model"], cfg["d_ff"], cfg["n_heads"], cfg["d_head"]
+    nb = (3 * D * D + D * D + 2 * F * D + D * F) * 2 + (n0 + 1) * Hh * dh * 2 * 2 + Hh * dh * 2 * 2
+    med = float(np.median(us))
+    kv1.close()
+    m1.close()
+    return {"us_per_step_median": round(med, 2), "us_per_step_min": round(us[0], 2), "steps": steps,
+            "step_bytes_at_201_keys": nb, "achieved_GBps": round(nb / (med * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nb / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "workload": "one full-width temporal block (d_model 4096, 32 x 128 heads, d_ff 11264), bf16, "
+                        "ring loaded with 200 frames, steps at positions 200..%d, embedding sum and final norm "
+                        "included" % (n0 + steps - 1)}
 
 
 def prefill_flops(cfg, T):
@@ -418,10 +462,19 @@ def cpu_baselines(cfg, want_prefill=True, want_depth=True):
         O.final(O.decode_step(O.embed(ids[0], W, sc), cfg["context"], cache, W, sc), W, sc)
 
     t, n = _best_of(decode_frame)
+    t1 = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t1, _ = _best_of(decode_frame, 1)
+    except ImportError:
+        pass
     out["decode"] = {"value": t * 1000.0 * cfg["n_layers"] / n_l, "unit": "ms/frame", "cores": cores,
                      "kind": "oracle",
                      "sample": "one decode frame through 2 of 32 full-width blocks at 3000 visible keys "
                                "(fp64 NumPy), best of %d, scaled x16 to 32 blocks" % n}
+    if t1 is not None:
+        out["decode"]["value_1thread"] = t1 * 1000.0 * cfg["n_layers"] / n_l
     del frames, ks, vs
     if want_prefill:
         T = 256
@@ -500,7 +553,7 @@ def main():
     fill_ring(kv, cfg, 9)
     torch.cuda.synchronize()
     print("setup %.1f s" % (time.time() - t0), file=sys.stderr, flush=True)
-    ids = synth.stream_ids(cfg, args.warmup + 2 * args.steps + 4, 10)
+    ids = synth.stream_ids(cfg, args.warmup + 3 * args.steps + 4, 10)
     h = torch.empty(cfg["d_model"], device="cuda")
     C = cfg["context"]
 
@@ -525,6 +578,18 @@ def main():
     # host per-launch events); --graph 1 times graph replays and the kernel separately.
     run(args.warmup, 0, args.graph == 1)
     probe = {}
+    def run_frames(n, first, graph):
+        """n frames, each bracketed by its own event pair: per-frame ms."""
+        model.set_graph(graph)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        for i in range(n):
+            evs[i][0].record()
+            model.decode_step(kv, ids[first + i], h)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in evs]
+
     if args.graph == 1:
         ms, _ = run(args.steps, args.warmup, True)
         _, (n_tr, us_win) = run(args.steps, args.warmup, False, args.trace_layer)
@@ -532,6 +597,7 @@ def main():
     else:
         ms, (n_tr, us_win) = run(args.steps, args.warmup, False, args.trace_layer)
         mode = 0
+    per_frame = sorted(run_frames(args.steps, args.warmup + 2 * args.steps, mode == 1))
     pos, _ = kv.info()
     fb = frame_bytes(cfg, C)
     win_b = w_in_bytes(cfg)
@@ -563,8 +629,13 @@ def main():
                      "unit": "GB/s", "frac": round(achieved_win / HBM_PEAK_GBPS, 4) if achieved_win else None,
                      "traffic": measured_traffic(), "bytes_per_launch": win_b, "mean_us": round(us_win, 3),
                      "launches_timed": n_tr},
+        "frame_ms": {"median": round(float(np.median(per_frame)), 4),
+                     "p90": round(float(np.percentile(per_frame, 90)), 4),
+                     "max": round(per_frame[-1], 4), "frames": len(per_frame),
+                     "timing": "one event pair per frame around each replay (a separate pass after the timed one)"},
         "final_position": pos,
     }
+    out["one_block"] = bench_one_block(W, cfg, 20, 5)
     # the extra workloads run after the headline decode timing (a prefill burst at full
     # matrix-core load leaves the clocks lower for a while)
     dc = dict(synth.FULL_DEPTH)
