@@ -817,6 +817,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a)
   kfirst += kb_lo * BKV;
 
   if (nkb > 0) issue(kfirst, 0);
+  // Q is waited for here, once (together with the first K / V block, issued just above):
+  // passed through an empty asm statement, its registers are no longer pending loads to the
+  // compiler, which would otherwise wait on the vector-memory counter before the score
+  // products of every key block -- a counter the K / V prefetch (issued by asm, invisible to
+  // the compiler) also counts, so those waits would drain the prefetch every block.
+#pragma unroll
+  for (int ks = 0; ks < DH / 16; ++ks) asm volatile("" : "+v"(qr[ks]));
   for (int kb = 0; kb < nkb; ++kb) {
     const int st = kb & 1, k0 = kfirst + kb * BKV;
     vm_wait_barrier<0>();
@@ -836,15 +843,20 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a)
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qr[ks], s[kt], 0, 0, 0);
       }
     }
+    // masking only where the block needs it (causal, window, end of keys, first visible
+    // key); the compiler flattens this branch into selects (one range test per score)
     const bool masked = k0 + BKV - 1 > ko + qw0 || k0 < ko + qw0 + 31 - a.C + 1 || k0 + BKV > nk || k0 < a.jlo;
     if (masked) {
+      // this lane's visible keys form one range [lo, hi]: one unsigned compare per score
+      const int lo = max(a.jlo, ko + qi - a.C + 1), hi_k = min(ko + qi, nk - 1);
+      const uint32_t span = (uint32_t)(hi_k - lo);  // huge (wrapped) when the range is empty
+      const int base = k0 + 4 * hi - lo;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int key = k0 + 32 * kt + 8 * (e >> 2) + 4 * hi + (e & 3);
-          const bool ok = key <= ko + qi && ko + qi - key < a.C && key < nk && key >= a.jlo;
-          s[kt][e] = ok ? s[kt][e] : -INFINITY;
+          const uint32_t off = (uint32_t)(base + 32 * kt + 8 * (e >> 2) + (e & 3));
+          s[kt][e] = (hi_k >= lo && off <= span) ? s[kt][e] : -INFINITY;
         }
     }
     float mb = s[0][0];
