@@ -742,7 +742,8 @@ hipError_t launch_gemm(int epi, bool bf16, const GemmArgs& g, int n_cu, hipStrea
 //                 of this product runs over the keys in the order the lane holds them,
 //                 which is the column order of the transposed V copy).
 // Softmax in base 2 with the 1/sqrt(d) scale folded into one FMA; the running max/sum
-// rescale O^T in registers only when some lane's max moved. Masks (causal, window, end of
+// rescale O^T in registers only when some lane's block max exceeds the reference max by
+// more than 8 (base-2 exponent units), so most key blocks skip it. Masks (causal, window, end of
 // sequence) are applied only on key blocks that need them; key blocks entirely in a
 // wave's future are skipped by that wave.
 // Key split (gridDim.y > 1): workgroup row y takes its share of the query block's key
@@ -866,17 +867,21 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a)
       for (int e = 0; e < 16; ++e) mb = fmaxf(mb, s[kt][e]);
     mb = fmaxf(mb, __shfl_xor(mb, 32, kWave));
     const float mn = fmaxf(m, mb);
-    const float mref = mn == -INFINITY ? 0.f : mn;  // rows with nothing visible yet
-    const float sc = __builtin_amdgcn_exp2f((m - mref) * c);
-    if (__ballot(mn != m)) {
+    // Lazy rescaling: the reference max m moves (and O, l are rescaled) only when some
+    // lane's block max exceeds it by more than 2^8 in probability terms, so p <= 256
+    // (exact in float16 to the same relative precision) and the final O / l is unchanged.
+    // Also taken while m is -inf (the comparison with NaN fails).
+    if (__ballot(!((mn - m) * c <= 8.f))) {
+      const float mref = mn == -INFINITY ? 0.f : mn;  // rows with nothing visible yet
+      const float sc = __builtin_amdgcn_exp2f((m - mref) * c);
       l *= sc;
 #pragma unroll
       for (int dt = 0; dt < DH / 32; ++dt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[dt][e] *= sc;
+      m = mn;
     }
-    m = mn;
-    const float moff = -mref * c;
+    const float moff = -(m == -INFINITY ? 0.f : m) * c;
 
     // ---- P^T (bf16) and O^T += V^T P^T, 16 keys per step
 #pragma unroll
