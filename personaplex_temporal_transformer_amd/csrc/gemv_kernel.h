@@ -116,64 +116,89 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, int g, const float (
 // Depth attention for every head into x (element i stored at xpos(i)): scores
 // q.k * scale over the keys of positions [aq_pos - awin + 1, aq_pos] (clipped at 0),
 // softmax with max subtraction, then the weighted sum of values. Wave w takes heads w,
-// w + nw, ...; lane l holds head dimensions l and l + 64 (d_head <= 128), so every q, K
-// and V read is a coalesced row segment. Keys go in batches of 8 (one batch for the usual
-// window of 8) whose K and V reads are all issued together; each score is a wave-wide sum
-// (every lane gets the same bits) and the softmax runs online across batches.
+// w + nw, ... two at a time (head pairs w + 2p*nw, w + (2p+1)*nw), issuing both heads' q,
+// K and V reads before either head's reductions, so the pair costs one memory latency;
+// lane l holds head dimensions l and l + 64 (d_head <= 128), so every q, K and V read is a
+// coalesced row segment. Keys go in batches of 8 (one batch for the usual window of 8) whose
+// K and V reads are all issued together; each score is a wave-wide sum (every lane gets the
+// same bits) and the softmax runs online across batches. Per head the arithmetic and its
+// order do not depend on the pairing.
 template <class XPos>
 __device__ void depth_attention(const GemvArgs& a, float* x, XPos xpos) {
-  constexpr int KB = 8;
+  constexpr int KB = 8, HP = 2;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int k0 = a.aq_pos - a.awin + 1 > 0 ? a.aq_pos - a.awin + 1 : 0;
   const int nk = a.aq_pos - k0 + 1;
   const int dh = a.adh;
   const bool on0 = lane < dh, on1 = lane + 64 < dh;
-  for (int h = w; h < a.aH; h += nw) {
-    const float* qh = a.aq + h * dh;
-    const float* kh = a.ak + ((size_t)h * a.acap + k0) * dh;
-    const float* vh = a.av + ((size_t)h * a.acap + k0) * dh;
-    const float q0 = on0 ? qh[lane] : 0.f, q1 = on1 ? qh[lane + 64] : 0.f;
-    float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-    for (int jb = 0; jb < nk; jb += KB) {
-      float kv0[KB], kv1[KB], vv0[KB], vv1[KB];
+  for (int hb = w; hb < a.aH; hb += HP * nw) {
+    bool hv[HP];
+    const float* kh[HP];
+    const float* vh[HP];
+    float q0[HP], q1[HP], m[HP], l[HP], o0[HP], o1[HP];
 #pragma unroll
-      for (int b = 0; b < KB; ++b) {
-        const int j = jb + b;
-        const bool ok = j < nk;
-        kv0[b] = ok && on0 ? kh[j * dh + lane] : 0.f;
-        kv1[b] = ok && on1 ? kh[j * dh + lane + 64] : 0.f;
-        vv0[b] = ok && on0 ? vh[j * dh + lane] : 0.f;
-        vv1[b] = ok && on1 ? vh[j * dh + lane + 64] : 0.f;
-      }
-      float sc[KB];
-      float mb = -INFINITY;
-#pragma unroll
-      for (int b = 0; b < KB; ++b) {
-        sc[b] = -INFINITY;
-        if (jb + b < nk) {
-          sc[b] = wave_sum(q0 * kv0[b] + q1 * kv1[b]) * a.ascale;
-          mb = fmaxf(mb, sc[b]);
-        }
-      }
-      const float mn = fmaxf(m, mb);                       // finite: the batch has >= 1 key
-      const float r = m == -INFINITY ? 0.f : expf(m - mn);  // rescale of the earlier batches
-      l *= r;
-      o0 *= r;
-      o1 *= r;
-#pragma unroll
-      for (int b = 0; b < KB; ++b) {
-        if (jb + b < nk) {
-          const float p = expf(sc[b] - mn);
-          l += p;
-          o0 += p * vv0[b];
-          o1 += p * vv1[b];
-        }
-      }
-      m = mn;
+    for (int u = 0; u < HP; ++u) {
+      const int h = hb + u * nw;
+      hv[u] = h < a.aH;
+      const int hc = hv[u] ? h : hb;  // a missing second head reads the first one's rows
+      const float* qh = a.aq + hc * dh;
+      kh[u] = a.ak + ((size_t)hc * a.acap + k0) * dh;
+      vh[u] = a.av + ((size_t)hc * a.acap + k0) * dh;
+      q0[u] = on0 ? qh[lane] : 0.f;
+      q1[u] = on1 ? qh[lane + 64] : 0.f;
+      m[u] = -INFINITY;
+      l[u] = o0[u] = o1[u] = 0.f;
     }
-    const float inv = 1.0f / l;
-    if (on0) x[xpos(h * dh + lane)] = o0 * inv;
-    if (on1) x[xpos(h * dh + lane + 64)] = o1 * inv;
+    for (int jb = 0; jb < nk; jb += KB) {
+      float kv0[HP][KB], kv1[HP][KB], vv0[HP][KB], vv1[HP][KB];
+#pragma unroll
+      for (int u = 0; u < HP; ++u)
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+          const int j = jb + b;
+          const bool ok = j < nk;
+          kv0[u][b] = ok && on0 ? kh[u][j * dh + lane] : 0.f;
+          kv1[u][b] = ok && on1 ? kh[u][j * dh + lane + 64] : 0.f;
+          vv0[u][b] = ok && on0 ? vh[u][j * dh + lane] : 0.f;
+          vv1[u][b] = ok && on1 ? vh[u][j * dh + lane + 64] : 0.f;
+        }
+#pragma unroll
+      for (int u = 0; u < HP; ++u) {
+        float sc[KB];
+        float mb = -INFINITY;
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+          sc[b] = -INFINITY;
+          if (jb + b < nk) {
+            sc[b] = wave_sum(q0[u] * kv0[u][b] + q1[u] * kv1[u][b]) * a.ascale;
+            mb = fmaxf(mb, sc[b]);
+          }
+        }
+        const float mn = fmaxf(m[u], mb);                          // finite: the batch has >= 1 key
+        const float r = m[u] == -INFINITY ? 0.f : expf(m[u] - mn);  // rescale of the earlier batches
+        l[u] *= r;
+        o0[u] *= r;
+        o1[u] *= r;
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+          if (jb + b < nk) {
+            const float p = expf(sc[b] - mn);
+            l[u] += p;
+            o0[u] += p * vv0[u][b];
+            o1[u] += p * vv1[u][b];
+          }
+        }
+        m[u] = mn;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < HP; ++u) {
+      if (!hv[u]) continue;
+      const int h = hb + u * nw;
+      const float inv = 1.0f / l[u];
+      if (on0) x[xpos(h * dh + lane)] = o0[u] * inv;
+      if (on1) x[xpos(h * dh + lane + 64)] = o1[u] * inv;
+    }
   }
 }
 
