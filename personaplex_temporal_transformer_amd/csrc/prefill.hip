@@ -5,13 +5,13 @@
 // -> W_O + residual -> RMSNorm -> W_in -> SiLU(g) * z -> W_out + residual.
 //
 // bf16 path: the matrix products are dense, so they run on the CDNA4 matrix cores
-// (fp32 accumulation). The weights are bfloat16; the activations of the four projections
-// enter as float16 (11-bit significand: eight times less rounding than bfloat16, at the
-// same matrix-core rate; v_mfma_f32_32x32x16_f16), and the bfloat16 weight fragments are
-// widened to float16 in registers -- exact for bfloat16 values in float16's normal range,
-// which covers weights of this scale. In attention, Q K^T is a bfloat16 product (keys are
-// bfloat16 in the ring, shared with decode) and P V a float16 one (P and the transposed V
-// copy in float16). Statistics and the residual stream stay fp32.
+// (fp32 accumulation). The activations of the four projections enter as float16 (11-bit
+// significand: eight times less rounding than bfloat16, at the same matrix-core rate;
+// v_mfma_f32_32x32x16_f16), and so do the weights, from a float16 copy of every bfloat16
+// matrix made once at model creation -- exact for bfloat16 values in float16's normal
+// range, which covers weights of this scale. In attention, Q K^T is a bfloat16 product (keys
+// are bfloat16 in the ring, shared with decode) and P V a float16 one (P and the transposed
+// V copy in float16). Statistics and the residual stream stay fp32.
 // float32 path (small shapes, fp32 parity): plain FMA kernels with the same epilogues.
 #include <stdlib.h>
 
@@ -142,6 +142,9 @@ __device__ __forceinline__ void lds_wait_barrier() { asm volatile("s_waitcnt lgk
 //     with tile kt+NS, and tile kt+1's first fragments are read under the last k-step's
 //     matrix products.
 // Rows of A past M read as zeros (out of the buffer's range) and are not stored.
+// Split-K (gridDim.y > 1): workgroup row y takes its share of the k-tiles and writes
+// float32 partial sums part[y][row][B row] in place of the epilogue (k_splitk_resid /
+// k_splitk_swiglu add the splits in order and apply it).
 // GEPI_SWIGLU: the B tile holds W_in rows j0..j0+BN/2-1 (g) and F+j0.. (z); wave (wm, wn)
 // multiplies g rows wn*16*NI.. (NI/2 tiles) and the z rows BN/2 + wn*16*NI.., so g and z
 // of one output share a lane.
