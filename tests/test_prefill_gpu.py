@@ -152,3 +152,22 @@ def test_full_width_bf16_prefill_two_blocks():
     e_pre, e_dec = norm_max_err(h, want[:293]), norm_max_err(h1.cpu().numpy(), want[293])
     print("full-width bf16 prefill: err %.3g, decode after prefill: err %.3g" % (e_pre, e_dec))
     assert e_pre <= BF16_TOL and e_dec <= BF16_TOL
+
+
+def test_full_width_bf16_short_chunk_splits_k():
+    """Two 4096-wide blocks with d_ff 2048: a 300-frame prefill, then a 100-frame chunk. At
+    these row counts the W_in product (32-96 output tiles) and W_O / W_out (32-96) have too
+    few tiles for the GPU, so K is split over several workgroups per tile: SiLU(g)*z and the
+    residual formed from float32 partials summed in split order. Against the oracle's full
+    forward."""
+    cfg = synth.with_(synth.FULL_TEMPORAL, n_layers=2, d_ff=2048)
+    W = synth.temporal_weights(cfg, 29, "bf16", with_text_head=False, shared_layer=True)
+    ids = synth.stream_ids(cfg, 400, 30)
+    model = _model(cfg, W, "bf16", 300)
+    kv = model.kv_alloc()
+    h0 = _prefill(model, kv, ids[:300])
+    h1 = _prefill(model, kv, ids[300:])
+    want = O.forward_full(ids, W, cfg)
+    e0, e1 = norm_max_err(h0, want[:300]), norm_max_err(h1, want[300:])
+    print("full-width bf16, d_ff 2048: prefill err %.3g, 100-frame chunk err %.3g" % (e0, e1))
+    assert e0 <= BF16_TOL and e1 <= BF16_TOL
