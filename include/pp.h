@@ -101,7 +101,8 @@ typedef struct pp_kv pp_kv;
  * not copied, except that max_batch > 1 keeps one copy of every matrix (and the text
  * head) rearranged for the batched products (13.4 GB at full size), and max_prefill_T > 0
  * with bf16 weights keeps a float16 copy of every block matrix for the prefill's
- * matrix-core products (13.15 GB), both made here. */
+ * matrix-core products (13.15 GB), both made here, plus 64 MB for the split-K and key-split
+ * partial sums of short prefill chunks. */
 pp_status pp_temporal_create(const pp_temporal_config* cfg, const pp_temporal_weights* w,
                              int32_t max_batch, int32_t max_prefill_T, pp_model** out);
 pp_status pp_temporal_destroy(pp_model* m);
