@@ -455,6 +455,39 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_f16(GemmArgs g) {
         }
       }
     }
+  } else if constexpr (EPI == GEPI_RESID) {
+    // x += C, one row of 32 x 32 tiles (i) at a time: its NI*16 residual values per lane are
+    // all loaded before the first of its stores (the loads are independent; interleaved with
+    // stores to the same array they would wait one memory round trip per pair), then added
+    // and stored. Lanes 0-31 / 32-63 cover 32 consecutive columns of one row (128-byte runs).
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      float xv[NI][16];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int row = m0 + wm * 32 * MI + i * 32 + 8 * jj + 4 * (lane >> 5) + ii;
+          const int rc = row < g.M ? row : g.M - 1;  // clamped: the loads are unconditional
+#pragma unroll
+          for (int j = 0; j < NI; ++j) {
+            const int col = tn * BN + wn * 32 * NI + j * 32 + (lane & 31);
+            xv[j][4 * jj + ii] = g.x[(size_t)rc * g.N + col];
+          }
+        }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int row = m0 + wm * 32 * MI + i * 32 + 8 * jj + 4 * (lane >> 5) + ii;
+          if (row >= g.M) continue;
+#pragma unroll
+          for (int j = 0; j < NI; ++j) {
+            const int col = tn * BN + wn * 32 * NI + j * 32 + (lane & 31);
+            g.x[(size_t)row * g.N + col] = xv[j][4 * jj + ii] + acc[i][j][4 * jj + ii];
+          }
+        }
+    }
   } else {
 #pragma unroll
   for (int i = 0; i < MI; ++i)
