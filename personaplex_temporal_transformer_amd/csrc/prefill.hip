@@ -400,8 +400,29 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_f16(GemmArgs g) {
               if (cl >= 0 && cl < HALF) T[rl * TPF + cl] = acc[i][j][4 * jj + ii];
             }
           }
+      // thread tid takes items idx = tid + it*NW*64 (row idx / CPR, 8-column chunk idx % CPR);
+      // the RoPE table values of all its items are loaded before the first store (loads
+      // interleaved with the stores would wait one memory round trip per item)
+      constexpr int NIT = (BM * CPR + NW * 64 - 1) / (NW * 64);
+      f32x4 rc0[NIT], rc1[NIT];
+      if (sec < 2) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          const int idx = tid + it * NW * 64;
+          const int rl = idx / CPR, c = idx - rl * CPR;
+          const int row = m0 + rl < g.M ? m0 + rl : g.M - 1;  // clamped: in-bounds, unused
+          const int wcol = tn * BN + half * HALF + c * 8 - sec * g.D;
+          const int d = wcol % g.dh;
+          const float* rp = g.rope + (size_t)row * g.dh + d;
+          rc0[it] = idx < BM * CPR ? *reinterpret_cast<const f32x4*>(rp) : f32x4{0.f, 0.f, 0.f, 0.f};
+          rc1[it] = idx < BM * CPR ? *reinterpret_cast<const f32x4*>(rp + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
       __syncthreads();
-      for (int idx = tid; idx < BM * CPR; idx += NW * 64) {
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int idx = tid + it * NW * 64;
+        if (idx >= BM * CPR) continue;
         const int rl = idx / CPR, c = idx - rl * CPR;
         const int row = m0 + rl;
         if (row >= g.M) continue;
@@ -411,8 +432,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_f16(GemmArgs g) {
         const f32x4 hi = *reinterpret_cast<const f32x4*>(T + rl * TPF + c * 8 + 4);
         float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         if (sec < 2) {
-          const f32x4 c0 = *reinterpret_cast<const f32x4*>(g.rope + (size_t)row * g.dh + d);
-          const f32x4 c1 = *reinterpret_cast<const f32x4*>(g.rope + (size_t)row * g.dh + d + 4);
+          const f32x4 c0 = rc0[it], c1 = rc1[it];
           const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
