@@ -349,10 +349,14 @@ pp_status pp_temporal_set_graph(pp_model* m, int32_t enable);
 
 /* Kernel timing for roofline reports: when layer >= 0, every decode step brackets the
  * W_in (RMSNorm + gate/linear projection + SiLU product) kernel of that layer with HIP
- * events on the caller's stream; pp_temporal_trace_read synchronises those events and
- * returns their count and mean duration in microseconds, then clears them. layer = -1
- * turns timing off. At most 4096 bracketed launches are kept. */
-pp_status pp_temporal_trace(pp_model* m, int32_t layer);
+ * events on the caller's stream. With repeat > 1 that kernel is launched `repeat` times
+ * back to back between the two events (it reads the residual and rewrites the same
+ * SwiGLU output, so the step's result is unchanged; only the step's time grows), which
+ * spreads the events' own cost over the launches. pp_temporal_trace_read synchronises the
+ * events and returns the number of timed launches (brackets x repeat) and the mean time
+ * per launch in microseconds, then clears them. layer = -1 turns timing off; repeat must
+ * be in [1, 64]. At most 2048 brackets are kept. */
+pp_status pp_temporal_trace(pp_model* m, int32_t layer, int32_t repeat);
 pp_status pp_temporal_trace_read(pp_model* m, int64_t* count, double* mean_us);
 
 #ifdef __cplusplus

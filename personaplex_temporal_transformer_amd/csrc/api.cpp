@@ -421,6 +421,8 @@ hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long 
     gi.W = w_in[l]; gi.x = x; gi.alpha = norm2[l]; gi.eps = (float)c.eps; gi.K = D;
     gi.n_groups = F; gi.out = this->s; gi.F = F;
     e = launch_gemv(PRO_RMSNORM, EPI_SWIGLU, bf16, 2, gi, gemv_blocks, s);
+    for (int r = 1; tr && r < trace_repeat && e == hipSuccess; ++r)
+      e = launch_gemv(PRO_RMSNORM, EPI_SWIGLU, bf16, 2, gi, gemv_blocks, s);
     if (tr) {
       (void)hipEventRecord(trace_ev[trace_used + 1], s);
       trace_used += 2;
@@ -609,15 +611,17 @@ pp_status pp_model::decode_batched(pp_kv* kv, const int32_t* ids_host, float* h_
 
 // ------------------------------------------------------------------ kernel timing
 
-extern "C" pp_status pp_temporal_trace(pp_model* m, int32_t layer) {
+extern "C" pp_status pp_temporal_trace(pp_model* m, int32_t layer, int32_t repeat) {
   if (!m) return pp_fail(PP_E_ARG, "model is NULL");
   if (layer >= m->cfg.n_layers) return pp_fail(PP_E_ARG, "layer out of range");
+  if (repeat < 1 || repeat > 64) return pp_fail(PP_E_ARG, "repeat outside [1, 64]");
   if (layer >= 0 && m->trace_ev.empty()) {
     m->trace_ev.resize(4096);
     for (auto& ev : m->trace_ev)
       if (hipEventCreate(&ev) != hipSuccess) return pp_fail(PP_E_HIP, "hipEventCreate failed");
   }
   m->trace_layer = layer < 0 ? -1 : layer;
+  m->trace_repeat = repeat;
   m->trace_used = 0;
   return PP_OK;
 }
@@ -634,8 +638,8 @@ extern "C" pp_status pp_temporal_trace_read(pp_model* m, int64_t* count, double*
     tot += ms;
     ++n;
   }
-  *count = n;
-  *mean_us = n ? tot * 1000.0 / n : 0.0;
+  *count = n * m->trace_repeat;
+  *mean_us = n ? tot * 1000.0 / ((double)n * m->trace_repeat) : 0.0;
   m->trace_used = 0;
   return PP_OK;
 }

@@ -102,6 +102,7 @@ struct pp_model {
   bool use_graph = true;
   int graph_gen = 0;
   int trace_layer = -1;
+  int trace_repeat = 1;
   std::vector<hipEvent_t> trace_ev;
   size_t trace_used = 0;
 

@@ -112,7 +112,7 @@ def load():
         "pp_depformer_step": [VP, VP, P(I32), P(I32), I32, VP, VP, VP],
         "pp_temporal_set_graph": [VP, I32],
         "pp_depformer_set_graph": [VP, I32],
-        "pp_temporal_trace": [VP, I32],
+        "pp_temporal_trace": [VP, I32, I32],
         "pp_temporal_trace_read": [VP, P(I64), P(ctypes.c_double)],
         "pp_sample_top_k": [VP, I32, I32, ctypes.c_float, I32, VP, VP, VP],
         "pp_generator_create": [VP, VP, VP, P(GeneratorConfig), P(VP)],
@@ -255,8 +255,8 @@ class TemporalModel:
     def set_visible(self, n_visible):
         _check(load().pp_readers_set_visible(self.handle, int(n_visible)))
 
-    def trace(self, layer):
-        _check(load().pp_temporal_trace(self.handle, int(layer)))
+    def trace(self, layer, repeat=1):
+        _check(load().pp_temporal_trace(self.handle, int(layer), int(repeat)))
 
     def trace_read(self):
         n, us = ctypes.c_int64(), ctypes.c_double()

@@ -75,6 +75,31 @@ def test_graph_and_direct_launch_are_bit_identical_and_reset_replays():
     assert np.array_equal(a, b)
 
 
+def test_kernel_timing_repeats_leave_the_result_unchanged():
+    """Timing brackets around layer 1's W_in kernel, one launch or five back to back per
+    event pair: the steps' outputs are bit-identical to untimed steps (the kernel rewrites
+    the same SwiGLU output from the same residual), the count is brackets x repeat, and the
+    repeat count is validated."""
+    cfg = synth.TINY_TEMPORAL
+    W = synth.temporal_weights(cfg, 5, "fp32")
+    ids = synth.stream_ids(cfg, 6, 6)
+    model, _ = _model(cfg, W, "fp32")
+    kv = model.kv_alloc()
+    model.set_graph(True)
+    want, _ = _decode_all(model, kv, ids, with_logits=False)
+    for repeat in (1, 5):
+        kv.reset()
+        model.trace(1, repeat)
+        got, _ = _decode_all(model, kv, ids, with_logits=False)
+        n, us = model.trace_read()
+        model.trace(-1)
+        assert np.array_equal(got, want)
+        assert n == ids.shape[0] * repeat and us > 0
+    for bad in (0, 65):
+        with pytest.raises(pp.PPError):
+            model.trace(1, bad)
+
+
 def test_invalid_ids_rejected_before_enqueue():
     import torch
     cfg = synth.TINY_TEMPORAL
