@@ -144,8 +144,9 @@ pp_status pp_model::alloc_decode(int D, int F, int H, int dh) {
   const size_t orp = take(sizeof(float) * dh);
   // batched decode: per-session residuals, queries, float16 activations, attention partials
   const size_t nb = max_batch > 1 ? (size_t)max_batch : 0;
+  const size_t nb16 = (nb + 15) / 16 * 16;   // float16 operands in whole 16-session fragment tiles
   const size_t obx = take(sizeof(float) * nb * D), obq = take(sizeof(float) * nb * D);
-  const size_t obu = take(2 * nb * D), obo = take(2 * nb * D), obs = take(2 * nb * F);
+  const size_t obu = take(2 * nb16 * D), obo = take(2 * nb16 * D), obs = take(2 * nb16 * F);
   const size_t obp = take(sizeof(float) * nb * H * S * dh), obm = take(sizeof(float) * nb * H * S * 2);
   if (hipMalloc(&ws, bytes) != hipSuccess) return pp_fail(PP_E_HIP, "hipMalloc of decode workspace failed");
   if (hipMemset(ws, 0, bytes) != hipSuccess) return pp_fail(PP_E_HIP, "hipMemset of decode workspace failed");
@@ -519,7 +520,7 @@ pp_status pp_model::decode(pp_kv* kv, const int32_t* ids_host, const int32_t* id
   pp_status st = run_layers(kv, s);
   if (st) return st;
 
-  e = launch_rmsnorm_rows(x, out_norm, (float)c.eps, c.d_model, 1, h_out_dev, nullptr, s);
+  e = launch_rmsnorm_rows(x, out_norm, (float)c.eps, c.d_model, 1, h_out_dev, nullptr, false, s);
   if (e == hipSuccess && text_logits_dev) {
     GemvArgs g{};
     g.W = text_head; g.x = x; g.alpha = out_norm; g.eps = (float)c.eps; g.K = c.d_model;
@@ -549,7 +550,7 @@ hipError_t pp_model::enqueue_layers_batched(pp_kv* kv, hipStream_t s, long long 
   for (int l = 0; l < c.n_layers && e == hipSuccess; ++l) {
     char* kbase = static_cast<char*>(kv->ring) + (size_t)(2 * l) * per_kv;
     char* vbase = kbase + per_kv;
-    if ((e = launch_rmsnorm_rows(bx, norm1[l], (float)c.eps, D, B, nullptr, bu16, s)) != hipSuccess) break;
+    if ((e = launch_rmsnorm_rows(bx, norm1[l], (float)c.eps, D, B, nullptr, bu16, true, s)) != hipSuccess) break;
     SgemmArgs g{};
     g.act = bu16; g.W = pk_qkv[l]; g.B = B; g.K = D; g.N = 3 * D;
     g.q_out = bq; g.kc = kbase; g.vc = vbase; g.kv_bstride = bstride; g.rope = rope; g.state = state;
@@ -563,7 +564,7 @@ hipError_t pp_model::enqueue_layers_batched(pp_kv* kv, hipStream_t s, long long 
     SgemmArgs go{};
     go.act = bo16; go.W = pk_o[l]; go.B = B; go.K = D; go.N = D; go.x = bx;
     if ((e = launch_sgemm(SEPI_RESID, go, s)) != hipSuccess) break;
-    if ((e = launch_rmsnorm_rows(bx, norm2[l], (float)c.eps, D, B, nullptr, bu16, s)) != hipSuccess) break;
+    if ((e = launch_rmsnorm_rows(bx, norm2[l], (float)c.eps, D, B, nullptr, bu16, true, s)) != hipSuccess) break;
     SgemmArgs gi{};
     gi.act = bu16; gi.W = pk_in[l]; gi.B = B; gi.K = D; gi.N = F; gi.F = F; gi.s_out = bs16;
     if ((e = launch_sgemm(SEPI_SWIGLU, gi, s)) != hipSuccess) break;
@@ -598,7 +599,7 @@ pp_status pp_model::decode_batched(pp_kv* kv, const int32_t* ids_host, float* h_
   hipError_t e = launch_embed(a, bf16, s);
   if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("embed: ") + hipGetErrorString(e));
   if ((st = run_layers(kv, s))) return st;
-  e = launch_rmsnorm_rows(bx, out_norm, (float)c.eps, D, B, h_out_dev, text_logits_dev ? bu16 : nullptr, s);
+  e = launch_rmsnorm_rows(bx, out_norm, (float)c.eps, D, B, h_out_dev, text_logits_dev ? bu16 : nullptr, true, s);
   if (e == hipSuccess && text_logits_dev) {
     SgemmArgs g{};
     g.act = bu16; g.W = pk_head; g.B = B; g.K = D; g.N = c.text_vocab - 1; g.out = text_logits_dev;

@@ -61,9 +61,8 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(AttnDecodeArgs a) {
     L += w * pml[2 * i + 1];
     o += w * po[i * DH + t];
   }
-  const size_t oi = b * a.H * DH + h * DH + t;
-  if (a.out16) a.out16[oi] = f32_to_f16(o / L);
-  else a.out[oi] = o / L;
+  if (a.out16) a.out16[frag_act_index((int)b, h * DH + t, a.H * DH)] = f32_to_f16(o / L);
+  else a.out[b * a.H * DH + h * DH + t] = o / L;
 }
 
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, bool bf16, int dh, hipStream_t s) {

@@ -70,11 +70,12 @@ hipError_t launch_embed(const EmbedArgs& a, bool bf16, hipStream_t s) {
 }
 
 // One block per row; float32 statistics; writes float32 and/or float16 output (the
-// float16 rows are the activation operand of the prefill's matrix products).
+// float16 rows are the activation operand of the prefill's matrix products, row-major, or
+// with f16_frag set of the batched decode's skinny products, in their fragment order).
 __global__ __launch_bounds__(kBlock) void k_rmsnorm_rows(const float* __restrict__ x,
                                                          const float* __restrict__ alpha, float eps,
                                                          int D, float* __restrict__ out_f32,
-                                                         uint16_t* __restrict__ out_f16) {
+                                                         uint16_t* __restrict__ out_f16, int f16_frag) {
   __shared__ float red[4];
   const float* xr = x + (size_t)blockIdx.x * D;
   float ss = 0.f;
@@ -91,15 +92,18 @@ __global__ __launch_bounds__(kBlock) void k_rmsnorm_rows(const float* __restrict
     if (out_f16) {
       const uint32_t lo = (uint32_t)f32_to_f16(y.x) | ((uint32_t)f32_to_f16(y.y) << 16);
       const uint32_t hi = (uint32_t)f32_to_f16(y.z) | ((uint32_t)f32_to_f16(y.w) << 16);
-      *reinterpret_cast<uint2*>(out_f16 + (size_t)blockIdx.x * D + i) = make_uint2(lo, hi);
+      // four consecutive k (i % 4 == 0) stay within one 8-value fragment run
+      const size_t oi = f16_frag ? frag_act_index((int)blockIdx.x, i, D) : (size_t)blockIdx.x * D + i;
+      *reinterpret_cast<uint2*>(out_f16 + oi) = make_uint2(lo, hi);
     }
   }
 }
 
 hipError_t launch_rmsnorm_rows(const float* x, const float* alpha, float eps, int D, int rows,
-                               float* out_f32, void* out_f16, hipStream_t s) {
+                               float* out_f32, void* out_f16, bool f16_frag, hipStream_t s) {
+  if (f16_frag && D % 32) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_rmsnorm_rows, dim3(rows), dim3(kBlock), 0, s, x, alpha, eps, D, out_f32,
-                     static_cast<uint16_t*>(out_f16));
+                     static_cast<uint16_t*>(out_f16), f16_frag ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -100,7 +100,7 @@ struct AttnDecodeArgs {
   // several sessions at one position (batched decode): session b's query, ring and
   // partials follow at b * H*dh floats, b * kv_bstride elements and b * H*S*(dh | 2)
   // floats; the combine kernel writes session b's output at b * H*dh (float16 to out16
-  // when it is set)
+  // when it is set, in the skinny products' fragment order: frag_act_index(b, h*dh + d, H*dh))
   int batch;
   long long kv_bstride;
   uint16_t* out16;
@@ -118,8 +118,10 @@ bool qkv_attn_supported(bool bf16, int D, int dh, int H, int S, int n_cu);
 hipError_t launch_qkv_attn(const GemvArgs& g, const AttnDecodeArgs& at, const QkvAttnFuse& f, hipStream_t s);
 
 // ---------------------------------------------------------------- row RMSNorm
+// rows x D; float32 and/or float16 outputs (either may be null); f16_frag: the float16 rows in
+// the skinny products' fragment order (frag_act_index, D % 32 == 0) instead of row-major
 hipError_t launch_rmsnorm_rows(const float* x, const float* alpha, float eps, int D, int rows,
-                               float* out_f32, void* out_f16, hipStream_t s);
+                               float* out_f32, void* out_f16, bool f16_frag, hipStream_t s);
 
 }  // namespace pp
 
@@ -305,12 +307,13 @@ enum SgemmEpi { SEPI_STORE = 0, SEPI_RESID = 1, SEPI_QKV = 2, SEPI_SWIGLU = 3 };
 // out[b][n] = sum_k act[b][k] W[n][k] for the B sessions of a batched decode step:
 // float16 activations, bf16 weights widened to float16, float32 accumulation.
 struct SgemmArgs {
-  const uint16_t* act;   // [B][K] float16 (rows >= B are not read)
+  const uint16_t* act;   // [B][K] float16 in fragment order (frag_act_index; K % 32 == 0;
+                         // the buffer holds whole 16-row tiles, rows >= B are not read)
   const void* W;         // bfloat16 weights packed by launch_sgemm_pack (rows = N, or 2F g|z rows)
   int B, K, N;           // N = output columns (SEPI_SWIGLU: F)
   float* out;            // SEPI_STORE: [B][N] float32
   float* x;              // SEPI_RESID: [B][N] float32, += product
-  uint16_t* s_out;       // SEPI_SWIGLU: [B][F] float16 SiLU(g) * z
+  uint16_t* s_out;       // SEPI_SWIGLU: [B][F] float16 SiLU(g) * z, in fragment order
   int F;
   // SEPI_QKV: columns Q | K | V of width D; RoPE on Q and K with rope[dh] (cos, sin pairs of
   // this position); Q -> q_out [B][D] float32; K, V -> slot pos mod C of session b's ring

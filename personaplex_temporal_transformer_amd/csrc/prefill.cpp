@@ -163,7 +163,7 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
       e = launch_gather_history(ga, bf, s);
       if (e != hipSuccess) return hip_fail("prefill history gather", e);
     }
-    e = launch_rmsnorm_rows(m->px, m->norm1[l], (float)c.eps, D, T, u32, u16, s);
+    e = launch_rmsnorm_rows(m->px, m->norm1[l], (float)c.eps, D, T, u32, u16, false, s);
     if (e != hipSuccess) return hip_fail("prefill norm1", e);
 
     GemmArgs g{};
@@ -195,7 +195,7 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
     e = launch_gemm(GEPI_RESID, bf, go, m->n_cu, s);
     if (e != hipSuccess) return hip_fail("prefill W_O", e);
 
-    e = launch_rmsnorm_rows(m->px, m->norm2[l], (float)c.eps, D, T, u32, u16, s);
+    e = launch_rmsnorm_rows(m->px, m->norm2[l], (float)c.eps, D, T, u32, u16, false, s);
     if (e != hipSuccess) return hip_fail("prefill norm2", e);
 
     GemmArgs gi{};
@@ -210,7 +210,7 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
     e = launch_gemm(GEPI_RESID, bf, gw, m->n_cu, s);
     if (e != hipSuccess) return hip_fail("prefill W_out", e);
   }
-  e = launch_rmsnorm_rows(m->px, m->out_norm, (float)c.eps, D, T, h_out_dev, nullptr, s);
+  e = launch_rmsnorm_rows(m->px, m->out_norm, (float)c.eps, D, T, h_out_dev, nullptr, false, s);
   if (e != hipSuccess) return hip_fail("prefill final norm", e);
   kv->pos = p0 + T;
   return PP_OK;

@@ -12,7 +12,11 @@
 // lane holds D[session 4 * (lane / 16) + i][column lane % 16]. The weights are read from a
 // copy packed once per model in exactly that fragment order -- tile, 32-element step,
 // lane, 8 elements -- so each load instruction of a wave reads 1 KB of contiguous memory
-// (the row-major matrix would give 16 rows x 64 bytes per instruction). The waves' partial tiles
+// (the row-major matrix would give 16 rows x 64 bytes per instruction). The float16
+// activations are written in the same order by their producers (the row RMSNorm, the
+// attention combine and this file's SiLU-product epilogue; frag_act_index), so their loads
+// are 1 KB contiguous as well (row-major [B][K] they were 16 rows x 64 bytes, and the
+// batched step took 3-16 % longer at B = 16-64). The waves' partial tiles
 // are summed in LDS in wave order (fixed order: reproducible), then the epilogue applies
 // RoPE / ring append, the residual add, the SiLU product or a plain store.
 #include <stdlib.h>
@@ -30,21 +34,21 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
   __shared__ float tile[NBT * 16][NT * 16 + 1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15, g = lane >> 4;
+  const int n = lane & 15;
   const int nsteps = a.K / 32;
   const int tile0 = blockIdx.x * NT;
   // packed fragments of this workgroup's tiles: [tile][step][lane][8]
   const uint16_t* Wr = static_cast<const uint16_t*>(a.W) + ((size_t)tile0 * nsteps * 64 + lane) * 8;
   const size_t tstride = (size_t)nsteps * 512;
   const int s0 = w * nsteps / kSgWaves, s1 = (w + 1) * nsteps / kSgWaves;
-  // this lane's session row in each session tile (rows past B contribute zeros)
+  // this lane's activation fragments in each session tile (fragment order: tile, step,
+  // lane, 8 values -- frag_act_index); lanes of sessions past B read zeros
   const uint16_t* Ar[NBT];
   bool live[NBT];
 #pragma unroll
   for (int t = 0; t < NBT; ++t) {
-    const int b = t * 16 + n;
-    live[t] = b < a.B;
-    Ar[t] = a.act + (size_t)(live[t] ? b : 0) * a.K + 8 * g;
+    live[t] = t * 16 + n < a.B;
+    Ar[t] = a.act + ((size_t)t * nsteps * 64 + lane) * 8;
   }
   f32x4 acc[NT][NBT];
 #pragma unroll
@@ -63,7 +67,7 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
       for (int j = 0; j < NT; ++j) wv[buf][u][j] = load_stream(Wr + j * tstride + (size_t)(st0 + u) * 512);
 #pragma unroll
       for (int t = 0; t < NBT; ++t)
-        av[buf][u][t] = live[t] ? *reinterpret_cast<const u32x4*>(Ar[t] + (size_t)(st0 + u) * 32) : u32x4{0u, 0u, 0u, 0u};
+        av[buf][u][t] = live[t] ? *reinterpret_cast<const u32x4*>(Ar[t] + (size_t)(st0 + u) * 512) : u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto mul_group = [&](int buf) {
@@ -91,7 +95,7 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
     u32x4 a1[NBT];
 #pragma unroll
     for (int t = 0; t < NBT; ++t)
-      a1[t] = live[t] ? *reinterpret_cast<const u32x4*>(Ar[t] + (size_t)st * 32) : u32x4{0u, 0u, 0u, 0u};
+      a1[t] = live[t] ? *reinterpret_cast<const u32x4*>(Ar[t] + (size_t)st * 512) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const f16x8 wf = bf16x8_to_f16(load_stream(Wr + j * tstride + (size_t)st * 512));
@@ -129,7 +133,7 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
     } else if constexpr (EPI == SEPI_RESID) {
       a.x[(size_t)b * a.N + tl * 16 + c] += v;
     } else if constexpr (EPI == SEPI_SWIGLU) {
-      if (c < 8) a.s_out[(size_t)b * a.F + tl * 8 + c] = f32_to_f16(silu(v) * tile[b][cc + 8]);
+      if (c < 8) a.s_out[frag_act_index(b, tl * 8 + c, a.F)] = f32_to_f16(silu(v) * tile[b][cc + 8]);
     } else {
       const int col = tl * 16 + c;
       const int sec = col / a.D, wcol = col - sec * a.D;
