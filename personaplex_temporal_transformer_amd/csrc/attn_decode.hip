@@ -18,6 +18,7 @@
 #include <stdlib.h>
 
 #include "attn_body.h"
+#include "frag_layout.h"
 
 namespace pp {
 

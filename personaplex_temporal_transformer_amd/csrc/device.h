@@ -73,15 +73,6 @@ template <> struct Elem<bf16_t> {
 __device__ __forceinline__ u32x4 load_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
-// Float16 activations of the skinny matrix products (batched decode) are kept in the order
-// their MFMA fragments read them: 16-session tiles, then 32-element k-steps, then 64 lanes of
-// 8 values, lane = session % 16 + 16 * ((k % 32) / 8). Element (b, k) of a [B][K] matrix
-// (K a multiple of 32) sits at this index; a wave's load of one tile and step is 1 KB of
-// contiguous memory.
-__device__ __forceinline__ size_t frag_act_index(int b, int k, int K) {
-  return ((((size_t)(b >> 4) * (size_t)(K >> 5) + (size_t)(k >> 5)) * 64 + (size_t)((b & 15) + 16 * ((k & 31) >> 3))) << 3) +
-         (size_t)(k & 7);
-}
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

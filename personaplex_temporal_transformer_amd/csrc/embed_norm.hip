@@ -6,6 +6,7 @@
 // RMSNorm: same page, section 3 'One of the 32 temporal blocks' -- float32 arithmetic,
 // x * alpha / sqrt(mean(x^2) + eps), no mean subtraction.
 #include "device.h"
+#include "frag_layout.h"
 #include "internal.h"
 
 namespace pp {

@@ -22,6 +22,7 @@
 #include <stdlib.h>
 
 #include "device.h"
+#include "frag_layout.h"
 #include "internal.h"
 
 namespace pp {
