@@ -95,7 +95,7 @@ typedef struct pp_kv pp_kv;
 
 /* Create a temporal model on the current device. max_batch (1..64) bounds the sessions a
  * KV ring may hold for batched decode (B is the tensors' leading axis, audit section 3;
- * the pages' server runs B = 1); max_batch > 1 needs bf16 weights, d_model % 16 == 0,
+ * the pages' server runs B = 1); max_batch > 1 needs bf16 weights, d_model % 32 == 0,
  * d_ff % 32 == 0 and text-head rows % 16 == 0. max_prefill_T (0..context) sizes the
  * prefill workspace. The library allocates its workspace here (hipMalloc); weights are
  * not copied, except that max_batch > 1 keeps one copy of every matrix (and the text

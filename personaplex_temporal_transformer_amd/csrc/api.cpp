@@ -73,8 +73,8 @@ extern "C" pp_status pp_temporal_create(const pp_temporal_config* cfg, const pp_
   if (max_batch < 1 || max_batch > kSgemmMaxBatch) return pp_fail(PP_E_ARG, "max_batch must be in [1, 64]");
   if (max_batch > 1 && cfg->wdtype != PP_BF16)
     return pp_fail(PP_E_ARG, "batched decode (max_batch > 1) needs bf16 weights");
-  if (max_batch > 1 && (cfg->d_model % 16 || cfg->d_ff % 32 || (cfg->text_vocab - 1) % 16))
-    return pp_fail(PP_E_ARG, "batched decode needs d_model % 16, d_ff % 32 and the text head rows % 16 == 0");
+  if (max_batch > 1 && (cfg->d_model % 32 || cfg->d_ff % 32 || (cfg->text_vocab - 1) % 16))
+    return pp_fail(PP_E_ARG, "batched decode needs d_model % 32, d_ff % 32 and the text head rows % 16 == 0");
   if (max_prefill_T < 0 || max_prefill_T > cfg->context)
     return pp_fail(PP_E_CAPACITY, "max_prefill_T must be in [0, context]");
   int n_cu = 0;
