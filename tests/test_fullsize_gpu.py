@@ -224,37 +224,47 @@ def test_full_prefill_chunk_after_full_ring():
     assert np.array_equal(rc[:, :, :, :, 256:], rd[:, :, :, :, 256:])   # untouched slots agree bit for bit
 
 
-def test_full_batched_decode_ctx3000_matches_single_sessions():
-    """4 sessions decoded together (every weight byte shared, float16 activations into the
-    matrix cores) against the same 4 sessions decoded one at a time, rings full at 3000
-    random frames, 2 frames at positions 3000 and 3001 (keys wrap): 2 x 2e-2."""
+@pytest.mark.parametrize("B,sessions", [(4, (0, 1, 2, 3)), (64, (0, 15, 16, 33, 48, 63))])
+def test_full_batched_decode_ctx3000_matches_single_sessions(B, sessions):
+    """B sessions decoded together (every weight byte shared, float16 activations into the
+    matrix cores) against the same sessions decoded one at a time, rings full at 3000
+    random frames, 2 frames at positions 3000 and 3001 (keys wrap): 2 x 2e-2. B = 64 is the
+    largest batch (4 session tiles; about 230 GB of device memory with its 100 GB of rings);
+    it checks the sessions at the tile boundaries."""
+    import gc
     import torch
     cfg = dict(synth.FULL_TEMPORAL)
     C, L, D, H, dh = cfg["context"], cfg["n_layers"], cfg["d_model"], cfg["n_heads"], cfg["d_head"]
     W = synth.temporal_weights(cfg, 70, "bf16", with_text_head=False, shared_layer=True)
     require_gpu()
-    B = 4
+    gc.collect()
+    torch.cuda.empty_cache()
     model = pp.TemporalModel(cfg, to_device(W), "bf16", max_batch=B)
     g = torch.Generator(device="cuda")
     g.manual_seed(71)
-    frames = torch.randn((L, 2, B, H, C, dh), generator=g, device="cuda").to(torch.bfloat16)
+    frames = torch.randn((L, 2, B, H, C, dh), generator=g, device="cuda", dtype=torch.bfloat16)
     ids = synth.stream_ids(cfg, 2, 72, batch=B)
     kv = model.kv_alloc(B)
     kv.load(frames, C)
+    one = {b: frames[:, :, b:b + 1].contiguous() for b in sessions}
+    del frames
+    torch.cuda.empty_cache()
     hb = torch.empty((2, B, D), device="cuda")
     for t in range(2):
         model.decode_step(kv, ids[:, t], hb[t])
     errs = []
-    for b in range(B):
+    for b in sessions:
         kv1 = model.kv_alloc(1)
-        kv1.load(frames[:, :, b:b + 1].contiguous(), C)
+        kv1.load(one[b], C)
         h1 = torch.empty((2, D), device="cuda")
         for t in range(2):
             model.decode_step(kv1, ids[b, t], h1[t])
         torch.cuda.synchronize()
         errs.append(norm_max_err(hb[:, b].cpu().numpy(), h1.cpu().numpy()))
         kv1.close()
-    print("full batched decode B=4 vs single sessions: errs %s" % ["%.3g" % e for e in errs])
+    print("full batched decode B=%d vs single sessions %s: errs %s" % (B, list(sessions), ["%.3g" % e for e in errs]))
+    kv.close()
+    model.close()
     assert max(errs) <= 2 * BF16_TOL
 
 
