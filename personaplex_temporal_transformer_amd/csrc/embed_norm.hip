@@ -79,16 +79,7 @@ __global__ __launch_bounds__(kBlock) void k_rmsnorm_rows(const float* __restrict
                                                          uint16_t* __restrict__ out_f16, int f16_frag) {
   __shared__ float red[4];
   const float* xr = x + (size_t)blockIdx.x * D;
-  float ss = 0.f;
-  for (int i = threadIdx.x * 4; i < D; i += kBlock * 4) {
-    f32x4 v = *reinterpret_cast<const f32x4*>(xr + i);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-  }
-  const float r = 1.0f / sqrtf(block_sum_256(ss, red) / (float)D + eps);
-  for (int i = threadIdx.x * 4; i < D; i += kBlock * 4) {
-    f32x4 v = *reinterpret_cast<const f32x4*>(xr + i);
-    f32x4 al = *reinterpret_cast<const f32x4*>(alpha + i);
-    f32x4 y = (v * r) * al;
+  auto emit = [&](int i, f32x4 y) {
     if (out_f32) *reinterpret_cast<f32x4*>(out_f32 + (size_t)blockIdx.x * D + i) = y;
     if (out_f16) {
       const uint32_t lo = (uint32_t)f32_to_f16(y.x) | ((uint32_t)f32_to_f16(y.y) << 16);
@@ -97,6 +88,40 @@ __global__ __launch_bounds__(kBlock) void k_rmsnorm_rows(const float* __restrict
       const size_t oi = f16_frag ? frag_act_index((int)blockIdx.x, i, D) : (size_t)blockIdx.x * D + i;
       *reinterpret_cast<uint2*>(out_f16 + oi) = make_uint2(lo, hi);
     }
+  };
+  // Rows of up to kBlock * 16 values stay in registers between the sum of squares and the
+  // scaling, with the scales loaded alongside (one memory round trip instead of two); the
+  // per-thread sums run over the same elements in the same order either way.
+  constexpr int NV = 4;
+  float ss = 0.f;
+  if (D <= kBlock * 4 * NV) {
+    f32x4 v[NV], al[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int i = (threadIdx.x + j * kBlock) * 4;
+      v[j] = i < D ? *reinterpret_cast<const f32x4*>(xr + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+      al[j] = i < D ? *reinterpret_cast<const f32x4*>(alpha + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      if ((threadIdx.x + j * kBlock) * 4 < D) ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+    const float r = 1.0f / sqrtf(block_sum_256(ss, red) / (float)D + eps);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int i = (threadIdx.x + j * kBlock) * 4;
+      if (i < D) emit(i, (v[j] * r) * al[j]);
+    }
+    return;
+  }
+  for (int i = threadIdx.x * 4; i < D; i += kBlock * 4) {
+    f32x4 v = *reinterpret_cast<const f32x4*>(xr + i);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  const float r = 1.0f / sqrtf(block_sum_256(ss, red) / (float)D + eps);
+  for (int i = threadIdx.x * 4; i < D; i += kBlock * 4) {
+    f32x4 v = *reinterpret_cast<const f32x4*>(xr + i);
+    f32x4 al = *reinterpret_cast<const f32x4*>(alpha + i);
+    emit(i, (v * r) * al);
   }
 }
 
