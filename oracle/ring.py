@@ -8,7 +8,7 @@ the declared temporal mask admits keys with 0 <= query - key < context.
 
 Two labellings are provided:
   * stated_positions: each slot carries the latest absolute position written to it --
-    the reading this build implements (all `capacity` slots usable once the ring is full);
+    the reading the library implements (all `capacity` slots usable once the ring is full);
   * compat_positions: the mapping the audit reproduced from the released ring cache,
     where slots are labelled relative to the write cursor and the slot under the cursor
     is labelled with the (future) end offset. The audit's integer examples pin it.

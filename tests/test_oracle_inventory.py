@@ -84,7 +84,7 @@ def test_ring_examples():
         if labels != "-":
             assert got == [int(x) for x in labels.split(",")]
         assert len(ring.visible(got, query, cap)) == n_vis
-        # The stated mask (this build's reading) keeps every slot of a full ring usable.
+        # The stated mask (the library's reading) keeps every slot of a full ring usable.
         stated = ring.stated_positions(cap, end)
         assert len(ring.visible(stated, end - 1, cap)) == cap
 
