@@ -9,7 +9,7 @@ and section 6 "Three distinct caches" (temporal attention cache). Cross-checked 
 "Learnings: PersonaPlex/Moshi full-duplex S2S export + real-time ORT inference"
 (onnxruntime/mobius issue #369), section 1 "Architecture".
 
-Conventions (the readings are listed in the design doc):
+Conventions (readings of the pages where they leave a step open):
   * weights are given as NumPy arrays, either float32/float64 or uint16 holding the
     bit pattern of bfloat16; every value is widened exactly to fp64 before use;
   * linear weights use the [out_features, in_features] orientation, so y = W @ x;
