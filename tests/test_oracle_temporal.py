@@ -156,7 +156,9 @@ def test_swiglu_hand_example():
 def _perm(n, shift):
     P = np.zeros((n, n))
     for i in range(n):
-        P[(i + shift) % n, (3 * i + 1) % n] = 1.0      # not symmetric, not the identity
+        P[(i + shift) % n, (3 * i + 1) % n] = 1.0
+    # a transposed operand must show: odd shifts give an involution (P = P^T) at n = 8
+    assert not np.array_equal(P, P.T)
     return P
 
 
@@ -167,7 +169,7 @@ def test_block_with_hand_built_weights_single_frame():
     cfg = small_cfg()
     D, F = 8, 4
     rng = np.random.default_rng(3)
-    Pv, Po = _perm(D, 2), _perm(D, 5)
+    Pv, Po = _perm(D, 2), _perm(D, 6)
     Wqkv = np.concatenate([rng.standard_normal((D, D)), rng.standard_normal((D, D)), Pv])
     Win = np.zeros((2 * F, D))
     for i in range(F):
@@ -274,3 +276,69 @@ def test_shift_of_all_positions_leaves_outputs_unchanged():
     a = O.forward_full(ids[:6], W, cfg, p0=0)
     b = O.forward_full(ids[:6], W, cfg, p0=1234)
     assert np.max(np.abs(a - b)) < 1e-9
+
+
+def _two_frame_qk_setup():
+    """A 1-block stack of width 256 = 2 heads x 128 whose projections are built by hand
+    (audit section 3, 'One of the 32 temporal blocks': one fused [Q, K, V] projection).
+
+    Head h's query coordinate 0 is 4 u[2h] (Q section, rows h*128) and its key coordinate 0
+    is 3 u[2h+1] (K section, rows 256 + h*128); every other query / key coordinate is 0, so
+    RoPE rotates only pair 0, whose frequency is 1 for any theta. V = u (V section = I),
+    W_O = I and the feed-forward is zero, so the block output is x + A."""
+    D, H, dh = 256, 2, 128
+    cfg = dict(n_layers=1, d_model=D, n_heads=H, d_head=dh, d_ff=4, context=3000,
+               text_vocab=5, audio_vocab=7, n_audio=2, rope_theta=10000.0, eps=1e-8)
+    Wqkv = np.zeros((3 * D, D))
+    for h in range(H):
+        Wqkv[h * dh, 2 * h] = 4.0                 # q_h[0] = 4 u[2h]
+        Wqkv[D + h * dh, 2 * h + 1] = 3.0         # k_h[0] = 3 u[2h+1]
+    Wqkv[2 * D:] = np.eye(D)
+    alpha = np.linspace(0.6, 1.4, D)
+    W = {"transformer.layers.0.norm1.alpha": alpha, "transformer.layers.0.norm2.alpha": np.ones(D),
+         "transformer.layers.0.self_attn.in_proj_weight": Wqkv,
+         "transformer.layers.0.self_attn.out_proj.weight": np.eye(D),
+         "transformer.layers.0.gating.linear_in.weight": np.zeros((8, D)),
+         "transformer.layers.0.gating.linear_out.weight": np.zeros((D, 4))}
+    rng = np.random.default_rng(11)
+    X = rng.standard_normal((2, D))
+    X[:, :4] = [[1.5, -1.0, 0.8, 1.2], [1.1, 0.9, -1.3, 0.7]]
+    return cfg, W, X, alpha
+
+
+def _two_frame_qk_expected(X, alpha, pos):
+    """Scalar closed form of the hand-built block above: frame 0 sees only itself (A = u_0);
+    frame 1 weighs keys 0 and 1 by the softmax of s_j = q.k_j / sqrt(128), where
+    q.k_j = 4 u_1[2h] * 3 u_j[2h+1] * cos(p_1 - p_j) (two pair-0 vectors rotated by their
+    positions differ by the angle p_1 - p_j)."""
+    D, dh = 256, 128
+    U = []
+    for t in range(2):
+        rms = math.sqrt(sum(v * v for v in X[t]) / D + 1e-8)
+        U.append([alpha[i] * X[t][i] / rms for i in range(D)])
+    out0 = [X[0][i] + U[0][i] for i in range(D)]
+    out1 = list(X[1])
+    for h in range(2):
+        s = [4.0 * U[1][2 * h] * 3.0 * U[j][2 * h + 1] * math.cos(pos[1] - pos[j]) / math.sqrt(dh)
+             for j in range(2)]
+        m = max(s)
+        e = [math.exp(v - m) for v in s]
+        w = [v / sum(e) for v in e]
+        for i in range(h * dh, (h + 1) * dh):
+            out1[i] += w[0] * U[0][i] + w[1] * U[1][i]
+    return np.array([out0, out1]), w
+
+
+def test_two_frame_block_fixes_q_before_k_and_score_scale():
+    """Fixes the Q | K | V order of the fused projection, the head split and the
+    1/sqrt(d_head) score scale (audit section 3, 'One of the 32 temporal blocks' and
+    'Positions, attention mask and final text head'), on both code paths."""
+    cfg, W, X, alpha = _two_frame_qk_setup()
+    pos = [5, 6]
+    want, w = _two_frame_qk_expected(X, alpha, pos)
+    assert 0.05 < w[0] < 0.95            # the two keys really compete
+    got = O.block_full(X, np.array(pos), 0, W, cfg)
+    assert np.allclose(got, want, atol=1e-12)
+    cache = O.Cache(1)
+    inc = np.stack([O.decode_step(X[t], pos[t], cache, W, cfg) for t in range(2)])
+    assert np.allclose(inc, want, atol=1e-12)
