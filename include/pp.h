@@ -133,7 +133,10 @@ pp_status pp_kv_restore(pp_kv* kv, const void* src_dev, int64_t position, void* 
  * x = sum over the n_audio+1 streams of that stream's table row, in stream order,
  * accumulated in float32; ID -1 adds nothing (an exact zero vector).
  * ids_host [batch][T][n_audio+1]: stream 0 = agent text, 1..8 agent audio, 9..16 user
- * audio. Any ID < -1 or >= that stream's vocab gives PP_E_ID. x_out_dev [batch][T][d_model]. */
+ * audio. Any ID < -1 or >= that stream's vocab gives PP_E_ID. x_out_dev [batch][T][d_model].
+ * 1 <= batch <= max_batch; one frame (batch * T == 1) is always accepted, more frames go
+ * through the model's ID region of max_prefill_T x max_batch frames: beyond it,
+ * PP_E_CAPACITY. */
 pp_status pp_embed_sum(const pp_model* m, const int32_t* ids_host, int32_t batch, int32_t T,
                        float* x_out_dev, void* stream);
 
@@ -346,6 +349,14 @@ const char* pp_last_error(void);
 /* Decode-step launch mode of a temporal model: 0 = launch each kernel, 1 = replay a
  * captured HIP graph of the layer stack (default). */
 pp_status pp_temporal_set_graph(pp_model* m, int32_t enable);
+
+/* Split-K factor of the batch-1 decode attention: each head's visible keys are shared by
+ * `splits` workgroups whose partial softmax results are merged afterwards (inside the W_O
+ * product for up to 8 splits, else by a separate merge kernel). 0 = automatic (about one
+ * workgroup per compute unit over all heads: 8 for 32 heads on 256 CUs); 1..64 forces a
+ * value. The result does not depend on it beyond float32 rounding. Batched decode always
+ * uses the automatic value. */
+pp_status pp_temporal_set_attn_splits(pp_model* m, int32_t splits);
 
 /* Kernel timing for roofline reports: when layer >= 0, every decode step brackets the
  * W_in (RMSNorm + gate/linear projection + SiLU product) kernel of that layer with HIP

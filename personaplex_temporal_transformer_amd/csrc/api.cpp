@@ -41,12 +41,13 @@ pp_status pp_device_check(int* n_cu) {
   return PP_OK;
 }
 
-int env_int(const char* name, int dflt) {
-  const char* v = std::getenv(name);
-  return v && *v ? std::atoi(v) : dflt;
-}
-
 // ------------------------------------------------------------------ temporal model
+
+// Split-K factor of the decode attention: about one workgroup per CU over all heads.
+static int auto_splits(int n_cu, int H) {
+  const int S = (n_cu + H - 1) / H;
+  return S < 1 ? 1 : (S > kMaxAttnSplits ? kMaxAttnSplits : S);
+}
 
 static pp_status validate_temporal_config(const pp_temporal_config* c) {
   if (!c) return pp_fail(PP_E_ARG, "config is NULL");
@@ -106,22 +107,13 @@ extern "C" pp_status pp_temporal_create(const pp_temporal_config* cfg, const pp_
   m->text_head = w->text_head;
   m->max_batch = max_batch;
   m->max_T = max_prefill_T;
-  m->use_graph = env_int("PP_GRAPH", 1) != 0;
-  m->gemv_blocks = env_int("PP_GEMV_BLOCKS_PER_CU", 1) * n_cu;
-  m->wout_rb = env_int("PP_WOUT_ROWS", 2) == 2 && cfg->d_model % 2 == 0 ? 2 : 1;
+  m->use_graph = true;
+  m->gemv_blocks = n_cu;   // one 8-wave GEMV workgroup per CU
+  m->wout_rb = cfg->d_model % 2 == 0 ? 2 : 1;
 
   const int D = cfg->d_model, F = cfg->d_ff, H = cfg->n_heads, dh = cfg->d_head;
-  // attention splits: about one block per CU over all heads (at most 64)
-  int S = (n_cu + H - 1) / H;
-  S = env_int("PP_ATTN_SPLITS", S);
-  m->S = S < 1 ? 1 : (S > 64 ? 64 : S);
-
-  // The fused QKV + attention launch is correct (tested against the two-launch path) but
-  // measured no faster on one GPU: the attention split can only start once its head's
-  // rows are published, which is near the end of the QKV product, so only the launch gap
-  // is saved and the publishing costs about as much. Off unless PP_FUSE_QKV_ATTN=1.
-  m->fuse_qkv_attn = env_int("PP_FUSE_QKV_ATTN", 0) != 0 && m->gemv_blocks == n_cu &&
-                     qkv_attn_supported(m->bf16, D, dh, H, m->S, n_cu);
+  // attention splits: about one block per CU over all heads (at most kMaxAttnSplits)
+  m->S = m->S_auto = auto_splits(n_cu, H);
   st = m->alloc_decode(D, F, H, dh);
   if (!st) st = m->alloc_prefill();
   if (!st && max_batch > 1) st = m->pack_batched();
@@ -137,17 +129,17 @@ pp_status pp_model::alloc_decode(int D, int F, int H, int dh) {
   size_t bytes = 0;
   auto take = [&](size_t n) { size_t off = bytes; bytes += (n + 255) / 256 * 256; return off; };
   const size_t ox = take(sizeof(float) * D), oq = take(sizeof(float) * D), oo = take(sizeof(float) * D);
-  const size_t os = take(sizeof(float) * F), op = take(sizeof(float) * (size_t)H * S * dh);
-  const size_t oml = take(sizeof(float) * (size_t)H * S * 2);
+  // batch-1 partials for any split count pp_temporal_set_attn_splits may choose
+  const size_t os = take(sizeof(float) * F), op = take(sizeof(float) * (size_t)H * kMaxAttnSplits * dh);
+  const size_t oml = take(sizeof(float) * (size_t)H * kMaxAttnSplits * 2);
   const size_t ost = take(sizeof(long long) * 4);
-  const size_t ocnt = take(sizeof(unsigned long long) * (size_t)cfg.n_layers * H);
   const size_t orp = take(sizeof(float) * dh);
   // batched decode: per-session residuals, queries, float16 activations, attention partials
   const size_t nb = max_batch > 1 ? (size_t)max_batch : 0;
   const size_t nb16 = (nb + 15) / 16 * 16;   // float16 operands in whole 16-session fragment tiles
   const size_t obx = take(sizeof(float) * nb * D), obq = take(sizeof(float) * nb * D);
   const size_t obu = take(2 * nb16 * D), obo = take(2 * nb16 * D), obs = take(2 * nb16 * F);
-  const size_t obp = take(sizeof(float) * nb * H * S * dh), obm = take(sizeof(float) * nb * H * S * 2);
+  const size_t obp = take(sizeof(float) * nb * H * S_auto * dh), obm = take(sizeof(float) * nb * H * S_auto * 2);
   if (hipMalloc(&ws, bytes) != hipSuccess) return pp_fail(PP_E_HIP, "hipMalloc of decode workspace failed");
   if (hipMemset(ws, 0, bytes) != hipSuccess) return pp_fail(PP_E_HIP, "hipMemset of decode workspace failed");
   char* b = static_cast<char*>(ws);
@@ -158,10 +150,6 @@ pp_status pp_model::alloc_decode(int D, int F, int H, int dh) {
   part_o = reinterpret_cast<float*>(b + op);
   part_ml = reinterpret_cast<float*>(b + oml);
   state = reinterpret_cast<long long*>(b + ost);
-  head_cnt = reinterpret_cast<unsigned long long*>(b + ocnt);
-  if (hipHostMalloc(reinterpret_cast<void**>(&fuse_err), sizeof(int)) != hipSuccess)
-    return pp_fail(PP_E_HIP, "hipHostMalloc of the fused-wait status word failed");
-  *fuse_err = 0;
   rope = reinterpret_cast<float*>(b + orp);
   if (nb) {
     bx = reinterpret_cast<float*>(b + obx);
@@ -215,7 +203,6 @@ pp_model::~pp_model() {
   if (ws) (void)hipFree(ws);
   if (pk_ws) (void)hipFree(pk_ws);
   if (ids_pinned) (void)hipHostFree(ids_pinned);
-  if (fuse_err) (void)hipHostFree(fuse_err);
   if (ids_event) (void)hipEventDestroy(ids_event);
 }
 
@@ -228,6 +215,18 @@ extern "C" pp_status pp_temporal_destroy(pp_model* m) {
 extern "C" pp_status pp_temporal_set_graph(pp_model* m, int32_t enable) {
   if (!m) return pp_fail(PP_E_ARG, "model is NULL");
   m->use_graph = enable != 0;
+  return PP_OK;
+}
+
+extern "C" pp_status pp_temporal_set_attn_splits(pp_model* m, int32_t splits) {
+  if (!m) return pp_fail(PP_E_ARG, "model is NULL");
+  if (splits < 0 || splits > kMaxAttnSplits)
+    return pp_fail(PP_E_ARG, "splits outside [0, " + std::to_string(kMaxAttnSplits) + "]");
+  const int S = splits == 0 ? m->S_auto : splits;
+  if (S != m->S) {
+    m->S = S;
+    ++m->graph_gen;   // captured graphs hold the old launch shape
+  }
   return PP_OK;
 }
 
@@ -332,6 +331,9 @@ void pp_model::embed_tables(EmbedArgs& a) const {
 
 pp_status pp_model::stage_ids(const int32_t* ids_host, size_t n, hipStream_t s) {
   // IDs go through a pinned buffer owned by the model; the event guards its reuse.
+  if (n > ids_frames * (size_t)(cfg.n_audio + 1))
+    return pp_fail(PP_E_CAPACITY, "more IDs than the model's ID region holds (" + std::to_string(ids_frames) +
+                                      " frames: max_prefill_T x max_batch)");
   if (n > ids_cap) {
     if (ids_pinned) {
       (void)hipEventSynchronize(ids_event);
@@ -368,8 +370,8 @@ extern "C" pp_status pp_embed_sum(const pp_model* mc, const int32_t* ids_host, i
   if (frames == 1) {
     for (int k = 0; k < a.n_streams; ++k) a.ids_arg[k] = ids_host[k];
   } else {
-    if (frames > (size_t)m->max_T * m->max_batch)
-      return pp_fail(PP_E_CAPACITY, "batch*T exceeds the model's prefill workspace (max_prefill_T)");
+    if (frames > m->ids_frames)
+      return pp_fail(PP_E_CAPACITY, "batch*T exceeds max_prefill_T x max_batch frames");
     if ((st = m->stage_ids(ids_host, frames * a.n_streams, s))) return st;
     a.ids_dev = m->ids_dev;
   }
@@ -382,7 +384,7 @@ extern "C" pp_status pp_embed_sum(const pp_model* mc, const int32_t* ids_host, i
 
 // pos_arg: the frame's position, passed by value to the kernels of a direct launch; -1
 // when the launches are captured into a graph, whose kernels read it from `state`.
-hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long long pos_arg, long long seq_arg) {
+hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long long pos_arg) {
   const pp_temporal_config& c = cfg;
   const int D = c.d_model, F = c.d_ff, H = c.n_heads, dh = c.d_head, C = c.context;
   const size_t esz = bf16 ? 2 : 4;
@@ -401,13 +403,8 @@ hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long 
     at.scale = 1.0f / std::sqrt((float)dh); at.part_o = part_o; at.part_ml = part_ml; at.out = o;
     const bool merge_in_wo = S <= 8 && D <= 4096;
     at.combine = merge_in_wo ? 0 : 1;
-    if (fuse_qkv_attn && merge_in_wo) {
-      QkvAttnFuse f{head_cnt + (size_t)l * H, seq_arg, fuse_err};
-      e = launch_qkv_attn(g, at, f, s);
-    } else {
-      e = launch_gemv(PRO_RMSNORM, EPI_QKV, bf16, 2, g, gemv_blocks, s);
-      if (e == hipSuccess) e = launch_attn_decode(at, bf16, dh, s);
-    }
+    e = launch_gemv(PRO_RMSNORM, EPI_QKV, bf16, 2, g, gemv_blocks, s);
+    if (e == hipSuccess) e = launch_attn_decode(at, bf16, dh, s);
     if (e != hipSuccess) break;
 
     GemvArgs go{};
@@ -441,7 +438,7 @@ hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long 
 pp_status pp_model::run_layers(pp_kv* kv, hipStream_t s) {
   const bool traced = trace_layer >= 0;
   if (!use_graph || traced) {
-    hipError_t e = kv->B > 1 ? enqueue_layers_batched(kv, s, kv->pos) : enqueue_layers(kv, s, traced, kv->pos, fused_seq);
+    hipError_t e = kv->B > 1 ? enqueue_layers_batched(kv, s, kv->pos) : enqueue_layers(kv, s, traced, kv->pos);
     if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("decode launch: ") + hipGetErrorString(e));
     return PP_OK;
   }
@@ -455,7 +452,7 @@ pp_status pp_model::run_layers(pp_kv* kv, hipStream_t s) {
       return pp_fail(PP_E_HIP, "hipStreamCreate for graph capture failed");
     hipError_t e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
     if (e == hipSuccess) {
-      hipError_t le = kv->B > 1 ? enqueue_layers_batched(kv, cap, -1) : enqueue_layers(kv, cap, false, -1, -1);
+      hipError_t le = kv->B > 1 ? enqueue_layers_batched(kv, cap, -1) : enqueue_layers(kv, cap, false, -1);
       e = hipStreamEndCapture(cap, &kv->graph);
       if (le != hipSuccess) e = le;
     }
@@ -483,16 +480,11 @@ extern "C" pp_status pp_temporal_decode_step(pp_model* m, pp_kv* kv, const int32
 pp_status pp_model::decode(pp_kv* kv, const int32_t* ids_host, const int32_t* ids_dev, float* h_out_dev,
                            float* text_logits_dev, hipStream_t s) {
   if (text_logits_dev && !text_head) return pp_fail(PP_E_ARG, "text logits requested but the model has no text head");
-  if (fuse_err && __atomic_load_n(fuse_err, __ATOMIC_ACQUIRE)) {
-    *fuse_err = 0;
-    return pp_fail(PP_E_HIP, "an earlier decode step's cross-workgroup wait timed out (its output is invalid)");
-  }
   if (kv->B > 1) {
     if (readers.visible > 0) return pp_fail(PP_E_ARG, "memory readers run in batch-1 decode only");
     return decode_batched(kv, ids_host, h_out_dev, text_logits_dev, s);
   }
   const pp_temporal_config& c = cfg;
-  if (fuse_qkv_attn) ++fused_seq;
 
   EmbedArgs a{};
   embed_tables(a);
@@ -505,7 +497,6 @@ pp_status pp_model::decode(pp_kv* kv, const int32_t* ids_host, const int32_t* id
   a.rows = 1;
   a.state = state;
   a.pos = kv->pos;
-  a.seq = fused_seq;
   a.rope = rope;
   a.dh = c.d_head;
   // RoPE angles pos * theta^(-2j/d_head) formed in float64 on the host
@@ -557,7 +548,7 @@ hipError_t pp_model::enqueue_layers_batched(pp_kv* kv, hipStream_t s, long long 
     g.pos = pos_arg; g.D = D; g.dh = dh; g.C = C;
     if ((e = launch_sgemm(SEPI_QKV, g, s)) != hipSuccess) break;
     AttnDecodeArgs at{};
-    at.q = bq; at.k = kbase; at.v = vbase; at.state = state; at.pos = pos_arg; at.C = C; at.H = H; at.S = S;
+    at.q = bq; at.k = kbase; at.v = vbase; at.state = state; at.pos = pos_arg; at.C = C; at.H = H; at.S = S_auto;
     at.scale = 1.0f / std::sqrt((float)dh); at.part_o = bpart_o; at.part_ml = bpart_ml; at.combine = 1;
     at.batch = B; at.kv_bstride = bstride; at.out16 = bo16;
     if ((e = launch_attn_decode(at, true, dh, s)) != hipSuccess) break;

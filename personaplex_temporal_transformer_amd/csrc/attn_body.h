@@ -1,5 +1,4 @@
-// Decode attention body (split-K over keys), shared by the attention kernel and the fused
-// QKV + attention kernel.
+// Decode attention body (split-K over keys).
 //
 // "PersonaPlex native LM audit", section 3: ordinary multi-head attention (query, key and
 // value heads of d_head), scale 1/sqrt(d_head), softmax, no dropout; the declared mask
@@ -13,19 +12,6 @@
 
 namespace pp {
 
-// Fused mode: the frame's own K/V rows (slot p mod C) and its query are written by other
-// workgroups of the same kernel. They publish them with agent-scope stores and then add
-// the number of rows they wrote for head h to cnt[h]; this block waits until cnt[h]
-// reaches `target` (bounded: after kSpinLimit polls it records a failure in *err and goes
-// on), reads q at agent scope, and takes the frame's own key (re-read at agent scope)
-// after its other keys.
-struct AttnFuse {
-  const unsigned long long* cnt;  // [H] rows published per head (this layer)
-  unsigned long long target;      // cnt value once this frame's rows are all published
-  int* err;                       // host-visible failure word
-};
-constexpr unsigned kSpinLimit = 1u << 15;  // polls (about 50 ms); normal waits take a few
-
 // Block (s, h): one pass over its keys with an online softmax. A group of LPK lanes reads
 // one key row at a time (16 bytes per lane); the KPP groups of the block own contiguous,
 // equal runs of the block's keys. A round loads NB keys' K and V rows per thread with
@@ -34,8 +20,8 @@ constexpr unsigned kSpinLimit = 1u << 15;  // polls (about 50 ms); normal waits 
 // Each group keeps a running max m, sum l and output o (its lanes' EPC dimensions); the
 // groups are merged through LDS at the end, all threads taking part (PARTS partial
 // merges per output dimension, then their sum).
-template <typename KT, int DH, int NB, int NT, bool FUSED>
-__device__ __forceinline__ void attn_body(const AttnDecodeArgs& a, int s, int h, const AttnFuse& f) {
+template <typename KT, int DH, int NB, int NT>
+__device__ __forceinline__ void attn_body(const AttnDecodeArgs& a, int s, int h) {
   constexpr int EPC = Elem<KT>::kPerChunk;  // elements per 16-byte chunk
   constexpr int LPK = DH / EPC;             // lanes per key row
   constexpr int KPP = NT / LPK;             // key groups per block
@@ -57,13 +43,10 @@ __device__ __forceinline__ void attn_body(const AttnDecodeArgs& a, int s, int h,
   const int gbeg = kg * per_g;
   const int gend = gbeg + per_g < cnt ? gbeg + per_g : cnt;
   const int rounds = (per_g + NB - 1) / NB;   // the same for every group
-  const int jnew = (int)(pos % a.C) - j0;     // the frame's own slot, relative to j0
 
   float qv[EPC];
-  if constexpr (!FUSED) {
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) qv[e] = a.q[h * DH + sub * EPC + e] * (a.scale * kLog2e);
-  }
+  for (int e = 0; e < EPC; ++e) qv[e] = a.q[h * DH + sub * EPC + e] * (a.scale * kLog2e);
   const size_t base = ((size_t)h * a.C + j0) * DH;
   const auto rk = make_rsrc(static_cast<const KT*>(a.k) + base, (uint32_t)cnt * ROW);
   const auto rv = make_rsrc(static_cast<const KT*>(a.v) + base, (uint32_t)cnt * ROW);
@@ -76,7 +59,7 @@ __device__ __forceinline__ void attn_body(const AttnDecodeArgs& a, int s, int h,
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int j = gbeg + r * NB + b;
-      const int off = (r < rounds && j < gend && (!FUSED || j != jnew)) ? j * ROW + sub * 16 : kBufOutOfRange;
+      const int off = (r < rounds && j < gend) ? j * ROW + sub * 16 : kBufOutOfRange;
       ck[b] = buffer_load16_stream(rk, off);
       cv[b] = buffer_load16_stream(rv, off);
     }
@@ -93,7 +76,7 @@ __device__ __forceinline__ void attn_body(const AttnDecodeArgs& a, int s, int h,
       for (int e = 0; e < EPC; ++e) d += qv[e] * kf[e];
       d = group_sum<LPK>(d);
       const int j = gbeg + r * NB + b;
-      sc[b] = (j < gend && (!FUSED || j != jnew)) ? d : -INFINITY;
+      sc[b] = j < gend ? d : -INFINITY;
       mb = fmaxf(mb, sc[b]);
     }
     const float mn = fmaxf(m, mb);
@@ -117,24 +100,6 @@ __device__ __forceinline__ void attn_body(const AttnDecodeArgs& a, int s, int h,
   u32x4 ka[NB], va[NB], kb[NB], vb[NB];
   issue(ka, va, 0);
   issue(kb, vb, 1);
-  if constexpr (FUSED) {
-    // the ring loads above are in flight; now wait for this head's rows of the frame
-    if (tid == 0) {
-      unsigned it = 0;
-      while (load_agent(f.cnt + h) < f.target) {
-        if (++it > kSpinLimit) {
-          __hip_atomic_store(f.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-          break;
-        }
-        // another block already gave up: do not wait out the full limit as well
-        if ((it & 255) == 0 && __hip_atomic_load(f.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)) break;
-        __builtin_amdgcn_s_sleep(1);
-      }
-    }
-    lds_barrier();
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) qv[e] = load_agent(a.q + h * DH + sub * EPC + e) * (a.scale * kLog2e);
-  }
   for (int r = 0; r < rounds; r += 2) {
     consume(ka, va, r);
     if (r + 1 >= rounds) break;
@@ -143,30 +108,6 @@ __device__ __forceinline__ void attn_body(const AttnDecodeArgs& a, int s, int h,
     if (r + 2 >= rounds) break;
     issue(kb, vb, r + 3);
   }
-  if constexpr (FUSED) {
-    // the frame's own key, in the group whose run holds it (other lanes: no traffic, -inf)
-    const bool own = jnew >= gbeg && jnew < gend;
-    const u32x4 ck = buffer_load16_agent(rk, own ? jnew * ROW + sub * 16 : kBufOutOfRange);
-    const u32x4 cv = buffer_load16_agent(rv, own ? jnew * ROW + sub * 16 : kBufOutOfRange);
-    float kf[EPC];
-    Elem<KT>::widen(ck, kf);
-    float d = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) d += qv[e] * kf[e];
-    d = group_sum<LPK>(d);
-    const float sc = own ? d : -INFINITY;
-    const float mn = fmaxf(m, sc);
-    const float mref = mn == -INFINITY ? 0.f : mn;
-    const float scale = exp2_fast(m - mref);
-    const float p = exp2_fast(sc - mref);
-    float vf[EPC];
-    Elem<KT>::widen(cv, vf);
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[e] = acc[e] * scale + p * vf[e];
-    l = l * scale + p;
-    m = mn;
-  }
-
   // ---- merge the KPP groups of this block
   if (sub == 0) {
     gm[kg] = m;

@@ -15,14 +15,10 @@
 // The S partials of a head are merged in split order -- a fixed order, so results are
 // bit-reproducible -- in the W_O GEMV's prologue, or by a small combine kernel for more
 // than 8 splits.
-#include <stdlib.h>
-
 #include "attn_body.h"
 #include "frag_layout.h"
 
 namespace pp {
-
-constexpr int kMaxSplits = 64;
 
 // Block (s, h) of the split-K decode attention (see attn_body.h).
 template <typename KT, int DH, int NB, int NT>
@@ -35,7 +31,7 @@ __global__ __launch_bounds__(NT) void k_attn_decode(AttnDecodeArgs a) {
     a.part_o += b * a.H * a.S * DH;
     a.part_ml += b * a.H * a.S * 2;
   }
-  attn_body<KT, DH, NB, NT, false>(a, blockIdx.x, blockIdx.y, AttnFuse{});
+  attn_body<KT, DH, NB, NT>(a, blockIdx.x, blockIdx.y);
 }
 
 // Merge the S partials (o_s, m_s, l_s) of head h in split order:
@@ -43,7 +39,7 @@ __global__ __launch_bounds__(NT) void k_attn_decode(AttnDecodeArgs a) {
 // All partials of the head are first loaded into LDS in one parallel round.
 template <int DH>
 __global__ __launch_bounds__(kBlock) void k_attn_combine(AttnDecodeArgs a) {
-  __shared__ float po[kMaxSplits * DH], pml[kMaxSplits * 2];
+  __shared__ float po[kMaxAttnSplits * DH], pml[kMaxAttnSplits * 2];
   const int h = blockIdx.x, t = threadIdx.x;
   const size_t b = blockIdx.y;   // session (batched step)
   const float* part_o = a.part_o + b * a.H * a.S * DH;
@@ -68,22 +64,10 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(AttnDecodeArgs a) {
 
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, bool bf16, int dh, hipStream_t s) {
   const int nb = a.batch > 1 ? a.batch : 1;
-  if (a.S < 1 || a.S > kMaxSplits) return hipErrorInvalidValue;
+  if (a.S < 1 || a.S > kMaxAttnSplits) return hipErrorInvalidValue;
   const dim3 grid(a.S, a.H, nb);
-  static const int nb_env = [] {
-    const char* v = getenv("PP_ATTN_NB");
-    return v ? atoi(v) : 6;
-  }();
-  static const int nt_env = [] {
-    const char* v = getenv("PP_ATTN_THREADS");
-    return v ? atoi(v) : 512;
-  }();
-  if (bf16 && dh == 128) {
-    if (nt_env == 1024 && nb_env == 3) hipLaunchKernelGGL((k_attn_decode<bf16_t, 128, 3, 1024>), grid, dim3(1024), 0, s, a);
-    else if (nt_env == 1024) hipLaunchKernelGGL((k_attn_decode<bf16_t, 128, 4, 1024>), grid, dim3(1024), 0, s, a);
-    else if (nb_env == 4) hipLaunchKernelGGL((k_attn_decode<bf16_t, 128, 4, 512>), grid, dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((k_attn_decode<bf16_t, 128, 6, 512>), grid, dim3(512), 0, s, a);
-  } else if (bf16 && dh == 64) hipLaunchKernelGGL((k_attn_decode<bf16_t, 64, 6, 512>), grid, dim3(512), 0, s, a);
+  if (bf16 && dh == 128) hipLaunchKernelGGL((k_attn_decode<bf16_t, 128, 6, 512>), grid, dim3(512), 0, s, a);
+  else if (bf16 && dh == 64) hipLaunchKernelGGL((k_attn_decode<bf16_t, 64, 6, 512>), grid, dim3(512), 0, s, a);
   else if (!bf16 && dh == 128) hipLaunchKernelGGL((k_attn_decode<float, 128, 6, 512>), grid, dim3(512), 0, s, a);
   else if (!bf16 && dh == 64) hipLaunchKernelGGL((k_attn_decode<float, 64, 6, 512>), grid, dim3(512), 0, s, a);
   else return hipErrorInvalidValue;

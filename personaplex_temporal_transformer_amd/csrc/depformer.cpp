@@ -76,11 +76,9 @@ extern "C" pp_status pp_depformer_create(const pp_depth_config* cfg, const pp_de
   d->norm1.assign(w->norm1, w->norm1 + L);
   d->norm2.assign(w->norm2, w->norm2 + L);
   d->text_emb = w->text_emb;
-  d->gemv_blocks = env_int("PP_GEMV_BLOCKS_PER_CU", 1) * n_cu;
-  d->qkv_blocks = env_int("PP_DEPTH_QKV_BLOCKS", d->gemv_blocks);
-  d->attn_blocks = env_int("PP_DEPTH_ATTN_BLOCKS", d->gemv_blocks);
-  d->ffn_blocks = env_int("PP_DEPTH_FFN_BLOCKS", d->gemv_blocks);
-  d->use_graph = env_int("PP_GRAPH", 1) != 0;
+  d->gemv_blocks = n_cu;
+  d->qkv_blocks = d->attn_blocks = d->ffn_blocks = n_cu;
+  d->use_graph = true;
 
   const int D = cfg->d_model, F = cfg->d_ff, H = cfg->n_heads, dh = cfg->d_head;
   size_t bytes = 0;

@@ -25,10 +25,7 @@ __global__ __launch_bounds__(kEmbedThreads) void k_embed_sum(EmbedArgs a) {
   const int row = blockIdx.y;
   const int d = (blockIdx.x * kEmbedThreads + threadIdx.x) * EPC;
   if (a.state && row == 0 && blockIdx.x == 0) {
-    if (threadIdx.x == 0) {
-      a.state[0] = a.pos;
-      a.state[1] = a.seq;
-    }
+    if (threadIdx.x == 0) a.state[0] = a.pos;
     for (int i = threadIdx.x; a.rope && i < a.dh; i += kEmbedThreads) a.rope[i] = a.rope_cs[i];
   }
   if (d >= a.D) return;

@@ -45,7 +45,7 @@ __device__ __forceinline__ int row_of(const GemvArgs& a, int g, int r) {
 
 // pos: the frame's position and ropes: its cos/sin table in LDS (EPI_QKV; read in the
 // prologue, ahead of the weight loads, so the epilogue does not wait on global memory).
-template <typename WT, int RB, int EPI, bool PUB = false>
+template <typename WT, int RB, int EPI>
 __device__ __forceinline__ void epilogue(const GemvArgs& a, int g, const float (&acc)[RB], const float (&res)[RB],
                                          long long pos, const float* ropes) {
   if (EPI == EPI_STORE) {
@@ -77,24 +77,12 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, int g, const float (
         y1 = r1;
       }
       if (sec == 0) {
-        if constexpr (PUB) {
-          store_agent(a.out + w, y0);
-          store_agent(a.out + w + 1, y1);
-        } else {
-          a.out[w] = y0;
-          a.out[w + 1] = y1;
-        }
+        a.out[w] = y0;
+        a.out[w + 1] = y1;
       } else {
         WT* base = static_cast<WT*>(sec == 1 ? a.kc : a.vc) + ((size_t)head * a.C + slot) * a.dh + d;
-        if constexpr (PUB) {
-          static_assert(sizeof(WT) == 2, "published ring rows are bfloat16 pairs");
-          // d is even: the pair is one aligned 32-bit word
-          store_agent(reinterpret_cast<uint32_t*>(base),
-                      (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16));
-        } else {
-          Elem<WT>::store1(base, y0);
-          Elem<WT>::store1(base + 1, y1);
-        }
+        Elem<WT>::store1(base, y0);
+        Elem<WT>::store1(base + 1, y1);
       }
     }
   } else if (EPI == EPI_DEPTH_QKV) {
@@ -218,11 +206,8 @@ constexpr int kGemvWaves = 8;                 // waves per GEMV workgroup
 // MM: rows come from the pointer table a.mats (several matrices, rows_per_mat each);
 // FULL: every pass covers whole chunks (K / chunk is a multiple of 64*U), no guards.
 //
-// The body is a device function so that a fused kernel can run it as one phase: block
-// `blk` of `nblk` takes its share of the row groups, `xs` is the LDS copy of x. PUB: the
-// EPI_QKV outputs are stored with agent-scope (cross-XCD coherent) stores, for readers in
-// other workgroups of the same kernel.
-template <typename WT, int RB, int U, bool ONEPASS, int PRO, int EPI, bool MM, bool FULL, int XR, bool PUB = false>
+// Block `blk` of `nblk` takes its share of the row groups; `xs` is the LDS copy of x.
+template <typename WT, int RB, int U, bool ONEPASS, int PRO, int EPI, bool MM, bool FULL, int XR>
 __device__ __forceinline__ void gemv_body(const GemvArgs& a, float* xs, int blk, int nblk) {
   constexpr int NW = kGemvWaves, NT = NW * 64;
   __shared__ float red[NW];
@@ -455,7 +440,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a, float* xs, int blk,
     if (pp + 1 == np) {
 #pragma unroll
       for (int r = 0; r < RB; ++r) acc[r] = wave_sum(acc[r]);
-      if (lane == 0) epilogue<WT, RB, EPI, PUB>(a, gg, acc, rg, pos, ropes);
+      if (lane == 0) epilogue<WT, RB, EPI>(a, gg, acc, rg, pos, ropes);
 #pragma unroll
       for (int r = 0; r < RB; ++r) acc[r] = 0.f;
     }

@@ -8,6 +8,7 @@ namespace pp {
 
 constexpr int kMaxStreams = 32;   // text + audio streams of the embedding sum
 constexpr int kBlock = 256;       // threads per workgroup (4 waves) for every kernel here
+constexpr int kMaxAttnSplits = 64;  // split-K factor of the decode attention, at most
 
 // ---------------------------------------------------------------- embedding sum
 struct EmbedArgs {
@@ -15,8 +16,8 @@ struct EmbedArgs {
   int32_t ids_arg[kMaxStreams];     // one frame's IDs when ids_dev == nullptr
   const int32_t* ids_dev;           // [rows][n_streams] device IDs (prefill) or nullptr
   float* out;                       // [rows][D]
-  long long* state;                 // if non-null, state[0] := pos, state[1] := seq
-  long long pos, seq;
+  long long* state;                 // if non-null, state[0] := pos
+  long long pos;
   int n_streams, D, rows;
   // RoPE table of this position (decode), computed on the host in float64 and rounded:
   // rope_cs[2j] = cos(pos * omega_j), rope_cs[2j+1] = sin(pos * omega_j), with
@@ -56,7 +57,7 @@ struct GemvArgs {
   int D, dh, C;         // model width, head width, ring capacity (slots)
   void* kc;             // K ring of this layer, batch 0: [H][C][dh]   (depth: [H][C][dh] fp32)
   void* vc;
-  const long long* state;  // state[0] = position of this frame (slot = pos mod C), state[1] = fused frame count
+  const long long* state;  // state[0] = position of this frame (slot = pos mod C)
   long long pos;           // >= 0: the position itself (direct launches); -1: read state[0]
   const float* rope;       // [dh] cos/sin pairs of this frame's position
   int slot_override;    // depth: >= 0 gives the cache row directly
@@ -106,16 +107,6 @@ struct AttnDecodeArgs {
   uint16_t* out16;
 };
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, bool bf16, int dh, hipStream_t s);
-
-// ---------------------------------------------------------------- fused QKV + attention (decode)
-struct QkvAttnFuse {
-  unsigned long long* cnt;  // [H] rows published per head for this layer (monotonic, zeroed at creation)
-  long long seq;            // >= 1: fused frames so far including this one; -1: read state[1]
-  int* err;                 // host-visible word set when a wait times out
-};
-bool qkv_attn_supported(bool bf16, int D, int dh, int H, int S, int n_cu);
-// grid H*S workgroups: QKV rows (g, published) then attention split (blk % S, head blk / S)
-hipError_t launch_qkv_attn(const GemvArgs& g, const AttnDecodeArgs& at, const QkvAttnFuse& f, hipStream_t s);
 
 // ---------------------------------------------------------------- row RMSNorm
 // rows x D; float32 and/or float16 outputs (either may be null); f16_frag: the float16 rows in

@@ -11,7 +11,6 @@
 
 pp_status pp_fail(pp_status st, const std::string& msg);
 pp_status pp_device_check(int* n_cu);
-int env_int(const char* name, int dflt);
 
 struct pp_kv;
 
@@ -37,11 +36,7 @@ struct pp_model {
   float* s = nullptr;        // SiLU(g) * z [F]
   float* part_o = nullptr;   // attention partial outputs [H][S][dh]
   float* part_ml = nullptr;  // attention partial (max, sum) [H][S][2]
-  long long* state = nullptr;  // [0] = position of the frame being decoded, [1] = fused frame count
-  unsigned long long* head_cnt = nullptr;  // [L][H] rows published per head (fused QKV + attention)
-  bool fuse_qkv_attn = false;  // decode runs QKV and attention as one launch
-  long long fused_seq = 0;     // frames decoded with the fused launch
-  int* fuse_err = nullptr;     // pinned host word: a fused wait timed out
+  long long* state = nullptr;  // [0] = position of the frame being decoded
   float* rope = nullptr;       // [dh] cos/sin table of that position
   // batched decode (max_batch > 1): residuals [B][D], queries [B][D] float32; float16
   // normalised rows [B][D], attention outputs [B][D], SiLU products [B][F]; partials
@@ -56,13 +51,15 @@ struct pp_model {
   void* pk_ws = nullptr;
   std::vector<const void*> pk_qkv, pk_o, pk_in, pk_out;
   const void* pk_head = nullptr;
-  int S = 16;                // attention splits per head
+  int S = 16;                // attention splits per head (batch-1 decode)
+  int S_auto = 16;           // the automatic split count (batched decode always uses it)
   int gemv_blocks = 256;     // workgroups per GEMV launch (one per CU)
   int wout_rb = 1;           // rows per group of the W_out GEMV
 
   // prefill workspace (one hipMalloc, sized by max_T)
   void* pws = nullptr;
-  int32_t* ids_dev = nullptr;  // [max_T][n_streams]
+  int32_t* ids_dev = nullptr;  // [ids_frames][n_streams]
+  size_t ids_frames = 0;       // frames of IDs the device region holds
   float* px = nullptr;         // residual stream [T][D] float32
   void* pu = nullptr;          // normalised rows [T][D]: float16 (bf16-weight path) or float32
   void* pq = nullptr;          // rotated Q [H][T][dh]: bfloat16 (bf16-weight path) or float32
@@ -113,7 +110,7 @@ struct pp_model {
   pp_status check_ids(const int32_t* ids, size_t frames) const;
   void embed_tables(pp::EmbedArgs& a) const;
   pp_status stage_ids(const int32_t* ids_host, size_t n, hipStream_t s);
-  hipError_t enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long long pos_arg, long long seq_arg);
+  hipError_t enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long long pos_arg);
   pp_status run_layers(pp_kv* kv, hipStream_t s);
   pp_status decode(pp_kv* kv, const int32_t* ids_host, const int32_t* ids_dev, float* h_out_dev,
                    float* text_logits_dev, hipStream_t s);

@@ -28,7 +28,11 @@ pp_status pp_model::alloc_prefill() {
   const int ns = cfg.n_audio + 1;
   size_t bytes = 0;
   auto take = [&](size_t n) { size_t off = bytes; bytes += (n + 255) / 256 * 256; return off; };
-  const size_t oid = take(sizeof(int32_t) * (T > (size_t)max_batch ? T : (size_t)max_batch) * ns);
+  // host IDs staged for one call: a prefill (T frames), a batched step (max_batch frames) or
+  // an embedding sum over batch x T frames (up to max_T x max_batch)
+  const size_t id_frames = max_T > 0 ? T * (size_t)max_batch : (size_t)max_batch;
+  ids_frames = id_frames;
+  const size_t oid = take(sizeof(int32_t) * id_frames * ns);
   size_t ox = 0, ou = 0, oq = 0, oa = 0, og = 0, orope = 0, ovt = 0, okx = 0, ovx = 0, osplit = 0;
   // key space of a chunk: up to context + 15 history keys (start rounded to 16) + T
   x_pitch = (int)((T + cfg.context + 16 + 63) / 64 * 64);

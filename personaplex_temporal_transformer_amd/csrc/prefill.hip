@@ -721,12 +721,7 @@ static hipError_t launch_cfg(const GemmArgs& g, int n_cu, hipStream_t s) {
 template <int EPI>
 static hipError_t gemm_dispatch(bool bf16, const GemmArgs& g, int n_cu, hipStream_t s) {
   if (bf16) {
-    static const int forced = [] {
-      const char* v = getenv("PP_GEMM_CFG");
-      return v ? atoi(v) : -1;
-    }();
-    int c = forced >= 0 && forced < kNumGemmCfgs && cfg_fits(kGemmCfgs[forced], g, EPI) ? forced
-                                                                                        : pick_cfg(g, EPI, n_cu > 0 ? n_cu : 256);
+    const int c = pick_cfg(g, EPI, n_cu > 0 ? n_cu : 256);
     switch (c) {
 #define PP_CFG_CASE(id, wm, wn, mi, ni, ns, kb, late) \
   case id:                                            \

@@ -188,11 +188,7 @@ static hipError_t launch_epi(const SgemmArgs& a, hipStream_t s) {
   const int nbt = (a.B + 15) / 16;
   // two column tiles per workgroup (each activation fragment feeds two products) when
   // there are enough tiles to keep every CU busy
-  static const int nt_env = [] {
-    const char* v = getenv("PP_SGEMM_NT");
-    return v ? atoi(v) : 2;
-  }();
-  const bool two = nt_env == 2 && tiles % 2 == 0 && tiles >= 512 && nbt <= 2;
+  const bool two = tiles % 2 == 0 && tiles >= 512 && nbt <= 2;
   if (two) {
     const dim3 grid(tiles / 2);
     if (nbt == 1) hipLaunchKernelGGL((k_sgemm<EPI, 1, 2>), grid, block, 0, s, a);

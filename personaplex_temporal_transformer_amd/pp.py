@@ -22,7 +22,7 @@ STATUS_NAMES = {0: "PP_OK", 1: "PP_E_ARG", 2: "PP_E_ID", 3: "PP_E_CAPACITY", 4: 
 EXPORTS = ["pp_temporal_create", "pp_temporal_destroy", "pp_kv_alloc", "pp_kv_free", "pp_kv_reset",
            "pp_kv_info", "pp_kv_load", "pp_kv_store", "pp_embed_sum", "pp_temporal_decode_step",
            "pp_temporal_prefill", "pp_depformer_create", "pp_depformer_destroy", "pp_depformer_step",
-           "pp_last_error", "pp_temporal_set_graph", "pp_temporal_trace", "pp_temporal_trace_read",
+           "pp_last_error", "pp_temporal_set_graph", "pp_temporal_set_attn_splits", "pp_temporal_trace", "pp_temporal_trace_read",
            "pp_depformer_set_graph", "pp_kv_restore", "pp_sample_top_k", "pp_generator_create", "pp_generator_destroy",
            "pp_generator_step", "pp_generator_inspect", "pp_readers_attach", "pp_readers_write",
            "pp_readers_set_visible"]
@@ -111,6 +111,7 @@ def load():
         "pp_depformer_destroy": [VP],
         "pp_depformer_step": [VP, VP, P(I32), P(I32), I32, VP, VP, VP],
         "pp_temporal_set_graph": [VP, I32],
+        "pp_temporal_set_attn_splits": [VP, I32],
         "pp_depformer_set_graph": [VP, I32],
         "pp_temporal_trace": [VP, I32, I32],
         "pp_temporal_trace_read": [VP, P(I64), P(ctypes.c_double)],
@@ -232,6 +233,9 @@ class TemporalModel:
 
     def set_graph(self, enable):
         _check(load().pp_temporal_set_graph(self.handle, 1 if enable else 0))
+
+    def set_attn_splits(self, splits):
+        _check(load().pp_temporal_set_attn_splits(self.handle, int(splits)))
 
     def attach_readers(self, blocks, weights, mem_dim, max_slots, ln_eps=1e-5):
         """pp_readers_attach: reader i after block blocks[i], weights named readers.{i}.norm /
