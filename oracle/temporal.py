@@ -145,8 +145,13 @@ def _lw(W, l, name):
 
 # --------------------------------------------------------------------------- full sequence
 
-def block_full(X, pos, l, W, cfg):
-    """One pre-norm temporal block on a whole sequence X [T, D] at absolute positions pos [T]."""
+def block_full(X, pos, l, W, cfg, cache=None):
+    """One pre-norm temporal block on a whole sequence X [T, D] at absolute positions pos [T].
+
+    cache: optional history (a Cache holding earlier positions of this sequence). Each
+    query then attends to every key of the history and of the sequence inside its window
+    (the same declared mask), and the sequence's post-RoPE keys and raw values are appended
+    to layer l of the cache afterwards."""
     D, H, dh, F = cfg["d_model"], cfg["n_heads"], cfg["d_head"], cfg["d_ff"]
     eps, theta, C = cfg["eps"], cfg["rope_theta"], cfg["context"]
     T = X.shape[0]
@@ -157,25 +162,36 @@ def block_full(X, pos, l, W, cfg):
     V = qkv[:, 2 * D:3 * D].reshape(T, H, dh)
     Q = rope(Q, np.asarray(pos)[:, None], theta)
     K = rope(K, np.asarray(pos)[:, None], theta)
+    kpos, Ka, Va = np.asarray(pos), K, V
+    if cache is not None:
+        # history keys that any query of the sequence can see: 0 <= pos[-1] - p < C + T - 1
+        hist = cache.visible(l, int(pos[-1]), C + T - 1)
+        if hist is not None:
+            kpos = np.concatenate([hist[0], kpos])
+            Ka = np.concatenate([hist[1], K])
+            Va = np.concatenate([hist[2], V])
+        cache.add_block(l, pos, K, V)
     A = np.empty((T, H, dh))
     for h in range(H):
-        A[:, h, :] = attention(Q[:, h], K[:, h], V[:, h], pos, pos, C)
+        A[:, h, :] = attention(Q[:, h], Ka[:, h], Va[:, h], pos, kpos, C)
     y = X + A.reshape(T, D) @ f64(_lw(W, l, "self_attn.out_proj.weight")).T
     gz = rmsnorm(y, _lw(W, l, "norm2.alpha"), eps) @ f64(_lw(W, l, "gating.linear_in.weight")).T
     return y + swiglu(gz, F) @ f64(_lw(W, l, "gating.linear_out.weight")).T
 
 
-def forward_full(ids, W, cfg, p0=0, with_logits=False, after_block=None):
+def forward_full(ids, W, cfg, p0=0, with_logits=False, after_block=None, cache=None):
     """h = final RMSNorm of the 32-block stack over frames ids [T, n_audio+1] placed at
     positions p0 .. p0+T-1 (audit section 3). Returns h [T, D] (and logits [T, V_text-1]
     from the untied text head when with_logits). after_block: optional {l: f} applied to
-    every row of the residual stream after block l (a memory reader)."""
+    every row of the residual stream after block l (a memory reader). cache: optional
+    history of earlier positions (a prompt replayed into a live cache, audit section 9);
+    the frames' keys and values are appended to it."""
     ids = np.asarray(ids)
     T = ids.shape[0]
     pos = np.arange(p0, p0 + T)
     X = np.stack([embed(ids[t], W, cfg) for t in range(T)])
     for l in range(cfg["n_layers"]):
-        X = block_full(X, pos, l, W, cfg)
+        X = block_full(X, pos, l, W, cfg, cache)
         if after_block and l in after_block:
             X = np.stack([after_block[l](X[t]) for t in range(T)])
     h = rmsnorm(X, W["out_norm.alpha"], cfg["eps"])
@@ -199,7 +215,8 @@ class Cache:
         self.layers[l].append((np.asarray(positions, np.int64), k, v))
 
     def visible(self, l, pos, window):
-        """Positions, keys and values (fp64) of layer l inside the window of query pos."""
+        """Positions, keys and values (fp64) of layer l inside the window of query pos, or
+        None when no stored key is inside it."""
         ps, ks, vs = [], [], []
         for p, k, v in self.layers[l]:
             sel = (pos - p >= 0) & (pos - p < window)
@@ -207,6 +224,8 @@ class Cache:
                 ps.append(p[sel])
                 ks.append(f64(k[sel]))
                 vs.append(f64(v[sel]))
+        if not ps:
+            return None
         return np.concatenate(ps), np.concatenate(ks), np.concatenate(vs)
 
 

@@ -151,6 +151,7 @@ pp_status pp_model::alloc_decode(int D, int F, int H, int dh) {
   part_ml = reinterpret_cast<float*>(b + oml);
   state = reinterpret_cast<long long*>(b + ost);
   rope = reinterpret_cast<float*>(b + orp);
+  db = DecodeBufs{x, q, o, s, part_o, part_ml, state, rope};
   if (nb) {
     bx = reinterpret_cast<float*>(b + obx);
     bq = reinterpret_cast<float*>(b + obq);
@@ -384,7 +385,8 @@ extern "C" pp_status pp_embed_sum(const pp_model* mc, const int32_t* ids_host, i
 
 // pos_arg: the frame's position, passed by value to the kernels of a direct launch; -1
 // when the launches are captured into a graph, whose kernels read it from `state`.
-hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long long pos_arg) {
+hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long long pos_arg,
+                                     const DecodeBufs& b) {
   const pp_temporal_config& c = cfg;
   const int D = c.d_model, F = c.d_ff, H = c.n_heads, dh = c.d_head, C = c.context;
   const size_t esz = bf16 ? 2 : 4;
@@ -395,12 +397,12 @@ hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long 
     char* vbase = kbase + per_kv;
 
     GemvArgs g{};
-    g.W = w_qkv[l]; g.x = x; g.alpha = norm1[l]; g.eps = (float)c.eps; g.K = D;
-    g.n_groups = 3 * D / 2; g.out = q; g.D = D; g.dh = dh; g.C = C; g.kc = kbase; g.vc = vbase;
-    g.state = state; g.pos = pos_arg; g.rope = rope;
+    g.W = w_qkv[l]; g.x = b.x; g.alpha = norm1[l]; g.eps = (float)c.eps; g.K = D;
+    g.n_groups = 3 * D / 2; g.out = b.q; g.D = D; g.dh = dh; g.C = C; g.kc = kbase; g.vc = vbase;
+    g.state = b.state; g.pos = pos_arg; g.rope = b.rope;
     AttnDecodeArgs at{};
-    at.q = q; at.k = kbase; at.v = vbase; at.state = state; at.pos = pos_arg; at.C = C; at.H = H; at.S = S;
-    at.scale = 1.0f / std::sqrt((float)dh); at.part_o = part_o; at.part_ml = part_ml; at.out = o;
+    at.q = b.q; at.k = kbase; at.v = vbase; at.state = b.state; at.pos = pos_arg; at.C = C; at.H = H; at.S = S;
+    at.scale = 1.0f / std::sqrt((float)dh); at.part_o = b.part_o; at.part_ml = b.part_ml; at.out = b.o;
     const bool merge_in_wo = S <= 8 && D <= 4096;
     at.combine = merge_in_wo ? 0 : 1;
     e = launch_gemv(PRO_RMSNORM, EPI_QKV, bf16, 2, g, gemv_blocks, s);
@@ -408,16 +410,16 @@ hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long 
     if (e != hipSuccess) break;
 
     GemvArgs go{};
-    go.W = w_o[l]; go.x = o; go.K = D; go.n_groups = D / 2; go.out = x;
-    go.po = part_o; go.pml = part_ml; go.pS = S; go.adh = dh;
+    go.W = w_o[l]; go.x = b.o; go.K = D; go.n_groups = D / 2; go.out = b.x;
+    go.po = b.part_o; go.pml = b.part_ml; go.pS = S; go.adh = dh;
     e = launch_gemv(merge_in_wo ? PRO_ATTN_MERGE : PRO_COPY, EPI_RESID, bf16, 2, go, gemv_blocks, s);
     if (e != hipSuccess) break;
 
     const bool tr = traced && l == trace_layer && trace_used + 2 <= trace_ev.size();
     if (tr) (void)hipEventRecord(trace_ev[trace_used], s);
     GemvArgs gi{};
-    gi.W = w_in[l]; gi.x = x; gi.alpha = norm2[l]; gi.eps = (float)c.eps; gi.K = D;
-    gi.n_groups = F; gi.out = this->s; gi.F = F;
+    gi.W = w_in[l]; gi.x = b.x; gi.alpha = norm2[l]; gi.eps = (float)c.eps; gi.K = D;
+    gi.n_groups = F; gi.out = b.s; gi.F = F;
     e = launch_gemv(PRO_RMSNORM, EPI_SWIGLU, bf16, 2, gi, gemv_blocks, s);
     for (int r = 1; tr && r < trace_repeat && e == hipSuccess; ++r)
       e = launch_gemv(PRO_RMSNORM, EPI_SWIGLU, bf16, 2, gi, gemv_blocks, s);
@@ -428,9 +430,9 @@ hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long 
     if (e != hipSuccess) break;
 
     GemvArgs gw{};
-    gw.W = w_out[l]; gw.x = this->s; gw.K = F; gw.n_groups = D / wout_rb; gw.out = x;
+    gw.W = w_out[l]; gw.x = b.s; gw.K = F; gw.n_groups = D / wout_rb; gw.out = b.x;
     e = launch_gemv(PRO_COPY, EPI_RESID, bf16, wout_rb, gw, gemv_blocks, s);
-    if (e == hipSuccess) e = enqueue_reader(l, s);
+    if (e == hipSuccess) e = enqueue_reader(l, s, b);
   }
   return e;
 }
@@ -438,7 +440,7 @@ hipError_t pp_model::enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long 
 pp_status pp_model::run_layers(pp_kv* kv, hipStream_t s) {
   const bool traced = trace_layer >= 0;
   if (!use_graph || traced) {
-    hipError_t e = kv->B > 1 ? enqueue_layers_batched(kv, s, kv->pos) : enqueue_layers(kv, s, traced, kv->pos);
+    hipError_t e = kv->B > 1 ? enqueue_layers_batched(kv, s, kv->pos) : enqueue_layers(kv, s, traced, kv->pos, db);
     if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("decode launch: ") + hipGetErrorString(e));
     return PP_OK;
   }
@@ -452,7 +454,7 @@ pp_status pp_model::run_layers(pp_kv* kv, hipStream_t s) {
       return pp_fail(PP_E_HIP, "hipStreamCreate for graph capture failed");
     hipError_t e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
     if (e == hipSuccess) {
-      hipError_t le = kv->B > 1 ? enqueue_layers_batched(kv, cap, -1) : enqueue_layers(kv, cap, false, -1);
+      hipError_t le = kv->B > 1 ? enqueue_layers_batched(kv, cap, -1) : enqueue_layers(kv, cap, false, -1, db);
       e = hipStreamEndCapture(cap, &kv->graph);
       if (le != hipSuccess) e = le;
     }
@@ -484,6 +486,14 @@ pp_status pp_model::decode(pp_kv* kv, const int32_t* ids_host, const int32_t* id
     if (readers.visible > 0) return pp_fail(PP_E_ARG, "memory readers run in batch-1 decode only");
     return decode_batched(kv, ids_host, h_out_dev, text_logits_dev, s);
   }
+  return decode_one(kv, ids_host, ids_dev, h_out_dev, text_logits_dev, s, db, true);
+}
+
+// One batch-1 frame with the step's intermediates in `b`. graph: replay / capture the layer
+// stack as a HIP graph when the model is in graph mode (the model's own buffers only);
+// otherwise every kernel is launched directly with the position passed by value.
+pp_status pp_model::decode_one(pp_kv* kv, const int32_t* ids_host, const int32_t* ids_dev, float* h_out_dev,
+                               float* text_logits_dev, hipStream_t s, const DecodeBufs& b, bool graph) {
   const pp_temporal_config& c = cfg;
 
   EmbedArgs a{};
@@ -493,11 +503,11 @@ pp_status pp_model::decode(pp_kv* kv, const int32_t* ids_host, const int32_t* id
   } else {
     for (int k = 0; k < a.n_streams; ++k) a.ids_arg[k] = ids_host[k];
   }
-  a.out = x;
+  a.out = b.x;
   a.rows = 1;
-  a.state = state;
+  a.state = b.state;
   a.pos = kv->pos;
-  a.rope = rope;
+  a.rope = b.rope;
   a.dh = c.d_head;
   // RoPE angles pos * theta^(-2j/d_head) formed in float64 on the host
   for (int j = 0; j < c.d_head / 2; ++j) {
@@ -508,13 +518,17 @@ pp_status pp_model::decode(pp_kv* kv, const int32_t* ids_host, const int32_t* id
   hipError_t e = launch_embed(a, bf16, s);
   if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("embed: ") + hipGetErrorString(e));
 
-  pp_status st = run_layers(kv, s);
-  if (st) return st;
+  if (graph) {
+    pp_status st = run_layers(kv, s);
+    if (st) return st;
+  } else if ((e = enqueue_layers(kv, s, false, kv->pos, b)) != hipSuccess) {
+    return pp_fail(PP_E_HIP, std::string("decode launch: ") + hipGetErrorString(e));
+  }
 
-  e = launch_rmsnorm_rows(x, out_norm, (float)c.eps, c.d_model, 1, h_out_dev, nullptr, false, s);
+  e = launch_rmsnorm_rows(b.x, out_norm, (float)c.eps, c.d_model, 1, h_out_dev, nullptr, false, s);
   if (e == hipSuccess && text_logits_dev) {
     GemvArgs g{};
-    g.W = text_head; g.x = x; g.alpha = out_norm; g.eps = (float)c.eps; g.K = c.d_model;
+    g.W = text_head; g.x = b.x; g.alpha = out_norm; g.eps = (float)c.eps; g.K = c.d_model;
     g.n_groups = (c.text_vocab - 1) / 2; g.out = text_logits_dev;
     if ((c.text_vocab - 1) % 2 == 0) {
       e = launch_gemv(PRO_RMSNORM, EPI_STORE, bf16, 2, g, gemv_blocks, s);

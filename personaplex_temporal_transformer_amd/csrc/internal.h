@@ -172,14 +172,15 @@ struct GemmArgs {
   float* x;             // GEPI_RESID: x[row][col] += (A W^T)[row][col], float32 [M][N]
   void* s_out;          // GEPI_SWIGLU: [M][F] = SiLU(g) * z (float16 on the bf16-weight path)
   int F;
-  // GEPI_QKV, bf16 only: Q goes to q_out as bfloat16; if non-null, V is also written
+  // GEPI_QKV, bf16 only: Q goes to q_out as float16; if non-null, V is also written
   // transposed as float16, vt[H][dh][vt_pitch]: key index j in column vt_perm(j) (bits 2
   // and 3 of j swapped), for the prefill attention; row `row` is key index xoff + row
   void* vt;
   int vt_pitch;
-  // GEPI_QKV, a chunk that starts past position 0: K (and on the float32 path V) are also
-  // written to the chunk's contiguous key space kx / vx [H][x_pitch][dh] at key index
-  // xoff + row (xoff a multiple of 16), where the attention reads them
+  // GEPI_QKV: K (and on the float32 path V) are also written to the chunk's contiguous key
+  // space kx / vx [H][x_pitch][dh] at key index xoff + row (xoff a multiple of 16), where
+  // the attention reads them -- always on the bf16 path (K as float16), on the float32 path
+  // for a chunk that starts past position 0
   void* kx;
   void* vx;
   int x_pitch, xoff;
@@ -198,8 +199,9 @@ hipError_t launch_bf16_to_f16(const void* src, void* dst, size_t n_elems, hipStr
 // space: key index j is position p0 - koff + j, query i is key index koff + i. Keys
 // [jlo, koff) are the history gathered from the ring, [koff, koff + T) the chunk's own.
 struct AttnPrefillArgs {
-  const void* q;        // [H][T][dh] rotated queries (bfloat16 on the bf16 path)
-  const void* k;        // keys [H][k_pitch][dh] (the ring itself when koff == 0)
+  const void* q;        // [H][T][dh] rotated queries (float16 on the bf16 path)
+  const void* k;        // keys [H][k_pitch][dh]: the key space (float16 on the bf16 path), or on
+                        // the float32 path for koff == 0 the ring itself
   const void* v;        // float32 path: values, same layout as k
   const void* vt;       // bf16 path: V transposed, float16 [H][dh][vt_pitch], key j in column vt_perm(j)
   int vt_pitch, k_pitch;
@@ -218,8 +220,9 @@ struct AttnPrefillArgs {
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, bool bf16, int dh, hipStream_t s);
 
 // History of a chunk at p0 > 0: keys [jlo, jhi) of its key space (positions q0 + j) are
-// copied from their ring slots (q0 + j) mod C -- K to kx, V to vt (bf16 path, transposed
-// float16) or vx (float32 path) -- and keys [0, jlo) are zero-filled. jhi is a multiple of 16.
+// copied from their ring slots (q0 + j) mod C -- K to kx (float16 on the bf16 path), V to vt
+// (bf16 path, transposed float16) or vx (float32 path) -- and keys [0, jlo) are zero-filled.
+// jhi is a multiple of 16.
 struct GatherArgs {
   const void* kring;
   const void* vring;    // this layer's ring [H][C][dh]

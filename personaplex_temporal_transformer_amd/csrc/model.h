@@ -14,6 +14,18 @@ pp_status pp_device_check(int* n_cu);
 
 struct pp_kv;
 
+// The per-step intermediates of a batch-1 decode frame (device memory).
+struct DecodeBufs {
+  float* x;          // residual stream [D] float32
+  float* q;          // rotated query [D]
+  float* o;          // attention output [D]
+  float* s;          // SiLU(g) * z [F]
+  float* part_o;     // attention partial outputs [H][S][dh]
+  float* part_ml;    // attention partial (max, sum) [H][S][2]
+  long long* state;  // [0] = position of the frame being decoded (read by graph replays)
+  float* rope;       // [dh] cos/sin table of that position
+};
+
 struct pp_model {
   pp_temporal_config cfg{};
   bool bf16 = true;
@@ -38,6 +50,7 @@ struct pp_model {
   float* part_ml = nullptr;  // attention partial (max, sum) [H][S][2]
   long long* state = nullptr;  // [0] = position of the frame being decoded
   float* rope = nullptr;       // [dh] cos/sin table of that position
+  DecodeBufs db{};             // the above, as one set
   // batched decode (max_batch > 1): residuals [B][D], queries [B][D] float32; float16
   // normalised rows [B][D], attention outputs [B][D], SiLU products [B][F]; partials
   float* bx = nullptr;
@@ -62,14 +75,14 @@ struct pp_model {
   size_t ids_frames = 0;       // frames of IDs the device region holds
   float* px = nullptr;         // residual stream [T][D] float32
   void* pu = nullptr;          // normalised rows [T][D]: float16 (bf16-weight path) or float32
-  void* pq = nullptr;          // rotated Q [H][T][dh]: bfloat16 (bf16-weight path) or float32
+  void* pq = nullptr;          // rotated Q [H][T][dh]: float16 (bf16-weight path) or float32
   void* pa = nullptr;          // attention output [T][D], same element type
   void* pg = nullptr;          // SiLU(g)*z [T][F], same element type
   float* psplit = nullptr;     // bf16-weight path: split-K partial sums of the small-M products
   size_t psplit_bytes = 0;
   float* prope = nullptr;      // RoPE table [T][dh] (cos, sin pairs)
   void* pvt = nullptr;         // bf16-weight path: V transposed, float16 [H][dh][vt_pitch] of a chunk's key space
-  void* pkx = nullptr;         // a chunk's key space: K [H][x_pitch][dh] (wdtype)
+  void* pkx = nullptr;         // a chunk's key space: K [H][x_pitch][dh] (float16 on the bf16-weight path, else float32)
   void* pvx = nullptr;         // float32 path: V [H][x_pitch][dh]
   int vt_pitch = 0, x_pitch = 0;
   void* pf16_ws = nullptr;     // bf16-weight path: float16 copies of the block matrices (one allocation)
@@ -93,7 +106,7 @@ struct pp_model {
     void* ws = nullptr;
     ~ReaderSet();
   } readers;
-  hipError_t enqueue_reader(int l, hipStream_t s);
+  hipError_t enqueue_reader(int l, hipStream_t s, const DecodeBufs& b);
 
   // launch mode and timing
   bool use_graph = true;
@@ -110,10 +123,12 @@ struct pp_model {
   pp_status check_ids(const int32_t* ids, size_t frames) const;
   void embed_tables(pp::EmbedArgs& a) const;
   pp_status stage_ids(const int32_t* ids_host, size_t n, hipStream_t s);
-  hipError_t enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long long pos_arg);
+  hipError_t enqueue_layers(pp_kv* kv, hipStream_t s, bool traced, long long pos_arg, const DecodeBufs& b);
   pp_status run_layers(pp_kv* kv, hipStream_t s);
   pp_status decode(pp_kv* kv, const int32_t* ids_host, const int32_t* ids_dev, float* h_out_dev,
                    float* text_logits_dev, hipStream_t s);
+  pp_status decode_one(pp_kv* kv, const int32_t* ids_host, const int32_t* ids_dev, float* h_out_dev,
+                       float* text_logits_dev, hipStream_t s, const DecodeBufs& b, bool graph);
   hipError_t enqueue_layers_batched(pp_kv* kv, hipStream_t s, long long pos_arg);
   pp_status pack_batched();
   pp_status decode_batched(pp_kv* kv, const int32_t* ids_host, float* h_out_dev, float* text_logits_dev,

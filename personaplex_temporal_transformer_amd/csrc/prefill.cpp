@@ -175,7 +175,7 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
     g.q_out = m->pq; g.kc = kbase; g.vc = vbase; g.rope = m->prope;
     g.D = D; g.dh = dh; g.C = C; g.p0 = (int)(p0 % C);
     g.vt = m->pvt; g.vt_pitch = m->vt_pitch;
-    if (koff > 0) {
+    if (koff > 0 || bf) {   // the bf16-weight path's attention always reads float16 K from the key space
       g.kx = m->pkx; g.vx = bf ? nullptr : m->pvx; g.x_pitch = m->x_pitch; g.xoff = koff;
     }
     e = launch_gemm(GEPI_QKV, bf, g, m->n_cu, s);
@@ -183,7 +183,7 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
 
     AttnPrefillArgs at{};
     at.q = m->pq; at.vt = m->pvt; at.vt_pitch = m->vt_pitch; at.out = m->pa;
-    if (koff > 0) {
+    if (koff > 0 || bf) {
       at.k = m->pkx; at.v = m->pvx; at.k_pitch = m->x_pitch;
     } else {
       at.k = kbase; at.v = vbase; at.k_pitch = C;

@@ -88,7 +88,7 @@ __device__ __forceinline__ int swz(int r, int kc) { return r * 8 + swz_slot(r, k
 
 // Column of key t in the transposed V copy: bits 2 and 3 of t swapped, so that within
 // each group of 16 keys the order is 0-3, 8-11, 4-7, 12-15 -- the order in which one
-// lane holds probabilities after the S^T product (see k_attn_prefill_bf16).
+// lane holds probabilities after the S^T product (see k_attn_prefill_f16).
 __device__ __forceinline__ int vt_perm(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
 
 // Wait until at most N vector-memory operations of this wave are outstanding and all its
@@ -441,18 +441,26 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_f16(GemmArgs g) {
             v[2 * k + 1] = e * sn + o * cc;
           }
         }
-        // Q, K and V are bfloat16 (K and V in the ring, as in decode; Q meets K in a
-        // bfloat16 product)
-        uint32_t pk[4];
+        // K and V go to the ring as bfloat16 (the cache type, read by decode). The chunk's
+        // own attention takes Q and K as float16 (Q here, K in the key space): an 8-bit
+        // significand on both sides of Q.K^T costs about as much accuracy per block as the
+        // ring's rounding itself.
+        uint32_t pk[4], ph[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) pk[k] = (uint32_t)f32_to_bf16(v[2 * k]) | ((uint32_t)f32_to_bf16(v[2 * k + 1]) << 16);
-        uint16_t* dst;
-        if (sec == 0) dst = static_cast<uint16_t*>(g.q_out) + ((size_t)head * g.M + row) * g.dh + d;
-        else dst = static_cast<uint16_t*>(sec == 1 ? g.kc : g.vc) + ((size_t)head * g.C + (g.p0 + row) % g.C) * g.dh + d;
-        *reinterpret_cast<u32x4*>(dst) = u32x4{pk[0], pk[1], pk[2], pk[3]};
-        if (sec == 1 && g.kx)
-          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.kx) + ((size_t)head * g.x_pitch + g.xoff + row) * g.dh + d) =
-              u32x4{pk[0], pk[1], pk[2], pk[3]};
+        for (int k = 0; k < 4; ++k) {
+          pk[k] = (uint32_t)f32_to_bf16(v[2 * k]) | ((uint32_t)f32_to_bf16(v[2 * k + 1]) << 16);
+          ph[k] = (uint32_t)f32_to_f16(v[2 * k]) | ((uint32_t)f32_to_f16(v[2 * k + 1]) << 16);
+        }
+        if (sec == 0) {
+          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.q_out) + ((size_t)head * g.M + row) * g.dh + d) =
+              u32x4{ph[0], ph[1], ph[2], ph[3]};
+        } else {
+          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(sec == 1 ? g.kc : g.vc) +
+                                    ((size_t)head * g.C + (g.p0 + row) % g.C) * g.dh + d) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+          if (sec == 1 && g.kx)
+            *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.kx) + ((size_t)head * g.x_pitch + g.xoff + row) * g.dh + d) =
+                u32x4{ph[0], ph[1], ph[2], ph[3]};
+        }
       }
       if (sec == 2 && g.vt) {
         // key t of the tile sits in column xoff + vt_perm(t) (xoff is a multiple of 16);
@@ -779,13 +787,13 @@ hipError_t launch_gemm(int epi, bool bf16, const GemmArgs& g, int n_cu, hipStrea
   return hipErrorInvalidValue;
 }
 
-// ---------------------------------------------------------------- bf16 flash attention
+// ---------------------------------------------------------------- flash attention (bf16-weight path)
 
 // Workgroup = 128 queries of one head, 4 waves; wave w owns queries qb*128 + 32w .. +31,
 // one per lane column (lane % 32). Keys go by blocks of 64 through two LDS stages, loaded
-// straight from global memory: K rows of the chunk's key space (the ring itself for a
-// prefill from position 0) and the matching 64 columns of the transposed V copy. Query i
-// is key index koff + i. Per key block:
+// straight from global memory: float16 K rows of the chunk's key space and the matching 64
+// columns of the transposed float16 V copy; Q is float16 as well. Query i is key index
+// koff + i. Per key block:
 //   S^T = K Q^T   (A = K rows from LDS, B = Q^T kept in registers): lane (q, half) holds
 //                 q's scores for 32 of the 64 keys, its partner lane (lane ^ 32) the other
 //                 32, so the row max and sum need one exchange;
@@ -801,7 +809,7 @@ hipError_t launch_gemm(int epi, bool bf16, const GemmArgs& g, int n_cu, hipStrea
 // blocks and writes the unnormalised O, the running max and the sum, float32, for
 // k_attn_prefill_combine.
 template <int DH>
-__global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void k_attn_prefill_f16(AttnPrefillArgs a) {
   constexpr int BQ = 128, BKV = 64;
   constexpr int KCH = DH / 8;                  // 16-byte chunks per K row
   // slot of chunk c of K row r: 256-byte rows (d_head 128) span the bank window, so XOR
@@ -824,10 +832,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a)
   const int qi = qw0 + ql;                     // this lane's query
   const int qrow = qi < a.T ? qi : a.T - 1;
 
-  bf16x8 qr[DH / 16];
+  f16x8 qr[DH / 16];
   const uint16_t* Q = static_cast<const uint16_t*>(a.q) + ((size_t)h * a.T + qrow) * DH;
 #pragma unroll
-  for (int ks = 0; ks < DH / 16; ++ks) qr[ks] = *reinterpret_cast<const bf16x8*>(Q + ks * 16 + 8 * hi);
+  for (int ks = 0; ks < DH / 16; ++ks) qr[ks] = *reinterpret_cast<const f16x8*>(Q + ks * 16 + 8 * hi);
 
   const int ko = a.koff, nk = a.koff + a.T;
   const u32x4 krs = rsrc_words(static_cast<const uint16_t*>(a.k) + (size_t)h * a.k_pitch * DH, (uint32_t)((size_t)nk * DH * 2));
@@ -891,8 +899,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(AttnPrefillArgs a)
 #pragma unroll
       for (int ks = 0; ks < DH / 16; ++ks) {
         const int r = kt * 32 + ql, ch = ks * 2 + hi;
-        const bf16x8 ka = __builtin_bit_cast(bf16x8, Ks[st][r * KCH + kslot(r, ch)]);
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qr[ks], s[kt], 0, 0, 0);
+        const f16x8 ka = __builtin_bit_cast(f16x8, Ks[st][r * KCH + kslot(r, ch)]);
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qr[ks], s[kt], 0, 0, 0);
       }
     }
     // masking only where the block needs it (causal, window, end of keys, first visible
@@ -1084,8 +1092,8 @@ hipError_t launch_attn_prefill(const AttnPrefillArgs& a, bool bf16, int dh, hipS
       while (sp > 1 && (keys_min / 64 / sp < 4 || per_split * sp > a.part_bytes)) --sp;
     }
     const dim3 grid(wgs, sp);
-    if (dh == 128) hipLaunchKernelGGL(k_attn_prefill_bf16<128>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(k_attn_prefill_bf16<64>, grid, dim3(256), 0, s, a);
+    if (dh == 128) hipLaunchKernelGGL(k_attn_prefill_f16<128>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_attn_prefill_f16<64>, grid, dim3(256), 0, s, a);
     if (sp > 1) {
       const long long rows = (long long)a.T * a.H;  // 8 (d_head 128) or 16 (64) rows per workgroup
       if (dh == 128) hipLaunchKernelGGL(k_attn_prefill_combine<128>, dim3((unsigned)((rows + 7) / 8)), dim3(256), 0, s, a, sp);
@@ -1120,6 +1128,29 @@ __global__ __launch_bounds__(kBlock) void k_gather_rows(GatherArgs a, const void
     v = *reinterpret_cast<const u32x4*>(static_cast<const T*>(ring) + ((size_t)h * a.C + pos % a.C) * a.dh + c * EPC);
   }
   *reinterpret_cast<u32x4*>(static_cast<T*>(dst) + ((size_t)h * a.x_pitch + j) * a.dh + c * EPC) = v;
+}
+
+// bf16 path, K rows widened to float16 (the prefill attention's key operand): one thread
+// per 8 values of a row. bfloat16 -> float16 is exact inside float16's normal range.
+__global__ __launch_bounds__(kBlock) void k_gather_k16(GatherArgs a) {
+  const int cpr = a.dh / 8;
+  const long long n = (long long)a.H * a.jhi * cpr;
+  const long long i = (long long)blockIdx.x * kBlock + threadIdx.x;
+  if (i >= n) return;
+  const int c = (int)(i % cpr);
+  const long long hj = i / cpr;
+  const int j = (int)(hj % a.jhi), h = (int)(hj / a.jhi);
+  u32x4 v = u32x4{0u, 0u, 0u, 0u};
+  if (j >= a.jlo) {
+    const long long pos = a.q0 + j;   // >= 0 for j >= jlo
+    v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.kring) + ((size_t)h * a.C + pos % a.C) * a.dh + c * 8);
+  }
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    w[e] = (uint32_t)f32_to_f16(bf16_lo(v[e])) | ((uint32_t)f32_to_f16(bf16_hi(v[e])) << 16);
+  *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.kx) + ((size_t)h * a.x_pitch + j) * a.dh + c * 8) =
+      u32x4{w[0], w[1], w[2], w[3]};
 }
 
 // bf16 path, V transposed to float16 through LDS: one workgroup per (64 keys, head). The
@@ -1164,7 +1195,7 @@ hipError_t launch_gather_history(const GatherArgs& a, bool bf16, hipStream_t s) 
   if (bf16) {
     // V^T tiles of 64 columns (the last one up to a multiple of 64) inside the V^T rows
     if (!a.vt || a.dh > 128 || (a.jhi + 63) / 64 * 64 > a.vt_pitch) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_gather_rows<uint16_t>, gr, dim3(kBlock), 0, s, a, a.kring, a.kx);
+    hipLaunchKernelGGL(k_gather_k16, gr, dim3(kBlock), 0, s, a);
     hipLaunchKernelGGL(k_gather_vt, dim3((unsigned)((a.jhi + 63) / 64), (unsigned)a.H), dim3(256), 0, s, a);
   } else {
     if (!a.vx) return hipErrorInvalidValue;

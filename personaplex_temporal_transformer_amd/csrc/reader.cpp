@@ -98,26 +98,26 @@ extern "C" pp_status pp_readers_set_visible(pp_model* m, int32_t n_visible) {
 }
 
 // The reader after block l, if any and if some memory row is visible (decode, batch 1).
-hipError_t pp_model::enqueue_reader(int l, hipStream_t s) {
+hipError_t pp_model::enqueue_reader(int l, hipStream_t s, const DecodeBufs& b) {
   if (readers.visible <= 0) return hipSuccess;
   const pp_temporal_config& c = cfg;
   const int D = c.d_model, H = c.n_heads, dh = c.d_head;
   for (const Reader& r : readers.r) {
     if (r.block != l) continue;
     GemvArgs gq{};
-    gq.W = r.w.w_q; gq.x = x; gq.alpha = r.w.ln_w; gq.beta = r.w.ln_b; gq.eps = (float)readers.eps;
-    gq.K = D; gq.n_groups = D / 2; gq.out = q; gq.add = r.w.b_q;
+    gq.W = r.w.w_q; gq.x = b.x; gq.alpha = r.w.ln_w; gq.beta = r.w.ln_b; gq.eps = (float)readers.eps;
+    gq.K = D; gq.n_groups = D / 2; gq.out = b.q; gq.add = r.w.b_q;
     hipError_t e = launch_gemv(PRO_LAYERNORM, EPI_STORE, bf16, 2, gq, gemv_blocks, s);
     if (e != hipSuccess) return e;
     const bool merge_in_wo = S <= 8 && D <= 4096;
     AttnDecodeArgs at{};
-    at.q = q; at.k = r.K; at.v = r.V; at.state = state; at.pos = readers.visible - 1; at.C = readers.max_slots;
-    at.H = H; at.S = S; at.scale = 1.0f / std::sqrt((float)dh); at.part_o = part_o; at.part_ml = part_ml;
-    at.out = o; at.combine = merge_in_wo ? 0 : 1;
+    at.q = b.q; at.k = r.K; at.v = r.V; at.state = b.state; at.pos = readers.visible - 1; at.C = readers.max_slots;
+    at.H = H; at.S = S; at.scale = 1.0f / std::sqrt((float)dh); at.part_o = b.part_o; at.part_ml = b.part_ml;
+    at.out = b.o; at.combine = merge_in_wo ? 0 : 1;
     if ((e = launch_attn_decode(at, bf16, dh, s)) != hipSuccess) return e;
     GemvArgs go{};
-    go.W = r.w.w_o; go.x = o; go.K = D; go.n_groups = D / 2; go.out = x; go.add = r.w.b_o;
-    go.po = part_o; go.pml = part_ml; go.pS = S; go.adh = dh;
+    go.W = r.w.w_o; go.x = b.o; go.K = D; go.n_groups = D / 2; go.out = b.x; go.add = r.w.b_o;
+    go.po = b.part_o; go.pml = b.part_ml; go.pS = S; go.adh = dh;
     return launch_gemv(merge_in_wo ? PRO_ATTN_MERGE : PRO_COPY, EPI_RESID, bf16, 2, go, gemv_blocks, s);
   }
   return hipSuccess;

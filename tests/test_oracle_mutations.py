@@ -63,6 +63,8 @@ MUTATIONS = [
      'y = f64(_lw(W, l, "self_attn.out_proj.weight")) @ a.reshape(D)'),
     ("stream k reads audio table k", "temporal.py",
      'W["emb.%d.weight" % (k - 1)]', 'W["emb.%d.weight" % (k % 16)]'),
+    ("chunk ignores the history", "temporal.py",
+     "hist = cache.visible(l, int(pos[-1]), C + T - 1)", "hist = None"),
     ("depth FFN g/z swapped", "depformer.py",
      "(silu(gz[:F]) * gz[F:])", "(silu(gz[F:]) * gz[:F])"),
     ("depth FFN of position q+1", "depformer.py",

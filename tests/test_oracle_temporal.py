@@ -342,3 +342,37 @@ def test_two_frame_block_fixes_q_before_k_and_score_scale():
     cache = O.Cache(1)
     inc = np.stack([O.decode_step(X[t], pos[t], cache, W, cfg) for t in range(2)])
     assert np.allclose(inc, want, atol=1e-12)
+
+
+@pytest.mark.parametrize("context", [3000, 4])
+def test_chunk_over_history_equals_full_sequence(context):
+    """A sequence split into two chunks, the second run against the history the first left
+    in a cache (a prompt replayed into a live cache, audit section 9), gives the rows of
+    the one full-sequence forward; with context 4 the second chunk's window also drops
+    history keys."""
+    cfg, W, ids = _tiny()
+    cfg = synth.with_(cfg, context=context)
+    full = O.forward_full(ids, W, cfg)
+    c = O.Cache(cfg["n_layers"])
+    a = O.forward_full(ids[:9], W, cfg, cache=c)
+    b = O.forward_full(ids[9:], W, cfg, p0=9, cache=c)
+    assert np.max(np.abs(a - full[:9])) < 1e-12
+    assert np.max(np.abs(b - full[9:])) < 1e-12
+    assert [blk[0][0] for blk in c.layers[0]] == [0, 9]   # both chunks' keys were appended
+
+
+def test_chunk_over_synthetic_history_equals_incremental_decode():
+    """History keys/values that no forward produced (random, as a loaded ring): a 5-frame
+    chunk at positions 20..24 against a 6-key window equals frame-by-frame decode over the
+    same history."""
+    cfg, W, ids = _tiny()
+    cfg = synth.with_(cfg, context=6)
+    L, H, dh = cfg["n_layers"], cfg["n_heads"], cfg["d_head"]
+    rng = np.random.default_rng(7)
+    ks = [rng.standard_normal((20, H, dh)) for _ in range(L)]
+    vs = [rng.standard_normal((20, H, dh)) for _ in range(L)]
+    c1 = O.cache_from_blocks(ks, vs, np.arange(20), L)
+    c2 = O.cache_from_blocks(ks, vs, np.arange(20), L)
+    got = O.forward_full(ids[:5], W, cfg, p0=20, cache=c1)
+    want = O.decode_incremental(ids[:5], W, cfg, p0=20, cache=c2)
+    assert np.max(np.abs(got - want)) < 1e-12
