@@ -154,6 +154,21 @@ pp_status pp_embed_sum(const pp_model* m, const int32_t* ids_host, int32_t batch
 pp_status pp_temporal_decode_step(pp_model* m, pp_kv* kv, const int32_t* ids_host,
                                   float* h_out_dev, float* text_logits_dev, void* stream);
 
+/* For callers that cannot allocate device memory during a step (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same batch-1 frame
+ * as pp_temporal_decode_step, with the same results bit for bit, that calls no allocating
+ * routine. Every kernel is launched directly (no graph is captured), and the step's
+ * intermediates live in a 1 MiB device array that the library holds on each GPU until the
+ * process ends, instead of the model's workspace. The step needs
+ * 4*(3*d_model + d_ff + n_heads*splits*(d_head + 2) + d_head) + 32 bytes of it (each of its
+ * eight regions rounded up to 256 bytes; 228 KB at full size with the automatic 8
+ * splits); more gives PP_E_CAPACITY. All calls on one GPU share that array: calls that
+ * overlap on one GPU (two streams, threads or models) race. The first call on a device
+ * looks up the array's address there. Requirements: a batch-1 ring, no visible memory
+ * readers (else PP_E_ARG), the model's device current (else PP_E_DEVICE). */
+pp_status pp_temporal_decode_step_noalloc(pp_model* m, pp_kv* kv, const int32_t* ids_host,
+                                          float* h_out_dev, float* text_logits_dev, void* stream);
+
 /* Full-sequence forward of T frames at positions p..p+T-1, p = the ring's position
  * (audit section 3; section 9 for prompts replayed into a live ring): causal attention
  * among the frames and, when p > 0, over the keys of the ring still inside each frame's

@@ -20,7 +20,7 @@ STATUS_NAMES = {0: "PP_OK", 1: "PP_E_ARG", 2: "PP_E_ID", 3: "PP_E_CAPACITY", 4: 
 
 # Every entry point declared in include/pp.h.
 EXPORTS = ["pp_temporal_create", "pp_temporal_destroy", "pp_kv_alloc", "pp_kv_free", "pp_kv_reset",
-           "pp_kv_info", "pp_kv_load", "pp_kv_store", "pp_embed_sum", "pp_temporal_decode_step",
+           "pp_kv_info", "pp_kv_load", "pp_kv_store", "pp_embed_sum", "pp_temporal_decode_step", "pp_temporal_decode_step_noalloc",
            "pp_temporal_prefill", "pp_depformer_create", "pp_depformer_destroy", "pp_depformer_step",
            "pp_last_error", "pp_temporal_set_graph", "pp_temporal_set_attn_splits", "pp_temporal_trace", "pp_temporal_trace_read",
            "pp_depformer_set_graph", "pp_kv_restore", "pp_sample_top_k", "pp_generator_create", "pp_generator_destroy",
@@ -106,6 +106,7 @@ def load():
         "pp_kv_restore": [VP, VP, I64, VP],
         "pp_embed_sum": [VP, P(I32), I32, I32, VP, VP],
         "pp_temporal_decode_step": [VP, VP, P(I32), VP, VP, VP],
+        "pp_temporal_decode_step_noalloc": [VP, VP, P(I32), VP, VP, VP],
         "pp_temporal_prefill": [VP, VP, P(I32), I32, VP, VP],
         "pp_depformer_create": [P(DepthConfig), P(DepthWeights), P(VP)],
         "pp_depformer_destroy": [VP],
@@ -224,6 +225,11 @@ class TemporalModel:
         arr, p = _ids(ids)
         _check(load().pp_temporal_decode_step(self.handle, kv.handle, p, _ptr(h_out), _ptr(logits_out),
                                               _stream(stream)))
+
+    def decode_step_noalloc(self, kv, ids, h_out, logits_out=None, stream=None):
+        arr, p = _ids(ids)
+        _check(load().pp_temporal_decode_step_noalloc(self.handle, kv.handle, p, _ptr(h_out), _ptr(logits_out),
+                                                      _stream(stream)))
 
     def prefill(self, kv, ids, h_out, stream=None):
         ids = np.asarray(ids, np.int32)

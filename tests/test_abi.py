@@ -62,6 +62,7 @@ def test_null_handles_are_argument_errors():
     assert lib.pp_depformer_step(None, None, None, None, 1, None, None, None) == pp.PP_E_ARG
     assert lib.pp_temporal_trace(None, 0, 1) == pp.PP_E_ARG
     assert lib.pp_temporal_set_attn_splits(None, 0) == pp.PP_E_ARG
+    assert lib.pp_temporal_decode_step_noalloc(None, None, None, None, None, None) == pp.PP_E_ARG
     assert lib.pp_temporal_trace_read(None, None, None) == pp.PP_E_ARG
     assert b"NULL" in lib.pp_last_error() or lib.pp_last_error()
 
