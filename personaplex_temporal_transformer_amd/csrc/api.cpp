@@ -115,6 +115,7 @@ extern "C" pp_status pp_temporal_create(const pp_temporal_config* cfg, const pp_
   // attention splits: about one block per CU over all heads (at most kMaxAttnSplits)
   m->S = m->S_auto = auto_splits(n_cu, H);
   st = m->alloc_decode(D, F, H, dh);
+  if (!st && m->bf16 && (max_prefill_T > 0 || max_batch > 1)) st = m->compute_f16_scales();
   if (!st) st = m->alloc_prefill();
   if (!st && max_batch > 1) st = m->pack_batched();
   if (st) {
@@ -176,22 +177,23 @@ pp_status pp_model::pack_batched() {
   char* p = static_cast<char*>(pk_ws);
   hipError_t e = hipSuccess;
   for (size_t l = 0; l < L && e == hipSuccess; ++l) {
+    const F16Exps& fe = f16e[l];
     pk_qkv.push_back(p);
-    e = launch_sgemm_pack(w_qkv[l], p, (int)(3 * D), (int)D, 0, false, nullptr);
+    e = launch_sgemm_pack(w_qkv[l], p, (int)(3 * D), (int)D, 0, false, fe.w_qkv, nullptr);
     p += 3 * D * D * 2;
     pk_o.push_back(p);
-    if (e == hipSuccess) e = launch_sgemm_pack(w_o[l], p, (int)D, (int)D, 0, false, nullptr);
+    if (e == hipSuccess) e = launch_sgemm_pack(w_o[l], p, (int)D, (int)D, 0, false, fe.w_o, nullptr);
     p += D * D * 2;
     pk_in.push_back(p);
-    if (e == hipSuccess) e = launch_sgemm_pack(w_in[l], p, (int)F, (int)D, (int)F, true, nullptr);
+    if (e == hipSuccess) e = launch_sgemm_pack(w_in[l], p, (int)F, (int)D, (int)F, true, fe.w_in, nullptr);
     p += 2 * F * D * 2;
     pk_out.push_back(p);
-    if (e == hipSuccess) e = launch_sgemm_pack(w_out[l], p, (int)D, (int)F, 0, false, nullptr);
+    if (e == hipSuccess) e = launch_sgemm_pack(w_out[l], p, (int)D, (int)F, 0, false, fe.w_out, nullptr);
     p += D * F * 2;
   }
   if (e == hipSuccess && text_head) {
     pk_head = p;
-    e = launch_sgemm_pack(text_head, p, (int)V, (int)D, 0, false, nullptr);
+    e = launch_sgemm_pack(text_head, p, (int)V, (int)D, 0, false, f16e_whead, nullptr);
   }
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("packing weights for batched decode: ") + hipGetErrorString(e));
@@ -555,26 +557,28 @@ hipError_t pp_model::enqueue_layers_batched(pp_kv* kv, hipStream_t s, long long 
   for (int l = 0; l < c.n_layers && e == hipSuccess; ++l) {
     char* kbase = static_cast<char*>(kv->ring) + (size_t)(2 * l) * per_kv;
     char* vbase = kbase + per_kv;
-    if ((e = launch_rmsnorm_rows(bx, norm1[l], (float)c.eps, D, B, nullptr, bu16, true, s)) != hipSuccess) break;
+    const F16Exps& fe = f16e[l];
+    if ((e = launch_rmsnorm_rows(bx, norm1[l], (float)c.eps, D, B, nullptr, bu16, true, s, fe.u1)) != hipSuccess) break;
     SgemmArgs g{};
-    g.act = bu16; g.W = pk_qkv[l]; g.B = B; g.K = D; g.N = 3 * D;
+    g.act = bu16; g.W = pk_qkv[l]; g.B = B; g.K = D; g.N = 3 * D; g.acc_exp = fe.u1 + fe.w_qkv;
     g.q_out = bq; g.kc = kbase; g.vc = vbase; g.kv_bstride = bstride; g.rope = rope; g.state = state;
     g.pos = pos_arg; g.D = D; g.dh = dh; g.C = C;
     if ((e = launch_sgemm(SEPI_QKV, g, s)) != hipSuccess) break;
     AttnDecodeArgs at{};
     at.q = bq; at.k = kbase; at.v = vbase; at.state = state; at.pos = pos_arg; at.C = C; at.H = H; at.S = S_auto;
     at.scale = 1.0f / std::sqrt((float)dh); at.part_o = bpart_o; at.part_ml = bpart_ml; at.combine = 1;
-    at.batch = B; at.kv_bstride = bstride; at.out16 = bo16;
+    at.batch = B; at.kv_bstride = bstride; at.out16 = bo16; at.o16_exp = fe.v;
     if ((e = launch_attn_decode(at, true, dh, s)) != hipSuccess) break;
     SgemmArgs go{};
-    go.act = bo16; go.W = pk_o[l]; go.B = B; go.K = D; go.N = D; go.x = bx;
+    go.act = bo16; go.W = pk_o[l]; go.B = B; go.K = D; go.N = D; go.x = bx; go.acc_exp = fe.v + fe.w_o;
     if ((e = launch_sgemm(SEPI_RESID, go, s)) != hipSuccess) break;
-    if ((e = launch_rmsnorm_rows(bx, norm2[l], (float)c.eps, D, B, nullptr, bu16, true, s)) != hipSuccess) break;
+    if ((e = launch_rmsnorm_rows(bx, norm2[l], (float)c.eps, D, B, nullptr, bu16, true, s, fe.u2)) != hipSuccess) break;
     SgemmArgs gi{};
     gi.act = bu16; gi.W = pk_in[l]; gi.B = B; gi.K = D; gi.N = F; gi.F = F; gi.s_out = bs16;
+    gi.acc_exp = fe.u2 + fe.w_in; gi.s16_exp = fe.s;
     if ((e = launch_sgemm(SEPI_SWIGLU, gi, s)) != hipSuccess) break;
     SgemmArgs gw{};
-    gw.act = bs16; gw.W = pk_out[l]; gw.B = B; gw.K = F; gw.N = D; gw.x = bx;
+    gw.act = bs16; gw.W = pk_out[l]; gw.B = B; gw.K = F; gw.N = D; gw.x = bx; gw.acc_exp = fe.s + fe.w_out;
     e = launch_sgemm(SEPI_RESID, gw, s);
   }
   return e;
@@ -604,10 +608,12 @@ pp_status pp_model::decode_batched(pp_kv* kv, const int32_t* ids_host, float* h_
   hipError_t e = launch_embed(a, bf16, s);
   if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("embed: ") + hipGetErrorString(e));
   if ((st = run_layers(kv, s))) return st;
-  e = launch_rmsnorm_rows(bx, out_norm, (float)c.eps, D, B, h_out_dev, text_logits_dev ? bu16 : nullptr, true, s);
+  e = launch_rmsnorm_rows(bx, out_norm, (float)c.eps, D, B, h_out_dev, text_logits_dev ? bu16 : nullptr, true, s,
+                          f16e_uout);
   if (e == hipSuccess && text_logits_dev) {
     SgemmArgs g{};
     g.act = bu16; g.W = pk_head; g.B = B; g.K = D; g.N = c.text_vocab - 1; g.out = text_logits_dev;
+    g.acc_exp = f16e_uout + f16e_whead;
     e = launch_sgemm(SEPI_STORE, g, s);
   }
   if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("final norm / text head: ") + hipGetErrorString(e));

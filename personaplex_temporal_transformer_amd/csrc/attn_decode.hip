@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(AttnDecodeArgs a) {
     L += w * pml[2 * i + 1];
     o += w * po[i * DH + t];
   }
-  if (a.out16) a.out16[frag_act_index((int)b, h * DH + t, a.H * DH)] = f32_to_f16(o / L);
+  if (a.out16) a.out16[frag_act_index((int)b, h * DH + t, a.H * DH)] = f32_to_f16_sat(o / L * ldexpf(1.0f, -a.o16_exp));
   else a.out[b * a.H * DH + h * DH + t] = o / L;
 }
 

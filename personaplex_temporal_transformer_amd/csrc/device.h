@@ -48,6 +48,11 @@ __device__ __forceinline__ uint16_t f32_to_f16(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+// float32 -> float16 bits, round to nearest even, saturated to +-65504.
+__device__ __forceinline__ uint16_t f32_to_f16_sat(float f) {
+  return f32_to_f16(fminf(fmaxf(f, -65504.f), 65504.f));
+}
+
 // Storage-type helpers for weights / cache elements (float or bfloat16).
 template <typename T> struct Elem;
 template <> struct Elem<float> {

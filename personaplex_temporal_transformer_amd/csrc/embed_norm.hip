@@ -5,6 +5,8 @@
 // 8 agent audio, 8 user audio); ID -1 contributes an exact zero vector.
 // RMSNorm: same page, section 3 'One of the 32 temporal blocks' -- float32 arithmetic,
 // x * alpha / sqrt(mean(x^2) + eps), no mean subtraction.
+#include <cmath>
+
 #include "device.h"
 #include "frag_layout.h"
 #include "internal.h"
@@ -73,14 +75,15 @@ hipError_t launch_embed(const EmbedArgs& a, bool bf16, hipStream_t s) {
 __global__ __launch_bounds__(kBlock) void k_rmsnorm_rows(const float* __restrict__ x,
                                                          const float* __restrict__ alpha, float eps,
                                                          int D, float* __restrict__ out_f32,
-                                                         uint16_t* __restrict__ out_f16, int f16_frag) {
+                                                         uint16_t* __restrict__ out_f16, int f16_frag, float f16_scale) {
   __shared__ float red[4];
   const float* xr = x + (size_t)blockIdx.x * D;
   auto emit = [&](int i, f32x4 y) {
     if (out_f32) *reinterpret_cast<f32x4*>(out_f32 + (size_t)blockIdx.x * D + i) = y;
     if (out_f16) {
-      const uint32_t lo = (uint32_t)f32_to_f16(y.x) | ((uint32_t)f32_to_f16(y.y) << 16);
-      const uint32_t hi = (uint32_t)f32_to_f16(y.z) | ((uint32_t)f32_to_f16(y.w) << 16);
+      const f32x4 z = y * f16_scale;   // a power of two: the float16 operand's scale
+      const uint32_t lo = (uint32_t)f32_to_f16(z.x) | ((uint32_t)f32_to_f16(z.y) << 16);
+      const uint32_t hi = (uint32_t)f32_to_f16(z.z) | ((uint32_t)f32_to_f16(z.w) << 16);
       // four consecutive k (i % 4 == 0) stay within one 8-value fragment run
       const size_t oi = f16_frag ? frag_act_index((int)blockIdx.x, i, D) : (size_t)blockIdx.x * D + i;
       *reinterpret_cast<uint2*>(out_f16 + oi) = make_uint2(lo, hi);
@@ -123,10 +126,10 @@ __global__ __launch_bounds__(kBlock) void k_rmsnorm_rows(const float* __restrict
 }
 
 hipError_t launch_rmsnorm_rows(const float* x, const float* alpha, float eps, int D, int rows,
-                               float* out_f32, void* out_f16, bool f16_frag, hipStream_t s) {
+                               float* out_f32, void* out_f16, bool f16_frag, hipStream_t s, int f16_exp) {
   if (f16_frag && D % 32) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_rmsnorm_rows, dim3(rows), dim3(kBlock), 0, s, x, alpha, eps, D, out_f32,
-                     static_cast<uint16_t*>(out_f16), f16_frag ? 1 : 0);
+                     static_cast<uint16_t*>(out_f16), f16_frag ? 1 : 0, std::ldexp(1.0f, -f16_exp));
   return hipGetLastError();
 }
 

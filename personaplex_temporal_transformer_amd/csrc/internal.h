@@ -105,14 +105,19 @@ struct AttnDecodeArgs {
   int batch;
   long long kv_bstride;
   uint16_t* out16;
+  int o16_exp;          // out16 holds o * 2^-o16_exp
 };
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, bool bf16, int dh, hipStream_t s);
 
 // ---------------------------------------------------------------- row RMSNorm
 // rows x D; float32 and/or float16 outputs (either may be null); f16_frag: the float16 rows in
 // the skinny products' fragment order (frag_act_index, D % 32 == 0) instead of row-major
+// the float16 rows are written as y * 2^-f16_exp
 hipError_t launch_rmsnorm_rows(const float* x, const float* alpha, float eps, int D, int rows,
-                               float* out_f32, void* out_f16, bool f16_frag, hipStream_t s);
+                               float* out_f32, void* out_f16, bool f16_frag, hipStream_t s, int f16_exp = 0);
+
+// Per row of a bf16 matrix [rows][K] (K % 8 == 0): sum of squares and largest |w|.
+hipError_t launch_row_stats(const void* W, int rows, int K, float* ss, float* amax, hipStream_t s);
 
 }  // namespace pp
 
@@ -190,10 +195,15 @@ struct GemmArgs {
   // NULL: never split.
   float* part;
   size_t part_bytes;
+  // bf16-weight path: the epilogue multiplies the products by 2^acc_exp (undoing the
+  // scales of the float16 operands); the float16 outputs it writes are Q * 2^-q16_exp, the
+  // K copy * 2^-k16_exp, V^T * 2^-vt_exp, SiLU(g) * z * 2^-s16_exp. Zero: no scaling.
+  int acc_exp, q16_exp, k16_exp, vt_exp, s16_exp;
 };
 hipError_t launch_gemm(int epi, bool bf16, const GemmArgs& g, int n_cu, hipStream_t s);
-// float16 copy of n_elems bfloat16 values (n_elems % 8 == 0), exact
-hipError_t launch_bf16_to_f16(const void* src, void* dst, size_t n_elems, hipStream_t s);
+// float16 copy w * 2^-w_exp of n_elems bfloat16 values (n_elems % 8 == 0), round to nearest
+// even: exact unless the scaled value falls below float16's normal range (2^-14)
+hipError_t launch_bf16_to_f16(const void* src, void* dst, size_t n_elems, int w_exp, hipStream_t s);
 
 // The attention of a chunk of T frames at positions p0..p0+T-1 runs in a contiguous key
 // space: key index j is position p0 - koff + j, query i is key index koff + i. Keys
@@ -230,6 +240,7 @@ struct GatherArgs {
   void* vx;
   void* vt;
   int x_pitch, vt_pitch, C, H, dh;
+  int k16_exp, vt_exp;  // the float16 copies hold K * 2^-k16_exp, V * 2^-vt_exp (saturated)
   long long q0;
   int jlo, jhi;
 };
@@ -320,12 +331,17 @@ struct SgemmArgs {
   const long long* state;
   long long pos;         // >= 0: the position; -1: read state[0]
   int D, dh, C;
+  // the products are multiplied by 2^acc_exp (undoing the float16 operand scales); the
+  // SiLU products are written as SiLU(g) * z * 2^-s16_exp
+  int acc_exp, s16_exp;
 };
 constexpr int kSgemmMaxBatch = 64;
 hipError_t launch_sgemm(int epi, const SgemmArgs& a, hipStream_t s);
 // Copy of a row-major [rows][K] bf16 matrix in the fragment order the skinny products
 // read (same byte count); rows_out = N (or F for the SiLU-gated W_in with 2F rows).
-hipError_t launch_sgemm_pack(const void* W, void* packed, int rows_out, int K, int F, bool swiglu, hipStream_t s);
+// The packed copy holds w * 2^-w_exp (exact in bfloat16 for the exponents used).
+hipError_t launch_sgemm_pack(const void* W, void* packed, int rows_out, int K, int F, bool swiglu, int w_exp,
+                             hipStream_t s);
 }  // namespace pp
 
 namespace pp {

@@ -14,6 +14,16 @@ pp_status pp_device_check(int* n_cu);
 
 struct pp_kv;
 
+// Power-of-two exponents of the float16 operands of one layer (csrc/f16_scales.hip): the
+// float16 copy of a matrix holds w * 2^-w_*, a float16 activation a * 2^-(its exponent).
+struct F16Exps {
+  int u1, u2;        // normalised rows entering QKV / W_in
+  int q, k, v;       // prefill: Q and the K copy of the attention, the transposed V copy
+                     // (so the attention output too); batched decode: its attention output
+  int s;             // SiLU(g) * z entering W_out
+  int w_qkv, w_o, w_in, w_out;
+};
+
 // The per-step intermediates of a batch-1 decode frame (device memory).
 struct DecodeBufs {
   float* x;          // residual stream [D] float32
@@ -88,6 +98,11 @@ struct pp_model {
   void* pf16_ws = nullptr;     // bf16-weight path: float16 copies of the block matrices (one allocation)
   std::vector<const void*> f16_qkv, f16_o, f16_in, f16_out;   // keys of the key space: max_T + context + 16, rounded up to 64
 
+  // float16 operand exponents (bf16 weights with prefill or batched decode): per layer, and
+  // the final norm's rows / the text head of the batched step
+  std::vector<F16Exps> f16e;
+  int f16e_uout = 0, f16e_whead = 0;
+
   int32_t* ids_pinned = nullptr;
   size_t ids_cap = 0;
   hipEvent_t ids_event = nullptr;
@@ -118,6 +133,7 @@ struct pp_model {
 
   ~pp_model();
   pp_status alloc_decode(int D, int F, int H, int dh);
+  pp_status compute_f16_scales();
   pp_status alloc_prefill();
   void free_prefill();
   pp_status check_ids(const int32_t* ids, size_t frames) const;

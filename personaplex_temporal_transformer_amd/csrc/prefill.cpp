@@ -58,23 +58,23 @@ pp_status pp_model::alloc_prefill() {
   if (hipMalloc(&pws, bytes) != hipSuccess) return pp_fail(PP_E_HIP, "hipMalloc of prefill workspace failed");
   if (max_T > 0 && bf16) {
     // the matrix-core products take float16 operands: one float16 copy of every matrix,
-    // converted once here (13.15 GB at full size)
+    // w * 2^-e with e per matrix (f16e), converted once here (13.15 GB at full size)
     const size_t L = cfg.n_layers;
     const size_t per_layer = (3 * D * D + D * D + 2 * F * D + D * F) * 2;
     if (hipMalloc(&pf16_ws, L * per_layer) != hipSuccess)
       return pp_fail(PP_E_HIP, "hipMalloc of the prefill float16 weights failed");
     char* p = static_cast<char*>(pf16_ws);
     hipError_t e = hipSuccess;
-    auto conv = [&](const void* src, size_t n, std::vector<const void*>& dst) {
+    auto conv = [&](const void* src, size_t n, int w_exp, std::vector<const void*>& dst) {
       dst.push_back(p);
-      if (e == hipSuccess) e = launch_bf16_to_f16(src, p, n, nullptr);
+      if (e == hipSuccess) e = launch_bf16_to_f16(src, p, n, w_exp, nullptr);
       p += n * 2;
     };
     for (size_t l = 0; l < L; ++l) {
-      conv(w_qkv[l], 3 * D * D, f16_qkv);
-      conv(w_o[l], D * D, f16_o);
-      conv(w_in[l], 2 * F * D, f16_in);
-      conv(w_out[l], D * F, f16_out);
+      conv(w_qkv[l], 3 * D * D, f16e[l].w_qkv, f16_qkv);
+      conv(w_o[l], D * D, f16e[l].w_o, f16_o);
+      conv(w_in[l], 2 * F * D, f16e[l].w_in, f16_in);
+      conv(w_out[l], D * F, f16e[l].w_out, f16_out);
     }
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("converting prefill weights: ") + hipGetErrorString(e));
@@ -159,21 +159,24 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
   for (int l = 0; l < c.n_layers; ++l) {
     char* kbase = static_cast<char*>(kv->ring) + (size_t)(2 * l) * per_kv;
     char* vbase = kbase + per_kv;
+    const F16Exps fe = bf ? m->f16e[l] : F16Exps{};   // float16 operand scales (zero: none)
     if (koff > 0) {
       GatherArgs ga{};
+      ga.k16_exp = fe.k; ga.vt_exp = fe.v;
       ga.kring = kbase; ga.vring = vbase; ga.kx = m->pkx; ga.vx = m->pvx; ga.vt = m->pvt;
       ga.x_pitch = m->x_pitch; ga.vt_pitch = m->vt_pitch; ga.C = C; ga.H = H; ga.dh = dh;
       ga.q0 = q0; ga.jlo = jlo; ga.jhi = koff;
       e = launch_gather_history(ga, bf, s);
       if (e != hipSuccess) return hip_fail("prefill history gather", e);
     }
-    e = launch_rmsnorm_rows(m->px, m->norm1[l], (float)c.eps, D, T, u32, u16, false, s);
+    e = launch_rmsnorm_rows(m->px, m->norm1[l], (float)c.eps, D, T, u32, u16, false, s, fe.u1);
     if (e != hipSuccess) return hip_fail("prefill norm1", e);
 
     GemmArgs g{};
     g.A = m->pu; g.B = bf ? m->f16_qkv[l] : m->w_qkv[l]; g.M = T; g.N = 3 * D; g.K = D;
     g.q_out = m->pq; g.kc = kbase; g.vc = vbase; g.rope = m->prope;
     g.D = D; g.dh = dh; g.C = C; g.p0 = (int)(p0 % C);
+    g.acc_exp = fe.u1 + fe.w_qkv; g.q16_exp = fe.q; g.k16_exp = fe.k; g.vt_exp = fe.v;
     g.vt = m->pvt; g.vt_pitch = m->vt_pitch;
     if (koff > 0 || bf) {   // the bf16-weight path's attention always reads float16 K from the key space
       g.kx = m->pkx; g.vx = bf ? nullptr : m->pvx; g.x_pitch = m->x_pitch; g.xoff = koff;
@@ -188,28 +191,33 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
     } else {
       at.k = kbase; at.v = vbase; at.k_pitch = C;
     }
-    at.T = T; at.H = H; at.C = C; at.koff = koff; at.jlo = jlo; at.scale = 1.0f / std::sqrt((float)dh);
+    // scores of the scaled float16 Q and K copies: the scale gains 2^(q + k)
+    at.T = T; at.H = H; at.C = C; at.koff = koff; at.jlo = jlo;
+    at.scale = (float)std::ldexp(1.0 / std::sqrt((double)dh), fe.q + fe.k);
     at.part = m->psplit; at.part_bytes = m->psplit_bytes; at.n_cu = m->n_cu;
     e = launch_attn_prefill(at, bf, dh, s);
     if (e != hipSuccess) return hip_fail("prefill attention", e);
 
     GemmArgs go{};
     go.A = m->pa; go.B = bf ? m->f16_o[l] : m->w_o[l]; go.M = T; go.N = D; go.K = D; go.x = m->px;
+    go.acc_exp = fe.v + fe.w_o;
     go.part = m->psplit; go.part_bytes = m->psplit_bytes;
     e = launch_gemm(GEPI_RESID, bf, go, m->n_cu, s);
     if (e != hipSuccess) return hip_fail("prefill W_O", e);
 
-    e = launch_rmsnorm_rows(m->px, m->norm2[l], (float)c.eps, D, T, u32, u16, false, s);
+    e = launch_rmsnorm_rows(m->px, m->norm2[l], (float)c.eps, D, T, u32, u16, false, s, fe.u2);
     if (e != hipSuccess) return hip_fail("prefill norm2", e);
 
     GemmArgs gi{};
     gi.A = m->pu; gi.B = bf ? m->f16_in[l] : m->w_in[l]; gi.M = T; gi.N = F; gi.K = D; gi.F = F; gi.s_out = m->pg;
+    gi.acc_exp = fe.u2 + fe.w_in; gi.s16_exp = fe.s;
     gi.part = m->psplit; gi.part_bytes = m->psplit_bytes;
     e = launch_gemm(GEPI_SWIGLU, bf, gi, m->n_cu, s);
     if (e != hipSuccess) return hip_fail("prefill W_in", e);
 
     GemmArgs gw{};
     gw.A = m->pg; gw.B = bf ? m->f16_out[l] : m->w_out[l]; gw.M = T; gw.N = D; gw.K = F; gw.x = m->px;
+    gw.acc_exp = fe.s + fe.w_out;
     gw.part = m->psplit; gw.part_bytes = m->psplit_bytes;
     e = launch_gemm(GEPI_RESID, bf, gw, m->n_cu, s);
     if (e != hipSuccess) return hip_fail("prefill W_out", e);

@@ -13,7 +13,7 @@
 // are bfloat16 in the ring, shared with decode) and P V a float16 one (P and the transposed
 // V copy in float16). Statistics and the residual stream stay fp32.
 // float32 path (small shapes, fp32 parity): plain FMA kernels with the same epilogues.
-#include <stdlib.h>
+#include <cmath>
 
 #include <type_traits>
 
@@ -128,8 +128,8 @@ __device__ __forceinline__ void vm_wait_tiles(int a) {
 __device__ __forceinline__ void lds_wait_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // C[M][N] = A[M][K] B[N][K]^T with float16 A (activations) and B (the model's float16
-// weight copy, converted once from bf16 -- exactly, so the products equal those of the
-// bf16 weights). Workgroup = WM x WN waves, tile BM x BN with BM = WM*32*MI,
+// weight copy, converted once from bf16, scaled by a power of two that the epilogue
+// undoes: g.acc_exp). Workgroup = WM x WN waves, tile BM x BN with BM = WM*32*MI,
 // BN = WN*32*NI; wave (wm, wn) owns rows wm*32*MI.. and 32*NI columns as MI x NI tiles of
 // 32 x 32 (v_mfma_f32_32x32x16_f16, fp32 accumulation).
 // k-tiles of KB columns go from global memory straight into LDS (buffer loads with the LDS
@@ -374,6 +374,16 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_f16(GemmArgs g) {
         }
     return;
   }
+  // the float16 operands are scaled copies (power-of-two exponents): undo them, exactly
+  if (g.acc_exp != 0) {
+    const float am = ldexpf(1.0f, g.acc_exp);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] *= am;
+  }
   if constexpr (EPI == GEPI_QKV) {
     // Half a tile at a time (128-byte-aligned column halves): the waves holding those
     // columns write their fp32 values into LDS, then every thread takes 8 consecutive
@@ -446,10 +456,11 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_f16(GemmArgs g) {
         // significand on both sides of Q.K^T costs about as much accuracy per block as the
         // ring's rounding itself.
         uint32_t pk[4], ph[4];
+        const float hs = ldexpf(1.0f, -(sec == 0 ? g.q16_exp : g.k16_exp));   // float16 copy scale
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           pk[k] = (uint32_t)f32_to_bf16(v[2 * k]) | ((uint32_t)f32_to_bf16(v[2 * k + 1]) << 16);
-          ph[k] = (uint32_t)f32_to_f16(v[2 * k]) | ((uint32_t)f32_to_f16(v[2 * k + 1]) << 16);
+          ph[k] = (uint32_t)f32_to_f16(v[2 * k] * hs) | ((uint32_t)f32_to_f16(v[2 * k + 1] * hs) << 16);
         }
         if (sec == 0) {
           *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.q_out) + ((size_t)head * g.M + row) * g.dh + d) =
@@ -473,10 +484,11 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_f16(GemmArgs g) {
           const int wcol = tn * BN + half * HALF + cl - 2 * g.D;
           const int head = wcol / g.dh, d = wcol - head * g.dh;
           uint32_t wv[4];
+          const float vs = ldexpf(1.0f, -g.vt_exp);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r0 = vt_perm(p + 2 * e) - m0, r1 = vt_perm(p + 2 * e + 1) - m0;
-            wv[e] = (uint32_t)f32_to_f16(T[r0 * TPF + cl]) | ((uint32_t)f32_to_f16(T[r1 * TPF + cl]) << 16);
+            wv[e] = (uint32_t)f32_to_f16(T[r0 * TPF + cl] * vs) | ((uint32_t)f32_to_f16(T[r1 * TPF + cl] * vs) << 16);
           }
           *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.vt) + ((size_t)head * g.dh + d) * g.vt_pitch + g.xoff + p) =
               u32x4{wv[0], wv[1], wv[2], wv[3]};
@@ -530,7 +542,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_f16(GemmArgs g) {
             const float gv = acc[i][j][4 * jj + ii], zv = acc[i][j + NI / 2][4 * jj + ii];
             if (row < g.M) {
               const int col = tn * (BN / 2) + wn * 16 * NI + j * 32 + (lane & 31);
-              static_cast<uint16_t*>(g.s_out)[(size_t)row * g.F + col] = f32_to_f16(silu(gv) * zv);
+              static_cast<uint16_t*>(g.s_out)[(size_t)row * g.F + col] = f32_to_f16(silu(gv) * zv * ldexpf(1.0f, -g.s16_exp));
             }
           }
         } else {
@@ -665,17 +677,17 @@ static int pick_cfg(const GemmArgs& g, int epi, int n_cu) {
 
 // Split-K sums, added in split order: x[r][c] += part[0][r][c] + part[1][r][c] + ...
 __global__ __launch_bounds__(kBlock) void k_splitk_resid(const float* __restrict__ part, float* __restrict__ x,
-                                                         long long mn, int n_split) {
+                                                         long long mn, int n_split, int acc_exp) {
   const long long i = ((long long)blockIdx.x * kBlock + threadIdx.x) * 4;
   if (i >= mn) return;
   f32x4 acc = *reinterpret_cast<const f32x4*>(part + i);
   for (int s = 1; s < n_split; ++s) acc += *reinterpret_cast<const f32x4*>(part + (size_t)s * mn + i);
   f32x4* xp = reinterpret_cast<f32x4*>(x + i);
-  *xp = *xp + acc;
+  *xp = *xp + acc * ldexpf(1.0f, acc_exp);
 }
 // s_out[r][j] = SiLU(g) * z as float16, g = the split sums of B row j, z of B row F + j.
 __global__ __launch_bounds__(kBlock) void k_splitk_swiglu(const float* __restrict__ part, uint16_t* __restrict__ s_out,
-                                                          int M, int F, int n_split) {
+                                                          int M, int F, int n_split, int acc_exp, int s16_exp) {
   const long long i = ((long long)blockIdx.x * kBlock + threadIdx.x) * 4;  // (r, j), j % 4 == 0
   if (i >= (long long)M * F) return;
   const long long r = i / F, j = i - r * F;
@@ -686,8 +698,11 @@ __global__ __launch_bounds__(kBlock) void k_splitk_swiglu(const float* __restric
     gs += *reinterpret_cast<const f32x4*>(p + s * ms);
     zs += *reinterpret_cast<const f32x4*>(p + s * ms + F);
   }
-  const uint32_t lo = (uint32_t)f32_to_f16(silu(gs.x) * zs.x) | ((uint32_t)f32_to_f16(silu(gs.y) * zs.y) << 16);
-  const uint32_t hi = (uint32_t)f32_to_f16(silu(gs.z) * zs.z) | ((uint32_t)f32_to_f16(silu(gs.w) * zs.w) << 16);
+  const float am = ldexpf(1.0f, acc_exp), ss = ldexpf(1.0f, -s16_exp);
+  gs *= am;
+  zs *= am;
+  const uint32_t lo = (uint32_t)f32_to_f16(silu(gs.x) * zs.x * ss) | ((uint32_t)f32_to_f16(silu(gs.y) * zs.y * ss) << 16);
+  const uint32_t hi = (uint32_t)f32_to_f16(silu(gs.z) * zs.z * ss) | ((uint32_t)f32_to_f16(silu(gs.w) * zs.w * ss) << 16);
   *reinterpret_cast<u32x2*>(s_out + i) = u32x2{lo, hi};
 }
 
@@ -716,11 +731,11 @@ static hipError_t launch_cfg(const GemmArgs& g, int n_cu, hipStream_t s) {
     if (EPI == GEPI_RESID) {
       const long long mn = (long long)g.M * g.N;
       hipLaunchKernelGGL(k_splitk_resid, dim3((unsigned)((mn / 4 + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, g.part, g.x,
-                         mn, sp);
+                         mn, sp, g.acc_exp);
     } else if (EPI == GEPI_SWIGLU) {
       const long long mf = (long long)g.M * g.F;
       hipLaunchKernelGGL(k_splitk_swiglu, dim3((unsigned)((mf / 4 + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, g.part,
-                         static_cast<uint16_t*>(g.s_out), g.M, g.F, sp);
+                         static_cast<uint16_t*>(g.s_out), g.M, g.F, sp, g.acc_exp, g.s16_exp);
     }
   }
   return hipGetLastError();
@@ -747,20 +762,27 @@ static hipError_t gemm_dispatch(bool bf16, const GemmArgs& g, int n_cu, hipStrea
   return hipGetLastError();
 }
 
-// The prefill's float16 copy of a bf16 matrix: one 16-byte word (8 values) per thread,
-// widened exactly (bfloat16's significand is the shorter; values below float16's range
-// flush toward zero).
+// The prefill's float16 copy of a bf16 matrix, w * 2^-w_exp: one 16-byte word (8 values)
+// per thread. The exponent is chosen per matrix so its largest |w| lands in [2^14, 2^15);
+// bfloat16's significand is the shorter, so values inside float16's normal range convert
+// exactly, and the rest (below 2^-14 after scaling) round to nearest even.
 __global__ __launch_bounds__(kBlock) void k_bf16_to_f16(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                                        long long n16) {
+                                                        long long n16, float scale) {
   const long long i = (long long)blockIdx.x * kBlock + threadIdx.x;
-  if (i < n16) dst[i] = __builtin_bit_cast(u32x4, bf16x8_to_f16(src[i]));
+  if (i >= n16) return;
+  const u32x4 v = src[i];
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    o[e] = (uint32_t)f32_to_f16(bf16_lo(v[e]) * scale) | ((uint32_t)f32_to_f16(bf16_hi(v[e]) * scale) << 16);
+  dst[i] = o;
 }
 
-hipError_t launch_bf16_to_f16(const void* src, void* dst, size_t n_elems, hipStream_t s) {
+hipError_t launch_bf16_to_f16(const void* src, void* dst, size_t n_elems, int w_exp, hipStream_t s) {
   if (n_elems % 8) return hipErrorInvalidValue;
   const long long n16 = (long long)(n_elems / 8);
   hipLaunchKernelGGL(k_bf16_to_f16, dim3((unsigned)((n16 + kBlock - 1) / kBlock)), dim3(kBlock), 0, s,
-                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16, std::ldexp(1.0f, -w_exp));
   return hipGetLastError();
 }
 
@@ -1146,9 +1168,10 @@ __global__ __launch_bounds__(kBlock) void k_gather_k16(GatherArgs a) {
     v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.kring) + ((size_t)h * a.C + pos % a.C) * a.dh + c * 8);
   }
   uint32_t w[4];
+  const float ks = ldexpf(1.0f, -a.k16_exp);
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    w[e] = (uint32_t)f32_to_f16(bf16_lo(v[e])) | ((uint32_t)f32_to_f16(bf16_hi(v[e])) << 16);
+    w[e] = (uint32_t)f32_to_f16_sat(bf16_lo(v[e]) * ks) | ((uint32_t)f32_to_f16_sat(bf16_hi(v[e]) * ks) << 16);
   *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.kx) + ((size_t)h * a.x_pitch + j) * a.dh + c * 8) =
       u32x4{w[0], w[1], w[2], w[3]};
 }
@@ -1167,10 +1190,11 @@ __global__ __launch_bounds__(256) void k_gather_vt(GatherArgs a) {
     const int jr = q / cpr, c = q - jr * cpr, j = j0 + jr;
     u32x4 v = u32x4{0u, 0u, 0u, 0u};
     if (j >= a.jlo && j < a.jhi) v = *reinterpret_cast<const u32x4*>(V + (size_t)((a.q0 + j) % a.C) * dh + c * 8);
+    const float vs = ldexpf(1.0f, -a.vt_exp);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      tile[(c * 8 + 2 * e) * P + jr] = f32_to_f16(bf16_to_f32((uint16_t)(v[e] & 0xffffu)));
-      tile[(c * 8 + 2 * e + 1) * P + jr] = f32_to_f16(bf16_to_f32((uint16_t)(v[e] >> 16)));
+      tile[(c * 8 + 2 * e) * P + jr] = f32_to_f16_sat(bf16_lo(v[e]) * vs);
+      tile[(c * 8 + 2 * e + 1) * P + jr] = f32_to_f16_sat(bf16_hi(v[e]) * vs);
     }
   }
   __syncthreads();

@@ -19,7 +19,7 @@
 // batched step took 3-16 % longer at B = 16-64). The waves' partial tiles
 // are summed in LDS in wave order (fixed order: reproducible), then the epilogue applies
 // RoPE / ring append, the residual add, the SiLU product or a plain store.
-#include <stdlib.h>
+#include <cmath>
 
 #include "device.h"
 #include "frag_layout.h"
@@ -128,20 +128,21 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
     if (b >= a.B) continue;
     const int j = cc >> 4, c = cc & 15;
     const int tl = tile0 + j;     // this column's 16-column tile
-    const float v = tile[b][cc];
+    const float am = ldexpf(1.0f, a.acc_exp);   // undoes the float16 operand scales (exact)
+    const float v = tile[b][cc] * am;
     if constexpr (EPI == SEPI_STORE) {
       a.out[(size_t)b * a.N + tl * 16 + c] = v;
     } else if constexpr (EPI == SEPI_RESID) {
       a.x[(size_t)b * a.N + tl * 16 + c] += v;
     } else if constexpr (EPI == SEPI_SWIGLU) {
-      if (c < 8) a.s_out[frag_act_index(b, tl * 8 + c, a.F)] = f32_to_f16(silu(v) * tile[b][cc + 8]);
+      if (c < 8) a.s_out[frag_act_index(b, tl * 8 + c, a.F)] = f32_to_f16(silu(v) * (tile[b][cc + 8] * am) * ldexpf(1.0f, -a.s16_exp));
     } else {
       const int col = tl * 16 + c;
       const int sec = col / a.D, wcol = col - sec * a.D;
       const int head = wcol / a.dh, d = wcol - head * a.dh;
       float y = v;
       if (sec < 2) {
-        const float partner = tile[b][cc ^ 1];
+        const float partner = tile[b][cc ^ 1] * am;
         const float cs = a.rope[d & ~1], sn = a.rope[d | 1];
         y = (d & 1) ? partner * sn + v * cs : v * cs - partner * sn;
       }
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
 // columns; SiLU-gated: g rows 8t.. and z rows F+8t..), step s, lane l, element e holds
 // W[row(t, l % 16)][32 s + 8 (l / 16) + e]. One thread per 16-byte fragment.
 __global__ __launch_bounds__(kBlock) void k_sgemm_pack(const uint16_t* __restrict__ W, uint16_t* __restrict__ P,
-                                                       int tiles, int K, int F, int swiglu) {
+                                                       int tiles, int K, int F, int swiglu, float scale) {
   const int nsteps = K / 32;
   const long long i = (long long)blockIdx.x * kBlock + threadIdx.x;
   if (i >= (long long)tiles * nsteps * 64) return;
@@ -169,15 +170,22 @@ __global__ __launch_bounds__(kBlock) void k_sgemm_pack(const uint16_t* __restric
   const int st = (int)(ts % nsteps), t = (int)(ts / nsteps);
   const int n = l & 15, g = l >> 4;
   const int row = swiglu ? (n < 8 ? t * 8 + n : F + t * 8 + (n - 8)) : t * 16 + n;
-  *reinterpret_cast<u32x4*>(P + (size_t)i * 8) = *reinterpret_cast<const u32x4*>(W + (size_t)row * K + st * 32 + 8 * g);
+  const u32x4 v = *reinterpret_cast<const u32x4*>(W + (size_t)row * K + st * 32 + 8 * g);
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)   // w * 2^-w_exp: exact in bfloat16 (same significand)
+    o[e] = (uint32_t)f32_to_bf16(bf16_lo(v[e]) * scale) | ((uint32_t)f32_to_bf16(bf16_hi(v[e]) * scale) << 16);
+  *reinterpret_cast<u32x4*>(P + (size_t)i * 8) = o;
 }
 
-hipError_t launch_sgemm_pack(const void* W, void* packed, int rows_out, int K, int F, bool swiglu, hipStream_t s) {
+hipError_t launch_sgemm_pack(const void* W, void* packed, int rows_out, int K, int F, bool swiglu, int w_exp,
+                             hipStream_t s) {
   if (K % 32 || (swiglu ? F % 8 : rows_out % 16)) return hipErrorInvalidValue;
   const int tiles = swiglu ? F / 8 : rows_out / 16;
   const long long n = (long long)tiles * (K / 32) * 64;
   hipLaunchKernelGGL(k_sgemm_pack, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, s,
-                     static_cast<const uint16_t*>(W), static_cast<uint16_t*>(packed), tiles, K, F, swiglu ? 1 : 0);
+                     static_cast<const uint16_t*>(W), static_cast<uint16_t*>(packed), tiles, K, F, swiglu ? 1 : 0,
+                     std::ldexp(1.0f, -w_exp));
   return hipGetLastError();
 }
 
