@@ -430,6 +430,33 @@ def _blas_threads():
         return os.cpu_count() or 1
 
 
+def _host():
+    """What the oracle's times ran on: CPU model, logical CPUs, BLAS threads."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "blas_threads": int(_blas_threads())}
+
+
+def _timed_both(fn, n=3):
+    """Best of n at the BLAS pool's threads, and once at one thread (seconds)."""
+    t, _ = _best_of(fn, n)
+    t1 = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t1, _ = _best_of(fn, 1)
+    except ImportError:
+        pass
+    return t, t1
+
+
 def _best_of(fn, n=3):
     times = []
     for _ in range(n):
@@ -449,7 +476,36 @@ def cpu_baselines(cfg, want_prefill=True, want_depth=True):
     from oracle import temporal as O
     from personaplex_temporal_transformer_amd import synth
     cores = int(_blas_threads())
-    out = {}
+    out = {"host": _host()}
+    # the tiny temporal stack (2 blocks, 256 wide, 16 frames, fp32): full sequence and
+    # frame-by-frame decode
+    tc = synth.TINY_TEMPORAL
+    TW = synth.temporal_weights(tc, 0, "fp32")
+    tids = synth.stream_ids(tc, 16, 1)
+    tf, tf1 = _timed_both(lambda: O.forward_full(tids, TW, tc))
+    ti, ti1 = _timed_both(lambda: O.decode_incremental(tids, TW, tc))
+    out["tiny"] = {"full_sequence_ms": tf * 1e3, "incremental_ms": ti * 1e3, "cores": cores,
+                   "full_sequence_ms_1thread": tf1 * 1e3 if tf1 else None,
+                   "incremental_ms_1thread": ti1 * 1e3 if ti1 else None, "kind": "oracle",
+                   "sample": "the whole tiny workload: 2 blocks, d_model 256, 16 frames, fp32 weights, best of 3"}
+    del TW
+    # one full-width block step at 201 visible keys (the one-block workload)
+    oc = synth.with_(cfg, n_layers=1)
+    OW = synth.temporal_weights(oc, 2, "bf16", with_text_head=False)
+    ofr = synth.cache_frames(oc, 200, 3)
+    oids = synth.stream_ids(oc, 1, 4)
+
+    def block_step():
+        cache = O.cache_from_blocks([ofr[0, 0, 0].transpose(1, 0, 2)], [ofr[0, 1, 0].transpose(1, 0, 2)],
+                                    np.arange(200), 1)
+        O.final(O.decode_step(O.embed(oids[0], OW, oc), 200, cache, OW, oc), OW, oc)
+
+    tb, tb1 = _timed_both(block_step)
+    out["one_block"] = {"value": tb * 1e3, "unit": "ms/step", "cores": cores, "kind": "oracle",
+                        "value_1thread": tb1 * 1e3 if tb1 else None,
+                        "sample": "the whole one-block step (embedding, one full-width block at 201 keys, final "
+                                  "norm; fp64 NumPy), best of 3"}
+    del OW, ofr
     n_l = 2
     sc = synth.with_(cfg, n_layers=n_l)
     W = synth.temporal_weights(sc, 8, "bf16", with_text_head=False)
@@ -674,7 +730,9 @@ def main():
         dep.close()
     if not args.no_cpu_baseline:
         cb = cpu_baselines(cfg, want_prefill="prefill" in out, want_depth="depformer" in out)
-        out["cpu_baseline"] = cb["decode"]
+        out["cpu_baseline"] = dict(cb["decode"], host=cb["host"], tiny=cb["tiny"])
+        if "one_block" in out:
+            out["one_block"]["cpu_baseline"] = cb["one_block"]
         if "prefill" in cb:
             out["prefill"]["cpu_baseline"] = cb["prefill"]
         if "depth" in cb:

@@ -179,6 +179,14 @@ pp_status pp_temporal_decode_step_noalloc(pp_model* m, pp_kv* kv, const int32_t*
 pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* ids_host, int32_t T,
                               float* h_out_dev, void* stream);
 
+/* The same forward with the first block's inputs given directly: x_dev [T][d_model] float32
+ * holds each frame's summed embedding (audit section 9: a cached voice prompt replays the
+ * native summed embeddings instead of token IDs). Everything else as pp_temporal_prefill
+ * (batch 1, positions p..p+T-1, K/V into the ring, position := p+T). x_dev is read only
+ * during the call's stream work and may be reused once the stream has passed it. */
+pp_status pp_temporal_prefill_embedded(pp_model* m, pp_kv* kv, const float* x_dev, int32_t T,
+                                       float* h_out_dev, void* stream);
+
 /* ------------------------------------------------------------------ depth transformer */
 
 /* Shapes of the depth transformer (audit section 4). Full size: 6 layers, d_model 1024,
@@ -303,6 +311,16 @@ pp_status pp_generator_destroy(pp_generator* g);
  * The cursor advances by one per call. */
 pp_status pp_generator_step(pp_generator* g, const int32_t* provided_host, const double* uniforms_host,
                             int32_t* out_dev, int32_t* has_output_host, void* stream);
+
+/* Snapshot of a generator session's delayed-code ring (audit section 9: after a cached
+ * prompt, the short token ring is restored): pp_generator_info gives the cursor s (calls
+ * made so far) and the size of the ring state; pp_generator_store copies that state to
+ * dst_dev; pp_generator_restore copies a stored state back from src_dev and sets the
+ * cursor (>= 0). Together with pp_kv_store / pp_kv_restore of the model's ring this resumes
+ * a session exactly where it was stored. */
+pp_status pp_generator_info(const pp_generator* g, int64_t* cursor, uint64_t* state_bytes);
+pp_status pp_generator_store(const pp_generator* g, void* dst_dev, void* stream);
+pp_status pp_generator_restore(pp_generator* g, const void* src_dev, int64_t cursor, void* stream);
 
 /* Copies of the last model step's intermediate values (any pointer may be NULL):
  * inputs_dev [n_streams] the temporal input IDs; chosen_dev [n_streams] the selection per

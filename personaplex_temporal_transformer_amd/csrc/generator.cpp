@@ -85,6 +85,31 @@ extern "C" pp_status pp_generator_create(pp_model* m, pp_kv* kv, pp_depformer* d
   return PP_OK;
 }
 
+extern "C" pp_status pp_generator_info(const pp_generator* g, int64_t* cursor, uint64_t* state_bytes) {
+  if (!g) return pp_fail(PP_E_ARG, "generator is NULL");
+  if (cursor) *cursor = g->s;
+  if (state_bytes) *state_bytes = sizeof(GenState);
+  return PP_OK;
+}
+
+extern "C" pp_status pp_generator_store(const pp_generator* g, void* dst_dev, void* stream) {
+  if (!g || !dst_dev) return pp_fail(PP_E_ARG, "NULL argument");
+  const hipError_t e = hipMemcpyAsync(dst_dev, g->g, sizeof(GenState), hipMemcpyDeviceToDevice,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("pp_generator_store: ") + hipGetErrorString(e));
+  return PP_OK;
+}
+
+extern "C" pp_status pp_generator_restore(pp_generator* g, const void* src_dev, int64_t cursor, void* stream) {
+  if (!g || !src_dev) return pp_fail(PP_E_ARG, "NULL argument");
+  if (cursor < 0) return pp_fail(PP_E_ARG, "negative cursor");
+  const hipError_t e = hipMemcpyAsync(g->g, src_dev, sizeof(GenState), hipMemcpyDeviceToDevice,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("pp_generator_restore: ") + hipGetErrorString(e));
+  g->s = cursor;
+  return PP_OK;
+}
+
 extern "C" pp_status pp_generator_destroy(pp_generator* g) {
   if (!g) return pp_fail(PP_E_ARG, "generator is NULL");
   delete g;

@@ -114,9 +114,11 @@ static pp_status hip_fail(const char* what, hipError_t e) {
   return pp_fail(PP_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* ids_host, int32_t T,
-                                         float* h_out_dev, void* stream) {
-  if (!m || !kv || !ids_host || !h_out_dev) return pp_fail(PP_E_ARG, "NULL argument");
+// The prefill of T frames whose first-layer inputs are the embedding sums of ids_host, or
+// (ids_host == nullptr) given as x_dev [T][d_model] float32 (cached summed embeddings).
+static pp_status prefill_impl(pp_model* m, pp_kv* kv, const int32_t* ids_host, const float* x_dev, int32_t T,
+                              float* h_out_dev, void* stream) {
+  if (!m || !kv || (!ids_host && !x_dev) || !h_out_dev) return pp_fail(PP_E_ARG, "NULL argument");
   if (kv->m != m) return pp_fail(PP_E_ARG, "kv ring belongs to another model");
   if (kv->B != 1) return pp_fail(PP_E_ARG, "prefill needs a batch-1 ring");
   if (m->readers.visible > 0) return pp_fail(PP_E_ARG, "memory readers run in batch-1 decode only");
@@ -130,7 +132,7 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
   } else if (dh != 64 && dh != 128) {
     return pp_fail(PP_E_ARG, "prefill needs d_head 64 or 128");
   }
-  pp_status st = m->check_ids(ids_host, (size_t)T * kv->B);
+  pp_status st = ids_host ? m->check_ids(ids_host, (size_t)T * kv->B) : PP_OK;
   if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = m->bf16;
@@ -141,14 +143,20 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
   int jlo = koff - (int)(p0 < (long long)C - 1 ? p0 : (long long)C - 1);   // the oldest key some query sees
   if (jlo < 0) jlo = 0;
 
-  EmbedArgs a{};
-  m->embed_tables(a);
-  a.out = m->px;
-  a.rows = T;
-  if ((st = m->stage_ids(ids_host, (size_t)T * a.n_streams, s))) return st;
-  a.ids_dev = m->ids_dev;
-  hipError_t e = launch_embed(a, bf, s);
-  if (e != hipSuccess) return hip_fail("prefill embed", e);
+  hipError_t e = hipSuccess;
+  if (ids_host) {
+    EmbedArgs a{};
+    m->embed_tables(a);
+    a.out = m->px;
+    a.rows = T;
+    if ((st = m->stage_ids(ids_host, (size_t)T * a.n_streams, s))) return st;
+    a.ids_dev = m->ids_dev;
+    e = launch_embed(a, bf, s);
+    if (e != hipSuccess) return hip_fail("prefill embed", e);
+  } else {
+    e = hipMemcpyAsync(m->px, x_dev, sizeof(float) * (size_t)T * D, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_fail("prefill input copy", e);
+  }
   e = launch_rope_rows(m->prope, T, p0, dh, std::log(c.rope_theta), s);
   if (e != hipSuccess) return hip_fail("prefill rope table", e);
 
@@ -226,4 +234,16 @@ extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* 
   if (e != hipSuccess) return hip_fail("prefill final norm", e);
   kv->pos = p0 + T;
   return PP_OK;
+}
+
+extern "C" pp_status pp_temporal_prefill(pp_model* m, pp_kv* kv, const int32_t* ids_host, int32_t T,
+                                         float* h_out_dev, void* stream) {
+  if (!ids_host) return pp_fail(PP_E_ARG, "NULL argument");
+  return prefill_impl(m, kv, ids_host, nullptr, T, h_out_dev, stream);
+}
+
+extern "C" pp_status pp_temporal_prefill_embedded(pp_model* m, pp_kv* kv, const float* x_dev, int32_t T,
+                                                  float* h_out_dev, void* stream) {
+  if (!x_dev) return pp_fail(PP_E_ARG, "NULL argument");
+  return prefill_impl(m, kv, nullptr, x_dev, T, h_out_dev, stream);
 }

@@ -24,7 +24,8 @@ EXPORTS = ["pp_temporal_create", "pp_temporal_destroy", "pp_kv_alloc", "pp_kv_fr
            "pp_temporal_prefill", "pp_depformer_create", "pp_depformer_destroy", "pp_depformer_step",
            "pp_last_error", "pp_temporal_set_graph", "pp_temporal_set_attn_splits", "pp_temporal_trace", "pp_temporal_trace_read",
            "pp_depformer_set_graph", "pp_kv_restore", "pp_sample_top_k", "pp_generator_create", "pp_generator_destroy",
-           "pp_generator_step", "pp_generator_inspect", "pp_readers_attach", "pp_readers_write",
+           "pp_generator_step", "pp_generator_inspect", "pp_generator_info", "pp_generator_store",
+           "pp_generator_restore", "pp_temporal_prefill_embedded", "pp_readers_attach", "pp_readers_write",
            "pp_readers_set_visible"]
 
 
@@ -121,6 +122,10 @@ def load():
         "pp_generator_destroy": [VP],
         "pp_generator_step": [VP, P(I32), P(ctypes.c_double), VP, P(I32), VP],
         "pp_generator_inspect": [VP, VP, VP, VP, VP, VP],
+        "pp_generator_info": [VP, P(I64), P(ctypes.c_uint64)],
+        "pp_generator_store": [VP, VP, VP],
+        "pp_generator_restore": [VP, VP, I64, VP],
+        "pp_temporal_prefill_embedded": [VP, VP, VP, I32, VP, VP],
         "pp_readers_attach": [VP, P(ReaderConfig), P(ReaderWeights)],
         "pp_readers_write": [VP, VP, I32, I32, VP],
         "pp_readers_set_visible": [VP, I32],
@@ -236,6 +241,11 @@ class TemporalModel:
         arr, p = _ids(ids)
         T = ids.shape[-2]
         _check(load().pp_temporal_prefill(self.handle, kv.handle, p, T, _ptr(h_out), _stream(stream)))
+
+    def prefill_embedded(self, kv, x, h_out, stream=None):
+        """Prefill from summed embeddings x [T, d_model] (a float32 CUDA tensor)."""
+        _check(load().pp_temporal_prefill_embedded(self.handle, kv.handle, _ptr(x), int(x.shape[0]), _ptr(h_out),
+                                                   _stream(stream)))
 
     def set_graph(self, enable):
         _check(load().pp_temporal_set_graph(self.handle, 1 if enable else 0))
@@ -432,3 +442,14 @@ class Generator:
         _check(load().pp_generator_inspect(self.handle, _ptr(inputs), _ptr(chosen), _ptr(text_logits),
                                            _ptr(depth_logits), _stream(stream)))
 
+
+    def info(self):
+        cur, nb = ctypes.c_int64(), ctypes.c_uint64()
+        _check(load().pp_generator_info(self.handle, ctypes.byref(cur), ctypes.byref(nb)))
+        return cur.value, nb.value
+
+    def store(self, dst, stream=None):
+        _check(load().pp_generator_store(self.handle, _ptr(dst), _stream(stream)))
+
+    def restore(self, src, cursor, stream=None):
+        _check(load().pp_generator_restore(self.handle, _ptr(src), int(cursor), _stream(stream)))

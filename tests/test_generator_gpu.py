@@ -152,3 +152,42 @@ def test_generator_greedy_and_defaults_validation():
         gen.step(None, np.full(17, 1.0), b["out"])         # draw outside [0, 1)
     with pytest.raises(pp.PPError):
         pp.Generator(model, kv, dep, delays=(0,) * 16)     # wrong stream count
+
+
+def test_generator_session_store_and_restore_resume_exactly():
+    """A session stored after some calls (the model's ring with pp_kv_store and the
+    delayed-code ring with pp_generator_store) and restored later resumes exactly: the same
+    supplied codes and draws give the same selections, outputs and logits, bit for bit."""
+    import torch
+    (Wt, ct, Wd, cd), (model, kv, dep, gen), b = _setup_generator(seed=5)
+    g = np.random.default_rng(21)
+    n0, n1 = 5, 4
+    prov = _user_codes(g, n0 + n1, 0.3)
+    U = g.random((n0 + n1, 17))
+    for s in range(n0):
+        gen.step(prov[s], U[s], b["out"])
+    cur, nbytes = gen.info()
+    assert cur == n0
+    ring = torch.empty(kv.info()[1] // 4, dtype=torch.float32, device="cuda")
+    kv.store(ring)
+    state = torch.empty((nbytes + 3) // 4, dtype=torch.int32, device="cuda")
+    gen.store(state)
+    pos = kv.info()[0]
+    runs = []
+    for rep in range(2):
+        if rep == 1:
+            kv.restore(ring, pos)
+            gen.restore(state, cur)
+            assert gen.info()[0] == cur
+        got = []
+        for s in range(n0, n0 + n1):
+            has = gen.step(prov[s], U[s], b["out"])
+            gen.inspect(b["inputs"], b["chosen"], b["text_logits"], b["depth_logits"])
+            torch.cuda.synchronize()
+            got.append((has, b["out"].cpu().numpy().copy() if has else None, b["chosen"].cpu().numpy().copy(),
+                        b["text_logits"].cpu().numpy().copy(), b["depth_logits"].cpu().numpy().copy()))
+        runs.append(got)
+    for a, c in zip(runs[0], runs[1]):
+        assert a[0] == c[0]
+        for x, y in zip(a[1:], c[1:]):
+            assert (x is None and y is None) or np.array_equal(x, y)

@@ -159,3 +159,48 @@ def test_snapshot_restore_and_reprime_are_exact():
     shape = (cfg["n_layers"], 2, 1, cfg["n_heads"], cfg["context"], cfg["d_head"])
     got, ref = _ring(kv, "bf16").view(shape), snap.view(shape)
     assert torch.equal(got[..., :p, :], ref[..., :p, :])
+
+
+@pytest.mark.parametrize("wdtype", ["fp32", "bf16"])
+def test_prefill_from_summed_embeddings(wdtype):
+    """pp_temporal_prefill_embedded (a cached prompt replayed as summed embeddings): with
+    each frame's embedding sum as input (the fixed-order float32 sum the ID path's gather
+    forms) it gives the token-ID prefill's rows bit for bit, as a first prompt and as a
+    chunk after it; with inputs no IDs produce (the sums scaled by
+    0.5) it matches the oracle's forward over those inputs."""
+    import torch
+    cfg = synth.TINY_TEMPORAL
+    W = synth.temporal_weights(cfg, 39, wdtype, with_text_head=False)
+    ids = synth.stream_ids(cfg, 90, 40)
+    model = _model(cfg, W, wdtype, 64)
+    X = np.stack([O.embed(ids[t], W, cfg) for t in range(90)])
+    X32 = np.stack([O.embed(ids[t], W, cfg, precision="f32") for t in range(90)])   # the GPU gather's bits
+    tol = 1e-4 if wdtype == "fp32" else 2e-2
+    metric = max_abs_err if wdtype == "fp32" else norm_max_err
+    kv = model.kv_alloc()
+    h = torch.empty((90, cfg["d_model"]), device="cuda")
+    model.prefill(kv, ids[:60], h[:60])
+    model.prefill(kv, ids[60:], h[60:])
+    kv2 = model.kv_alloc()
+    h2 = torch.empty_like(h)
+    x32 = torch.from_numpy(X32).cuda()
+    model.prefill_embedded(kv2, x32[:60], h2[:60])
+    model.prefill_embedded(kv2, x32[60:], h2[60:])
+    torch.cuda.synchronize()
+    assert kv2.info()[0] == 90
+    assert torch.equal(h, h2)                 # the same float32 sums in: the same bits out
+    xd = torch.from_numpy(X.astype(np.float32)).cuda()
+    # inputs that are not embedding sums of any IDs, against the oracle's forward over them
+    kv3 = model.kv_alloc()
+    h3 = torch.empty((60, cfg["d_model"]), device="cuda")
+    model.prefill_embedded(kv3, (0.5 * xd[:60]).contiguous(), h3)
+    torch.cuda.synchronize()
+    Xh = 0.5 * X[:60]
+    pos = np.arange(60)
+    Y = Xh
+    for l in range(cfg["n_layers"]):
+        Y = O.block_full(Y, pos, l, W, cfg)
+    want = O.rmsnorm(Y, W["out_norm.alpha"], cfg["eps"])
+    err = metric(h3.cpu().numpy(), want)
+    print("prefill from summed embeddings (%s): scaled-input err %.3g" % (wdtype, err))
+    assert err <= tol
