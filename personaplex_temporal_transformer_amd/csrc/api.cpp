@@ -363,6 +363,9 @@ extern "C" pp_status pp_embed_sum(const pp_model* mc, const int32_t* ids_host, i
   if (!m || !ids_host || !x_out_dev) return pp_fail(PP_E_ARG, "NULL argument");
   if (batch < 1 || batch > m->max_batch || T < 1) return pp_fail(PP_E_ARG, "batch or T out of range");
   const size_t frames = (size_t)batch * T;
+  // sizes first: the IDs are read only once the call is known to fit
+  if (frames > 1 && frames > m->ids_frames)
+    return pp_fail(PP_E_CAPACITY, "batch*T exceeds max_prefill_T x max_batch frames");
   pp_status st = m->check_ids(ids_host, frames);
   if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -373,8 +376,6 @@ extern "C" pp_status pp_embed_sum(const pp_model* mc, const int32_t* ids_host, i
   if (frames == 1) {
     for (int k = 0; k < a.n_streams; ++k) a.ids_arg[k] = ids_host[k];
   } else {
-    if (frames > m->ids_frames)
-      return pp_fail(PP_E_CAPACITY, "batch*T exceeds max_prefill_T x max_batch frames");
     if ((st = m->stage_ids(ids_host, frames * a.n_streams, s))) return st;
     a.ids_dev = m->ids_dev;
   }

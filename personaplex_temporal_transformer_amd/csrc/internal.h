@@ -199,6 +199,7 @@ struct GemmArgs {
   // scales of the float16 operands); the float16 outputs it writes are Q * 2^-q16_exp, the
   // K copy * 2^-k16_exp, V^T * 2^-vt_exp, SiLU(g) * z * 2^-s16_exp. Zero: no scaling.
   int acc_exp, q16_exp, k16_exp, vt_exp, s16_exp;
+  int tag;   // 1: the W_out product (a separate kernel name in profiles; same code)
 };
 hipError_t launch_gemm(int epi, bool bf16, const GemmArgs& g, int n_cu, hipStream_t s);
 // float16 copy w * 2^-w_exp of n_elems bfloat16 values (n_elems % 8 == 0), round to nearest

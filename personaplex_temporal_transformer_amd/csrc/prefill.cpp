@@ -225,7 +225,7 @@ static pp_status prefill_impl(pp_model* m, pp_kv* kv, const int32_t* ids_host, c
 
     GemmArgs gw{};
     gw.A = m->pg; gw.B = bf ? m->f16_out[l] : m->w_out[l]; gw.M = T; gw.N = D; gw.K = F; gw.x = m->px;
-    gw.acc_exp = fe.s + fe.w_out;
+    gw.acc_exp = fe.s + fe.w_out; gw.tag = 1;
     gw.part = m->psplit; gw.part_bytes = m->psplit_bytes;
     e = launch_gemm(GEPI_RESID, bf, gw, m->n_cu, s);
     if (e != hipSuccess) return hip_fail("prefill W_out", e);

@@ -148,7 +148,9 @@ __device__ __forceinline__ void lds_wait_barrier() { asm volatile("s_waitcnt lgk
 // GEPI_SWIGLU: the B tile holds W_in rows j0..j0+BN/2-1 (g) and F+j0.. (z); wave (wm, wn)
 // multiplies g rows wn*16*NI.. (NI/2 tiles) and the z rows BN/2 + wn*16*NI.., so g and z
 // of one output share a lane.
-template <int EPI, int WM, int WN, int MI, int NI, int NS, int KB, bool LATE>
+// TAG only names the instantiation (the W_out product's residual launches are TAG 1, so a
+// kernel profile lists them apart from W_O's); the code does not depend on it.
+template <int EPI, int WM, int WN, int MI, int NI, int NS, int KB, bool LATE, int TAG>
 __global__ __launch_bounds__(WM * WN * 64) void k_gemm_f16(GemmArgs g) {
   constexpr int NW = WM * WN;
   constexpr int BM = WM * 32 * MI, BN = WN * 32 * NI;
@@ -726,7 +728,10 @@ static hipError_t launch_cfg(const GemmArgs& g, int n_cu, hipStream_t s) {
   const int n_tn = EPI == GEPI_SWIGLU ? g.F / (BN / 2) : g.N / BN;
   const int n_tm = (g.M + BM - 1) / BM;
   const int sp = pick_split(EPI, g, n_tm * n_tn, n_cu);
-  hipLaunchKernelGGL((k_gemm_f16<EPI, WM, WN, MI, NI, NS, KB, LATE>), dim3(n_tm * n_tn, sp), dim3(WM * WN * 64), 0, s, g);
+  if (EPI == GEPI_RESID && g.tag == 1)
+    hipLaunchKernelGGL((k_gemm_f16<EPI, WM, WN, MI, NI, NS, KB, LATE, 1>), dim3(n_tm * n_tn, sp), dim3(WM * WN * 64), 0, s, g);
+  else
+    hipLaunchKernelGGL((k_gemm_f16<EPI, WM, WN, MI, NI, NS, KB, LATE, 0>), dim3(n_tm * n_tn, sp), dim3(WM * WN * 64), 0, s, g);
   if (sp > 1) {
     if (EPI == GEPI_RESID) {
       const long long mn = (long long)g.M * g.N;
