@@ -564,6 +564,7 @@ hipError_t pp_model::enqueue_layers_batched(pp_kv* kv, hipStream_t s, long long 
     g.act = bu16; g.W = pk_qkv[l]; g.B = B; g.K = D; g.N = 3 * D; g.acc_exp = fe.u1 + fe.w_qkv;
     g.q_out = bq; g.kc = kbase; g.vc = vbase; g.kv_bstride = bstride; g.rope = rope; g.state = state;
     g.pos = pos_arg; g.D = D; g.dh = dh; g.C = C;
+    g.n_cu = n_cu;
     if ((e = launch_sgemm(SEPI_QKV, g, s)) != hipSuccess) break;
     AttnDecodeArgs at{};
     at.q = bq; at.k = kbase; at.v = vbase; at.state = state; at.pos = pos_arg; at.C = C; at.H = H; at.S = S_auto;
@@ -572,14 +573,17 @@ hipError_t pp_model::enqueue_layers_batched(pp_kv* kv, hipStream_t s, long long 
     if ((e = launch_attn_decode(at, true, dh, s)) != hipSuccess) break;
     SgemmArgs go{};
     go.act = bo16; go.W = pk_o[l]; go.B = B; go.K = D; go.N = D; go.x = bx; go.acc_exp = fe.v + fe.w_o;
+    go.n_cu = n_cu;
     if ((e = launch_sgemm(SEPI_RESID, go, s)) != hipSuccess) break;
     if ((e = launch_rmsnorm_rows(bx, norm2[l], (float)c.eps, D, B, nullptr, bu16, true, s, fe.u2)) != hipSuccess) break;
     SgemmArgs gi{};
     gi.act = bu16; gi.W = pk_in[l]; gi.B = B; gi.K = D; gi.N = F; gi.F = F; gi.s_out = bs16;
     gi.acc_exp = fe.u2 + fe.w_in; gi.s16_exp = fe.s;
+    gi.n_cu = n_cu;
     if ((e = launch_sgemm(SEPI_SWIGLU, gi, s)) != hipSuccess) break;
     SgemmArgs gw{};
     gw.act = bs16; gw.W = pk_out[l]; gw.B = B; gw.K = F; gw.N = D; gw.x = bx; gw.acc_exp = fe.s + fe.w_out;
+    gw.n_cu = n_cu;
     e = launch_sgemm(SEPI_RESID, gw, s);
   }
   return e;
@@ -615,6 +619,7 @@ pp_status pp_model::decode_batched(pp_kv* kv, const int32_t* ids_host, float* h_
     SgemmArgs g{};
     g.act = bu16; g.W = pk_head; g.B = B; g.K = D; g.N = c.text_vocab - 1; g.out = text_logits_dev;
     g.acc_exp = f16e_uout + f16e_whead;
+    g.n_cu = n_cu;
     e = launch_sgemm(SEPI_STORE, g, s);
   }
   if (e != hipSuccess) return pp_fail(PP_E_HIP, std::string("final norm / text head: ") + hipGetErrorString(e));

@@ -335,6 +335,7 @@ struct SgemmArgs {
   // the products are multiplied by 2^acc_exp (undoing the float16 operand scales); the
   // SiLU products are written as SiLU(g) * z * 2^-s16_exp
   int acc_exp, s16_exp;
+  int n_cu;              // compute units (0: 256); one session tile runs one workgroup per CU
 };
 constexpr int kSgemmMaxBatch = 64;
 hipError_t launch_sgemm(int epi, const SgemmArgs& a, hipStream_t s);

@@ -29,7 +29,11 @@ namespace pp {
 
 constexpr int kSgWaves = 8;
 
-template <int EPI, int NBT, int NT>
+// BAL: the grid has one workgroup per CU (at most), and workgroup b owns the contiguous
+// column tiles [b * tiles / grid, (b + 1) * tiles / grid) -- at most NT of them, nt at run
+// time -- so every CU streams an equal share; otherwise workgroup b owns tiles b*NT ..
+// b*NT + NT-1.
+template <int EPI, int NBT, int NT, bool BAL>
 __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
   __shared__ float red[kSgWaves][NT * NBT][64][4];
   __shared__ float tile[NBT * 16][NT * 16 + 1];
@@ -37,7 +41,9 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;
   const int nsteps = a.K / 32;
-  const int tile0 = blockIdx.x * NT;
+  const int tiles = EPI == SEPI_SWIGLU ? a.F / 8 : a.N / 16;
+  const int tile0 = BAL ? (int)((long long)blockIdx.x * tiles / gridDim.x) : (int)blockIdx.x * NT;
+  const int nt = BAL ? (int)((long long)(blockIdx.x + 1) * tiles / gridDim.x) - tile0 : NT;   // <= NT
   // packed fragments of this workgroup's tiles: [tile][step][lane][8]
   const uint16_t* Wr = static_cast<const uint16_t*>(a.W) + ((size_t)tile0 * nsteps * 64 + lane) * 8;
   const size_t tstride = (size_t)nsteps * 512;
@@ -65,7 +71,8 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
-      for (int j = 0; j < NT; ++j) wv[buf][u][j] = load_stream(Wr + j * tstride + (size_t)(st0 + u) * 512);
+      for (int j = 0; j < NT; ++j)
+        if (j < nt) wv[buf][u][j] = load_stream(Wr + j * tstride + (size_t)(st0 + u) * 512);
 #pragma unroll
       for (int t = 0; t < NBT; ++t)
         av[buf][u][t] = live[t] ? *reinterpret_cast<const u32x4*>(Ar[t] + (size_t)(st0 + u) * 512) : u32x4{0u, 0u, 0u, 0u};
@@ -76,6 +83,7 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
+        if (j >= nt) continue;
         const f16x8 wf = bf16x8_to_f16(wv[buf][u][j]);
 #pragma unroll
         for (int t = 0; t < NBT; ++t)
@@ -99,6 +107,7 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
       a1[t] = live[t] ? *reinterpret_cast<const u32x4*>(Ar[t] + (size_t)st * 512) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
+      if (j >= nt) continue;
       const f16x8 wf = bf16x8_to_f16(load_stream(Wr + j * tstride + (size_t)st * 512));
 #pragma unroll
       for (int t = 0; t < NBT; ++t)
@@ -112,7 +121,7 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[w][j * NBT + t][lane][i] = acc[j][t][i];
   __syncthreads();
-  for (int o = tid; o < NT * NBT * 256; o += kSgWaves * 64) {
+  for (int o = tid; o < nt * NBT * 256; o += kSgWaves * 64) {
     const int jt = o >> 8, l = (o >> 2) & 63, i = o & 3;
     const int j = jt / NBT, t = jt - j * NBT;
     float v = 0.f;
@@ -123,8 +132,8 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
   __syncthreads();
 
   // epilogue: thread -> (session b, column c of the workgroup's NT * 16)
-  for (int o = tid; o < NBT * 16 * NT * 16; o += kSgWaves * 64) {
-    const int b = o / (NT * 16), cc = o - b * (NT * 16);
+  for (int o = tid; o < NBT * 16 * nt * 16; o += kSgWaves * 64) {
+    const int b = o / (nt * 16), cc = o - b * (nt * 16);
     if (b >= a.B) continue;
     const int j = cc >> 4, c = cc & 15;
     const int tl = tile0 + j;     // this column's 16-column tile
@@ -189,25 +198,42 @@ hipError_t launch_sgemm_pack(const void* W, void* packed, int rows_out, int K, i
   return hipGetLastError();
 }
 
+template <int EPI, int NT>
+static void launch_bal(const SgemmArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_sgemm<EPI, 1, NT, true>), dim3(grid), dim3(kSgWaves * 64), 0, s, a);
+}
+
 template <int EPI>
 static hipError_t launch_epi(const SgemmArgs& a, hipStream_t s) {
   const int tiles = EPI == SEPI_SWIGLU ? a.F / 8 : a.N / 16;
   const dim3 block(kSgWaves * 64);
   const int nbt = (a.B + 15) / 16;
+  if (nbt == 1) {
+    // one session tile: one workgroup per CU, each with an equal run of column tiles
+    const int n_cu = a.n_cu > 0 ? a.n_cu : 256;
+    const int grid = tiles < n_cu ? tiles : n_cu;
+    const int per = (tiles + grid - 1) / grid;   // tiles of the busiest workgroup
+    if (per <= 1) launch_bal<EPI, 1>(a, grid, s);
+    else if (per <= 2) launch_bal<EPI, 2>(a, grid, s);
+    else if (per <= 3) launch_bal<EPI, 3>(a, grid, s);
+    else if (per <= 4) launch_bal<EPI, 4>(a, grid, s);
+    else if (per <= 6) launch_bal<EPI, 6>(a, grid, s);
+    else if (per <= 8) launch_bal<EPI, 8>(a, grid, s);
+    else launch_bal<EPI, 8>(a, (tiles + 7) / 8, s);
+    return hipGetLastError();
+  }
   // two column tiles per workgroup (each activation fragment feeds two products) when
   // there are enough tiles to keep every CU busy
-  const bool two = tiles % 2 == 0 && tiles >= 512 && nbt <= 2;
+  const bool two = tiles % 2 == 0 && tiles >= 512 && nbt == 2;
   if (two) {
     const dim3 grid(tiles / 2);
-    if (nbt == 1) hipLaunchKernelGGL((k_sgemm<EPI, 1, 2>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_sgemm<EPI, 2, 2>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((k_sgemm<EPI, 2, 2, false>), grid, block, 0, s, a);
     return hipGetLastError();
   }
   const dim3 grid(tiles);
-  if (nbt == 1) hipLaunchKernelGGL((k_sgemm<EPI, 1, 1>), grid, block, 0, s, a);
-  else if (nbt == 2) hipLaunchKernelGGL((k_sgemm<EPI, 2, 1>), grid, block, 0, s, a);
-  else if (nbt == 3) hipLaunchKernelGGL((k_sgemm<EPI, 3, 1>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((k_sgemm<EPI, 4, 1>), grid, block, 0, s, a);
+  if (nbt == 2) hipLaunchKernelGGL((k_sgemm<EPI, 2, 1, false>), grid, block, 0, s, a);
+  else if (nbt == 3) hipLaunchKernelGGL((k_sgemm<EPI, 3, 1, false>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((k_sgemm<EPI, 4, 1, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
