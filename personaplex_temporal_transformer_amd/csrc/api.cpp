@@ -559,9 +559,16 @@ hipError_t pp_model::enqueue_layers_batched(pp_kv* kv, hipStream_t s, long long 
     char* kbase = static_cast<char*>(kv->ring) + (size_t)(2 * l) * per_kv;
     char* vbase = kbase + per_kv;
     const F16Exps& fe = f16e[l];
-    if ((e = launch_rmsnorm_rows(bx, norm1[l], (float)c.eps, D, B, nullptr, bu16, true, s, fe.u1)) != hipSuccess) break;
+    // up to kSgemmNormMaxBatch sessions the QKV and W_in products form the row norm in
+    // their prologue; beyond, one row-norm launch writes their float16 activations
+    const bool fold = B <= kSgemmNormMaxBatch && D <= kSgemmNormMaxK;
+    if (!fold && (e = launch_rmsnorm_rows(bx, norm1[l], (float)c.eps, D, B, nullptr, bu16, true, s, fe.u1)) != hipSuccess)
+      break;
     SgemmArgs g{};
     g.act = bu16; g.W = pk_qkv[l]; g.B = B; g.K = D; g.N = 3 * D; g.acc_exp = fe.u1 + fe.w_qkv;
+    if (fold) {
+      g.xin = bx; g.alpha = norm1[l]; g.eps = (float)c.eps; g.act_exp = fe.u1;
+    }
     g.q_out = bq; g.kc = kbase; g.vc = vbase; g.kv_bstride = bstride; g.rope = rope; g.state = state;
     g.pos = pos_arg; g.D = D; g.dh = dh; g.C = C;
     g.n_cu = n_cu;
@@ -575,10 +582,14 @@ hipError_t pp_model::enqueue_layers_batched(pp_kv* kv, hipStream_t s, long long 
     go.act = bo16; go.W = pk_o[l]; go.B = B; go.K = D; go.N = D; go.x = bx; go.acc_exp = fe.v + fe.w_o;
     go.n_cu = n_cu;
     if ((e = launch_sgemm(SEPI_RESID, go, s)) != hipSuccess) break;
-    if ((e = launch_rmsnorm_rows(bx, norm2[l], (float)c.eps, D, B, nullptr, bu16, true, s, fe.u2)) != hipSuccess) break;
+    if (!fold && (e = launch_rmsnorm_rows(bx, norm2[l], (float)c.eps, D, B, nullptr, bu16, true, s, fe.u2)) != hipSuccess)
+      break;
     SgemmArgs gi{};
     gi.act = bu16; gi.W = pk_in[l]; gi.B = B; gi.K = D; gi.N = F; gi.F = F; gi.s_out = bs16;
     gi.acc_exp = fe.u2 + fe.w_in; gi.s16_exp = fe.s;
+    if (fold) {
+      gi.xin = bx; gi.alpha = norm2[l]; gi.eps = (float)c.eps; gi.act_exp = fe.u2;
+    }
     gi.n_cu = n_cu;
     if ((e = launch_sgemm(SEPI_SWIGLU, gi, s)) != hipSuccess) break;
     SgemmArgs gw{};

@@ -169,24 +169,6 @@ __device__ __forceinline__ float block_sum_256(float v, float* scratch) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
-// Agent-scope (all XCDs) relaxed atomic stores and loads. On this multi-XCD part each XCD
-// has its own L2, which is not coherent with the others for ordinary accesses; these
-// bypass the non-coherent cache level, so a value stored by one workgroup is seen by a
-// workgroup on another XCD once the store has completed (s_waitcnt) and the reader has
-// observed a counter that was bumped after it.
-template <typename T>
-__device__ __forceinline__ void store_agent(T* p, T v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T>
-__device__ __forceinline__ T load_agent(const T* p) {
-  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// 16-byte buffer load at agent scope (sc1: not served from a possibly stale L2 line).
-__device__ __forceinline__ u32x4 buffer_load16_agent(__amdgpu_buffer_rsrc_t r, int byte_offset) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 16 /* sc1 */);
-}
-
 // 2^x with the hardware exponential (exp2(-inf) = 0); used where x <= 0 (softmax weights).
 constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

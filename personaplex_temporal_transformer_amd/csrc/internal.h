@@ -336,8 +336,17 @@ struct SgemmArgs {
   // SiLU products are written as SiLU(g) * z * 2^-s16_exp
   int acc_exp, s16_exp;
   int n_cu;              // compute units (0: 256); one session tile runs one workgroup per CU
+  // RMSNorm prologue (B <= kSgemmNormMaxBatch, K <= kSgemmNormMaxK; act is then unused):
+  // the activations are alpha * x / sqrt(mean(x^2) + eps) of the float32 rows xin [B][K],
+  // formed by every workgroup and written to its LDS as float16 * 2^-act_exp
+  const float* xin;
+  const float* alpha;
+  float eps;
+  int act_exp;
 };
 constexpr int kSgemmMaxBatch = 64;
+constexpr int kSgemmNormMaxBatch = 8;
+constexpr int kSgemmNormMaxK = 4096;
 hipError_t launch_sgemm(int epi, const SgemmArgs& a, hipStream_t s);
 // Copy of a row-major [rows][K] bf16 matrix in the fragment order the skinny products
 // read (same byte count); rows_out = N (or F for the SiLU-gated W_in with 2F rows).

@@ -16,7 +16,8 @@
 // activations are written in the same order by their producers (the row RMSNorm, the
 // attention combine and this file's SiLU-product epilogue; frag_act_index), so their loads
 // are 1 KB contiguous as well (row-major [B][K] they were 16 rows x 64 bytes, and the
-// batched step took 3-16 % longer at B = 16-64). The waves' partial tiles
+// batched step took 3-16 % longer at B = 16-64); up to 8 sessions, the products that
+// follow a row norm form it themselves into LDS (NORM below). The waves' partial tiles
 // are summed in LDS in wave order (fixed order: reproducible), then the epilogue applies
 // RoPE / ring append, the residual add, the SiLU product or a plain store.
 #include <cmath>
@@ -33,10 +34,24 @@ constexpr int kSgWaves = 8;
 // column tiles [b * tiles / grid, (b + 1) * tiles / grid) -- at most NT of them, nt at run
 // time -- so every CU streams an equal share; otherwise workgroup b owns tiles b*NT ..
 // b*NT + NT-1.
-template <int EPI, int NBT, int NT, bool BAL>
+// NORM (one session tile, B <= kSgemmNormMaxBatch, K <= kSgemmNormMaxK): the activations
+// are the RMSNorm of the float32 rows a.xin ("PersonaPlex native LM audit", section 3: the
+// pre-norm of the block's attention and gated-MLP halves), formed by every workgroup: the
+// rows are loaded ahead of the first weights, each session's sum of squares is reduced
+// (per thread, then per wave, then over the waves in wave order) while those weights are in
+// flight, and the normalised rows are written to LDS as float16 fragments, which the
+// product then reads in place of a.act. This replaces a separate row-norm launch per
+// product; at small B re-reading B rows per workgroup (served by the L2) costs less than
+// the launch.
+template <int EPI, int NBT, int NT, bool BAL, bool NORM>
 __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
+  static_assert(!NORM || (NBT == 1 && BAL), "the RMSNorm prologue serves one session tile");
+  constexpr int BN = kSgemmNormMaxBatch;
   __shared__ float red[kSgWaves][NT * NBT][64][4];
   __shared__ float tile[NBT * 16][NT * 16 + 1];
+  // NORM: float16 fragments of the normalised rows, [32-element step][k group][session][8]
+  __shared__ u32x4 act_lds[NORM ? kSgemmNormMaxK / 32 * 4 * BN : 1];
+  __shared__ float red_n[NORM ? kSgWaves : 1][BN];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;
@@ -55,8 +70,25 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
 #pragma unroll
   for (int t = 0; t < NBT; ++t) {
     live[t] = t * 16 + n < a.B;
-    Ar[t] = a.act + ((size_t)t * nsteps * 64 + lane) * 8;
+    Ar[t] = NORM ? nullptr : a.act + ((size_t)t * nsteps * 64 + lane) * 8;
   }
+  // Every load below is unconditional, so no branch stands between a load and its use and
+  // the compiler waits for each group of loads alone (a load under a branch makes it wait
+  // for all outstanding loads, which would drain the next group's prefetch): lanes of
+  // sessions past B load their own fragment slot (the float16 buffers hold whole 16-session
+  // tiles) and then zero it; column tiles past nt re-read tile nt - 1 and their products
+  // are dropped.
+  // this lane's activation fragment of step st in session tile t
+  auto load_act = [&](int t, int st) -> u32x4 {
+    u32x4 v;
+    if constexpr (NORM)
+      v = act_lds[(st * 4 + (lane >> 4)) * BN + (n < BN ? n : BN - 1)];
+    else
+      v = *reinterpret_cast<const u32x4*>(Ar[t] + (size_t)st * 512);
+    return live[t] ? v : u32x4{0u, 0u, 0u, 0u};
+  };
+  // this lane's weight fragment of step st in column tile j of the workgroup
+  auto wptr = [&](int j, int st) { return Wr + (j < nt ? j : nt - 1) * tstride + (size_t)st * 512; };
   f32x4 acc[NT][NBT];
 #pragma unroll
   for (int j = 0; j < NT; ++j)
@@ -67,15 +99,30 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
   // multiplied (loads complete in issue order, so the wait for a group is exact)
   constexpr int U = NT * NBT == 1 ? 8 : (NT * NBT == 2 ? 4 : 2);
   u32x4 wv[2][U][NT], av[2][U][NBT];
+  auto load_w = [&](int buf, int st0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) wv[buf][u][j] = load_stream(wptr(j, st0 + u));
+  };
+  auto load_a = [&](int buf, int st0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int t = 0; t < NBT; ++t) av[buf][u][t] = load_act(t, st0 + u);
+  };
   auto load_group = [&](int buf, int st0) {
+    if constexpr (NORM) {
+      load_w(buf, st0);
+      load_a(buf, st0);
+    } else {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < U; ++u) {
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
-        if (j < nt) wv[buf][u][j] = load_stream(Wr + j * tstride + (size_t)(st0 + u) * 512);
+        for (int j = 0; j < NT; ++j) wv[buf][u][j] = load_stream(wptr(j, st0 + u));
 #pragma unroll
-      for (int t = 0; t < NBT; ++t)
-        av[buf][u][t] = live[t] ? *reinterpret_cast<const u32x4*>(Ar[t] + (size_t)(st0 + u) * 512) : u32x4{0u, 0u, 0u, 0u};
+        for (int t = 0; t < NBT; ++t) av[buf][u][t] = load_act(t, st0 + u);
+      }
     }
   };
   auto mul_group = [&](int buf) {
@@ -83,7 +130,6 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        if (j >= nt) continue;
         const f16x8 wf = bf16x8_to_f16(wv[buf][u][j]);
 #pragma unroll
         for (int t = 0; t < NBT; ++t)
@@ -91,8 +137,89 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
       }
   };
   const int ng = (s1 - s0) / U;
-  if (ng > 0) load_group(0, s0);
-  for (int gi = 0; gi < ng; gi += 2) {
+  int gi0 = 0;   // first group of the main loop
+  if constexpr (NORM) {
+    // rows and scales first, then the first weights, so the reductions below wait for the
+    // rows alone. The rows are buffer loads bounded by the B rows: the loads of rows past B
+    // (and of k past K) return zeros without memory traffic, and none sits under a branch.
+    constexpr int NX = kSgemmNormMaxK / (kSgWaves * 64 * 4);   // float4 per thread and row
+    const int K = a.K;
+    const auto xr = make_rsrc(a.xin, (uint32_t)((size_t)a.B * K * 4));
+    const auto ar = make_rsrc(a.alpha, (uint32_t)K * 4);
+    f32x4 xv[BN][NX], al[NX];
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int k = (i * kSgWaves * 64 + tid) * 4;
+      const int kk = k < K ? k : 1 << 24;   // k past K: past every row, a zero read
+      al[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ar, kk * 4, 0, 0));
+#pragma unroll
+      for (int b = 0; b < BN; ++b)
+        xv[b][i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (b * K + kk) * 4, 0, 0));
+    }
+    // the first two groups' weights, both buffers (with no branch around them, so that
+    // the reductions below wait for the rows alone; steps past the wave's run load its
+    // last step again and are never used): they stream while the norm is formed
+#pragma unroll
+    for (int g2 = 0; g2 < 2; ++g2)
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const int st = s0 + g2 * U + u;
+          wv[g2][u][j] = load_stream(wptr(j, st < nsteps ? st : nsteps - 1));
+        }
+    float ss[BN];
+#pragma unroll
+    for (int b = 0; b < BN; ++b) {
+      ss[b] = 0.f;
+#pragma unroll
+      for (int i = 0; i < NX; ++i) {
+        const f32x4 v = xv[b][i];
+        const float q = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        ss[b] += (i * kSgWaves * 64 + tid) * 4 < K ? q : 0.f;
+      }
+      ss[b] = wave_sum(ss[b]);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int b = 0; b < BN; ++b) red_n[w][b] = ss[b];
+    }
+    lds_barrier();
+    const float osc = ldexpf(1.0f, -a.act_exp);   // the float16 operand's scale (a power of two)
+    uint2* al2 = reinterpret_cast<uint2*>(act_lds);
+#pragma unroll
+    for (int b = 0; b < BN; ++b) {
+      float tot = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kSgWaves; ++ww) tot += red_n[ww][b];
+      const float r = 1.0f / sqrtf(tot / (float)K + a.eps);
+#pragma unroll
+      for (int i = 0; i < NX; ++i) {
+        const int k = (i * kSgWaves * 64 + tid) * 4;   // four consecutive k: one half fragment
+        if (b < a.B && k < K) {
+          const f32x4 y = ((xv[b][i] * r) * al[i]) * osc;
+          const uint32_t lo = (uint32_t)f32_to_f16(y.x) | ((uint32_t)f32_to_f16(y.y) << 16);
+          const uint32_t hi = (uint32_t)f32_to_f16(y.z) | ((uint32_t)f32_to_f16(y.w) << 16);
+          al2[(((k >> 5) * 4 + ((k & 31) >> 3)) * BN + b) * 2 + ((k & 7) >> 2)] = make_uint2(lo, hi);
+        }
+      }
+    }
+    lds_barrier();
+    // the first iteration of the loop below, with both groups' weights already loaded
+    if (ng > 0) {
+      load_a(0, s0);
+      if (ng > 1) load_a(1, s0 + U);
+      mul_group(0);
+      if (ng > 1) {
+        if (ng > 2) load_group(0, s0 + 2 * U);
+        mul_group(1);
+      }
+    }
+    gi0 = 2;
+  } else {
+    if (ng > 0) load_group(0, s0);
+  }
+  for (int gi = gi0; gi < ng; gi += 2) {
     if (gi + 1 < ng) load_group(1, s0 + (gi + 1) * U);
     mul_group(0);
     if (gi + 1 < ng) {
@@ -103,12 +230,10 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
   for (int st = s0 + ng * U; st < s1; ++st) {
     u32x4 a1[NBT];
 #pragma unroll
-    for (int t = 0; t < NBT; ++t)
-      a1[t] = live[t] ? *reinterpret_cast<const u32x4*>(Ar[t] + (size_t)st * 512) : u32x4{0u, 0u, 0u, 0u};
+    for (int t = 0; t < NBT; ++t) a1[t] = load_act(t, st);
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      if (j >= nt) continue;
-      const f16x8 wf = bf16x8_to_f16(load_stream(Wr + j * tstride + (size_t)st * 512));
+      const f16x8 wf = bf16x8_to_f16(load_stream(wptr(j, st)));
 #pragma unroll
       for (int t = 0; t < NBT; ++t)
         acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a1[t]), wf, acc[j][t], 0, 0, 0);
@@ -198,9 +323,24 @@ hipError_t launch_sgemm_pack(const void* W, void* packed, int rows_out, int K, i
   return hipGetLastError();
 }
 
-template <int EPI, int NT>
+template <int EPI, int NT, bool NORM>
 static void launch_bal(const SgemmArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_sgemm<EPI, 1, NT, true>), dim3(grid), dim3(kSgWaves * 64), 0, s, a);
+  hipLaunchKernelGGL((k_sgemm<EPI, 1, NT, true, NORM>), dim3(grid), dim3(kSgWaves * 64), 0, s, a);
+}
+
+// One session tile: one workgroup per CU, each with an equal run of column tiles.
+template <int EPI, bool NORM>
+static void launch_one_tile(const SgemmArgs& a, int tiles, hipStream_t s) {
+  const int n_cu = a.n_cu > 0 ? a.n_cu : 256;
+  const int grid = tiles < n_cu ? tiles : n_cu;
+  const int per = (tiles + grid - 1) / grid;   // tiles of the busiest workgroup
+  if (per <= 1) launch_bal<EPI, 1, NORM>(a, grid, s);
+  else if (per <= 2) launch_bal<EPI, 2, NORM>(a, grid, s);
+  else if (per <= 3) launch_bal<EPI, 3, NORM>(a, grid, s);
+  else if (per <= 4) launch_bal<EPI, 4, NORM>(a, grid, s);
+  else if (per <= 6) launch_bal<EPI, 6, NORM>(a, grid, s);
+  else if (per <= 8) launch_bal<EPI, 8, NORM>(a, grid, s);
+  else launch_bal<EPI, 8, NORM>(a, (tiles + 7) / 8, s);
 }
 
 template <int EPI>
@@ -208,18 +348,15 @@ static hipError_t launch_epi(const SgemmArgs& a, hipStream_t s) {
   const int tiles = EPI == SEPI_SWIGLU ? a.F / 8 : a.N / 16;
   const dim3 block(kSgWaves * 64);
   const int nbt = (a.B + 15) / 16;
+  if (a.xin) {
+    if constexpr (EPI == SEPI_QKV || EPI == SEPI_SWIGLU) {
+      launch_one_tile<EPI, true>(a, tiles, s);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
   if (nbt == 1) {
-    // one session tile: one workgroup per CU, each with an equal run of column tiles
-    const int n_cu = a.n_cu > 0 ? a.n_cu : 256;
-    const int grid = tiles < n_cu ? tiles : n_cu;
-    const int per = (tiles + grid - 1) / grid;   // tiles of the busiest workgroup
-    if (per <= 1) launch_bal<EPI, 1>(a, grid, s);
-    else if (per <= 2) launch_bal<EPI, 2>(a, grid, s);
-    else if (per <= 3) launch_bal<EPI, 3>(a, grid, s);
-    else if (per <= 4) launch_bal<EPI, 4>(a, grid, s);
-    else if (per <= 6) launch_bal<EPI, 6>(a, grid, s);
-    else if (per <= 8) launch_bal<EPI, 8>(a, grid, s);
-    else launch_bal<EPI, 8>(a, (tiles + 7) / 8, s);
+    launch_one_tile<EPI, false>(a, tiles, s);
     return hipGetLastError();
   }
   // two column tiles per workgroup (each activation fragment feeds two products) when
@@ -227,13 +364,13 @@ static hipError_t launch_epi(const SgemmArgs& a, hipStream_t s) {
   const bool two = tiles % 2 == 0 && tiles >= 512 && nbt == 2;
   if (two) {
     const dim3 grid(tiles / 2);
-    hipLaunchKernelGGL((k_sgemm<EPI, 2, 2, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((k_sgemm<EPI, 2, 2, false, false>), grid, block, 0, s, a);
     return hipGetLastError();
   }
   const dim3 grid(tiles);
-  if (nbt == 2) hipLaunchKernelGGL((k_sgemm<EPI, 2, 1, false>), grid, block, 0, s, a);
-  else if (nbt == 3) hipLaunchKernelGGL((k_sgemm<EPI, 3, 1, false>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((k_sgemm<EPI, 4, 1, false>), grid, block, 0, s, a);
+  if (nbt == 2) hipLaunchKernelGGL((k_sgemm<EPI, 2, 1, false, false>), grid, block, 0, s, a);
+  else if (nbt == 3) hipLaunchKernelGGL((k_sgemm<EPI, 3, 1, false, false>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((k_sgemm<EPI, 4, 1, false, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
@@ -241,6 +378,7 @@ hipError_t launch_sgemm(int epi, const SgemmArgs& a, hipStream_t s) {
   if (a.B < 1 || a.B > kSgemmMaxBatch || a.K % 32 || a.K <= 0) return hipErrorInvalidValue;
   if (epi == SEPI_SWIGLU ? (a.F <= 0 || a.F % 8) : (a.N <= 0 || a.N % 16)) return hipErrorInvalidValue;
   if (epi == SEPI_QKV && (a.N != 3 * a.D || a.dh % 2 || a.D % a.dh)) return hipErrorInvalidValue;
+  if (a.xin && (a.B > kSgemmNormMaxBatch || a.K > kSgemmNormMaxK || a.K % 4 || !a.alpha)) return hipErrorInvalidValue;
   switch (epi) {
     case SEPI_STORE: return launch_epi<SEPI_STORE>(a, s);
     case SEPI_RESID: return launch_epi<SEPI_RESID>(a, s);

@@ -33,10 +33,11 @@ def _run(cfg, W, B, ids, graph=True, logits=False, kv_frames=None):
     return model, kv, h.cpu().numpy(), (lg.cpu().numpy() if logits else None)
 
 
-@pytest.mark.parametrize("B", [2, 5, 16, 17, 40, 64])
+@pytest.mark.parametrize("B", [2, 5, 8, 9, 16, 17, 40, 64])
 def test_tiny_batched_matches_oracle_per_session(B):
-    """B sessions of 5 frames from position 0; 17, 40 and 64 (the maximum) sessions use 2, 3
-    and 4 tiles of 16."""
+    """B sessions of 5 frames from position 0; up to 8 sessions the QKV and W_in products
+    form the row norm in their prologue (9 and more: a row-norm launch); 17, 40 and 64 (the
+    maximum) sessions use 2, 3 and 4 tiles of 16."""
     cfg = synth.TINY_TEMPORAL
     W = synth.temporal_weights(cfg, 61, "bf16", with_text_head=True)
     ids = synth.stream_ids(cfg, 5, 62, batch=B)            # [B, 5, 17]
