@@ -65,27 +65,26 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_sgemm(SgemmArgs a) {
   const int s0 = w * nsteps / kSgWaves, s1 = (w + 1) * nsteps / kSgWaves;
   // this lane's activation fragments in each session tile (fragment order: tile, step,
   // lane, 8 values -- frag_act_index); lanes of sessions past B read zeros
-  const uint16_t* Ar[NBT];
   bool live[NBT];
 #pragma unroll
-  for (int t = 0; t < NBT; ++t) {
-    live[t] = t * 16 + n < a.B;
-    Ar[t] = NORM ? nullptr : a.act + ((size_t)t * nsteps * 64 + lane) * 8;
-  }
-  // Every load below is unconditional, so no branch stands between a load and its use and
-  // the compiler waits for each group of loads alone (a load under a branch makes it wait
-  // for all outstanding loads, which would drain the next group's prefetch): lanes of
-  // sessions past B load their own fragment slot (the float16 buffers hold whole 16-session
-  // tiles) and then zero it; column tiles past nt re-read tile nt - 1 and their products
-  // are dropped.
+  for (int t = 0; t < NBT; ++t) live[t] = t * 16 + n < a.B;
+  // No load below sits under a branch, so the compiler waits for each group of loads alone
+  // (a load under a branch makes it wait for all outstanding loads, which would drain the
+  // next group's prefetch): lanes of sessions past B read their activations through a
+  // buffer resource at an offset past its end, which returns zeros without memory traffic
+  // (in LDS: a slot of a live session, then zeroed); column tiles past nt re-read tile
+  // nt - 1 and their products are dropped.
+  const auto act_rs = make_rsrc(NORM ? nullptr : a.act, (uint32_t)(NBT * nsteps * 1024));
+  const int dead_off = 1 << 30;   // past any activation buffer (at most 4 x 352 x 1 KB)
   // this lane's activation fragment of step st in session tile t
   auto load_act = [&](int t, int st) -> u32x4 {
-    u32x4 v;
-    if constexpr (NORM)
-      v = act_lds[(st * 4 + (lane >> 4)) * BN + (n < BN ? n : BN - 1)];
-    else
-      v = *reinterpret_cast<const u32x4*>(Ar[t] + (size_t)st * 512);
-    return live[t] ? v : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (NORM) {
+      const u32x4 v = act_lds[(st * 4 + (lane >> 4)) * BN + (n < BN ? n : BN - 1)];
+      return live[0] ? v : u32x4{0u, 0u, 0u, 0u};
+    } else {
+      const int off = ((t * nsteps + st) * 64 + lane) * 16 + (live[t] ? 0 : dead_off);
+      return __builtin_amdgcn_raw_buffer_load_b128(act_rs, off, 0, 0);
+    }
   };
   // this lane's weight fragment of step st in column tile j of the workgroup
   auto wptr = [&](int j, int st) { return Wr + (j < nt ? j : nt - 1) * tstride + (size_t)st * 512; };
