@@ -69,6 +69,18 @@ def test_sampler_ties_and_degenerate_rows():
     assert set(got.tolist()) == set(range(10))
 
 
+def test_sampler_exact_boundaries():
+    """Equal top weights put the threshold u * total exactly on a running sum at u = j / k;
+    both sides take the first candidate whose running sum exceeds it strictly."""
+    n = 300
+    logits = np.full((6, n), -30.0, np.float32)
+    logits[:, 10:14] = 0.0                          # four equal top logits, weights 1 each
+    u = np.array([0.25, 0.5, 0.75, 0.25 - 2.0 ** -40, 0.0, 0.5 - 2.0 ** -40])
+    _check_rows(logits, 1.0, 4, u, "exact boundaries k=4")
+    got = _gpu_sample(logits, 1.0, 4, u)
+    assert got.tolist() == [11, 12, 13, 10, 10, 11]
+
+
 def _setup_generator(seed=0, **overrides):
     import torch
     require_gpu()

@@ -52,26 +52,45 @@ def test_window_only_matters_past_its_length():
     assert np.max(np.abs(l8[8:] - l16[8:])) > 1e-6
 
 
-def test_position_q_uses_slice_q():
-    """Perturbing position q' weights (packed slices, FFN q', head q', projection q')
-    leaves logits of positions < q' bit-unchanged and changes logits at q'."""
-    cfg, W, h = _setup(seed=3)
-    forced = synth.depth_codes(cfg, 8)
-    _, base = DF.step_logits(h, 11, forced, W, cfg)
+def _perturb(W, cfg, qp, family):
+    """A copy of W with one weight family of position qp changed: the packed QKV rows or
+    W_O rows of slice qp in every layer, the FFN matrices of position qp, its head or its
+    projection of the temporal hidden state."""
     D = cfg["d_model"]
-    for qp in (3, 12):
-        W2 = dict(W)
-        for m in range(cfg["n_layers"]):
-            p = "depformer.layers.%d." % m
+    W2 = dict(W)
+    for m in range(cfg["n_layers"]):
+        p = "depformer.layers.%d." % m
+        if family == "qkv":
             a = W[p + "self_attn.in_proj_weight"].copy()
             a[qp * 3 * D:(qp + 1) * 3 * D] *= 1.5
             W2[p + "self_attn.in_proj_weight"] = a
+        elif family == "out":
             o = W[p + "self_attn.out_proj.weight"].copy()
             o[qp * D:(qp + 1) * D] *= -1.0
             W2[p + "self_attn.out_proj.weight"] = o
-        _, pert = DF.step_logits(h, 11, forced, W2, cfg)
-        assert np.array_equal(base[:qp], pert[:qp])
-        assert np.max(np.abs(base[qp] - pert[qp])) > 1e-6
+        elif family in ("linear_in", "linear_out"):
+            n = p + "gating.%d.%s.weight" % (qp, family)
+            W2[n] = W[n] * -1.0
+    if family == "head":
+        W2["linears.%d.weight" % qp] = W["linears.%d.weight" % qp] * 0.5
+    if family == "proj":
+        W2["depformer_in.%d.weight" % qp] = W["depformer_in.%d.weight" % qp] * 2.0
+    return W2
+
+
+def test_position_q_uses_slice_q():
+    """Perturbing one weight family of position q' alone -- its packed QKV slice, its W_O
+    slice, its FFN input or output matrix, its head, its projection -- leaves the logits of
+    positions < q' bit-unchanged and changes the logits at q' (the per-step weights:
+    position q reads slice / matrix q of each family)."""
+    cfg, W, h = _setup(seed=3)
+    forced = synth.depth_codes(cfg, 8)
+    _, base = DF.step_logits(h, 11, forced, W, cfg)
+    for qp in (3, 12):
+        for family in ("qkv", "out", "linear_in", "linear_out", "head", "proj"):
+            _, pert = DF.step_logits(h, 11, forced, _perturb(W, cfg, qp, family), cfg)
+            assert np.array_equal(base[:qp], pert[:qp]), (qp, family)
+            assert np.max(np.abs(base[qp] - pert[qp])) > 1e-6, (qp, family)
 
 
 def test_first_position_attention_sees_one_key():

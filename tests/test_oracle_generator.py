@@ -15,11 +15,21 @@ from personaplex_temporal_transformer_amd import synth
 DELAY = np.array(OG.DELAYS)
 
 
+_WEIGHTS = []
+
+
+def make_weights():
+    """The tiny temporal and depth weights the generator pins run on (built once)."""
+    if not _WEIGHTS:
+        ct = synth.TINY_TEMPORAL
+        cd = synth.TINY_DEPTH
+        _WEIGHTS.append((synth.temporal_weights(ct, 3, "fp32"), ct, synth.depth_weights(cd, 4, "fp32"), cd))
+    return _WEIGHTS[0]
+
+
 @pytest.fixture(scope="module")
 def weights():
-    ct = synth.TINY_TEMPORAL
-    cd = synth.TINY_DEPTH
-    return (synth.temporal_weights(ct, 3, "fp32"), ct, synth.depth_weights(cd, 4, "fp32"), cd)
+    return make_weights()
 
 
 def _codes(g, n):
@@ -27,6 +37,23 @@ def _codes(g, n):
     c[:, 0] = g.integers(0, 32000, n)
     c[:, 1:] = g.integers(0, 2048, (n, 16))
     return c
+
+
+def test_first_model_step_reads_the_initial_tokens(weights):
+    """Nothing supplied: the first call only primes the ring; the second (the first model
+    step) feeds the temporal step the initial tokens -- text 32000, every audio stream
+    2048 -- and a code supplied at the first call replaces its stream's initial token."""
+    W_t, ct, W_d, cd = weights
+    g = OG.Generator(W_t, ct, W_d, cd)
+    assert g.step() is None
+    g.step(uniforms=np.zeros(17))
+    assert g.last_inputs.tolist() == [32000] + [2048] * 16
+    g2 = OG.Generator(W_t, ct, W_d, cd)
+    sup = np.full(17, -1)
+    sup[9] = 77                       # user codebook 0, delay 0: slot 0 at the first call
+    assert g2.step(provided=sup) is None
+    g2.step(uniforms=np.zeros(17))
+    assert g2.last_inputs.tolist() == [32000] + [2048] * 8 + [77] + [2048] * 7
 
 
 def test_delay_table():

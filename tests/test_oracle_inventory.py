@@ -89,6 +89,18 @@ def test_ring_examples():
         assert len(ring.visible(stated, end - 1, cap)) == cap
 
 
+def test_ring_mask_edges():
+    """The declared mask 0 <= query - key < context on labels around both edges: with
+    context 4 and query 10 the key 6 (four back) is out, 7..10 are in, 11 (future) is out;
+    a full stated ring of 4 slots after positions 0..9 holds 6..9, all visible to 9 and
+    three of them (7..9) to 10."""
+    assert ring.visible([5, 6, 7, 8, 9, 10, 11], 10, 4) == [7, 8, 9, 10]
+    assert ring.visible([None, 3, 4], 4, 1) == [4]
+    stated = ring.stated_positions(4, 10)
+    assert sorted(stated) == [6, 7, 8, 9]
+    assert len(ring.visible(stated, 9, 4)) == 4 and sorted(ring.visible(stated, 10, 4)) == [7, 8, 9]
+
+
 def test_stated_positions_brute_force():
     # Brute force: write positions 0..end-1 into slot p mod cap, remember the last writer.
     for cap in (1, 3, 4, 7):

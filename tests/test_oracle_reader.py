@@ -78,6 +78,11 @@ def test_softmax_weights_by_construction():
     out = ORD.reader(z, np.stack([m1, m2]), 2, R, 0, H) - z
     assert np.allclose(out[:DH], 0.75 * m1[:DH] + 0.25 * m2[:DH], atol=1e-12)
     assert np.allclose(out[DH:], 0.5 * (m1[DH:] + m2[DH:]), atol=1e-12)
+    # values projected by 2 I, keys still by I: the weights stay 3/4, 1/4 and the output
+    # doubles (keys taken from the value projection would square the odds to 9 : 1)
+    R[p + "v_proj.weight"] = 2.0 * np.eye(D)
+    out2 = ORD.reader(z, np.stack([m1, m2]), 2, R, 0, H) - z
+    assert np.allclose(out2[:DH], 2.0 * (0.75 * m1[:DH] + 0.25 * m2[:DH]), atol=1e-12)
 
 
 def test_row_order_invariance_and_prefix_visibility():

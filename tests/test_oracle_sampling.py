@@ -40,6 +40,16 @@ def test_two_candidates_boundary_closed_form():
     assert sample_top_k(l, 1.0, 3, (1 + math.exp(-1)) / Z + 1e-9) == 2
 
 
+def test_draw_exactly_on_a_boundary_takes_the_next_candidate():
+    """Two equal top logits have weights 1 and 1 (running sums 1, 2); u = 0.5 puts the
+    threshold u * 2 = 1 exactly on the first running sum. The draw is the first candidate
+    whose running sum exceeds the threshold strictly: index 1 (u = 0.5 - 2^-40: index 0)."""
+    l = np.array([0.0, 0.0, -50.0], np.float32)
+    assert sample_top_k(l, 1.0, 2, 0.5) == 1
+    assert sample_top_k(l, 1.0, 2, 0.5 - 2.0 ** -40) == 0
+    assert sample_top_k(l, 1.0, 3, 0.0) == 0
+
+
 def test_order_and_ties_at_the_cut():
     """Equal logits are ordered by lower index, also across the top-k cut."""
     l = np.array([0, 5, 3, 5, 3, 3], np.float32)

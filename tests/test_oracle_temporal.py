@@ -233,6 +233,28 @@ def test_text_head_orientation():
     assert np.allclose(logits, [h[5], -2 * h[0], 0.5 * h[7]], atol=1e-15)
 
 
+def test_zero_blocks_leave_the_final_norm_of_the_embedding():
+    """With every block matrix zero each block is the identity (q = k = v = 0, so the
+    attention output is 0; SiLU(0) * 0 = 0), and h is the final RMSNorm of the embedding
+    sum on both code paths: a text row holding 3 and 4 in a 256-wide model has
+    mean(x^2) = 25 / 256, so h = (3, 4) * 16 / 5 = (9.6, 12.8) with unit scales."""
+    cfg = synth.TINY_TEMPORAL
+    W = synth.temporal_weights(cfg, 0, "fp32")
+    for k in list(W):
+        if k.startswith("transformer.layers.") and not k.endswith("alpha"):
+            W[k] = np.zeros_like(W[k])
+        if k == "text_emb.weight" or k.startswith("emb."):
+            W[k] = np.zeros_like(W[k])
+    W["text_emb.weight"][5, 0:2] = [3.0, 4.0]
+    W["out_norm.alpha"] = np.ones(cfg["d_model"], np.float32)
+    ids = np.full((2, 17), -1)
+    ids[:, 0] = 5
+    want = np.zeros(cfg["d_model"])
+    want[0:2] = [9.6, 12.8]
+    for h in (O.forward_full(ids, W, cfg), O.decode_incremental(ids, W, cfg)):
+        assert np.allclose(h, want[None, :], rtol=1e-6, atol=1e-12)
+
+
 # --------------------------------------------------------------------------- whole forward
 
 def _tiny():
