@@ -289,6 +289,33 @@ def bench_prefill(model, cfg, T, steps, warmup):
                         "K/V written to ring slots 0..T-1" % T}
 
 
+def bench_vendor_gemm(cfg, T, steps=10):
+    """For comparison only (not the product path): the vendor library's plain float16
+    products (torch.matmul, no fused epilogues) on the prefill's four GEMM shapes at M = T,
+    random operands; mean us per product over `steps` back-to-back calls."""
+    import torch
+    D, F = cfg["d_model"], cfg["d_ff"]
+    out = {}
+    for name, N, K in (("QKV", 3 * D, D), ("W_O", D, D), ("W_in", 2 * F, D), ("W_out", D, F)):
+        A = torch.randn(T, K, device="cuda", dtype=torch.float16)
+        B = torch.randn(N, K, device="cuda", dtype=torch.float16)
+        for _ in range(3):
+            C = A @ B.t()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(steps):
+            C = A @ B.t()
+        e.record()
+        torch.cuda.synchronize()
+        us = s.elapsed_time(e) * 1000.0 / steps
+        out[name] = {"us": round(us, 1), "M": T, "N": N, "K": K, "TFLOPs": round(2.0 * T * N * K / us / 1e6, 1)}
+        del A, B, C
+    out["note"] = ("vendor library (torch.matmul / hipBLASLt) plain float16 products on the same shapes, "
+                   "for comparison; the library's own products carry fused epilogues")
+    return out
+
+
 def bench_chunk(model, kv, cfg, T, steps, warmup):
     """Prefill chunks of T frames into the live, full ring (prompt replay at position > 0):
     each chunk's queries see the 3000-key window of history plus the chunk."""
@@ -589,6 +616,8 @@ def main():
     ap.add_argument("--chunk-T", type=int, default=256, help="0: skip the prefill-chunk line")
     ap.add_argument("--batches", default="4,16,32", help="batched-decode sizes ('' to skip)")
     ap.add_argument("--reader-slots", default="1024,8192", help="visible memory rows for the reader line ('' to skip)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="also time the vendor library's plain products on the prefill GEMM shapes (comparison)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the run, copy 1 GiB device-to-device 3 times (counter calibration)")
     args = ap.parse_args()
@@ -718,6 +747,8 @@ def main():
     if args.prefill_T > 0:
         kv.close()
         out["prefill"] = bench_prefill(model, cfg, args.prefill_T, args.prefill_steps, 1)
+    if args.vendor_gemm and args.prefill_T > 0:
+        out["vendor_gemm"] = bench_vendor_gemm(cfg, args.prefill_T)
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
