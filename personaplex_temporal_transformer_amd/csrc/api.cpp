@@ -2,6 +2,7 @@
 // KV-ring ownership, and the launch order of one decode step / prefill / depth frame.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -554,6 +555,9 @@ hipError_t pp_model::enqueue_layers_batched(pp_kv* kv, hipStream_t s, long long 
   const int D = c.d_model, F = c.d_ff, H = c.n_heads, dh = c.d_head, C = c.context, B = kv->B;
   const size_t per_kv = (size_t)B * H * C * dh * 2;
   const long long bstride = (long long)H * C * dh;
+  // attention splits: about one block per CU over the B x H heads (one split once the
+  // sessions fill the grid, whose blocks then write the head outputs themselves)
+  const int Sb = std::max(1, std::min(S_auto, (n_cu + H * B - 1) / (H * B)));
   hipError_t e = hipSuccess;
   for (int l = 0; l < c.n_layers && e == hipSuccess; ++l) {
     char* kbase = static_cast<char*>(kv->ring) + (size_t)(2 * l) * per_kv;
@@ -574,7 +578,7 @@ hipError_t pp_model::enqueue_layers_batched(pp_kv* kv, hipStream_t s, long long 
     g.n_cu = n_cu;
     if ((e = launch_sgemm(SEPI_QKV, g, s)) != hipSuccess) break;
     AttnDecodeArgs at{};
-    at.q = bq; at.k = kbase; at.v = vbase; at.state = state; at.pos = pos_arg; at.C = C; at.H = H; at.S = S_auto;
+    at.q = bq; at.k = kbase; at.v = vbase; at.state = state; at.pos = pos_arg; at.C = C; at.H = H; at.S = Sb;
     at.scale = 1.0f / std::sqrt((float)dh); at.part_o = bpart_o; at.part_ml = bpart_ml; at.combine = 1;
     at.batch = B; at.kv_bstride = bstride; at.out16 = bo16; at.o16_exp = fe.v;
     if ((e = launch_attn_decode(at, true, dh, s)) != hipSuccess) break;

@@ -8,6 +8,7 @@
 #pragma once
 
 #include "device.h"
+#include "frag_layout.h"
 #include "internal.h"
 
 namespace pp {
@@ -19,9 +20,12 @@ namespace pp {
 // memory traffic); the next round is always issued before the current one is consumed.
 // Each group keeps a running max m, sum l and output o (its lanes' EPC dimensions); the
 // groups are merged through LDS at the end, all threads taking part (PARTS partial
-// merges per output dimension, then their sum).
+// merges per output dimension, then their sum). With one split and a float16 output
+// (a batched step whose sessions fill the grid) the block's merge is the head's output for
+// session sess, written in the skinny products' fragment order; otherwise the block
+// writes its partial.
 template <typename KT, int DH, int NB, int NT>
-__device__ __forceinline__ void attn_body(const AttnDecodeArgs& a, int s, int h) {
+__device__ __forceinline__ void attn_body(const AttnDecodeArgs& a, int s, int h, int sess) {
   constexpr int EPC = Elem<KT>::kPerChunk;  // elements per 16-byte chunk
   constexpr int LPK = DH / EPC;             // lanes per key row
   constexpr int KPP = NT / LPK;             // key groups per block
@@ -132,6 +136,7 @@ __device__ __forceinline__ void attn_body(const AttnDecodeArgs& a, int s, int h)
   po[part][d] = o;
   if (d == 0) pl[part] = L;
   __syncthreads();
+  const bool direct = a.S == 1 && a.out16;
   if (tid < DH) {
     o = 0.f;
     L = 0.f;
@@ -140,10 +145,14 @@ __device__ __forceinline__ void attn_body(const AttnDecodeArgs& a, int s, int h)
       o += po[i][tid];
       L += pl[i];
     }
-    a.part_o[((size_t)h * a.S + s) * DH + tid] = o;
-    if (tid == 0) {
-      a.part_ml[((size_t)h * a.S + s) * 2] = M;
-      a.part_ml[((size_t)h * a.S + s) * 2 + 1] = L;
+    if (direct) {   // L > 0: the key at the query's own position is visible
+      a.out16[frag_act_index(sess, h * DH + tid, a.H * DH)] = f32_to_f16_sat(o / L * ldexpf(1.0f, -a.o16_exp));
+    } else {
+      a.part_o[((size_t)h * a.S + s) * DH + tid] = o;
+      if (tid == 0) {
+        a.part_ml[((size_t)h * a.S + s) * 2] = M;
+        a.part_ml[((size_t)h * a.S + s) * 2 + 1] = L;
+      }
     }
   }
 }

@@ -14,7 +14,8 @@
 // those units: softmax weights 2^(s - m) equal e^(s' - m') for the natural-unit scores.
 // The S partials of a head are merged in split order -- a fixed order, so results are
 // bit-reproducible -- in the W_O GEMV's prologue, or by a small combine kernel for more
-// than 8 splits.
+// than 8 splits and for batched steps. A batched step with one split per head writes its
+// float16 output from the attention blocks themselves.
 #include "attn_body.h"
 #include "frag_layout.h"
 
@@ -31,7 +32,7 @@ __global__ __launch_bounds__(NT) void k_attn_decode(AttnDecodeArgs a) {
     a.part_o += b * a.H * a.S * DH;
     a.part_ml += b * a.H * a.S * 2;
   }
-  attn_body<KT, DH, NB, NT>(a, blockIdx.x, blockIdx.y);
+  attn_body<KT, DH, NB, NT>(a, blockIdx.x, blockIdx.y, (int)blockIdx.z);
 }
 
 // Merge the S partials (o_s, m_s, l_s) of head h in split order:
@@ -72,7 +73,7 @@ hipError_t launch_attn_decode(const AttnDecodeArgs& a, bool bf16, int dh, hipStr
   else if (!bf16 && dh == 64) hipLaunchKernelGGL((k_attn_decode<float, 64, 6, 512>), grid, dim3(512), 0, s, a);
   else return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !a.combine) return e;
+  if (e != hipSuccess || !a.combine || (a.S == 1 && a.out16)) return e;   // one split: written directly
   if (dh == 128) hipLaunchKernelGGL((k_attn_combine<128>), dim3(a.H, nb), dim3(kBlock), 0, s, a);
   else hipLaunchKernelGGL((k_attn_combine<64>), dim3(a.H, nb), dim3(kBlock), 0, s, a);
   return hipGetLastError();
