@@ -1157,49 +1157,49 @@ __global__ __launch_bounds__(kBlock) void k_gather_rows(GatherArgs a, const void
   *reinterpret_cast<u32x4*>(static_cast<T*>(dst) + ((size_t)h * a.x_pitch + j) * a.dh + c * EPC) = v;
 }
 
-// bf16 path, K rows widened to float16 (the prefill attention's key operand): one thread
-// per 8 values of a row. bfloat16 -> float16 is exact inside float16's normal range.
-__global__ __launch_bounds__(kBlock) void k_gather_k16(GatherArgs a) {
-  const int cpr = a.dh / 8;
-  const long long n = (long long)a.H * a.jhi * cpr;
-  const long long i = (long long)blockIdx.x * kBlock + threadIdx.x;
-  if (i >= n) return;
-  const int c = (int)(i % cpr);
-  const long long hj = i / cpr;
-  const int j = (int)(hj % a.jhi), h = (int)(hj / a.jhi);
-  u32x4 v = u32x4{0u, 0u, 0u, 0u};
-  if (j >= a.jlo) {
-    const long long pos = a.q0 + j;   // >= 0 for j >= jlo
-    v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.kring) + ((size_t)h * a.C + pos % a.C) * a.dh + c * 8);
-  }
-  uint32_t w[4];
-  const float ks = ldexpf(1.0f, -a.k16_exp);
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    w[e] = (uint32_t)f32_to_f16_sat(bf16_lo(v[e]) * ks) | ((uint32_t)f32_to_f16_sat(bf16_hi(v[e]) * ks) << 16);
-  *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.kx) + ((size_t)h * a.x_pitch + j) * a.dh + c * 8) =
-      u32x4{w[0], w[1], w[2], w[3]};
-}
-
-// bf16 path, V transposed to float16 through LDS: one workgroup per (64 keys, head). The
-// 64 x d_head tile is read as whole key rows (16-byte loads, 16 lanes per 256-byte row) and
-// written as whole 128-byte runs of a transposed row (8 columns per thread); column c of
-// the tile holds key vt_perm(c). Keys below jlo are zero; so are the columns past jhi up to
-// the tile end, which the chunk's own V (written later by the QKV epilogue) covers.
-__global__ __launch_bounds__(256) void k_gather_vt(GatherArgs a) {
+// bf16 path, one workgroup per (64 keys, head): the K rows widened to float16 (the prefill
+// attention's key operand; bfloat16 -> float16 is exact inside float16's normal range) and
+// V transposed to float16 through LDS. Every K and V load of a thread is issued before the
+// first conversion. The 64 x d_head V tile is read as whole key rows (16-byte loads, 16
+// lanes per 256-byte row) and written as whole 128-byte runs of a transposed row (8
+// columns per thread); column c of the tile holds key vt_perm(c). Keys below jlo are zero;
+// so are the V columns past jhi up to the tile end, which the chunk's own V (written later
+// by the QKV epilogue) covers. K rows are written below jhi only.
+__global__ __launch_bounds__(256) void k_gather_kv16(GatherArgs a) {
   constexpr int P = 66;                      // LDS row pitch in halves (bank spread)
+  constexpr int NQ = 64 * (128 / 8) / 256;   // 16-byte chunks per thread and tile, d_head <= 128
   __shared__ uint16_t tile[128 * P];         // [d][key], d_head <= 128
   const int j0 = blockIdx.x * 64, h = blockIdx.y, dh = a.dh, cpr = dh / 8;
+  const uint16_t* K = static_cast<const uint16_t*>(a.kring) + (size_t)h * a.C * dh;
   const uint16_t* V = static_cast<const uint16_t*>(a.vring) + (size_t)h * a.C * dh;
-  for (int q = threadIdx.x; q < 64 * cpr; q += 256) {
-    const int jr = q / cpr, c = q - jr * cpr, j = j0 + jr;
-    u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (j >= a.jlo && j < a.jhi) v = *reinterpret_cast<const u32x4*>(V + (size_t)((a.q0 + j) % a.C) * dh + c * 8);
-    const float vs = ldexpf(1.0f, -a.vt_exp);
+  u32x4 kv[NQ], vv[NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int q = threadIdx.x + 256 * i, jr = q / cpr, c = q - jr * cpr, j = j0 + jr;
+    kv[i] = vv[i] = u32x4{0u, 0u, 0u, 0u};
+    if (q < 64 * cpr && j >= a.jlo && j < a.jhi) {
+      const size_t off = (size_t)((a.q0 + j) % a.C) * dh + c * 8;
+      kv[i] = *reinterpret_cast<const u32x4*>(K + off);
+      vv[i] = *reinterpret_cast<const u32x4*>(V + off);
+    }
+  }
+  const float ks = ldexpf(1.0f, -a.k16_exp), vs = ldexpf(1.0f, -a.vt_exp);
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int q = threadIdx.x + 256 * i, jr = q / cpr, c = q - jr * cpr, j = j0 + jr;
+    if (q >= 64 * cpr) continue;
+    if (j < a.jhi) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = (uint32_t)f32_to_f16_sat(bf16_lo(kv[i][e]) * ks) | ((uint32_t)f32_to_f16_sat(bf16_hi(kv[i][e]) * ks) << 16);
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.kx) + ((size_t)h * a.x_pitch + j) * dh + c * 8) =
+          u32x4{w[0], w[1], w[2], w[3]};
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      tile[(c * 8 + 2 * e) * P + jr] = f32_to_f16_sat(bf16_lo(v[e]) * vs);
-      tile[(c * 8 + 2 * e + 1) * P + jr] = f32_to_f16_sat(bf16_hi(v[e]) * vs);
+      tile[(c * 8 + 2 * e) * P + jr] = f32_to_f16_sat(bf16_lo(vv[i][e]) * vs);
+      tile[(c * 8 + 2 * e + 1) * P + jr] = f32_to_f16_sat(bf16_hi(vv[i][e]) * vs);
     }
   }
   __syncthreads();
@@ -1224,8 +1224,7 @@ hipError_t launch_gather_history(const GatherArgs& a, bool bf16, hipStream_t s) 
   if (bf16) {
     // V^T tiles of 64 columns (the last one up to a multiple of 64) inside the V^T rows
     if (!a.vt || a.dh > 128 || (a.jhi + 63) / 64 * 64 > a.vt_pitch) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_gather_k16, gr, dim3(kBlock), 0, s, a);
-    hipLaunchKernelGGL(k_gather_vt, dim3((unsigned)((a.jhi + 63) / 64), (unsigned)a.H), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_gather_kv16, dim3((unsigned)((a.jhi + 63) / 64), (unsigned)a.H), dim3(256), 0, s, a);
   } else {
     if (!a.vx) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_gather_rows<float>, gr, dim3(kBlock), 0, s, a, a.kring, a.kx);
