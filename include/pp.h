@@ -388,7 +388,8 @@ pp_status pp_temporal_set_graph(pp_model* m, int32_t enable);
  * product for up to 8 splits, else by a separate merge kernel). 0 = automatic (about one
  * workgroup per compute unit over all heads: 8 for 32 heads on 256 CUs); 1..64 forces a
  * value. The result does not depend on it beyond float32 rounding. Batched decode always
- * uses the automatic value. */
+ * chooses its own: about one workgroup per compute unit over the B x H heads
+ * (ceil(CUs / (H B)), at most the automatic value, one from B = 8 on at 32 heads). */
 pp_status pp_temporal_set_attn_splits(pp_model* m, int32_t splits);
 
 /* Kernel timing for roofline reports: when layer >= 0, every decode step brackets the
