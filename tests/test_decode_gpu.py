@@ -36,13 +36,14 @@ def _decode_all(model, kv, ids, with_logits=True):
 # ----------------------------------------------------------------------------- fp32, tiny
 
 @pytest.mark.parametrize("context,d_ff,splits", [(3000, 704, None), (4, 704, None), (3000, 2312, None),
-                                                 (3000, 704, 8), (4, 704, 3)])
+                                                 (3000, 704, 8), (4, 704, 3), (3000, 704, 1)])
 @pytest.mark.parametrize("graph", [True, False])
 def test_tiny_fp32_decode_matches_oracle(context, d_ff, splits, graph):
     """d_ff 2312 makes the W_out rows (2312 floats) longer than one 512-chunk pass, so the
     multi-pass GEMV path (x from LDS, ragged last pass) is covered at small scale; with
     <= 8 attention splits the split merge runs inside the W_O GEMV instead of a separate
-    combine kernel (3 splits at context 4 also leaves splits empty)."""
+    combine kernel (3 splits at context 4 also leaves splits empty; 1 split makes the
+    merge a pass-through)."""
     cfg = synth.with_(synth.TINY_TEMPORAL, context=context, d_ff=d_ff)
     W = synth.temporal_weights(cfg, 0, "fp32")
     ids = synth.stream_ids(cfg, 16, 1)
