@@ -360,10 +360,12 @@ static hipError_t launch_epi(const SgemmArgs& a, hipStream_t s) {
   }
   // two column tiles per workgroup (each activation fragment feeds two products) when
   // there are enough tiles to keep every CU busy
-  const bool two = tiles % 2 == 0 && tiles >= 512 && nbt == 2;
+  const bool two = tiles % 2 == 0 && tiles >= 512;
   if (two) {
     const dim3 grid(tiles / 2);
-    hipLaunchKernelGGL((k_sgemm<EPI, 2, 2, false, false>), grid, block, 0, s, a);
+    if (nbt == 2) hipLaunchKernelGGL((k_sgemm<EPI, 2, 2, false, false>), grid, block, 0, s, a);
+    else if (nbt == 3) hipLaunchKernelGGL((k_sgemm<EPI, 3, 2, false, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_sgemm<EPI, 4, 2, false, false>), grid, block, 0, s, a);
     return hipGetLastError();
   }
   const dim3 grid(tiles);

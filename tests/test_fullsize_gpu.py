@@ -244,13 +244,15 @@ def test_full_prefill_chunk_after_full_ring():
     assert np.array_equal(ring[:, :, :, :, n:], frames[:, :, :, :, n:])
 
 
-@pytest.mark.parametrize("B,sessions,oracle_session", [(4, (0, 1, 2, 3), 3), (64, (0, 15, 16, 33, 48, 63), 33)])
+@pytest.mark.parametrize("B,sessions,oracle_session", [(4, (0, 1, 2, 3), 3), (40, (0, 16, 31, 32, 39), 39),
+                                                       (64, (0, 15, 16, 33, 48, 63), 33)])
 def test_full_batched_decode_ctx3000(B, sessions, oracle_session):
     """B sessions decoded together (every weight byte shared, float16 activations into the
     matrix cores), rings full at 3000 random frames, 2 frames at positions 3000 and 3001
     (keys wrap). One session against the oracle's decode of its own ring (2e-2); the
-    sampled sessions (tile boundaries at B = 64, the largest batch: 4 session tiles, about
-    230 GB of device memory with its 100 GB of rings) also against the same session decoded
+    sampled sessions (tile boundaries; B = 40: 3 session tiles, the last one partial; B = 64,
+    the largest batch: 4 session tiles, about 230 GB of device memory with its 100 GB of
+    rings) also against the same session decoded
     alone on the GPU, which rounds differently (float32 activations), to 2 x 2e-2."""
     import gc
     import torch
