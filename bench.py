@@ -234,12 +234,25 @@ def bench_one_block(W, cfg, steps, warmup):
         evs[i][1].record()
     torch.cuda.synchronize()
     us = sorted(a.elapsed_time(b) * 1000.0 for a, b in evs)
+    # the same steps back to back between one event pair (as the decode frames are timed):
+    # the per-step pairs above also carry each pair's own cost
+    kv1.load(buf, n0)
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s0.record()
+    for i in range(steps):
+        m1.decode_step(kv1, ids[warmup + i], h)
+    s1.record()
+    torch.cuda.synchronize()
+    mean_b2b = s0.elapsed_time(s1) * 1000.0 / steps
     D, F, Hh, dh = cfg["d_model"], cfg["d_ff"], cfg["n_heads"], cfg["d_head"]
     nb = (3 * D * D + D * D + 2 * F * D + D * F) * 2 + (n0 + 1) * Hh * dh * 2 * 2 + Hh * dh * 2 * 2
     med = float(np.median(us))
     kv1.close()
     m1.close()
     return {"us_per_step_median": round(med, 2), "us_per_step_min": round(us[0], 2), "steps": steps,
+            "us_per_step_back_to_back": round(mean_b2b, 2),
+            "hbm_frac_back_to_back": round(nb / (mean_b2b * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             "step_bytes_at_201_keys": nb, "achieved_GBps": round(nb / (med * 1e-6) / 1e9, 1),
             "hbm_frac": round(nb / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             "workload": "one full-width temporal block (d_model 4096, 32 x 128 heads, d_ff 11264), bf16, "
