@@ -327,7 +327,12 @@ pp_status pp_model::check_ids(const int32_t* ids, size_t frames) const {
 }
 
 void pp_model::embed_tables(EmbedArgs& a) const {
-  a.tables[0] = text_emb;
+  // slots past the model's streams read the text table with ID -1 (dropped), so the kernel
+  // loads every slot with no branch
+  for (int k = 0; k < kMaxStreams; ++k) {
+    a.tables[k] = text_emb;
+    a.ids_arg[k] = -1;
+  }
   for (int i = 0; i < cfg.n_audio; ++i) a.tables[i + 1] = audio_emb[i];
   a.n_streams = cfg.n_audio + 1;
   a.D = cfg.d_model;

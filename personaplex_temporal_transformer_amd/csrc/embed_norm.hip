@@ -17,12 +17,13 @@ namespace pp {
 // float32 features) of one frame; blocks of 64 threads, so a decode frame spreads over
 // D / 512 (bfloat16) workgroups. It loads the chunk of every stream's row first (all in
 // flight together), then adds them in stream order 0..n-1 in float32 -- a fixed order,
-// so the result is reproducible. Row 0 stands in for ID -1 and contributes +0.0, which
-// leaves the sum's bits unchanged (the running sum starts at +0.0 and cannot become -0.0).
+// so the result is reproducible. An ID of -1 leaves the running sum untouched.
 constexpr int kEmbedThreads = 64;
 
-template <typename WT>
-__global__ __launch_bounds__(kEmbedThreads) void k_embed_sum(EmbedArgs a) {
+// NSLOT table slots are read (17 for the model's text + 16 audio streams, else kMaxStreams).
+template <typename WT, bool DEVIDS, int NSLOT>
+__global__ __launch_bounds__(kEmbedThreads) __attribute__((amdgpu_waves_per_eu(1, 4)))
+void k_embed_sum(EmbedArgs a) {
   constexpr int EPC = Elem<WT>::kPerChunk;
   const int row = blockIdx.y;
   const int d = (blockIdx.x * kEmbedThreads + threadIdx.x) * EPC;
@@ -31,27 +32,31 @@ __global__ __launch_bounds__(kEmbedThreads) void k_embed_sum(EmbedArgs a) {
     for (int i = threadIdx.x; a.rope && i < a.dh; i += kEmbedThreads) a.rope[i] = a.rope_cs[i];
   }
   if (d >= a.D) return;
-  u32x4 raw[kMaxStreams];
-  float keep[kMaxStreams];
+  // Every row load is issued before the first is used, with no branch around any of them
+  // (a load under a branch makes the compiler wait for all earlier loads, which turned the
+  // 17 row reads into 17 memory round trips). The host fills the slots past n_streams with
+  // the text table and ID -1; every slot past n_streams, and every ID -1, reads row 0 of its
+  // table and is dropped by a select, so a dropped term adds nothing (not even 0 * inf).
+  const int n = a.n_streams;
+  u32x4 raw[NSLOT];
+  bool keep[NSLOT];
 #pragma unroll
-  for (int k = 0; k < kMaxStreams; ++k) {
-    if (k < a.n_streams) {
-      const int id = a.ids_dev ? a.ids_dev[(size_t)row * a.n_streams + k] : a.ids_arg[k];
-      raw[k] = load16(static_cast<const WT*>(a.tables[k]) + (size_t)(id < 0 ? 0 : id) * a.D + d);
-      keep[k] = id < 0 ? 0.f : 1.f;
-    }
+  for (int k = 0; k < NSLOT; ++k) {
+    const int id = DEVIDS ? a.ids_dev[(size_t)row * n + (k < n ? k : n - 1)] : a.ids_arg[k];
+    raw[k] = load16(static_cast<const WT*>(a.tables[k]) + (size_t)((k < n && id > 0) ? id : 0) * a.D + d);
+    keep[k] = (!DEVIDS || k < n) && id >= 0;
   }
+  // keeps the scheduler from pulling each sum step up behind its own load
+  __builtin_amdgcn_sched_barrier(0);
   float acc[EPC];
 #pragma unroll
   for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
 #pragma unroll
-  for (int k = 0; k < kMaxStreams; ++k) {
-    if (k < a.n_streams) {
-      float v[EPC];
-      Elem<WT>::widen(raw[k], v);
+  for (int k = 0; k < NSLOT; ++k) {
+    float v[EPC];
+    Elem<WT>::widen(raw[k], v);
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) acc[e] += keep[k] * v[e];
-    }
+    for (int e = 0; e < EPC; ++e) acc[e] = keep[k] ? acc[e] + v[e] : acc[e];
   }
   float* o = a.out + (size_t)row * a.D + d;
 #pragma unroll
@@ -62,10 +67,14 @@ hipError_t launch_embed(const EmbedArgs& a, bool bf16, hipStream_t s) {
   const int epc = bf16 ? 8 : 4;
   if (a.D % epc) return hipErrorInvalidValue;
   dim3 grid((a.D / epc + kEmbedThreads - 1) / kEmbedThreads, a.rows);
-  if (bf16)
-    hipLaunchKernelGGL(k_embed_sum<bf16_t>, grid, dim3(kEmbedThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_embed_sum<float>, grid, dim3(kEmbedThreads), 0, s, a);
+  if (a.n_streams < 1 || a.n_streams > kMaxStreams) return hipErrorInvalidValue;
+  const auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(kEmbedThreads), 0, s, a); };
+  constexpr int kModelStreams = 17;
+  const bool few = a.n_streams <= kModelStreams;
+  if (bf16 && a.ids_dev) few ? go(k_embed_sum<bf16_t, true, kModelStreams>) : go(k_embed_sum<bf16_t, true, kMaxStreams>);
+  else if (bf16) few ? go(k_embed_sum<bf16_t, false, kModelStreams>) : go(k_embed_sum<bf16_t, false, kMaxStreams>);
+  else if (a.ids_dev) few ? go(k_embed_sum<float, true, kModelStreams>) : go(k_embed_sum<float, true, kMaxStreams>);
+  else few ? go(k_embed_sum<float, false, kModelStreams>) : go(k_embed_sum<float, false, kMaxStreams>);
   return hipGetLastError();
 }
 
