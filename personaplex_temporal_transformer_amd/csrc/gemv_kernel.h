@@ -190,6 +190,84 @@ __device__ void depth_attention(const GemvArgs& a, float* x, XPos xpos) {
   }
 }
 
+// The depth attention's usual shape (at most two heads per wave, a window of at most 8
+// keys, d_head <= 64) in two halves: depth_attn_request issues every q, K and V read of the
+// wave's heads with no branch around any of them (rows past the window and lanes past
+// d_head read a valid clamped address, and their values are masked), so a caller can
+// request its weights behind them and wait for the attention's rows alone (loads complete
+// in order); depth_attn_finish then does what depth_attention does for one batch of keys,
+// with the same arithmetic in the same order per head.
+constexpr int kDepthFastKeys = 8;
+struct DepthRows {
+  float q[2], k[2][kDepthFastKeys], v[2][kDepthFastKeys];
+};
+
+__device__ __forceinline__ bool depth_attn_fast(const GemvArgs& a, int nw) {
+  return a.aH <= 2 * nw && a.awin <= kDepthFastKeys && a.adh <= 64;
+}
+
+__device__ __forceinline__ void depth_attn_request(const GemvArgs& a, DepthRows& r) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int k0 = a.aq_pos - a.awin + 1 > 0 ? a.aq_pos - a.awin + 1 : 0;
+  const int nk = a.aq_pos - k0 + 1;
+  const int dh = a.adh;
+  const int lc = lane < dh ? lane : 0;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int h = w + u * nw;
+    const int hc = h < a.aH ? h : 0;
+    r.q[u] = a.aq[hc * dh + lc];
+    const size_t base = ((size_t)hc * a.acap + k0) * dh + lc;
+#pragma unroll
+    for (int b = 0; b < kDepthFastKeys; ++b) {
+      const size_t j = (size_t)(b < nk ? b : nk - 1) * dh;
+      r.k[u][b] = a.ak[base + j];
+      r.v[u][b] = a.av[base + j];
+    }
+  }
+}
+
+template <class XPos>
+__device__ __forceinline__ void depth_attn_finish(const GemvArgs& a, const DepthRows& r, float* x, XPos xpos) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int k0 = a.aq_pos - a.awin + 1 > 0 ? a.aq_pos - a.awin + 1 : 0;
+  const int nk = a.aq_pos - k0 + 1;
+  const int dh = a.adh;
+  const bool on = lane < dh;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int h = w + u * nw;
+    if (h >= a.aH) continue;
+    const float q = on ? r.q[u] : 0.f;
+    float sc[kDepthFastKeys];
+    float mb = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < kDepthFastKeys; ++b) {
+      // the product and the scaled score are each rounded, as in depth_attention (left
+      // contractible, the product would fuse into the first cross-lane addition and the
+      // scaling into the softmax's subtraction)
+      float t;
+      {
+#pragma clang fp contract(off)
+        const float prod = q * r.k[u][b];
+        t = wave_sum(prod) * a.ascale;
+      }
+      sc[b] = b < nk ? t : -INFINITY;
+      mb = fmaxf(mb, sc[b]);
+    }
+    float l = 0.f, o = 0.f;
+#pragma unroll
+    for (int b = 0; b < kDepthFastKeys; ++b) {
+      if (b < nk) {
+        const float p = expf(sc[b] - mb);
+        l += p;
+        o += p * r.v[u][b];
+      }
+    }
+    if (on) x[xpos(h * dh + lane)] = o * (1.0f / l);
+  }
+}
+
 constexpr int kGemvWaves = 8;                 // waves per GEMV workgroup
 
 // Rows are processed in groups of RB rows; a lane streams 16-byte chunks c = p*64*U +
@@ -382,10 +460,17 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a, float* xs, int blk,
     if (ga >= gb1) return;
     if (gb < gb1) issue(wb, rb, gb, pb);
   } else {
-    // the first weights do not depend on the attention: request them first
+    // Usual shape: the attention's rows are requested first and the first two items'
+    // weights behind them, so the weights stream while the attention is computed.
+    // Otherwise the weights go first and the general loop follows.
+    const auto xpos = [&](int i) { return xq_index(i / EPC, (i % EPC) / 4) + (i % 4); };
+    const bool fast = depth_attn_fast(a, NW);
+    DepthRows dr;
+    if (fast) depth_attn_request(a, dr);
     if (ga < gb1) issue(wa, ra, ga, pa);
     if (gb < gb1) issue(wb, rb, gb, pb);
-    depth_attention(a, xs, [&](int i) { return xq_index(i / EPC, (i % EPC) / 4) + (i % 4); });
+    if (fast) depth_attn_finish(a, dr, xs, xpos);
+    else depth_attention(a, xs, xpos);
     __syncthreads();
     if (ga >= gb1) return;
   }
