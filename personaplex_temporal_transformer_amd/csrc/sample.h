@@ -107,12 +107,18 @@ __device__ __forceinline__ int block_sample_top_k(const float* __restrict__ lg, 
   const bool greedy = top_k <= 1 || !(temperature > 0.f);
   const int k = greedy ? 1 : min(top_k, n);
 
-  uint32_t key[PER];
+  // Every logit load is issued before the first is used: indices past n read the last
+  // logit (no branch around a load, which would make each wait for the one before) and
+  // take key 0, below every finite or infinite key.
+  float lv[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int i = j * NT + tid;
-    key[j] = i < n ? order_key(lg[i]) : 0u;   // 0 is below every finite or infinite key
+    lv[j] = lg[i < n ? i : n - 1];
   }
+  uint32_t key[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) key[j] = j * NT + tid < n ? order_key(lv[j]) : 0u;
   if (tid == 0) s.cnt = 0;
 
   // 2. T = the k-th largest key; each wave counts with ballots.
