@@ -359,7 +359,11 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a, float* xs, int blk,
       mv[sp] = ml[0];
       lv[sp] = ml[1];
     }
+    // partials, then the first weights, then the merge: waiting for the partials does not
+    // wait for the weights, and the weights are in flight during the merge
+    __builtin_amdgcn_sched_barrier(0);
     issue(wa, ra, g_first, 0);
+    __builtin_amdgcn_sched_barrier(0);
     float M = -INFINITY;
 #pragma unroll
     for (int sp = 0; sp < SM; ++sp) M = fmaxf(M, sp < a.pS ? mv[sp] : -INFINITY);
@@ -373,10 +377,11 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a, float* xs, int blk,
       o1 += w * ov[sp][1];
     }
     const float inv = 1.0f / L;
-    if (tid * 8 < K) {
-      *reinterpret_cast<f32x4*>(xs + xq_index(d0 / EPC, (d0 % EPC) / 4)) = o0 * inv;
-      *reinterpret_cast<f32x4*>(xs + xq_index((d0 + 4) / EPC, ((d0 + 4) % EPC) / 4)) = o1 * inv;
-    }
+    // Unconditional: a thread past K stores its clamped chunk's merge again (the same bits
+    // as the owner's). Under a bounds test the compiler would sink the partial loads into
+    // it, behind the weight loads.
+    *reinterpret_cast<f32x4*>(xs + xq_index(d0 / EPC, (d0 % EPC) / 4)) = o0 * inv;
+    *reinterpret_cast<f32x4*>(xs + xq_index((d0 + 4) / EPC, ((d0 + 4) % EPC) / 4)) = o1 * inv;
     lds_barrier();
     if (ga >= gb1) return;
     if (gb < gb1) issue(wb, rb, gb, pb);
