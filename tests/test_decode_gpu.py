@@ -182,6 +182,31 @@ def test_embed_sum_batch_times_frames_and_capacity():
     assert np.array_equal(x.cpu().numpy(), got)
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("n_audio,wdt", [(2, "bf16"), (2, "fp32"), (20, "bf16"), (31, "fp32")])
+def test_embed_sum_stream_counts(n_audio, wdt):
+    """The gather reads 17 table slots for up to 17 streams and 32 beyond, and drops the
+    slots past the stream count: with 3, 21 and 32 streams, bfloat16 and float32 tables,
+    IDs from the device and as kernel arguments, it is the fixed-order float32 sum."""
+    import torch
+    cfg = synth.with_(synth.TINY_TEMPORAL, n_audio=n_audio, n_layers=1)
+    W = synth.temporal_weights(cfg, 21, wdt, with_text_head=False)
+    model = pp.TemporalModel(cfg, to_device(W), wdt, max_prefill_T=8)
+    ids = synth.stream_ids(cfg, 8, 22)
+    ids[2] = -1
+    ids[4, 1:] = cfg["audio_vocab"] - 1
+    x = torch.empty((8, cfg["d_model"]), device="cuda")
+    model.embed_sum(ids, x)
+    x1 = torch.empty((cfg["d_model"],), device="cuda")
+    model.embed_sum(ids[5], x1)
+    torch.cuda.synchronize()
+    got = x.cpu().numpy()
+    for t in range(8):
+        assert np.array_equal(got[t], O.embed(ids[t], W, cfg, precision="f32")), t
+    assert np.all(got[2] == 0)
+    assert np.array_equal(x1.cpu().numpy(), got[5])
+
+
 # ----------------------------------------------------------------------------- one full block
 
 def _full_block_case(n_prefill, seed_w=2, seed_kv=3, seed_ids=4, n_layers=1):
