@@ -72,6 +72,28 @@ def test_windows_agree_before_they_bind():
     assert np.array_equal(l8[:8], l16[:8])
 
 
+def test_wide_fp32_general_paths():
+    """A depth stack outside the kernels' usual shapes: 18 heads (more than two per wave,
+    so the W_O product's attention prologue takes its general loop), d_model 1152 (more
+    than the selection kernel's 4 values per thread) and 2304 logits (more than its 8 per
+    thread). Forced codes give the oracle's logits; greedy codes are valid argmaxes of the
+    oracle's logits under the same choices."""
+    cfg = synth.with_(synth.TINY_DEPTH, n_layers=1, d_model=1152, n_heads=18, d_head=64, d_ff=256,
+                      n_steps=4, window=3, audio_vocab=2305, n_out=2304)
+    W = synth.depth_weights(cfg, 9, "fp32")
+    h = synth.hidden(cfg["d_temporal"], 10)
+    forced = synth.depth_codes(cfg, 11)
+    _, codes, logits = _run(cfg, W, "fp32", h, 123, forced)
+    _, want = DF.step_logits(h, 123, forced, W, cfg)
+    assert np.array_equal(codes, forced)
+    assert max_abs_err(logits, want) <= FP32_TOL
+    _, codes, logits = _run(cfg, W, "fp32", h, 123, None)
+    _, want = DF.step_logits(h, 123, codes, W, cfg)
+    assert max_abs_err(logits, want) <= FP32_TOL
+    for q in range(cfg["n_steps"]):
+        assert want[q][codes[q]] >= np.max(want[q]) - 2 * FP32_TOL, q
+
+
 def test_invalid_tokens_rejected():
     import torch
     cfg = synth.TINY_DEPTH
