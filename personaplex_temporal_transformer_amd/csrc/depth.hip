@@ -31,10 +31,11 @@ hipError_t launch_depth_setup(const DepthSetupArgs& a, hipStream_t s) {
 }
 
 // One block. For q > 0 it fixes the code of position q-1; for q < n_steps it forms z.
-// The reads that do not depend on the selection -- the logits row (when it fits SEL_PER
-// values per thread) and this position's projection row (up to Z_PER values per thread) --
-// are issued together first, unconditionally (clamped indices), so the greedy selection
-// and z cost two memory round trips: logits, then the chosen embedding row.
+// The reads that do not depend on the selection -- the logits row (kSelPer values per
+// thread cover up to 2048 logits) and this position's projection row (kZPer values per
+// thread, d_model up to 1024) -- are issued together first, unconditionally (clamped
+// indices), so the greedy selection and z cost two memory round trips: logits, then the
+// chosen embedding row. Longer rows take loops.
 constexpr int kSelPer = 8, kZPer = 4;
 
 // (value, index) of the larger value, the lower index on equal values
